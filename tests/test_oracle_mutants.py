@@ -1,0 +1,44 @@
+"""The pins catch plausible mistakes.
+
+Each case copies the oracle's C source, plants one mistake (on the CPU, in the
+copy), builds it, and runs the pin suite against that build in a child process:
+the suite must fail.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTANTS = {
+    "round_half_away": ("float r = rintf(t);", "float r = roundf(t);"),
+    "k3_wrong_short_slot": ("return (c % 11 == 10) ? 3 : 7;", "return (c % 11 == 0) ? 3 : 7;"),
+    "dropped_softmax_scale": ("e[t] = acc * scale;", "e[t] = acc;"),
+    "k_zero_wrong_channel": ("(double)L->k_zero[g * L->d + c];", "(double)L->k_zero[g * L->d];"),
+    "early_flush": ("L->N - L->Tq == L->R)", "L->N - L->Tq == L->R - 1)"),
+    "v_zero_from_scale": ("(double)L->v_zero[tt];", "(double)L->v_scale[tt];"),
+    "reversed_offset": ("float t = (x[(long)i * stride] - mn) / s;",
+                        "float t = (mx - x[(long)i * stride]) / s;"),
+    "pack_msb_first": ("*shift = bits * (c % per_word);",
+                       "*shift = 32 - bits * (1 + c % per_word);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(os.path.join(ROOT, "oracle", "kvq_oracle.c")).read()
+    assert src.count(old) == 1, "mutation site moved: " + old
+    (tmp_path / "kvq_oracle.c").write_text(src.replace(old, new))
+    shutil.copy(os.path.join(ROOT, "oracle", "kvq_oracle.h"), tmp_path / "kvq_oracle.h")
+    so = tmp_path / "mutant.so"
+    subprocess.check_call(["gcc", "-std=c99", "-O2", "-fno-fast-math", "-ffp-contract=off",
+                           "-fPIC", "-shared", str(tmp_path / "kvq_oracle.c"), "-o", str(so), "-lm"])
+    env = dict(os.environ, KVQ_ORACLE_SO=str(so))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, "pins did not catch mutant %s\n%s" % (name, r.stdout[-2000:])
