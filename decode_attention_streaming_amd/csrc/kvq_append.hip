@@ -1,0 +1,204 @@
+// kvq_append.hip -- streaming quantize-and-append kernels for gfx950.
+//
+// Key is quantized per channel over a group of G tokens, Value per token, each
+// with an fp32 scale s = (max - min) / qmax and zero z = min, codes
+// round-half-even((x - z) / s) clamped to [0, qmax] (KVTuner summary, A3 "KV
+// cache quantization basics"; KVmix notes, key design 2; KIVI notes, sections
+// 6.1-6.2).  Codes are packed into 32-bit words along head_dim, least
+// significant bits first; the 3-bit Key layout puts eleven channels in a word,
+// slot 10 at 2 bits (KVmix notes, key design 2).  Quantizing straight into the
+// packed history, with no intermediate buffer, follows KVmix key design 4.
+//
+// Bit-exactness with a serial CPU evaluation: min/max are exact in any order;
+// the subtraction and the IEEE fp32 division are correctly rounded (no fast
+// math, no contraction); rintf is round-half-even; zero scales and zero points
+// are stored as +0.
+#include "kvq_internal.h"
+
+#include <hip/hip_fp16.h>
+
+namespace kvq {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float widen16(uint16_t x, int bf16)
+{
+    if (bf16)
+        return __uint_as_float(static_cast<uint32_t>(x) << 16);
+    return __half2float(__ushort_as_half(x));
+}
+
+__device__ __forceinline__ int qmax_of(int bits, int c)
+{
+    if (bits == 3)
+        return (c % 11 == 10) ? 3 : 7;
+    return (1 << bits) - 1;
+}
+
+// Code of x for a group with minimum mn and scale s.
+__device__ __forceinline__ uint32_t code_of(float x, float mn, float s, int qmax)
+{
+#pragma clang fp contract(off)
+    if (s == 0.0f)
+        return 0u;
+    float r = rintf((x - mn) / s);
+    r = fminf(fmaxf(r, 0.0f), static_cast<float>(qmax));
+    return static_cast<uint32_t>(r);
+}
+
+__device__ __forceinline__ float wave_min(float v)
+{
+    for (int off = 32; off > 0; off >>= 1)
+        v = fminf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+    for (int off = 32; off > 0; off >>= 1)
+        v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+__device__ __forceinline__ const uint16_t *src_row(const FlushArgs &a, const uint16_t *ring,
+                                                   const uint16_t *fresh, int bh, int t)
+{
+    if (t < a.N0)
+        return ring + (static_cast<size_t>(bh) * a.L.R + (t % a.L.R)) * a.D;
+    return fresh + (static_cast<size_t>(bh) * a.n_new + (t - a.N0)) * a.D;
+}
+
+// One workgroup quantizes one group of one stream: K per channel, V per token.
+__global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a)
+{
+#pragma clang fp contract(off)
+    const int j = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+    const int D = a.D, G = a.L.G;
+    const int t0 = a.Tq0 + j * G;
+    const int gi = t0 / G;
+
+    __shared__ float red_mn[kThreads], red_mx[kThreads];
+    __shared__ float s_k[256], mn_k[256];
+
+    // ---- Key: min / max per channel over the G tokens ----
+    const int parts = kThreads / D;  // threads per channel (D divides 256)
+    const int c = tid % D, p = tid / D;
+    float mn = INFINITY, mx = -INFINITY;
+    for (int i = p; i < G; i += parts) {
+        float x = widen16(src_row(a, a.L.ring_k, a.k_new, bh, t0 + i)[c], a.kv_bf16);
+        mn = fminf(mn, x);
+        mx = fmaxf(mx, x);
+    }
+    red_mn[tid] = mn;
+    red_mx[tid] = mx;
+    __syncthreads();
+    if (p == 0) {
+        for (int q = 1; q < parts; ++q) {
+            mn = fminf(mn, red_mn[q * D + c]);
+            mx = fmaxf(mx, red_mx[q * D + c]);
+        }
+        float s = (mx - mn) / static_cast<float>(qmax_of(a.L.kb, c));
+        s_k[c] = s;
+        mn_k[c] = mn;
+        float *meta = a.L.k_meta + (static_cast<size_t>(bh) * (a.L.capq / G) + gi) * 2 * D;
+        meta[c] = (s == 0.0f) ? 0.0f : s;
+        meta[D + c] = (mn == 0.0f) ? 0.0f : mn;
+    }
+    __syncthreads();
+
+    // ---- Key: codes, one packed word per work item (token i, word w) ----
+    const int wk = a.L.wk;
+    for (int it = tid; it < G * wk; it += kThreads) {
+        const int i = it / wk, w = it % wk;
+        const uint16_t *row = src_row(a, a.L.ring_k, a.k_new, bh, t0 + i);
+        uint32_t word = 0;
+        if (a.L.kb == 3) {
+            for (int sl = 0; sl < 11; ++sl) {
+                const int cc = w * 11 + sl;
+                if (cc < D)
+                    word |= code_of(widen16(row[cc], a.kv_bf16), mn_k[cc], s_k[cc],
+                                    qmax_of(3, cc))
+                            << (3 * sl);
+            }
+        } else {
+            const int epw = 32 / a.L.kb;
+            for (int sl = 0; sl < epw; ++sl) {
+                const int cc = w * epw + sl;
+                word |= code_of(widen16(row[cc], a.kv_bf16), mn_k[cc], s_k[cc], (1 << a.L.kb) - 1)
+                        << (a.L.kb * sl);
+            }
+        }
+        a.L.k_words[(static_cast<size_t>(bh) * a.L.capq + t0 + i) * wk + w] = word;
+    }
+
+    // ---- Value: one wave per token, min / max over the D channels ----
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wv = a.L.wv, vb = a.L.vb, vq = (1 << vb) - 1, epw = 32 / vb;
+    for (int i = wave; i < G; i += kThreads / 64) {
+        const uint16_t *row = src_row(a, a.L.ring_v, a.v_new, bh, t0 + i);
+        float vmn = INFINITY, vmx = -INFINITY;
+        for (int cc = lane; cc < D; cc += 64) {
+            float x = widen16(row[cc], a.kv_bf16);
+            vmn = fminf(vmn, x);
+            vmx = fmaxf(vmx, x);
+        }
+        vmn = wave_min(vmn);
+        vmx = wave_max(vmx);
+        const float s = (vmx - vmn) / static_cast<float>(vq);
+        const size_t t = static_cast<size_t>(bh) * a.L.capq + t0 + i;
+        for (int w = lane; w < wv; w += 64) {
+            uint32_t word = 0;
+            for (int sl = 0; sl < epw; ++sl) {
+                const int cc = w * epw + sl;
+                word |= code_of(widen16(row[cc], a.kv_bf16), vmn, s, vq) << (vb * sl);
+            }
+            a.L.v_words[t * wv + w] = word;
+        }
+        if (lane == 0) {
+            a.L.v_meta[t * 2 + 0] = (s == 0.0f) ? 0.0f : s;
+            a.L.v_meta[t * 2 + 1] = (vmn == 0.0f) ? 0.0f : vmn;
+        }
+    }
+}
+
+// Copy the new tokens that stay recent into their ring slots, 16 bytes per item.
+__global__ __launch_bounds__(kThreads) void ring_write_kernel(RingArgs a)
+{
+    const int chunks = a.D / 8;  // 8 16-bit values per 16-byte chunk
+    const int ntok = a.t_last - a.t_first;
+    const long total = static_cast<long>(a.BH) * ntok * chunks;
+    for (long it = static_cast<long>(blockIdx.x) * kThreads + threadIdx.x; it < total;
+         it += static_cast<long>(gridDim.x) * kThreads) {
+        const int ch = static_cast<int>(it % chunks);
+        const long rest = it / chunks;
+        const int t = a.t_first + static_cast<int>(rest % ntok);
+        const int bh = static_cast<int>(rest / ntok);
+        const size_t src = (static_cast<size_t>(bh) * a.n_new + (t - a.N0)) * a.D + ch * 8;
+        const size_t dst = (static_cast<size_t>(bh) * a.L.R + (t % a.L.R)) * a.D + ch * 8;
+        *reinterpret_cast<uint4 *>(a.L.ring_k + dst) = *reinterpret_cast<const uint4 *>(a.k_new + src);
+        *reinterpret_cast<uint4 *>(a.L.ring_v + dst) = *reinterpret_cast<const uint4 *>(a.v_new + src);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_flush(const FlushArgs &a, hipStream_t st)
+{
+    dim3 grid(a.n_groups, a.BH);
+    hipLaunchKernelGGL(flush_kernel, grid, dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_ring_write(const RingArgs &a, hipStream_t st)
+{
+    const long total = static_cast<long>(a.BH) * (a.t_last - a.t_first) * (a.D / 8);
+    long blocks = (total + kThreads - 1) / kThreads;
+    if (blocks > 65536)
+        blocks = 65536;
+    hipLaunchKernelGGL(ring_write_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st,
+                       a);
+    return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,537 @@
+// kvq_runtime.cpp -- host side of libkvq: validation, workspace planning,
+// streaming counters, kernel dispatch, byte accounting and state export.
+// The C ABI is declared in include/kvq.h.
+#include "kvq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kvq_internal.h"
+
+namespace {
+
+thread_local std::string g_create_error = "no error";
+
+constexpr int kMaxSplits = 128;
+constexpr int kMaxG = 16;
+
+struct LayerState {
+    kvq::LayerDev dev;
+    size_t off_kw = 0, off_km = 0, off_vw = 0, off_vm = 0, off_rk = 0, off_rv = 0;
+    int N = 0, Tq = 0;
+};
+
+struct Plan {
+    std::vector<LayerState> layers;
+    size_t off_part = 0;
+    size_t total = 0;
+};
+
+int words_per_row(int d, int bits)
+{
+    if (bits == 3)
+        return (d + 10) / 11;
+    return d * bits / 32;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool valid_pair(int kb, int vb)
+{
+    if (kb == 16 || vb == 16)
+        return kb == 16 && vb == 16;
+    return (kb == 2 || kb == 3 || kb == 4 || kb == 8) && (vb == 2 || vb == 4 || vb == 8);
+}
+
+// Validates cfg and lays the workspace out.  Returns KVQ_OK or an error code
+// with a message in err.
+int plan_layout(const kvq_config *cfg, Plan *plan, std::string *err)
+{
+    char buf[256];
+    auto fail = [&](int code, const char *fmt, ...) {
+        va_list ap;
+        va_start(ap, fmt);
+        vsnprintf(buf, sizeof buf, fmt, ap);
+        va_end(ap);
+        *err = buf;
+        return code;
+    };
+    if (!cfg)
+        return fail(KVQ_EINVAL, "config is NULL");
+    if (cfg->n_layers < 1 || cfg->batch < 1 || cfg->n_q_heads < 1 || cfg->n_kv_heads < 1 ||
+        cfg->head_dim < 1 || cfg->max_context < 1 || cfg->group_size < 1)
+        return fail(KVQ_EINVAL, "n_layers, batch, heads, head_dim, max_context and group_size must be >= 1");
+    if (!cfg->layers)
+        return fail(KVQ_EINVAL, "layer table is NULL");
+    if (cfg->n_q_heads % cfg->n_kv_heads != 0)
+        return fail(KVQ_EINVAL, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)", cfg->n_q_heads,
+                    cfg->n_kv_heads);
+    if (cfg->n_q_heads / cfg->n_kv_heads > kMaxG)
+        return fail(KVQ_EUNSUPPORTED, "more than %d query heads per kv-head", kMaxG);
+    if (cfg->head_dim != 64 && cfg->head_dim != 128 && cfg->head_dim != 256)
+        return fail(KVQ_EUNSUPPORTED, "head_dim %d not in {64, 128, 256}", cfg->head_dim);
+    if (cfg->kv_dtype != KVQ_F16 && cfg->kv_dtype != KVQ_BF16)
+        return fail(KVQ_EINVAL, "kv_dtype must be KVQ_F16 or KVQ_BF16");
+    if (cfg->q_dtype != KVQ_F32 && cfg->q_dtype != KVQ_F16 && cfg->q_dtype != KVQ_BF16)
+        return fail(KVQ_EINVAL, "q_dtype must be KVQ_F32, KVQ_F16 or KVQ_BF16");
+    if (cfg->residual_len < cfg->group_size)
+        return fail(KVQ_EINVAL, "residual_len (%d) < group_size (%d)", cfg->residual_len, cfg->group_size);
+
+    const size_t BH = static_cast<size_t>(cfg->batch) * cfg->n_kv_heads;
+    const int D = cfg->head_dim, G = cfg->group_size;
+    const size_t A = KVQ_WORKSPACE_ALIGN;
+    size_t off = 0;
+    plan->layers.assign(cfg->n_layers, LayerState());
+    for (int l = 0; l < cfg->n_layers; ++l) {
+        const kvq_layer_cfg &lc = cfg->layers[l];
+        if (!valid_pair(lc.k_bits, lc.v_bits))
+            return fail(KVQ_EINVAL, "layer %d: (k_bits, v_bits) = (%d, %d) not supported", l, lc.k_bits,
+                        lc.v_bits);
+        LayerState &s = plan->layers[l];
+        kvq::LayerDev &d = s.dev;
+        d.kb = lc.k_bits;
+        d.vb = lc.v_bits;
+        d.G = G;
+        if (d.kb == 16) {
+            d.R = cfg->max_context;
+            d.capq = G;  // unused
+            d.wk = d.wv = 0;
+        } else {
+            d.R = lc.residual_len == 0 ? cfg->residual_len : lc.residual_len;
+            if (d.R < G)
+                return fail(KVQ_EINVAL, "layer %d: residual_len (%d) < group_size (%d)", l, d.R, G);
+            if (d.R < 0 || d.R > cfg->max_context + G)
+                return fail(KVQ_EINVAL, "layer %d: residual_len %d out of range", l, d.R);
+            d.capq = (cfg->max_context + G - 1) / G * G;
+            d.wk = words_per_row(D, d.kb);
+            d.wv = words_per_row(D, d.vb);
+        }
+        if (d.kb != 16) {
+            s.off_kw = off;
+            off = align_up(off + BH * d.capq * d.wk * 4, A);
+            s.off_km = off;
+            off = align_up(off + BH * (d.capq / G) * 2 * D * 4, A);
+            s.off_vw = off;
+            off = align_up(off + BH * d.capq * d.wv * 4, A);
+            s.off_vm = off;
+            off = align_up(off + BH * d.capq * 2 * 4, A);
+        }
+        s.off_rk = off;
+        off = align_up(off + BH * static_cast<size_t>(d.R) * D * 2, A);
+        s.off_rv = off;
+        off = align_up(off + BH * static_cast<size_t>(d.R) * D * 2, A);
+    }
+    plan->off_part = off;
+    off = align_up(off + static_cast<size_t>(cfg->batch) * cfg->n_q_heads * kMaxSplits * (D + 2) * 4, A);
+    plan->total = off;
+    return KVQ_OK;
+}
+
+}  // namespace
+
+struct kvq_handle {
+    kvq_config cfg;
+    std::vector<kvq_layer_cfg> table;
+    Plan plan;
+    char *ws = nullptr;
+    size_t ws_bytes = 0;
+    hipStream_t stream = nullptr;
+    int cu_count = 0;
+    int last_splits = 0, last_variant = -1;
+    bool touched = false;  // device work was enqueued
+    std::string err = "no error";
+
+    int fail(int code, const char *fmt, ...)
+    {
+        char buf[256];
+        va_list ap;
+        va_start(ap, fmt);
+        vsnprintf(buf, sizeof buf, fmt, ap);
+        va_end(ap);
+        err = buf;
+        return code;
+    }
+    int dev_fail(hipError_t e, const char *what)
+    {
+        return fail(KVQ_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+    }
+    int BH() const { return cfg.batch * cfg.n_kv_heads; }
+};
+
+extern "C" {
+
+size_t kvq_workspace_bytes(const kvq_config *cfg)
+{
+    Plan p;
+    std::string err;
+    if (plan_layout(cfg, &p, &err) != KVQ_OK) {
+        g_create_error = err;
+        return 0;
+    }
+    return p.total;
+}
+
+int kvq_create(const kvq_config *cfg, void *workspace, size_t ws_bytes, kvq_handle **out)
+{
+    if (!out) {
+        g_create_error = "out is NULL";
+        return KVQ_EINVAL;
+    }
+    *out = nullptr;
+    Plan p;
+    std::string err;
+    int rc = plan_layout(cfg, &p, &err);
+    if (rc != KVQ_OK) {
+        g_create_error = err;
+        return rc;
+    }
+    if (!workspace) {
+        g_create_error = "workspace is NULL";
+        return KVQ_ENOMEM;
+    }
+    if (reinterpret_cast<uintptr_t>(workspace) % KVQ_WORKSPACE_ALIGN != 0) {
+        g_create_error = "workspace is not 256-byte aligned";
+        return KVQ_ENOMEM;
+    }
+    if (ws_bytes < p.total) {
+        char buf[160];
+        snprintf(buf, sizeof buf, "workspace too small: %zu bytes given, %zu needed", ws_bytes, p.total);
+        g_create_error = buf;
+        return KVQ_ENOMEM;
+    }
+    kvq_handle *h = new kvq_handle();
+    h->cfg = *cfg;
+    h->table.assign(cfg->layers, cfg->layers + cfg->n_layers);
+    h->cfg.layers = h->table.data();
+    h->plan = std::move(p);
+    h->ws = static_cast<char *>(workspace);
+    h->ws_bytes = ws_bytes;
+    h->stream = static_cast<hipStream_t>(cfg->stream);
+    const size_t BH = static_cast<size_t>(h->BH());
+    for (LayerState &s : h->plan.layers) {
+        kvq::LayerDev &d = s.dev;
+        if (d.kb != 16) {
+            d.k_words = reinterpret_cast<uint32_t *>(h->ws + s.off_kw);
+            d.k_meta = reinterpret_cast<float *>(h->ws + s.off_km);
+            d.v_words = reinterpret_cast<uint32_t *>(h->ws + s.off_vw);
+            d.v_meta = reinterpret_cast<float *>(h->ws + s.off_vm);
+        }
+        d.ring_k = reinterpret_cast<uint16_t *>(h->ws + s.off_rk);
+        d.ring_v = reinterpret_cast<uint16_t *>(h->ws + s.off_rv);
+        (void)BH;
+    }
+    *out = h;
+    return KVQ_OK;
+}
+
+int kvq_append(kvq_handle *h, int layer, const void *k_new, const void *v_new, int n_new)
+{
+    if (!h)
+        return KVQ_EINVAL;
+    if (layer < 0 || layer >= h->cfg.n_layers)
+        return h->fail(KVQ_EINVAL, "layer %d out of range [0, %d)", layer, h->cfg.n_layers);
+    if (n_new < 0)
+        return h->fail(KVQ_EINVAL, "n_new = %d < 0", n_new);
+    if (n_new == 0)
+        return KVQ_OK;
+    if (!k_new || !v_new)
+        return h->fail(KVQ_EINVAL, "k_new or v_new is NULL");
+    if (reinterpret_cast<uintptr_t>(k_new) % 16 || reinterpret_cast<uintptr_t>(v_new) % 16)
+        return h->fail(KVQ_EINVAL, "k_new and v_new must be 16-byte aligned");
+    LayerState &s = h->plan.layers[layer];
+    kvq::LayerDev &d = s.dev;
+    if (static_cast<long>(s.N) + n_new > h->cfg.max_context)
+        return h->fail(KVQ_ECAPACITY, "layer %d: %d + %d tokens exceed max_context %d", layer, s.N, n_new,
+                       h->cfg.max_context);
+
+    const int N0 = s.N, N1 = s.N + n_new, Tq0 = s.Tq;
+    int Tq1 = Tq0;
+    if (d.kb != 16 && N1 > d.R) {
+        // tokens are flushed G at a time whenever the buffer is found full
+        const int over = N1 - d.R;
+        Tq1 = (over + d.G - 1) / d.G * d.G;
+        if (Tq1 < Tq0)
+            Tq1 = Tq0;
+    }
+    const int D = h->cfg.head_dim;
+    const int bf16 = h->cfg.kv_dtype == KVQ_BF16;
+    hipError_t e;
+    if (Tq1 > Tq0) {
+        kvq::FlushArgs fa;
+        fa.L = d;
+        fa.k_new = static_cast<const uint16_t *>(k_new);
+        fa.v_new = static_cast<const uint16_t *>(v_new);
+        fa.D = D;
+        fa.n_new = n_new;
+        fa.N0 = N0;
+        fa.Tq0 = Tq0;
+        fa.n_groups = (Tq1 - Tq0) / d.G;
+        fa.BH = h->BH();
+        fa.kv_bf16 = bf16;
+        e = kvq::launch_flush(fa, h->stream);
+        if (e != hipSuccess)
+            return h->dev_fail(e, "flush launch");
+    }
+    const int t_first = Tq1 > N0 ? Tq1 : N0;
+    if (N1 > t_first) {
+        kvq::RingArgs ra;
+        ra.L = d;
+        ra.k_new = static_cast<const uint16_t *>(k_new);
+        ra.v_new = static_cast<const uint16_t *>(v_new);
+        ra.D = D;
+        ra.n_new = n_new;
+        ra.N0 = N0;
+        ra.t_first = t_first;
+        ra.t_last = N1;
+        ra.BH = h->BH();
+        e = kvq::launch_ring_write(ra, h->stream);
+        if (e != hipSuccess)
+            return h->dev_fail(e, "ring write launch");
+    }
+    s.N = N1;
+    s.Tq = Tq1;
+    h->touched = true;
+    return KVQ_OK;
+}
+
+int kvq_decode_attention(kvq_handle *h, int layer, const void *q, float *out)
+{
+    if (!h)
+        return KVQ_EINVAL;
+    if (layer < 0 || layer >= h->cfg.n_layers)
+        return h->fail(KVQ_EINVAL, "layer %d out of range [0, %d)", layer, h->cfg.n_layers);
+    if (!q || !out)
+        return h->fail(KVQ_EINVAL, "q or out is NULL");
+    LayerState &s = h->plan.layers[layer];
+    if (s.N == 0)
+        return h->fail(KVQ_EINVAL, "layer %d holds no tokens", layer);
+    if (h->cu_count == 0) {
+        int dev = 0, n = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess)
+            e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess)
+            return h->dev_fail(e, "device query");
+        h->cu_count = n > 0 ? n : 256;
+    }
+    const int D = h->cfg.head_dim, BH = h->BH();
+    // splits: enough workgroups for about two per compute unit, >= 64 tokens each
+    int S = (2 * h->cu_count + BH - 1) / BH;
+    const char *env = getenv("KVQ_SPLITS");
+    if (env && atoi(env) > 0)
+        S = atoi(env);
+    const int max_by_len = (s.N + 63) / 64;
+    if (S > max_by_len)
+        S = max_by_len;
+    if (S > kMaxSplits)
+        S = kMaxSplits;
+    if (S < 1)
+        S = 1;
+    int tps = (s.N + S - 1) / S;
+    tps = (tps + 15) / 16 * 16;
+    S = (s.N + tps - 1) / tps;
+
+    kvq::AttnArgs a;
+    a.L = s.dev;
+    a.q = q;
+    a.out = out;
+    a.part = reinterpret_cast<float *>(h->ws + h->plan.off_part);
+    a.q_dtype = h->cfg.q_dtype;
+    a.kv_bf16 = h->cfg.kv_dtype == KVQ_BF16;
+    a.D = D;
+    a.g = h->cfg.n_q_heads / h->cfg.n_kv_heads;
+    a.Hkv = h->cfg.n_kv_heads;
+    a.N = s.N;
+    a.Tq = s.Tq;
+    a.BH = BH;
+    a.n_splits = S;
+    a.tps = tps;
+    a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D)));
+    hipError_t e = kvq::launch_attention_valu(a, h->stream);
+    if (e != hipSuccess)
+        return h->dev_fail(e, "attention launch");
+    e = kvq::launch_merge(a, h->stream);
+    if (e != hipSuccess)
+        return h->dev_fail(e, "merge launch");
+    h->last_splits = S;
+    h->last_variant = 0;
+    h->touched = true;
+    return KVQ_OK;
+}
+
+static void layer_bytes(const kvq_handle *h, const LayerState &s, kvq_bytes_info *info)
+{
+    const int64_t BH = h->BH(), D = h->cfg.head_dim;
+    const kvq::LayerDev &d = s.dev;
+    memset(info, 0, sizeof *info);
+    info->n_tokens = s.N;
+    info->n_quantized = s.Tq;
+    info->n_residual = s.N - s.Tq;
+    info->k_bits = d.kb;
+    info->v_bits = d.vb;
+    info->residual_len = d.R;
+    if (d.kb == 16) {
+        info->residual = BH * s.N * 4 * D;
+    } else {
+        info->k_words = d.wk;
+        info->v_words = d.wv;
+        info->k_codes = BH * s.Tq * 4 * d.wk;
+        info->v_codes = BH * s.Tq * 4 * d.wv;
+        info->k_meta = BH * (s.Tq / d.G) * 8 * D;
+        info->v_meta = BH * s.Tq * 8;
+        info->residual = BH * (s.N - s.Tq) * 4 * D;
+    }
+    info->total = info->k_codes + info->v_codes + info->k_meta + info->v_meta + info->residual;
+}
+
+int64_t kvq_bytes(const kvq_handle *h)
+{
+    if (!h)
+        return -1;
+    int64_t total = 0;
+    kvq_bytes_info info;
+    for (const LayerState &s : h->plan.layers) {
+        layer_bytes(h, s, &info);
+        total += info.total;
+    }
+    return total;
+}
+
+int kvq_bytes_layer(const kvq_handle *h, int layer, kvq_bytes_info *info)
+{
+    if (!h || !info)
+        return KVQ_EINVAL;
+    if (layer < 0 || layer >= h->cfg.n_layers)
+        return const_cast<kvq_handle *>(h)->fail(KVQ_EINVAL, "layer %d out of range", layer);
+    layer_bytes(h, h->plan.layers[layer], info);
+    return KVQ_OK;
+}
+
+int kvq_export_layer(kvq_handle *h, int layer, uint32_t *k_words, float *k_scale, float *k_zero,
+                     uint32_t *v_words, float *v_scale, float *v_zero, void *res_k, void *res_v)
+{
+    if (!h)
+        return KVQ_EINVAL;
+    if (layer < 0 || layer >= h->cfg.n_layers)
+        return h->fail(KVQ_EINVAL, "layer %d out of range", layer);
+    const LayerState &s = h->plan.layers[layer];
+    const kvq::LayerDev &d = s.dev;
+    const int BH = h->BH(), D = h->cfg.head_dim, Tq = s.Tq, Tr = s.N - s.Tq;
+    hipError_t e = hipStreamSynchronize(h->stream);
+    if (e != hipSuccess)
+        return h->dev_fail(e, "stream synchronize");
+    if (d.kb != 16 && Tq > 0) {
+        const int ng = Tq / d.G, ngcap = d.capq / d.G;
+        for (int bh = 0; bh < BH; ++bh) {
+            const size_t row0 = static_cast<size_t>(bh) * d.capq;
+            if (k_words &&
+                (e = hipMemcpy(k_words + static_cast<size_t>(bh) * Tq * d.wk, d.k_words + row0 * d.wk,
+                               static_cast<size_t>(Tq) * d.wk * 4, hipMemcpyDeviceToHost)) != hipSuccess)
+                return h->dev_fail(e, "export k_words");
+            if (v_words &&
+                (e = hipMemcpy(v_words + static_cast<size_t>(bh) * Tq * d.wv, d.v_words + row0 * d.wv,
+                               static_cast<size_t>(Tq) * d.wv * 4, hipMemcpyDeviceToHost)) != hipSuccess)
+                return h->dev_fail(e, "export v_words");
+            if (k_scale || k_zero) {
+                std::vector<float> m(static_cast<size_t>(ng) * 2 * D);
+                if ((e = hipMemcpy(m.data(), d.k_meta + static_cast<size_t>(bh) * ngcap * 2 * D,
+                                   m.size() * 4, hipMemcpyDeviceToHost)) != hipSuccess)
+                    return h->dev_fail(e, "export k_meta");
+                for (int gi = 0; gi < ng; ++gi)
+                    for (int c = 0; c < D; ++c) {
+                        const size_t o = (static_cast<size_t>(bh) * ng + gi) * D + c;
+                        if (k_scale)
+                            k_scale[o] = m[static_cast<size_t>(gi) * 2 * D + c];
+                        if (k_zero)
+                            k_zero[o] = m[static_cast<size_t>(gi) * 2 * D + D + c];
+                    }
+            }
+            if (v_scale || v_zero) {
+                std::vector<float> m(static_cast<size_t>(Tq) * 2);
+                if ((e = hipMemcpy(m.data(), d.v_meta + row0 * 2, m.size() * 4, hipMemcpyDeviceToHost)) !=
+                    hipSuccess)
+                    return h->dev_fail(e, "export v_meta");
+                for (int t = 0; t < Tq; ++t) {
+                    if (v_scale)
+                        v_scale[static_cast<size_t>(bh) * Tq + t] = m[2 * t];
+                    if (v_zero)
+                        v_zero[static_cast<size_t>(bh) * Tq + t] = m[2 * t + 1];
+                }
+            }
+        }
+    }
+    if ((res_k || res_v) && Tr > 0) {
+        std::vector<uint16_t> ring(static_cast<size_t>(d.R) * D);
+        for (int which = 0; which < 2; ++which) {
+            uint16_t *dst = static_cast<uint16_t *>(which ? res_v : res_k);
+            const uint16_t *src = which ? d.ring_v : d.ring_k;
+            if (!dst)
+                continue;
+            for (int bh = 0; bh < BH; ++bh) {
+                if ((e = hipMemcpy(ring.data(), src + static_cast<size_t>(bh) * d.R * D, ring.size() * 2,
+                                   hipMemcpyDeviceToHost)) != hipSuccess)
+                    return h->dev_fail(e, "export ring");
+                for (int i = 0; i < Tr; ++i) {
+                    const int t = Tq + i;
+                    memcpy(dst + (static_cast<size_t>(bh) * Tr + i) * D,
+                           ring.data() + static_cast<size_t>(t % d.R) * D, static_cast<size_t>(D) * 2);
+                }
+            }
+        }
+    }
+    return KVQ_OK;
+}
+
+int kvq_sync(kvq_handle *h)
+{
+    if (!h)
+        return KVQ_EINVAL;
+    hipError_t e = hipStreamSynchronize(h->stream);
+    if (e != hipSuccess)
+        return h->dev_fail(e, "stream synchronize");
+    return KVQ_OK;
+}
+
+int kvq_set_stream(kvq_handle *h, void *stream)
+{
+    if (!h)
+        return KVQ_EINVAL;
+    h->stream = static_cast<hipStream_t>(stream);
+    return KVQ_OK;
+}
+
+const char *kvq_last_error(const kvq_handle *h)
+{
+    if (!h)
+        return g_create_error.c_str();
+    return h->err.c_str();
+}
+
+void kvq_destroy(kvq_handle *h)
+{
+    if (!h)
+        return;
+    if (h->touched)
+        (void)hipStreamSynchronize(h->stream);
+    delete h;
+}
+
+int kvq_last_launch(const kvq_handle *h, int *splits, int *variant)
+{
+    if (!h)
+        return KVQ_EINVAL;
+    if (splits)
+        *splits = h->last_splits;
+    if (variant)
+        *variant = h->last_variant;
+    return KVQ_OK;
+}
+
+}  // extern "C"

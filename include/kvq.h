@@ -1,0 +1,188 @@
+/*
+ * kvq.h -- C ABI of libkvq: layer-wise mixed-precision quantized KV cache with
+ * streaming quantize-and-append and decode attention, for AMD MI355X (gfx950).
+ *
+ * What the library computes (cited by page title and section):
+ *   - Asymmetric uniform quantization Q(x) = round((x - z) / s), x^ = Q(x) s + z,
+ *     z = min, s = (max - min) / qmax.  (KVTuner summary, A3 "KV cache
+ *     quantization basics"; KVmix notes, key design 2.)  round() is
+ *     round-half-to-even of the IEEE fp32 quotient; s and z are fp32.
+ *   - Key quantized per channel over a group of G tokens (one fp32 scale and
+ *     zero per kv-head per channel per group); Value quantized per token (one
+ *     scale and zero per token).  (KIVI notes, sections 6.1-6.2; KVmix notes,
+ *     key design 2.)
+ *   - Codes packed into 32-bit words at 2, 4 or 8 bits, and for Key also the
+ *     3-bit layout of eleven codes per word, ten at 3 bits and the eleventh at
+ *     2 bits.  (KVmix notes, key design 2.)
+ *   - Streaming: the newest tokens stay in their 16-bit input format in a
+ *     recent-token buffer of R_l tokens shared by K and V; when an append finds
+ *     the buffer full, its oldest G tokens are quantized first.  (KIVI notes,
+ *     section 6.2; KVmix notes, key design 3 for a per-layer buffer length.)
+ *   - A static per-layer (k_bits, v_bits) table such as K8V4 or K4V2, fixed at
+ *     creation; no decision is taken online.  (KVTuner summary, A1 and A2.)
+ *   - Decode attention o = softmax(q K^T / sqrt(head_dim)) V over every token
+ *     appended so far, K and V dequantized on the fly, query heads of a GQA
+ *     group sharing one K/V read.  (KVTuner summary, A3 attention equation;
+ *     KIVI notes, sections 2.2 and 7.2 for GQA; KVmix notes, key design 4 for
+ *     dequantizing inside the matrix-vector product.)
+ *
+ * Conventions
+ *   - All device work is enqueued on the handle's HIP stream; calls return
+ *     without waiting unless documented otherwise.  Inputs must stay valid until
+ *     the stream has passed the call.  A handle is not thread-safe.
+ *   - Every argument is validated on the host before any device work.  On error
+ *     the call returns a negative KVQ_E* code, enqueues nothing, leaves the
+ *     handle's state unchanged and records a message for kvq_last_error().
+ *   - The caller owns every buffer, including the device workspace that holds
+ *     the whole cache state; the library allocates no device memory.
+ *   - Query head hq reads kv-head hq / g, g = n_q_heads / n_kv_heads.
+ *   - Every sequence of the batch has the same length.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define KVQ_OK 0
+#define KVQ_EINVAL (-1)       /* bad argument (null pointer, range, shape) */
+#define KVQ_ENOMEM (-2)       /* workspace missing, misaligned or too small */
+#define KVQ_ECAPACITY (-3)    /* append would exceed max_context */
+#define KVQ_EUNSUPPORTED (-4) /* valid request outside what the kernels support */
+#define KVQ_EDEVICE (-5)      /* a HIP call failed */
+
+/* Element formats. */
+#define KVQ_F32 0
+#define KVQ_F16 1  /* IEEE binary16 */
+#define KVQ_BF16 2 /* bfloat16 */
+
+/* Required alignment of the device workspace, in bytes. */
+#define KVQ_WORKSPACE_ALIGN 256
+
+/* One row of the per-layer precision table.
+ *   k_bits in {2, 3, 4, 8, 16}; v_bits in {2, 4, 8, 16}; 16 means the layer is
+ *   not quantized and must be given as the pair (16, 16).
+ *   residual_len: recent-token buffer length R_l for this layer; 0 selects the
+ *   config's residual_len.  Must be >= group_size.  Ignored for (16, 16). */
+typedef struct kvq_layer_cfg {
+    int32_t k_bits;
+    int32_t v_bits;
+    int32_t residual_len;
+} kvq_layer_cfg;
+
+/* Cache geometry.  All counts are >= 1.
+ *   n_q_heads must be a multiple of n_kv_heads, with n_q_heads / n_kv_heads
+ *   <= 16; head_dim in {64, 128, 256}; kv_dtype in {KVQ_F16, KVQ_BF16};
+ *   q_dtype in {KVQ_F32, KVQ_F16, KVQ_BF16}; group_size G >= 1;
+ *   residual_len R >= G; layers points to n_layers rows (copied at create);
+ *   stream is a hipStream_t (NULL selects the null stream). */
+typedef struct kvq_config {
+    int32_t n_layers;
+    int32_t batch;
+    int32_t n_q_heads;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    int32_t max_context;
+    int32_t kv_dtype;
+    int32_t q_dtype;
+    int32_t group_size;
+    int32_t residual_len;
+    const kvq_layer_cfg *layers;
+    void *stream;
+} kvq_config;
+
+typedef struct kvq_handle kvq_handle;
+
+/* Bytes of device workspace kvq_create() needs for cfg (the cache at
+ * max_context for every layer plus scratch for split partials).  Returns 0 if
+ * cfg is invalid or unsupported; kvq_last_error(NULL) then says why. */
+size_t kvq_workspace_bytes(const kvq_config *cfg);
+
+/* Create a cache in a caller-owned device workspace of ws_bytes bytes, aligned
+ * to KVQ_WORKSPACE_ALIGN, that must outlive the handle.  Every layer starts
+ * empty.  Does no device work.  On success *out receives the handle.
+ * Errors: KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_ENOMEM (see kvq_last_error(NULL)). */
+int kvq_create(const kvq_config *cfg, void *workspace, size_t ws_bytes, kvq_handle **out);
+
+/* Append n_new tokens to one layer, as if appended one at a time: before each
+ * token enters, a full recent-token buffer has its oldest G tokens quantized
+ * (K per channel over the group, V per token) and packed.
+ *   k_new, v_new: device pointers, [batch][n_kv_heads][n_new][head_dim] in
+ *   kv_dtype, contiguous.  n_new == 0 is a no-op.
+ * Errors: KVQ_EINVAL (bad layer, null pointer, n_new < 0), KVQ_ECAPACITY (the
+ * layer would hold more than max_context tokens), KVQ_EDEVICE. */
+int kvq_append(kvq_handle *h, int layer, const void *k_new, const void *v_new, int n_new);
+
+/* Decode attention of one query token per sequence over every token of `layer`
+ * (quantized tokens dequantized on the fly, recent tokens in 16 bits), scale
+ * 1/sqrt(head_dim).
+ *   q:   device pointer, [batch][n_q_heads][head_dim] in q_dtype.
+ *   out: device pointer, [batch][n_q_heads][head_dim] fp32.
+ * Errors: KVQ_EINVAL (bad layer, null pointer, empty layer), KVQ_EDEVICE. */
+int kvq_decode_attention(kvq_handle *h, int layer, const void *q, float *out);
+
+/* Live bytes of the cache state over all layers, host arithmetic only: per
+ * (sequence, kv-head): Tq rows of packed K and V codes (4 bytes per word), one
+ * fp32 scale and zero per channel per K group, one fp32 scale and zero per V
+ * token, and 2 bytes per element for the recent K and V tokens; a (16, 16)
+ * layer counts all its tokens at 2 bytes per element.  (KIVI notes, section 2.1
+ * for the 16-bit case.)  Returns -1 for a NULL handle. */
+int64_t kvq_bytes(const kvq_handle *h);
+
+typedef struct kvq_bytes_info {
+    int64_t k_codes, k_meta, v_codes, v_meta, residual, total;
+    int32_t n_tokens;     /* N: tokens appended */
+    int32_t n_quantized;  /* Tq: tokens held as codes */
+    int32_t n_residual;   /* Tr = N - Tq: tokens held in 16 bits */
+    int32_t k_words;      /* 32-bit words per packed K row */
+    int32_t v_words;      /* 32-bit words per packed V row */
+    int32_t k_bits, v_bits, residual_len;
+} kvq_bytes_info;
+
+/* Byte breakdown and token counts of one layer (host only). */
+int kvq_bytes_layer(const kvq_handle *h, int layer, kvq_bytes_info *info);
+
+/* Synchronously copy one layer's state to host memory in canonical order
+ * (waits for the stream).  Any pointer may be NULL to skip that part.  With
+ * B = batch, H = n_kv_heads, d = head_dim, Tq, Tr and words from
+ * kvq_bytes_layer():
+ *   k_words  uint32 [B][H][Tq][k_words]   row t = channels 0..d-1 of token t,
+ *            codes least-significant bits first (3-bit: channel c in word c/11,
+ *            bits 3(c%11), 2 bits wide in slot 10; unused slots 0)
+ *   k_scale, k_zero  float [B][H][Tq/G][d]
+ *   v_words  uint32 [B][H][Tq][v_words]
+ *   v_scale, v_zero  float [B][H][Tq]
+ *   res_k, res_v     kv_dtype [B][H][Tr][d], oldest token first
+ * For a (16, 16) layer Tq = 0 and res_* hold all N tokens. */
+int kvq_export_layer(kvq_handle *h, int layer, uint32_t *k_words, float *k_scale, float *k_zero,
+                     uint32_t *v_words, float *v_scale, float *v_zero, void *res_k, void *res_v);
+
+/* Wait for all work enqueued by the handle.  KVQ_EDEVICE reports an error the
+ * stream raised. */
+int kvq_sync(kvq_handle *h);
+
+/* Replace the handle's stream (for calls made after this one). */
+int kvq_set_stream(kvq_handle *h, void *stream);
+
+/* Message of the last failed call on h; with h == NULL, of the last failed
+ * kvq_workspace_bytes / kvq_create on this thread.  Never NULL. */
+const char *kvq_last_error(const kvq_handle *h);
+
+/* Release the handle (not the workspace).  Waits for the stream.  NULL is a no-op. */
+void kvq_destroy(kvq_handle *h);
+
+/* Launch configuration of the last kvq_decode_attention on h, for measurement:
+ * splits per (sequence, kv-head) and kernel variant (0 = vector ALU,
+ * 1 = matrix-core).  Either pointer may be NULL. */
+int kvq_last_launch(const kvq_handle *h, int *splits, int *variant);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,175 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Codes, scales, zeros and recent tokens bit-exact;
+attention within relative-L2 1e-3 and max-abs 5e-3 of the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+from decode_attention_streaming_amd import kvq, synth
+from gpu_common import (ad_hoc_workload, attention_error, check_attention, compare_export,
+                        make_cache, make_oracle, q_streams, stream_view)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _run_case(w, chunks, decode_checks=(), layer_cfg=None, seed=0):
+    """Append `chunks` (token counts) to one layer on both sides; compare the
+    state after every chunk listed in decode_checks (and at the end) and the
+    attention output."""
+    lc = layer_cfg or w.layers[0]
+    cache = make_cache(w, layers=[lc])
+    orc = make_oracle(w, lc, w.context)
+    st = synth.LayerStats(w, 0, seed)
+    t0 = 0
+    results = []
+    for i, n in enumerate(chunks):
+        k, v = synth.layer_tokens(w, 0, t0, n, DEV, stats=st, seed=seed)
+        cache.append(0, k, v)
+        orc.append(stream_view(k), stream_view(v))
+        t0 += n
+        if i in decode_checks or i == len(chunks) - 1:
+            q = synth.query(w, 0, i, DEV, seed=seed)
+            out = cache.decode_attention(0, q)
+            torch.cuda.synchronize()
+            compare_export(cache.export(0), orc.export())
+            ref = orc.attention(q_streams(q, w.g))
+            results.append(check_attention(out, ref, w.g, what="chunk %d N=%d" % (i, t0)))
+            info = cache.bytes_layer(0)
+            assert info.total == orc.bytes()
+    cache.close()
+    return results
+
+
+CASES = {
+    # name: (B, Hq, Hkv, d, kb, vb, G, R, ctx, kv, q, chunks)
+    "cfg1_k4v2_d64": (1, 1, 1, 64, 4, 2, 32, 32, 288, "f16", "f32", [288]),
+    "k8v4_g4_ragged": (2, 8, 2, 128, 8, 4, 32, 40, 320, "bf16", "bf16", [300, 1, 1, 7]),
+    "k3v4_mha_R50": (2, 2, 2, 128, 3, 4, 32, 50, 400, "f16", "f16", [333, 2]),
+    "k2v2_d256_g16": (1, 16, 1, 256, 2, 2, 16, 16, 300, "bf16", "f32", [250, 3]),
+    "k4v4_d64_g7_tiles": (2, 14, 2, 64, 4, 4, 64, 64, 1100, "bf16", "bf16", [1000, 1, 50]),
+    "plain16_g4": (2, 8, 2, 128, 16, 16, 32, 32, 600, "bf16", "f32", [513, 1]),
+    "k8v8_G1_R1": (1, 4, 1, 128, 8, 8, 1, 1, 80, "f16", "f32", [70, 1]),
+    "k4v2_G8_R9_tokenwise": (1, 2, 1, 64, 4, 2, 8, 9, 64, "f16", "f32", [1] * 40),
+    "k2v8_g3": (3, 9, 3, 128, 2, 8, 16, 24, 200, "bf16", "f16", [5, 150, 20]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_small_parity(name):
+    B, Hq, Hkv, d, kb, vb, G, R, ctx, kv, q, chunks = CASES[name]
+    w = ad_hoc_workload(200 + sorted(CASES).index(name), B, Hq, Hkv, d, kb, vb, G, R, ctx, kv, q)
+    print("case", name, flush=True)
+    _run_case(w, chunks, decode_checks=set(range(len(chunks))))
+
+
+def test_workload1_exact_state():
+    """The single-layer K4V2 workload: 256 quantized tokens + 32 recent."""
+    w = synth.workload(1)
+    print("workload 1", flush=True)
+    res = _run_case(w, [288])
+    assert res
+
+
+def test_prefill_equals_token_by_token_and_deterministic():
+    w = ad_hoc_workload(300, 2, 8, 2, 128, 4, 2, 32, 32, 200, "bf16", "bf16")
+    st = synth.LayerStats(w, 0)
+    k, v = synth.layer_tokens(w, 0, 0, 200, DEV, stats=st)
+    a = make_cache(w)
+    b = make_cache(w)
+    a.append(0, k, v)
+    for t in range(200):
+        b.append(0, k[:, :, t:t + 1].contiguous(), v[:, :, t:t + 1].contiguous())
+    q = synth.query(w, 0, 0, DEV)
+    oa1 = a.decode_attention(0, q)
+    oa2 = a.decode_attention(0, q)
+    ob = b.decode_attention(0, q)
+    torch.cuda.synchronize()
+    ea, eb = a.export(0), b.export(0)
+    compare_export(ea, {k_: (v_ if not isinstance(v_, np.ndarray) else v_) for k_, v_ in eb.items()})
+    assert torch.equal(oa1, oa2), "two runs differ"
+    assert torch.equal(oa1, ob), "prefill and token-by-token states attend differently"
+
+
+def test_degenerate_and_tiny_values():
+    """Constant channels (s = 0), constant tokens, signed zeros and values in
+    the fp16 subnormal range."""
+    w = ad_hoc_workload(301, 1, 4, 1, 128, 4, 4, 32, 32, 128, "f16", "f32")
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(7)
+    k = torch.randn((1, 1, 100, 128), generator=gen, device=DEV)
+    v = torch.randn((1, 1, 100, 128), generator=gen, device=DEV)
+    k[..., :40, 3] = 1.5            # constant channel within the first groups
+    k[..., 5] = 0.0
+    k[..., 0:32, 6] = -0.0          # signed zeros
+    k[..., 7] *= 2.0 ** -17         # fp16 subnormals
+    v[..., 10, :] = -2.25           # constant token
+    v[..., 11, ::2] = 0.0
+    v[..., 11, 1::2] = -0.0
+    v[..., 12, :] *= 2.0 ** -18
+    k, v = k.half().contiguous(), v.half().contiguous()
+    cache = make_cache(w)
+    orc = make_oracle(w, w.layers[0], w.context)
+    cache.append(0, k, v)
+    orc.append(stream_view(k), stream_view(v))
+    q = torch.randn((1, 4, 128), generator=gen, device=DEV)
+    out = cache.decode_attention(0, q)
+    torch.cuda.synchronize()
+    compare_export(cache.export(0), orc.export())
+    check_attention(out, orc.attention(q_streams(q, 4)), 4)
+    ex = cache.export(0)
+    assert (ex["v_scale"][0, 10] == 0.0) and ex["v_zero"][0, 10] == np.float32(-2.25)
+
+
+def test_bf16_tiny_values():
+    """bf16 values far below the fp32 normal range of the scale."""
+    w = ad_hoc_workload(302, 1, 2, 1, 64, 8, 4, 16, 16, 64, "bf16", "f32")
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(8)
+    k = (torch.randn((1, 1, 48, 64), generator=gen, device=DEV) * 1e-37).to(torch.bfloat16)
+    v = (torch.randn((1, 1, 48, 64), generator=gen, device=DEV) * 1e-36).to(torch.bfloat16)
+    cache = make_cache(w)
+    orc = make_oracle(w, w.layers[0], w.context)
+    cache.append(0, k.contiguous(), v.contiguous())
+    orc.append(stream_view(k), stream_view(v))
+    torch.cuda.synchronize()
+    compare_export(cache.export(0), orc.export())
+
+
+def test_capacity_and_empty_append():
+    w = ad_hoc_workload(303, 1, 2, 1, 64, 4, 2, 16, 16, 96, "f16", "f32")
+    cache = make_cache(w)
+    orc = make_oracle(w, w.layers[0], w.context)
+    k, v = synth.layer_tokens(w, 0, 0, 96, DEV)
+    cache.append(0, k, v)
+    orc.append(stream_view(k), stream_view(v))
+    e = torch.empty((1, 1, 0, 64), dtype=torch.float16, device=DEV)
+    cache.append(0, e, e)
+    k1, v1 = synth.layer_tokens(w, 0, 96, 1, DEV)
+    with pytest.raises(kvq.KvqError) as err:
+        cache.append(0, k1, v1)
+    assert err.value.code == kvq.KVQ_ECAPACITY
+    torch.cuda.synchronize()
+    compare_export(cache.export(0), orc.export())
+    q = synth.query(w, 0, 0, DEV)
+    check_attention(cache.decode_attention(0, q), orc.attention(q_streams(q, w.g)), w.g)
+
+
+def test_multi_layer_table():
+    """Several layers with different pairs in one cache; each attends to its own state."""
+    layers = [(8, 8, 0), (4, 2, 48), (16, 16, 0), (3, 4, 40), (2, 2, 0)]
+    w = synth.Workload(304, "multi", len(layers), 2, 8, 2, 128, 260, "bf16", "bf16", 32, 32,
+                       layers=layers)
+    cache = make_cache(w)
+    for l, lc in enumerate(layers):
+        orc = make_oracle(w, lc, w.context)
+        st = synth.LayerStats(w, l)
+        k, v = synth.layer_tokens(w, l, 0, 257, DEV, stats=st)
+        cache.append(l, k, v)
+        orc.append(stream_view(k), stream_view(v))
+        q = synth.query(w, l, 0, DEV)
+        out = cache.decode_attention(l, q)
+        torch.cuda.synchronize()
+        compare_export(cache.export(l), orc.export())
+        check_attention(out, orc.attention(q_streams(q, w.g)), w.g, what="layer %d" % l)
