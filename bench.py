@@ -1,0 +1,269 @@
+"""Decode-step benchmark of the quantized-KV cache on one MI355X.
+
+One step = for every layer: append one token per sequence (K and V, with a
+group flush whenever the recent-token buffer is full), then decode attention
+of one query token per sequence over the layer's whole cache.  Inputs are
+seeded synthetic tensors already resident in HBM.
+
+Default workload: Llama-3.1-8B-shaped decode (32 layers, 32 query / 8 KV heads,
+head_dim 128, batch 8, context 1024, bf16 K/V and q, a per-layer K/V bit table
+averaging 3.25 equivalent bits, G = R = 32).
+
+Prints one JSON line.  `value` is the whole-job effective bandwidth: the
+algorithmic bytes of every step (cache state read by attention + q + out, and
+the append/flush traffic) over the wall time of the timed steps.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def stream_state_bytes(d, kb, vb, G, N, Tq):
+    """Live bytes of one (sequence, kv-head) stream, as kvq_bytes documents."""
+    if kb == 16:
+        return N * 4 * d
+    wk = (d + 10) // 11 if kb == 3 else d * kb // 32
+    wv = d * vb // 32
+    return Tq * 4 * (wk + wv) + (Tq // G) * 8 * d + Tq * 8 + (N - Tq) * 4 * d
+
+
+def quantized_count(N, R, G, kb):
+    if kb == 16 or N <= R:
+        return 0
+    return G * (-(-(N - R) // G))
+
+
+def step_bytes(w, N_before, qbytes):
+    """Algorithmic bytes of one decode step over all layers, and of attention only."""
+    B, Hkv, Hq, d, G = w.batch, w.n_kv_heads, w.n_q_heads, w.head_dim, w.G
+    BH = B * Hkv
+    att = app = 0
+    for (kb, vb, R) in w.layers:
+        N1 = N_before + 1
+        Tq0 = quantized_count(N_before, R, G, kb)
+        Tq1 = quantized_count(N1, R, G, kb)
+        att += BH * stream_state_bytes(d, kb, vb, G, N1, Tq1) + B * Hq * d * (qbytes + 4)
+        app += BH * 2 * d * 2 * 2  # read new K and V, write them to the ring
+        if Tq1 > Tq0:  # flush: read G 16-bit K/V rows, write codes and metadata
+            wk = (d + 10) // 11 if kb == 3 else d * kb // 32
+            app += BH * (G * 4 * d + G * 4 * (wk + d * vb // 32) + 8 * d + 8 * G)
+    return att, app
+
+
+def cpu_baseline(w, seconds, layers_sample):
+    """Time the CPU oracle (single thread) on a sample of the same workload:
+    prefill the sampled layers (untimed), then repeat decode steps (append one
+    token + attention) until `seconds` have passed; scale to all layers."""
+    import numpy as np
+    import torch
+
+    from decode_attention_streaming_amd import synth
+    from oracle import oracle as ora
+
+    B, Hkv, g, d = w.batch, w.n_kv_heads, w.g, w.head_dim
+    BH = B * Hkv
+    qb = 2 if w.q_dtype != "f32" else 4
+    cap = w.context + 4096
+    layers = []
+    for l in layers_sample:
+        kb, vb, R = w.layers[l]
+        o = ora.Layer(BH, g, d, kb, vb, w.G, R, cap, w.kv_dtype == "bf16")
+        k, v = synth.layer_tokens(w, l, 0, w.context, "cpu")
+        o.append(synth.bits16(k.reshape(BH, w.context, d)), synth.bits16(v.reshape(BH, w.context, d)))
+        layers.append((l, o))
+    steps = 0
+    nbytes = 0
+    el = 0.0  # oracle time only; input generation is excluded
+    while el < seconds:
+        for l, o in layers:
+            k, v = synth.layer_tokens(w, l, o.N, 1, "cpu")
+            q = synth.as_f64(synth.query(w, l, steps, "cpu").reshape(BH, g, d))
+            kb16 = synth.bits16(k.reshape(BH, 1, d))
+            vb16 = synth.bits16(v.reshape(BH, 1, d))
+            t0 = time.perf_counter()
+            o.append(kb16, vb16)
+            o.attention(q)
+            el += time.perf_counter() - t0
+            nbytes += BH * stream_state_bytes(d, o.k_bits, o.v_bits, o.G, o.N, o.Tq) + \
+                B * w.n_q_heads * d * (qb + 4) + BH * 2 * d * 2 * 2
+        steps += 1
+    layer_steps = steps * len(layers)
+    step_time = el / layer_steps * len(w.layers)  # one full step over all layers
+    return {
+        "value": round(nbytes / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "tok_per_s": round(B / step_time, 3),
+        "sample": "%d decode steps (append 1 token + fp64 attention) on layers %s of %d, all %d "
+                  "streams, %.1f s of oracle time; tok/s scaled to all layers"
+                  % (steps, list(layers_sample), len(w.layers), BH, el),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--table", default="default", choices=["default", "k8v8"])
+    ap.add_argument("--kernel-rounds", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="also run a plain device copy of this size (counter scaling)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only; --gpus %d is not supported "
+              "(the sharded path is described in the design notes, not built)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from decode_attention_streaming_amd import kvq, synth
+
+    dev = "cuda"
+    w = synth.workload(args.workload)
+    if args.table == "k8v8":
+        w.layers = [(8, 8, r) for (_, _, r) in w.layers]
+    L, B, Hq, Hkv, d = w.n_layers, w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim
+    total = args.warmup + args.steps
+    qbytes = 4 if w.q_dtype == "f32" else 2
+    cache = kvq.Cache(L, B, Hq, Hkv, d, w.context + total, w.kv_dtype, w.q_dtype, w.G, w.R, w.layers)
+    stream = cache.stream
+
+    # prefill every layer, then stage all decode inputs in HBM
+    knew, vnew, qs = [], [], []
+    for l in range(L):
+        st = synth.LayerStats(w, l)
+        k, v = synth.layer_tokens(w, l, 0, w.context, dev, stats=st)
+        cache.append(l, k, v)
+        del k, v
+        k, v = synth.layer_tokens(w, l, w.context, total, dev, stats=st)
+        knew.append(k.permute(2, 0, 1, 3).contiguous().unsqueeze(3))  # [total, B, Hkv, 1, d]
+        vnew.append(v.permute(2, 0, 1, 3).contiguous().unsqueeze(3))
+        qs.append(synth.queries(w, l, total, dev))
+    outs = [torch.empty((B, Hq, d), dtype=torch.float32, device=dev) for _ in range(L)]
+    torch.cuda.synchronize()
+
+    def step(s):
+        for l in range(L):
+            cache.append(l, knew[l][s], vnew[l][s])
+            cache.decode_attention(l, qs[l][s], outs[l])
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+
+    att_bytes = app_bytes = 0
+    for s in range(args.warmup, total):
+        a, p = step_bytes(w, w.context + s, qbytes)
+        att_bytes += a
+        app_bytes += p
+
+    t0 = time.perf_counter()
+    for s in range(args.warmup, total):
+        step(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / args.steps * 1e3
+
+    # the state the library reports agrees with the byte model used above
+    N_end = w.context + total
+    for l, (kb, vb, R) in enumerate(w.layers):
+        info = cache.bytes_layer(l)
+        assert info.n_tokens == N_end
+        assert info.total == B * Hkv * stream_state_bytes(d, kb, vb, w.G, N_end,
+                                                         quantized_count(N_end, R, w.G, kb))
+
+    # dominant kernel: decode attention, timed per call with HIP events on the
+    # stream the library launches on (state fixed, every layer, several rounds)
+    with torch.cuda.stream(stream):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.kernel_rounds * L)]
+        i = 0
+        for r in range(args.kernel_rounds):
+            for l in range(L):
+                evs[i][0].record(stream)
+                cache.decode_attention(l, qs[l][total - 1], outs[l])
+                evs[i][1].record(stream)
+                i += 1
+    torch.cuda.synchronize()
+    call_ms = [a.elapsed_time(b) for a, b in evs]
+    avg_call_us = sum(call_ms) / len(call_ms) * 1e3
+    att_per_layer = []
+    for l, (kb, vb, R) in enumerate(w.layers):
+        Tq = quantized_count(N_end, R, w.G, kb)
+        att_per_layer.append(B * Hkv * stream_state_bytes(d, kb, vb, w.G, N_end, Tq) +
+                             B * Hq * d * (qbytes + 4))
+    avg_att_bytes = sum(att_per_layer) / L
+    achieved = avg_att_bytes / (avg_call_us * 1e-6) / 1e9
+    splits, variant = kvq.kvq_last_launch(cache.h)
+
+    if args.copy_mb > 0:  # a plain copy of known size, for scaling memory counters
+        n = args.copy_mb * (1 << 20)
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    value = (att_bytes + app_bytes) / wall / 1e9
+    res = {
+        "metric": "quantized-KV decode attention: effective HBM GB/s (% of peak), decode tok/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "tok_per_s": round(B * args.steps / wall, 1),
+        "attention_gbs_wall": round(att_bytes / wall / 1e9, 2),
+        "config": {
+            "workload": w.name,
+            "layers": L, "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": d,
+            "context_start": w.context, "G": w.G, "R": w.R,
+            "kv_dtype": w.kv_dtype, "q_dtype": w.q_dtype,
+            "table": "".join("K%dV%d " % (kb, vb) for kb, vb, _ in w.layers).strip(),
+            "equiv_bits": w.equiv_bits()["kv"],
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "decode attention call (split attention + merge), variant %d, %d splits"
+                      % (variant, splits),
+            "avg_call_us": round(avg_call_us, 3),
+            "bytes_per_call": int(avg_att_bytes),
+        },
+    }
+    if not args.no_cpu_baseline:
+        sample = [0, 1] if L >= 2 else [0]
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, sample)
+    cache.close()
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

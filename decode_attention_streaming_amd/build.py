@@ -14,7 +14,10 @@ OUT = os.path.join(PKG, "libkvq.so")
 BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["kvq_runtime.cpp", "kvq_append.hip", "kvq_attention.hip"]
+# (source, object name, extra flags); the matrix-core kernel is built once per head_dim
+SOURCES = [("kvq_runtime.cpp", "kvq_runtime", []), ("kvq_append.hip", "kvq_append", []),
+           ("kvq_attention.hip", "kvq_attention", [])] + [
+    ("kvq_attn_mfma.hip", "kvq_attn_mfma_d%d" % d, ["-DKVQ_D=%d" % d]) for d in (64, 128, 256)]
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
     # packed fp32 VALU instructions stay off: plain float code only
@@ -24,9 +27,10 @@ FLAGS = [
 ]
 
 
-def _compile(src):
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(item):
+    src, name, extra = item
+    obj = os.path.join(BUILD, name + ".o")
+    cmd = [HIPCC] + FLAGS + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))

@@ -4,23 +4,30 @@
 // with an fp32 scale s = (max - min) / qmax and zero z = min, codes
 // round-half-even((x - z) / s) clamped to [0, qmax] (KVTuner summary, A3 "KV
 // cache quantization basics"; KVmix notes, key design 2; KIVI notes, sections
-// 6.1-6.2).  Codes are packed into 32-bit words along head_dim, least
-// significant bits first; the 3-bit Key layout puts eleven channels in a word,
-// slot 10 at 2 bits (KVmix notes, key design 2).  Quantizing straight into the
-// packed history, with no intermediate buffer, follows KVmix key design 4.
+// 6.1-6.2).  Codes are packed into 32-bit words, least significant bits first;
+// the 3-bit Key layout puts eleven channels in a word, slot 10 at 2 bits
+// (KVmix notes, key design 2).  Quantizing straight into the packed history
+// follows KVmix key design 4.
+//
+// One workgroup quantizes one group of one stream.  The group's 16-bit K tile
+// is staged in LDS with 16-byte loads, reduced per channel (min/max over the G
+// tokens), encoded and packed; then the V tile is staged in the same LDS and
+// reduced per token with wavefront min/max.
 //
 // Bit-exactness with a serial CPU evaluation: min/max are exact in any order;
 // the subtraction and the IEEE fp32 division are correctly rounded (no fast
 // math, no contraction); rintf is round-half-even; zero scales and zero points
 // are stored as +0.
-#include "kvq_internal.h"
-
 #include <hip/hip_fp16.h>
+
+#include "kvq_internal.h"
+#include "kvq_layout.h"
 
 namespace kvq {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kTileElems = 16384;  // 16-bit elements of one staged G x D tile
 
 __device__ __forceinline__ float widen16(uint16_t x, int bf16)
 {
@@ -69,24 +76,40 @@ __device__ __forceinline__ const uint16_t *src_row(const FlushArgs &a, const uin
     return fresh + (static_cast<size_t>(bh) * a.n_new + (t - a.N0)) * a.D;
 }
 
-// One workgroup quantizes one group of one stream: K per channel, V per token.
+// Copy the G x D tile of tokens [t0, t0 + G) into LDS.
+__device__ __forceinline__ void stage(const FlushArgs &a, const uint16_t *ring, const uint16_t *fresh,
+                                      int bh, int t0, uint16_t *tile)
+{
+    const int D = a.D, chunks = D / 8;
+    for (int it = threadIdx.x; it < a.L.G * chunks; it += kThreads) {
+        const int i = it / chunks, ch = it % chunks;
+        const uint16_t *row = src_row(a, ring, fresh, bh, t0 + i);
+        *reinterpret_cast<uint4 *>(tile + i * D + ch * 8) = *reinterpret_cast<const uint4 *>(row + ch * 8);
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a)
 {
 #pragma clang fp contract(off)
     const int j = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int D = a.D, G = a.L.G;
     const int t0 = a.Tq0 + j * G;
     const int gi = t0 / G;
+    const int bf = a.kv_bf16;
 
+    __shared__ uint16_t tile[kTileElems];
     __shared__ float red_mn[kThreads], red_mx[kThreads];
-    __shared__ float s_k[256], mn_k[256];
+    __shared__ float s_c[256], mn_c[256];
 
     // ---- Key: min / max per channel over the G tokens ----
+    stage(a, a.L.ring_k, a.k_new, bh, t0, tile);
+    __syncthreads();
     const int parts = kThreads / D;  // threads per channel (D divides 256)
     const int c = tid % D, p = tid / D;
     float mn = INFINITY, mx = -INFINITY;
     for (int i = p; i < G; i += parts) {
-        float x = widen16(src_row(a, a.L.ring_k, a.k_new, bh, t0 + i)[c], a.kv_bf16);
+        const float x = widen16(tile[i * D + c], bf);
         mn = fminf(mn, x);
         mx = fmaxf(mx, x);
     }
@@ -94,70 +117,112 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a)
     red_mx[tid] = mx;
     __syncthreads();
     if (p == 0) {
-        for (int q = 1; q < parts; ++q) {
-            mn = fminf(mn, red_mn[q * D + c]);
-            mx = fmaxf(mx, red_mx[q * D + c]);
+        for (int r = 1; r < parts; ++r) {
+            mn = fminf(mn, red_mn[r * D + c]);
+            mx = fmaxf(mx, red_mx[r * D + c]);
         }
-        float s = (mx - mn) / static_cast<float>(qmax_of(a.L.kb, c));
-        s_k[c] = s;
-        mn_k[c] = mn;
+        const float s = (mx - mn) / static_cast<float>(qmax_of(a.L.kb, c));
+        s_c[c] = s;
+        mn_c[c] = mn;
         float *meta = a.L.k_meta + (static_cast<size_t>(bh) * (a.L.capq / G) + gi) * 2 * D;
         meta[c] = (s == 0.0f) ? 0.0f : s;
         meta[D + c] = (mn == 0.0f) ? 0.0f : mn;
     }
     __syncthreads();
 
-    // ---- Key: codes, one packed word per work item (token i, word w) ----
-    const int wk = a.L.wk;
+    // ---- Key codes: one packed word per work item (token i, word w) ----
+    const int wk = a.L.wk, kb = a.L.kb;
     for (int it = tid; it < G * wk; it += kThreads) {
         const int i = it / wk, w = it % wk;
-        const uint16_t *row = src_row(a, a.L.ring_k, a.k_new, bh, t0 + i);
+        const uint16_t *row = tile + i * D;
         uint32_t word = 0;
-        if (a.L.kb == 3) {
+        if (kb == 3) {
             for (int sl = 0; sl < 11; ++sl) {
                 const int cc = w * 11 + sl;
                 if (cc < D)
-                    word |= code_of(widen16(row[cc], a.kv_bf16), mn_k[cc], s_k[cc],
-                                    qmax_of(3, cc))
-                            << (3 * sl);
+                    word |= code_of(widen16(row[cc], bf), mn_c[cc], s_c[cc], qmax_of(3, cc)) << (3 * sl);
             }
         } else {
-            const int epw = 32 / a.L.kb;
+            const int epw = 32 / kb, qm = (1 << kb) - 1;
             for (int sl = 0; sl < epw; ++sl) {
                 const int cc = w * epw + sl;
-                word |= code_of(widen16(row[cc], a.kv_bf16), mn_k[cc], s_k[cc], (1 << a.L.kb) - 1)
-                        << (a.L.kb * sl);
+                word |= code_of(widen16(row[cc], bf), mn_c[cc], s_c[cc], qm) << (kb * sl);
             }
         }
         a.L.k_words[(static_cast<size_t>(bh) * a.L.capq + t0 + i) * wk + w] = word;
     }
+    __syncthreads();
 
     // ---- Value: one wave per token, min / max over the D channels ----
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wv = a.L.wv, vb = a.L.vb, vq = (1 << vb) - 1, epw = 32 / vb;
+    stage(a, a.L.ring_v, a.v_new, bh, t0, tile);
+    __syncthreads();
+    const int vb = a.L.vb, vq = (1 << vb) - 1;
     for (int i = wave; i < G; i += kThreads / 64) {
-        const uint16_t *row = src_row(a, a.L.ring_v, a.v_new, bh, t0 + i);
         float vmn = INFINITY, vmx = -INFINITY;
         for (int cc = lane; cc < D; cc += 64) {
-            float x = widen16(row[cc], a.kv_bf16);
+            const float x = widen16(tile[i * D + cc], bf);
             vmn = fminf(vmn, x);
             vmx = fmaxf(vmx, x);
         }
         vmn = wave_min(vmn);
         vmx = wave_max(vmx);
-        const float s = (vmx - vmn) / static_cast<float>(vq);
-        const size_t t = static_cast<size_t>(bh) * a.L.capq + t0 + i;
-        for (int w = lane; w < wv; w += 64) {
+        if (lane == 0) {
+            const float s = (vmx - vmn) / static_cast<float>(vq);
+            red_mn[i] = vmn;  // reuse: per-token minimum and scale
+            red_mx[i] = s;
+            float *vm = a.L.v_meta + (static_cast<size_t>(bh) * a.L.capq + t0 + i) * 2;
+            vm[0] = (s == 0.0f) ? 0.0f : s;
+            vm[1] = (vmn == 0.0f) ? 0.0f : vmn;
+        }
+    }
+    __syncthreads();
+
+    const int wv = a.L.wv;
+    uint32_t *vrow0 = a.L.v_words + (static_cast<size_t>(bh) * a.L.capq + t0) * wv;
+    if (a.L.v_tiled) {
+        // 32-token blocks of operand fragments (layout in kvq_layout.h)
+        const int fw = D * vb / 64, P = 16 / vb, blk_words = D * vb;
+        for (int it = tid; it < G * wv; it += kThreads) {
+            const int blk = it / blk_words, wi = it % blk_words;
+            const int frag = wi / fw, u = wi % fw;
+            const int q = frag >> 4, c16 = frag & 15;
+            uint32_t word = 0;
+            for (int jj = 0; jj < P; ++jj) {
+                const int R = u * P + jj, m = R >> 2;
+                for (int half = 0; half < 2; ++half) {
+                    const int s = 2 * (R & 3) + half;
+                    const int tb = (s >> 2) * 16 + 4 * q + (s & 3);
+                    const int i = blk * 32 + tb, cc = 16 * m + c16;
+                    word |= code_of(widen16(tile[i * D + cc], bf), red_mn[i], red_mx[i], vq)
+                            << (vb * jj + 16 * half);
+                }
+            }
+            vrow0[it] = word;
+        }
+    } else {
+        const int epw = 32 / vb;
+        for (int it = tid; it < G * wv; it += kThreads) {
+            const int i = it / wv, w = it % wv;
             uint32_t word = 0;
             for (int sl = 0; sl < epw; ++sl) {
                 const int cc = w * epw + sl;
-                word |= code_of(widen16(row[cc], a.kv_bf16), vmn, s, vq) << (vb * sl);
+                word |= code_of(widen16(tile[i * D + cc], bf), red_mn[i], red_mx[i], vq) << (vb * sl);
             }
-            a.L.v_words[t * wv + w] = word;
+            vrow0[it] = word;
         }
-        if (lane == 0) {
-            a.L.v_meta[t * 2 + 0] = (s == 0.0f) ? 0.0f : s;
-            a.L.v_meta[t * 2 + 1] = (vmn == 0.0f) ? 0.0f : vmn;
+    }
+
+    if (a.ring_after && j == 0) {
+        // single-token append: the new token takes the slot of the oldest
+        // flushed token, which was staged above
+        __syncthreads();
+        const size_t dst = (static_cast<size_t>(bh) * a.L.R + (a.N0 % a.L.R)) * D;
+        const size_t src = static_cast<size_t>(bh) * D;
+        for (int ch = tid; ch < D / 8; ch += kThreads) {
+            *reinterpret_cast<uint4 *>(a.L.ring_k + dst + ch * 8) =
+                *reinterpret_cast<const uint4 *>(a.k_new + src + ch * 8);
+            *reinterpret_cast<uint4 *>(a.L.ring_v + dst + ch * 8) =
+                *reinterpret_cast<const uint4 *>(a.v_new + src + ch * 8);
         }
     }
 }
@@ -181,6 +246,13 @@ __global__ __launch_bounds__(kThreads) void ring_write_kernel(RingArgs a)
     }
 }
 
+__global__ void zero_kernel(unsigned *p, int n)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n)
+        p[i] = 0u;
+}
+
 }  // namespace
 
 hipError_t launch_flush(const FlushArgs &a, hipStream_t st)
@@ -198,6 +270,12 @@ hipError_t launch_ring_write(const RingArgs &a, hipStream_t st)
         blocks = 65536;
     hipLaunchKernelGGL(ring_write_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st,
                        a);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero(unsigned *p, int n, hipStream_t st)
+{
+    hipLaunchKernelGGL(zero_kernel, dim3((n + 255) / 256), dim3(256), 0, st, p, n);
     return hipGetLastError();
 }
 

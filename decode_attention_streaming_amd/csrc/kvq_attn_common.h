@@ -1,0 +1,362 @@
+// kvq_attn_common.h -- device code shared by the decode-attention kernels:
+// the vector-ALU pass over a token range, and the log-sum-exp merge of split
+// partials done by the last workgroup of each stream to finish.
+//
+// Attention o = softmax(q K^T / sqrt(D)) V over one query token per sequence
+// (KVTuner summary, A3 attention equation), in the log2 domain: q is
+// prescaled by log2(e) / sqrt(D) and exp2 is used throughout.  Quantized
+// tokens are dequantized on the fly, x^ = code * s + z (KVmix notes, key
+// design 4); the query heads of one GQA group share each K/V read (KIVI notes,
+// section 7.2).
+#pragma once
+
+#include <hip/hip_fp16.h>
+
+#include "kvq_internal.h"
+#include "kvq_layout.h"
+
+namespace kvq {
+
+constexpr int kAttnThreads = 256;
+constexpr int kMaxG = 16;
+
+// Partial entry of one (stream, split, head): o[D], m, l, 2 pad floats.
+__device__ __forceinline__ int part_stride(int D) { return D + 4; }
+
+__device__ __forceinline__ float widen16(uint16_t x, int bf16)
+{
+    if (bf16)
+        return __uint_as_float(static_cast<uint32_t>(x) << 16);
+    return __half2float(__ushort_as_half(x));
+}
+
+__device__ __forceinline__ float load_q(const void *q, int dtype, size_t i)
+{
+    if (dtype == 0)
+        return static_cast<const float *>(q)[i];
+    return widen16(static_cast<const uint16_t *>(q)[i], dtype == 2);
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+    for (int off = 32; off > 0; off >>= 1)
+        v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+    for (int off = 32; off > 0; off >>= 1)
+        v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// K code of channel c in a token-major packed row.
+__device__ __forceinline__ uint32_t row_code(const uint32_t *row, int bits, int c)
+{
+    if (bits == 3) {
+        const int sl = c % 11;
+        return (row[c / 11] >> (3 * sl)) & (sl == 10 ? 3u : 7u);
+    }
+    const int bitpos = c * bits;
+    return (row[bitpos >> 5] >> (bitpos & 31)) & ((1u << bits) - 1u);
+}
+
+// V code of token t (quantized), channel c, in either V layout.
+__device__ __forceinline__ uint32_t v_code(const LayerDev &L, int bh, int t, int c, int D)
+{
+    const uint32_t *base = L.v_words + static_cast<size_t>(bh) * L.capq * L.wv;
+    if (L.v_tiled) {
+        int word, bit;
+        v_tile_pos(t & 31, c, L.vb, D, &word, &bit);
+        return (base[static_cast<size_t>(t & ~31) * L.wv + word] >> bit) & ((1u << L.vb) - 1u);
+    }
+    return row_code(base + static_cast<size_t>(t) * L.wv, L.vb, c);
+}
+
+// Tokens per tile of the vector-ALU pass: 16 KB of 16-bit K (or V) per tile.
+template <int D>
+constexpr int valu_tile() { return 8192 / D; }
+
+// Dynamic LDS bytes valu_range<D, GM>() needs: q[g][D], weights[g][TT],
+// K tile (16 KB), V tile (16 KB), reductions.
+__host__ __device__ inline int valu_lds_bytes(int g, int D)
+{
+    const int TT = 8192 / D;
+    return (g * D + g * TT + 4 * 4 * kMaxG) * 4 + 2 * 16384;
+}
+
+// Cooperative copy of n 32-bit words (16-byte aligned on both sides when n is a
+// multiple of 4) from global memory into LDS.
+__device__ __forceinline__ void stage_words(uint32_t *dst, const uint32_t *src, int n)
+{
+    if ((n & 3) == 0 && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+        for (int i = threadIdx.x; i < n / 4; i += kAttnThreads)
+            reinterpret_cast<uint4 *>(dst)[i] = reinterpret_cast<const uint4 *>(src)[i];
+    } else {
+        for (int i = threadIdx.x; i < n; i += kAttnThreads)
+            dst[i] = src[i];
+    }
+}
+
+// Cooperative copy of ring rows of tokens [t0, t0 + n) into LDS [n][D].
+template <int D>
+__device__ __forceinline__ void stage_ring(uint16_t *dst, const uint16_t *ring, int R, int t0, int n)
+{
+    constexpr int CH = D / 8;  // 16-byte chunks per row
+    for (int it = threadIdx.x; it < n * CH; it += kAttnThreads) {
+        const int i = it / CH, ch = it % CH;
+        reinterpret_cast<uint4 *>(dst + i * D)[ch] =
+            reinterpret_cast<const uint4 *>(ring + static_cast<size_t>((t0 + i) % R) * D)[ch];
+    }
+}
+
+// Vector-ALU attention of one workgroup (256 threads) over tokens [t_beg, t_end)
+// of stream bh; writes partial entry `slot` for each of the g heads.  Tiles of
+// TT tokens, each all quantized or all recent, are staged in LDS with 16-byte
+// loads.  Scores: P = 256 / TT threads per token, 32 channels each, reduced by
+// lane shuffles.  P.V: one thread per (channel, head slot), the value scale
+// folded into the weight, sum_t p_t (c_t s_t + z_t) = sum_t (p_t s_t) c_t +
+// sum_t p_t z_t.
+template <int D, int GM>
+__device__ void valu_range(const AttnArgs &a, int bh, int t_beg, int t_end, int slot, float *smem)
+{
+    constexpr int TT = valu_tile<D>();
+    constexpr int P = kAttnThreads / TT;  // threads per token in the score phase
+    constexpr int CPT = D / P;            // channels per thread (32)
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = a.g;
+    float *q_lds = smem;                         // [g][D]
+    float *p_lds = smem + g * D;                 // [g][TT]
+    float *red_lds = p_lds + g * TT;             // [4][4][kMaxG]
+    uint32_t *k_tile = reinterpret_cast<uint32_t *>(red_lds + 4 * 4 * kMaxG);  // 16 KB
+    uint32_t *v_tile = k_tile + 4096;                                           // 16 KB
+#define q_l(h, c) q_lds[(h) * D + (c)]
+#define p_l(h, i) p_lds[(h) * TT + (i)]
+#define red(k, w, h) red_lds[((k) * 4 + (w)) * kMaxG + (h)]
+    const int b = bh / a.Hkv, kvh = bh % a.Hkv;
+    const LayerDev &L = a.L;
+    const int bf = a.kv_bf16;
+
+    for (int i = tid; i < g * D; i += kAttnThreads) {
+        const int h = i / D, c = i % D;
+        const size_t qi = (static_cast<size_t>(b) * a.Hkv * g + kvh * g + h) * D + c;
+        q_l(h, c) = load_q(a.q, a.q_dtype, qi) * a.scale_log2;
+    }
+
+    const int oc = tid % D, oh0 = tid / D, hstep = kAttnThreads / D;
+    float o[GM], m[GM], l[GM];
+#pragma unroll
+    for (int k = 0; k < GM; ++k) {
+        o[k] = 0.0f;
+        m[k] = -INFINITY;
+        l[k] = 0.0f;
+    }
+
+    const int ngcap = L.capq / L.G;
+    const size_t row0 = static_cast<size_t>(bh) * L.capq;
+    for (int tile = t_beg; tile < t_end;) {
+        const bool quant = tile < a.Tq;
+        const int tend = min(min(tile + TT, t_end), quant ? a.Tq : t_end);
+        const int nt = tend - tile;
+        __syncthreads();  // previous tile's LDS reads are done (and q is staged)
+        if (quant) {
+            stage_words(k_tile, L.k_words + (row0 + tile) * L.wk, nt * L.wk);
+            stage_words(v_tile, L.v_words + (row0 + tile) * L.wv, nt * L.wv);
+        } else {
+            stage_ring<D>(reinterpret_cast<uint16_t *>(k_tile), L.ring_k + static_cast<size_t>(bh) * L.R * D,
+                          L.R, tile, nt);
+            stage_ring<D>(reinterpret_cast<uint16_t *>(v_tile), L.ring_v + static_cast<size_t>(bh) * L.R * D,
+                          L.R, tile, nt);
+        }
+        // per-thread metadata while the tile lands
+        const int ti = tid / P, part = tid % P, c0 = part * CPT;
+        const int t = tile + ti;
+        const bool valid = ti < nt;
+        float ks[CPT], kz[CPT];
+        float vs = 1.0f, vz = 0.0f;
+        if (quant && valid) {
+            const float *km = L.k_meta + (static_cast<size_t>(bh) * ngcap + t / L.G) * 2 * D + c0;
+#pragma unroll
+            for (int i = 0; i < CPT; i += 4) {
+                const float4 s4 = *reinterpret_cast<const float4 *>(km + i);
+                const float4 z4 = *reinterpret_cast<const float4 *>(km + D + i);
+                ks[i] = s4.x; ks[i + 1] = s4.y; ks[i + 2] = s4.z; ks[i + 3] = s4.w;
+                kz[i] = z4.x; kz[i + 1] = z4.y; kz[i + 2] = z4.z; kz[i + 3] = z4.w;
+            }
+            const float2 vm = *reinterpret_cast<const float2 *>(L.v_meta + (row0 + t) * 2);
+            vs = vm.x;
+            vz = vm.y;
+        }
+        __syncthreads();
+
+        // ---- scores: this thread's 32 channels of token ti ----
+        float sc[GM];
+#pragma unroll
+        for (int h = 0; h < GM; ++h)
+            sc[h] = 0.0f;
+        if (valid) {
+            if (quant) {
+                const uint32_t *row = k_tile + ti * L.wk;
+#pragma unroll 8
+                for (int i = 0; i < CPT; ++i) {
+                    const int c = c0 + i;
+                    const float x = __builtin_fmaf(static_cast<float>(row_code(row, L.kb, c)), ks[i], kz[i]);
+#pragma unroll
+                    for (int h = 0; h < GM; ++h)
+                        if (h < g)
+                            sc[h] = __builtin_fmaf(q_l(h, c), x, sc[h]);
+                }
+            } else {
+                const uint16_t *row = reinterpret_cast<const uint16_t *>(k_tile) + ti * D + c0;
+#pragma unroll 8
+                for (int i = 0; i < CPT; ++i) {
+                    const float x = widen16(row[i], bf);
+#pragma unroll
+                    for (int h = 0; h < GM; ++h)
+                        if (h < g)
+                            sc[h] = __builtin_fmaf(q_l(h, c0 + i), x, sc[h]);
+                }
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < GM; ++h)
+            for (int off = 1; off < P; off <<= 1)
+                sc[h] += __shfl_xor(sc[h], off, 64);
+
+        // ---- tile maximum, weights, normalizer and z-term per head ----
+#pragma unroll
+        for (int h = 0; h < GM; ++h) {
+            if (h < g) {
+                const float w = wave_max(valid ? sc[h] : -INFINITY);
+                if (lane == 0)
+                    red(0, wave, h) = w;
+            }
+        }
+        __syncthreads();
+        float alpha[GM];
+#pragma unroll
+        for (int h = 0; h < GM; ++h) {
+            if (h < g) {
+                const float tm = fmaxf(fmaxf(red(0, 0, h), red(0, 1, h)), fmaxf(red(0, 2, h), red(0, 3, h)));
+                const float mnew = fmaxf(m[h], tm);
+                alpha[h] = exp2f(m[h] - mnew);
+                if (tid == 0)
+                    red(3, 0, h) = alpha[h];
+                // one thread per token contributes to the sums
+                const float p = (valid && part == 0) ? exp2f(sc[h] - mnew) : 0.0f;
+                if (valid && part == 0)
+                    p_l(h, ti) = p * vs;
+                const float ps = wave_sum(p), pz = wave_sum(p * vz);
+                if (lane == 0) {
+                    red(1, wave, h) = ps;
+                    red(2, wave, h) = pz;
+                }
+                m[h] = mnew;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int h = 0; h < GM; ++h)
+            if (h < g)
+                l[h] = l[h] * alpha[h] + (red(1, 0, h) + red(1, 1, h) + red(1, 2, h) + red(1, 3, h));
+#pragma unroll
+        for (int k = 0; k < GM; ++k) {
+            const int h = oh0 + k * hstep;
+            if (h < g)
+                o[k] = o[k] * red(3, 0, h) + (red(2, 0, h) + red(2, 1, h) + red(2, 2, h) + red(2, 3, h));
+        }
+
+        // ---- P.V from the staged V tile ----
+        if (quant) {
+            for (int i = 0; i < nt; ++i) {
+                uint32_t code;
+                if (L.v_tiled) {
+                    int word, bit;
+                    v_tile_pos(i & 31, oc, L.vb, D, &word, &bit);
+                    code = (v_tile[(i & ~31) * L.wv + word] >> bit) & ((1u << L.vb) - 1u);
+                } else {
+                    code = row_code(v_tile + i * L.wv, L.vb, oc);
+                }
+                const float x = static_cast<float>(code);
+#pragma unroll
+                for (int k = 0; k < GM; ++k) {
+                    const int h = oh0 + k * hstep;
+                    if (h < g)
+                        o[k] = __builtin_fmaf(p_l(h, i), x, o[k]);
+                }
+            }
+        } else {
+            const uint16_t *vt = reinterpret_cast<const uint16_t *>(v_tile);
+            for (int i = 0; i < nt; ++i) {
+                const float x = widen16(vt[i * D + oc], bf);
+#pragma unroll
+                for (int k = 0; k < GM; ++k) {
+                    const int h = oh0 + k * hstep;
+                    if (h < g)
+                        o[k] = __builtin_fmaf(p_l(h, i), x, o[k]);
+                }
+            }
+        }
+        tile = tend;
+    }
+
+    const int ps = part_stride(D);
+    float *part = a.part + (static_cast<size_t>(bh) * a.n_part + slot) * g * ps;
+#pragma unroll
+    for (int k = 0; k < GM; ++k) {
+        const int h = oh0 + k * hstep;
+        if (h < g) {
+            part[h * ps + oc] = o[k];
+            if (oc == 0) {
+                part[h * ps + D] = m[h];
+                part[h * ps + D + 1] = l[h];
+            }
+        }
+    }
+#undef q_l
+#undef p_l
+#undef red
+}
+
+// Called by every workgroup at its end: the last one of stream bh to arrive
+// merges the n_part partial entries, out = sum_s 2^(m_s - M) o_s /
+// sum_s 2^(m_s - M) l_s, M = max_s m_s, and re-arms the stream's counter.
+__device__ __forceinline__ void arrive_and_merge(const AttnArgs &a, int bh, unsigned n_wgs)
+{
+    __shared__ int s_last;
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned prev = atomicAdd(a.counters + bh, 1u);
+        s_last = (prev == n_wgs - 1);
+    }
+    __syncthreads();
+    if (!s_last)
+        return;
+    __threadfence();
+    const int D = a.D, g = a.g, P = a.n_part, ps = part_stride(D);
+    const int b = bh / a.Hkv, kvh = bh % a.Hkv;
+    const float *part = a.part + static_cast<size_t>(bh) * P * g * ps;
+    for (int i = threadIdx.x; i < g * D; i += kAttnThreads) {
+        const int h = i / D, c = i % D;
+        float M = -INFINITY;
+#pragma unroll 8
+        for (int s = 0; s < P; ++s)
+            M = fmaxf(M, part[(s * g + h) * ps + D]);
+        float num = 0.0f, den = 0.0f;
+#pragma unroll 8
+        for (int s = 0; s < P; ++s) {
+            const float *e = part + (s * g + h) * ps;
+            const float ms = e[D];
+            const float w = (ms == -INFINITY) ? 0.0f : exp2f(ms - M);
+            num = __builtin_fmaf(w, e[c], num);
+            den = __builtin_fmaf(w, e[D + 1], den);
+        }
+        a.out[(static_cast<size_t>(b) * a.Hkv * g + kvh * g + h) * D + c] = num / den;
+    }
+    if (threadIdx.x == 0)
+        a.counters[bh] = 0u;
+}
+
+}  // namespace kvq

@@ -10,10 +10,19 @@ namespace kvq {
 
 // Physical layout of one layer in the workspace.  BH = batch * n_kv_heads
 // streams, each with its own rows; capq = quantized-token capacity per stream.
+//
+// K codes are token-major rows of wk words (channels along the row, least
+// significant bits first; 3-bit: eleven channels per word).
+//
+// V codes are either token-major rows (v_tiled == 0) or, for the matrix-core
+// path, 32-token blocks laid out as that kernel's operand fragments
+// (v_tiled == 1): inside a block, 64 fragments of D*vb/64 words, fragment
+// f = 16*q + c16 holding channels c16, c16+16, ... for the eight tokens
+// {4q..4q+3, 16+4q..16+4q+3}; see v_tile_bit() in kvq_layout.h.
 struct LayerDev {
-    uint32_t *k_words;  // [BH][capq][wk]         packed K rows, token-major
+    uint32_t *k_words;  // [BH][capq][wk]
     float *k_meta;      // [BH][capq / G][2][D]   per group: D scales, then D zeros
-    uint32_t *v_words;  // [BH][capq][wv]         packed V rows, token-major
+    uint32_t *v_words;  // [BH][capq][wv] (row-major or 32-token tiles, same size)
     float *v_meta;      // [BH][capq][2]          per token: scale, zero
     uint16_t *ring_k;   // [BH][R][D]             recent tokens, slot = t % R
     uint16_t *ring_v;   // [BH][R][D]
@@ -21,15 +30,19 @@ struct LayerDev {
     int wk, wv;         // 32-bit words per packed row
     int R;              // recent-token capacity (max_context for a 16-bit layer)
     int G;              // tokens per K group
-    int capq;           // quantized-token capacity per stream (multiple of G)
+    int capq;           // quantized-token capacity per stream (multiple of G and 32)
+    int v_tiled;        // V code layout, see above
 };
 
 // Quantize and pack groups [Tq0 + j*G, Tq0 + (j+1)*G), j < n_groups, for every
 // stream.  Token t comes from the ring (t < N0) or from the new tokens (t >= N0).
+// When ring_after != 0 (single-token append), the same workgroup afterwards
+// stores new token N0 into ring slot N0 % R.
 struct FlushArgs {
     LayerDev L;
     const uint16_t *k_new, *v_new;  // [BH][n_new][D]
     int D, n_new, N0, Tq0, n_groups, BH, kv_bf16;
+    int ring_after;
 };
 
 // Copy new tokens t in [t_first, t_last) (t >= N0) into ring slot t % R.
@@ -41,18 +54,26 @@ struct RingArgs {
 
 struct AttnArgs {
     LayerDev L;
-    const void *q;      // [B][Hq][D] in q_dtype
-    float *out;         // [B][Hq][D]
-    float *part;        // [BH][n_splits][g][D + 2]: o[D], m (log2 domain), l
+    const void *q;        // [B][Hq][D] in q_dtype
+    float *out;           // [B][Hq][D]
+    float *part;          // [BH][n_part][g][D + 2]: o[D], m (log2 domain), l
+    unsigned *counters;   // [BH] arrival counters, zero between calls
     int q_dtype, kv_bf16;
     int D, g, Hkv, N, Tq, BH;
-    int n_splits, tps;  // splits per stream, tokens per split
-    float scale_log2;   // log2(e) / sqrt(D)
+    int n_part;           // partial entries per stream
+    // vector-ALU ranges: wg_valu workgroups per stream cover tokens [valu_beg, N)
+    int valu_beg, valu_wgs, valu_tps;
+    // matrix-core units: units_q waves per stream cover groups [0, Tq / G),
+    // unit_groups groups each; mfma_wgs = ceil(units_q / 4) workgroups
+    int units_q, unit_groups, mfma_wgs;
+    float scale_log2;     // log2(e) / sqrt(D)
 };
 
 hipError_t launch_flush(const FlushArgs &a, hipStream_t st);
 hipError_t launch_ring_write(const RingArgs &a, hipStream_t st);
-hipError_t launch_attention_valu(const AttnArgs &a, hipStream_t st);
-hipError_t launch_merge(const AttnArgs &a, hipStream_t st);
+// True when the matrix-core kernel is built for this (k_bits, v_bits, D).
+bool mfma_supported(int kb, int vb, int D);
+hipError_t launch_attention(const AttnArgs &a, bool use_mfma, hipStream_t st);
+hipError_t launch_zero(unsigned *p, int n, hipStream_t st);
 
 }  // namespace kvq

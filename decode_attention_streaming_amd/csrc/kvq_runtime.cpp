@@ -14,13 +14,15 @@
 #include <vector>
 
 #include "kvq_internal.h"
+#include "kvq_layout.h"
 
 namespace {
 
 thread_local std::string g_create_error = "no error";
 
-constexpr int kMaxSplits = 128;
+constexpr int kMaxPart = 256;  // partial entries per stream (splits + units)
 constexpr int kMaxG = 16;
+constexpr int kMaxTileElems = 16384;  // group_size * head_dim staged by the flush kernel
 
 struct LayerState {
     kvq::LayerDev dev;
@@ -31,7 +33,9 @@ struct LayerState {
 struct Plan {
     std::vector<LayerState> layers;
     size_t off_part = 0;
+    size_t off_cnt = 0;
     size_t total = 0;
+    int v_tiled = 0;
 };
 
 int words_per_row(int d, int bits)
@@ -83,12 +87,18 @@ int plan_layout(const kvq_config *cfg, Plan *plan, std::string *err)
         return fail(KVQ_EINVAL, "q_dtype must be KVQ_F32, KVQ_F16 or KVQ_BF16");
     if (cfg->residual_len < cfg->group_size)
         return fail(KVQ_EINVAL, "residual_len (%d) < group_size (%d)", cfg->residual_len, cfg->group_size);
+    if (static_cast<long>(cfg->group_size) * cfg->head_dim > kMaxTileElems)
+        return fail(KVQ_EUNSUPPORTED, "group_size * head_dim = %ld exceeds %d", 
+                    static_cast<long>(cfg->group_size) * cfg->head_dim, kMaxTileElems);
 
     const size_t BH = static_cast<size_t>(cfg->batch) * cfg->n_kv_heads;
     const int D = cfg->head_dim, G = cfg->group_size;
     const size_t A = KVQ_WORKSPACE_ALIGN;
     size_t off = 0;
     plan->layers.assign(cfg->n_layers, LayerState());
+    // V codes use the matrix-core tile layout when groups are whole 32-token blocks
+    plan->v_tiled = (G % 32 == 0) ? 1 : 0;
+    const int cap_unit = G;
     for (int l = 0; l < cfg->n_layers; ++l) {
         const kvq_layer_cfg &lc = cfg->layers[l];
         if (!valid_pair(lc.k_bits, lc.v_bits))
@@ -99,6 +109,7 @@ int plan_layout(const kvq_config *cfg, Plan *plan, std::string *err)
         d.kb = lc.k_bits;
         d.vb = lc.v_bits;
         d.G = G;
+        d.v_tiled = plan->v_tiled;
         if (d.kb == 16) {
             d.R = cfg->max_context;
             d.capq = G;  // unused
@@ -109,7 +120,7 @@ int plan_layout(const kvq_config *cfg, Plan *plan, std::string *err)
                 return fail(KVQ_EINVAL, "layer %d: residual_len (%d) < group_size (%d)", l, d.R, G);
             if (d.R < 0 || d.R > cfg->max_context + G)
                 return fail(KVQ_EINVAL, "layer %d: residual_len %d out of range", l, d.R);
-            d.capq = (cfg->max_context + G - 1) / G * G;
+            d.capq = (cfg->max_context + cap_unit - 1) / cap_unit * cap_unit;
             d.wk = words_per_row(D, d.kb);
             d.wv = words_per_row(D, d.vb);
         }
@@ -129,7 +140,9 @@ int plan_layout(const kvq_config *cfg, Plan *plan, std::string *err)
         off = align_up(off + BH * static_cast<size_t>(d.R) * D * 2, A);
     }
     plan->off_part = off;
-    off = align_up(off + static_cast<size_t>(cfg->batch) * cfg->n_q_heads * kMaxSplits * (D + 2) * 4, A);
+    off = align_up(off + static_cast<size_t>(cfg->batch) * cfg->n_q_heads * kMaxPart * (D + 4) * 4, A);
+    plan->off_cnt = off;
+    off = align_up(off + BH * 4, A);
     plan->total = off;
     return KVQ_OK;
 }
@@ -146,6 +159,7 @@ struct kvq_handle {
     int cu_count = 0;
     int last_splits = 0, last_variant = -1;
     bool touched = false;  // device work was enqueued
+    bool counters_ready = false;
     std::string err = "no error";
 
     int fail(int code, const char *fmt, ...)
@@ -263,6 +277,8 @@ int kvq_append(kvq_handle *h, int layer, const void *k_new, const void *v_new, i
     const int D = h->cfg.head_dim;
     const int bf16 = h->cfg.kv_dtype == KVQ_BF16;
     hipError_t e;
+    const int t_first = Tq1 > N0 ? Tq1 : N0;
+    const bool fuse_ring = Tq1 > Tq0 && n_new == 1 && N1 > t_first;
     if (Tq1 > Tq0) {
         kvq::FlushArgs fa;
         fa.L = d;
@@ -275,12 +291,12 @@ int kvq_append(kvq_handle *h, int layer, const void *k_new, const void *v_new, i
         fa.n_groups = (Tq1 - Tq0) / d.G;
         fa.BH = h->BH();
         fa.kv_bf16 = bf16;
+        fa.ring_after = fuse_ring ? 1 : 0;
         e = kvq::launch_flush(fa, h->stream);
         if (e != hipSuccess)
             return h->dev_fail(e, "flush launch");
     }
-    const int t_first = Tq1 > N0 ? Tq1 : N0;
-    if (N1 > t_first) {
+    if (N1 > t_first && !fuse_ring) {
         kvq::RingArgs ra;
         ra.L = d;
         ra.k_new = static_cast<const uint16_t *>(k_new);
@@ -322,27 +338,21 @@ int kvq_decode_attention(kvq_handle *h, int layer, const void *q, float *out)
         h->cu_count = n > 0 ? n : 256;
     }
     const int D = h->cfg.head_dim, BH = h->BH();
-    // splits: enough workgroups for about two per compute unit, >= 64 tokens each
-    int S = (2 * h->cu_count + BH - 1) / BH;
-    const char *env = getenv("KVQ_SPLITS");
-    if (env && atoi(env) > 0)
-        S = atoi(env);
-    const int max_by_len = (s.N + 63) / 64;
-    if (S > max_by_len)
-        S = max_by_len;
-    if (S > kMaxSplits)
-        S = kMaxSplits;
-    if (S < 1)
-        S = 1;
-    int tps = (s.N + S - 1) / S;
-    tps = (tps + 15) / 16 * 16;
-    S = (s.N + tps - 1) / tps;
-
+    const kvq::LayerDev &d = s.dev;
+    hipError_t e;
+    unsigned *counters = reinterpret_cast<unsigned *>(h->ws + h->plan.off_cnt);
+    if (!h->counters_ready) {
+        e = kvq::launch_zero(counters, BH, h->stream);
+        if (e != hipSuccess)
+            return h->dev_fail(e, "counter init");
+        h->counters_ready = true;
+    }
     kvq::AttnArgs a;
-    a.L = s.dev;
+    a.L = d;
     a.q = q;
     a.out = out;
     a.part = reinterpret_cast<float *>(h->ws + h->plan.off_part);
+    a.counters = counters;
     a.q_dtype = h->cfg.q_dtype;
     a.kv_bf16 = h->cfg.kv_dtype == KVQ_BF16;
     a.D = D;
@@ -351,17 +361,60 @@ int kvq_decode_attention(kvq_handle *h, int layer, const void *q, float *out)
     a.N = s.N;
     a.Tq = s.Tq;
     a.BH = BH;
-    a.n_splits = S;
-    a.tps = tps;
     a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D)));
-    hipError_t e = kvq::launch_attention_valu(a, h->stream);
+    const char *force_valu = getenv("KVQ_FORCE_VALU");
+    const bool use_mfma = d.v_tiled && d.kb != 16 && kvq::mfma_supported(d.kb, d.vb, D) && s.Tq > 0 &&
+                          !(force_valu && atoi(force_valu) > 0);
+    int S = 0;
+    if (use_mfma) {
+        // matrix-core units over whole groups, vector-ALU workgroups over the
+        // recent tokens (256 per workgroup)
+        const int n_groups = s.Tq / d.G;
+        const int Tr = s.N - s.Tq;
+        a.valu_beg = s.Tq;
+        a.valu_tps = 256;
+        a.valu_wgs = (Tr + 255) / 256;
+        long ug = static_cast<long>(n_groups) * BH / (8L * h->cu_count);
+        const char *env = getenv("KVQ_UNIT_GROUPS");
+        if (env && atoi(env) > 0)
+            ug = atoi(env);
+        if (ug < 1)
+            ug = 1;
+        if (ug > n_groups)
+            ug = n_groups;
+        while ((n_groups + ug - 1) / ug + a.valu_wgs > kMaxPart)
+            ++ug;
+        a.unit_groups = static_cast<int>(ug);
+        a.units_q = static_cast<int>((n_groups + ug - 1) / ug);
+        a.mfma_wgs = (a.units_q + 3) / 4;
+        S = a.units_q;
+    } else {
+        // splits: about two workgroups per compute unit, >= 64 tokens each
+        S = (2 * h->cu_count + BH - 1) / BH;
+        const char *env = getenv("KVQ_SPLITS");
+        if (env && atoi(env) > 0)
+            S = atoi(env);
+        const int max_by_len = (s.N + 63) / 64;
+        if (S > max_by_len)
+            S = max_by_len;
+        if (S > kMaxPart)
+            S = kMaxPart;
+        if (S < 1)
+            S = 1;
+        int tps = (s.N + S - 1) / S;
+        tps = (tps + 127) / 128 * 128;  // whole LDS tiles and 32-token V blocks
+        S = (s.N + tps - 1) / tps;
+        a.valu_beg = 0;
+        a.valu_tps = tps;
+        a.valu_wgs = S;
+        a.units_q = a.unit_groups = a.mfma_wgs = 0;
+    }
+    a.n_part = a.units_q + a.valu_wgs;
+    e = kvq::launch_attention(a, use_mfma, h->stream);
     if (e != hipSuccess)
         return h->dev_fail(e, "attention launch");
-    e = kvq::launch_merge(a, h->stream);
-    if (e != hipSuccess)
-        return h->dev_fail(e, "merge launch");
     h->last_splits = S;
-    h->last_variant = 0;
+    h->last_variant = use_mfma ? 1 : 0;
     h->touched = true;
     return KVQ_OK;
 }
@@ -435,10 +488,30 @@ int kvq_export_layer(kvq_handle *h, int layer, uint32_t *k_words, float *k_scale
                 (e = hipMemcpy(k_words + static_cast<size_t>(bh) * Tq * d.wk, d.k_words + row0 * d.wk,
                                static_cast<size_t>(Tq) * d.wk * 4, hipMemcpyDeviceToHost)) != hipSuccess)
                 return h->dev_fail(e, "export k_words");
-            if (v_words &&
-                (e = hipMemcpy(v_words + static_cast<size_t>(bh) * Tq * d.wv, d.v_words + row0 * d.wv,
-                               static_cast<size_t>(Tq) * d.wv * 4, hipMemcpyDeviceToHost)) != hipSuccess)
-                return h->dev_fail(e, "export v_words");
+            if (v_words) {
+                uint32_t *dst = v_words + static_cast<size_t>(bh) * Tq * d.wv;
+                if (d.v_tiled) {
+                    // 32-token operand tiles -> token-major rows
+                    std::vector<uint32_t> tiles(static_cast<size_t>(Tq) * d.wv);
+                    if ((e = hipMemcpy(tiles.data(), d.v_words + row0 * d.wv, tiles.size() * 4,
+                                       hipMemcpyDeviceToHost)) != hipSuccess)
+                        return h->dev_fail(e, "export v_words");
+                    memset(dst, 0, tiles.size() * 4);
+                    const int epw = 32 / d.vb;
+                    const uint32_t mask = (1u << d.vb) - 1u;
+                    for (int t = 0; t < Tq; ++t)
+                        for (int c = 0; c < D; ++c) {
+                            int word, bit;
+                            kvq::v_tile_pos(t & 31, c, d.vb, D, &word, &bit);
+                            const uint32_t code =
+                                (tiles[static_cast<size_t>(t & ~31) * d.wv + word] >> bit) & mask;
+                            dst[static_cast<size_t>(t) * d.wv + c / epw] |= code << (d.vb * (c % epw));
+                        }
+                } else if ((e = hipMemcpy(dst, d.v_words + row0 * d.wv, static_cast<size_t>(Tq) * d.wv * 4,
+                                          hipMemcpyDeviceToHost)) != hipSuccess) {
+                    return h->dev_fail(e, "export v_words");
+                }
+            }
             if (k_scale || k_zero) {
                 std::vector<float> m(static_cast<size_t>(ng) * 2 * D);
                 if ((e = hipMemcpy(m.data(), d.k_meta + static_cast<size_t>(bh) * ngcap * 2 * D,

@@ -217,3 +217,11 @@ def bits16(t):
 
 def as_f64(t):
     return t.detach().to(torch.float64).cpu().numpy()
+
+
+def queries(w: Workload, layer: int, n_steps: int, device, seed=0):
+    """q for n_steps decode steps of one layer: [n_steps, B, Hq, d]."""
+    g = _gen(device, seed, "qs", w.cid, layer, n_steps)
+    q = torch.randn((n_steps, w.batch, w.n_q_heads, w.head_dim), generator=g, device=device,
+                    dtype=torch.float32)
+    return q.to(_TORCH[w.q_dtype]).contiguous()

@@ -53,6 +53,12 @@ CASES = {
     "k8v8_G1_R1": (1, 4, 1, 128, 8, 8, 1, 1, 80, "f16", "f32", [70, 1]),
     "k4v2_G8_R9_tokenwise": (1, 2, 1, 64, 4, 2, 8, 9, 64, "f16", "f32", [1] * 40),
     "k2v8_g3": (3, 9, 3, 128, 2, 8, 16, 24, 200, "bf16", "f16", [5, 150, 20]),
+    # groups of whole 32-token blocks: the matrix-core path
+    "mfma_k2v8_g16_d256": (1, 16, 1, 256, 2, 8, 32, 32, 300, "bf16", "f32", [290, 1]),
+    "mfma_k8v2_g1": (2, 2, 2, 128, 8, 2, 32, 48, 400, "f16", "f16", [330, 5]),
+    "mfma_k4v4_g8_G128": (1, 8, 1, 128, 4, 4, 128, 128, 700, "bf16", "bf16", [600, 3]),
+    "mfma_k2v4_g5_d64": (2, 10, 2, 64, 2, 4, 64, 70, 500, "f16", "f32", [400, 30]),
+    "mfma_k8v8_g4_long": (1, 4, 1, 128, 8, 8, 32, 32, 2100, "bf16", "bf16", [2050, 1]),
 }
 
 
@@ -173,3 +179,14 @@ def test_multi_layer_table():
         torch.cuda.synchronize()
         compare_export(cache.export(l), orc.export())
         check_attention(out, orc.attention(q_streams(q, w.g)), w.g, what="layer %d" % l)
+
+
+@pytest.mark.parametrize("ug", ["1", "3", "40"])
+def test_unit_sizes_and_column_merge(ug, monkeypatch):
+    """Matrix-core units of 1, 3 and 40 groups: windows holding up to 16 / g
+    groups per column set, merged per head at the end of each unit."""
+    monkeypatch.setenv("KVQ_UNIT_GROUPS", ug)
+    for (Hq, Hkv, kb, vb, G) in [(2, 2, 2, 2, 32), (16, 4, 4, 2, 32), (16, 2, 8, 4, 64)]:
+        w = ad_hoc_workload(400 + Hq + kb, 2, Hq, Hkv, 128, kb, vb, G, G, 1700, "bf16", "bf16")
+        print("unit groups", ug, "g", Hq // Hkv, "pair", (kb, vb), flush=True)
+        _run_case(w, [1650, 1])
