@@ -76,15 +76,26 @@ __device__ __forceinline__ const uint16_t *src_row(const FlushArgs &a, const uin
     return fresh + (static_cast<size_t>(bh) * a.n_new + (t - a.N0)) * a.D;
 }
 
-// Copy the G x D tile of tokens [t0, t0 + G) into LDS.
+// Copy the G x D tile of tokens [t0, t0 + G) into LDS: every thread issues all
+// of its 16-byte loads before storing any (one memory round trip).
 __device__ __forceinline__ void stage(const FlushArgs &a, const uint16_t *ring, const uint16_t *fresh,
                                       int bh, int t0, uint16_t *tile)
 {
-    const int D = a.D, chunks = D / 8;
-    for (int it = threadIdx.x; it < a.L.G * chunks; it += kThreads) {
-        const int i = it / chunks, ch = it % chunks;
-        const uint16_t *row = src_row(a, ring, fresh, bh, t0 + i);
-        *reinterpret_cast<uint4 *>(tile + i * D + ch * 8) = *reinterpret_cast<const uint4 *>(row + ch * 8);
+    constexpr int MAXI = kTileElems / 8 / kThreads;  // 16-byte chunks per thread at most
+    const int D = a.D, chunks = D / 8, n = a.L.G * chunks;
+    uint4 v[MAXI];
+#pragma unroll
+    for (int k = 0; k < MAXI; ++k) {
+        const int it = threadIdx.x + k * kThreads;
+        if (it < n)
+            v[k] = *reinterpret_cast<const uint4 *>(src_row(a, ring, fresh, bh, t0 + it / chunks) +
+                                                    (it % chunks) * 8);
+    }
+#pragma unroll
+    for (int k = 0; k < MAXI; ++k) {
+        const int it = threadIdx.x + k * kThreads;
+        if (it < n)
+            *reinterpret_cast<uint4 *>(tile + (it / chunks) * D + (it % chunks) * 8) = v[k];
     }
 }
 

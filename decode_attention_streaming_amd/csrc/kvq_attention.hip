@@ -46,14 +46,26 @@ bool mfma_supported(int kb, int vb, int D)
     return bits && (D == 64 || D == 128 || D == 256);
 }
 
+// a 16-bit layer runs only recent-token units: any instantiation serves
+static AttnArgs as_plain(const AttnArgs &a)
+{
+    AttnArgs b = a;
+    if (b.L.kb == 16) {
+        b.L.kb = 2;
+        b.L.vb = 2;
+    }
+    return b;
+}
+
 hipError_t launch_attention(const AttnArgs &a, bool use_mfma, hipStream_t st)
 {
     if (use_mfma) {
+        const AttnArgs b = as_plain(a);
         if (a.D == 64)
-            return launch_mfma_d64(a, st);
+            return launch_mfma_d64(b, st);
         if (a.D == 128)
-            return launch_mfma_d128(a, st);
-        return launch_mfma_d256(a, st);
+            return launch_mfma_d128(b, st);
+        return launch_mfma_d256(b, st);
     }
     dim3 grid(a.valu_wgs, a.BH);
     const size_t lds = valu_lds_bytes(a.g, a.D);

@@ -23,6 +23,20 @@ constexpr int kMaxG = 16;
 // Partial entry of one (stream, split, head): o[D], m, l, 2 pad floats.
 __device__ __forceinline__ int part_stride(int D) { return D + 4; }
 
+// Partials pass between workgroups of one launch, which may run on different
+// XCDs with separate L2 caches.  They are written and read with agent-scope
+// atomic accesses, which are coherent at the device level, so the hand-off
+// needs no whole-cache write-back or invalidation.
+__device__ __forceinline__ void part_store(float *p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float part_load(const float *p)
+{
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ float widen16(uint16_t x, int bf16)
 {
     if (bf16)
@@ -86,28 +100,83 @@ __host__ __device__ inline int valu_lds_bytes(int g, int D)
     return (g * D + g * TT + 4 * 4 * kMaxG) * 4 + 2 * 16384;
 }
 
-// Cooperative copy of n 32-bit words (16-byte aligned on both sides when n is a
-// multiple of 4) from global memory into LDS.
+// Cooperative copies into LDS.  Every thread first issues all of its global
+// loads (up to MAXI 16-byte chunks, predicated), then stores them: one memory
+// round trip per stage instead of one per loop iteration.
+
+// n 32-bit words from src (16-byte aligned when n is a multiple of 4).
+template <int MAXI>
 __device__ __forceinline__ void stage_words(uint32_t *dst, const uint32_t *src, int n)
 {
     if ((n & 3) == 0 && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
-        for (int i = threadIdx.x; i < n / 4; i += kAttnThreads)
-            reinterpret_cast<uint4 *>(dst)[i] = reinterpret_cast<const uint4 *>(src)[i];
+        uint4 v[MAXI];
+#pragma unroll
+        for (int k = 0; k < MAXI; ++k) {
+            const int i = threadIdx.x + k * kAttnThreads;
+            if (i < n / 4)
+                v[k] = reinterpret_cast<const uint4 *>(src)[i];
+        }
+#pragma unroll
+        for (int k = 0; k < MAXI; ++k) {
+            const int i = threadIdx.x + k * kAttnThreads;
+            if (i < n / 4)
+                reinterpret_cast<uint4 *>(dst)[i] = v[k];
+        }
     } else {
-        for (int i = threadIdx.x; i < n; i += kAttnThreads)
-            dst[i] = src[i];
+        uint32_t v[4 * MAXI];
+#pragma unroll
+        for (int k = 0; k < 4 * MAXI; ++k) {
+            const int i = threadIdx.x + k * kAttnThreads;
+            if (i < n)
+                v[k] = src[i];
+        }
+#pragma unroll
+        for (int k = 0; k < 4 * MAXI; ++k) {
+            const int i = threadIdx.x + k * kAttnThreads;
+            if (i < n)
+                dst[i] = v[k];
+        }
     }
 }
 
-// Cooperative copy of ring rows of tokens [t0, t0 + n) into LDS [n][D].
-template <int D>
+// Ring rows of tokens [t0, t0 + n) into LDS [n][D] (n * D / 8 <= MAXI * 256).
+template <int D, int MAXI>
 __device__ __forceinline__ void stage_ring(uint16_t *dst, const uint16_t *ring, int R, int t0, int n)
 {
     constexpr int CH = D / 8;  // 16-byte chunks per row
-    for (int it = threadIdx.x; it < n * CH; it += kAttnThreads) {
-        const int i = it / CH, ch = it % CH;
-        reinterpret_cast<uint4 *>(dst + i * D)[ch] =
-            reinterpret_cast<const uint4 *>(ring + static_cast<size_t>((t0 + i) % R) * D)[ch];
+    uint4 v[MAXI];
+#pragma unroll
+    for (int k = 0; k < MAXI; ++k) {
+        const int it = threadIdx.x + k * kAttnThreads;
+        if (it < n * CH)
+            v[k] = reinterpret_cast<const uint4 *>(ring + static_cast<size_t>((t0 + it / CH) % R) * D)[it % CH];
+    }
+#pragma unroll
+    for (int k = 0; k < MAXI; ++k) {
+        const int it = threadIdx.x + k * kAttnThreads;
+        if (it < n * CH)
+            reinterpret_cast<uint4 *>(dst + (it / CH) * D)[it % CH] = v[k];
+    }
+}
+
+// q of the g heads of stream (b, kvh), prescaled, into LDS [g][D].
+__device__ __forceinline__ void stage_q(const AttnArgs &a, int b, int kvh, float *q_l)
+{
+    constexpr int MAXQ = kMaxG * 256 / kAttnThreads;  // elements per thread at most
+    const int n = a.g * a.D;
+    const size_t base = (static_cast<size_t>(b) * a.Hkv * a.g + kvh * a.g) * a.D;
+    float v[MAXQ];
+#pragma unroll
+    for (int k = 0; k < MAXQ; ++k) {
+        const int i = threadIdx.x + k * kAttnThreads;
+        if (i < n)
+            v[k] = load_q(a.q, a.q_dtype, base + i);
+    }
+#pragma unroll
+    for (int k = 0; k < MAXQ; ++k) {
+        const int i = threadIdx.x + k * kAttnThreads;
+        if (i < n)
+            q_l[i] = v[k] * a.scale_log2;
     }
 }
 
@@ -138,11 +207,7 @@ __device__ void valu_range(const AttnArgs &a, int bh, int t_beg, int t_end, int 
     const LayerDev &L = a.L;
     const int bf = a.kv_bf16;
 
-    for (int i = tid; i < g * D; i += kAttnThreads) {
-        const int h = i / D, c = i % D;
-        const size_t qi = (static_cast<size_t>(b) * a.Hkv * g + kvh * g + h) * D + c;
-        q_l(h, c) = load_q(a.q, a.q_dtype, qi) * a.scale_log2;
-    }
+    stage_q(a, b, kvh, q_lds);
 
     const int oc = tid % D, oh0 = tid / D, hstep = kAttnThreads / D;
     float o[GM], m[GM], l[GM];
@@ -161,13 +226,13 @@ __device__ void valu_range(const AttnArgs &a, int bh, int t_beg, int t_end, int 
         const int nt = tend - tile;
         __syncthreads();  // previous tile's LDS reads are done (and q is staged)
         if (quant) {
-            stage_words(k_tile, L.k_words + (row0 + tile) * L.wk, nt * L.wk);
-            stage_words(v_tile, L.v_words + (row0 + tile) * L.wv, nt * L.wv);
+            stage_words<4>(k_tile, L.k_words + (row0 + tile) * L.wk, nt * L.wk);
+            stage_words<4>(v_tile, L.v_words + (row0 + tile) * L.wv, nt * L.wv);
         } else {
-            stage_ring<D>(reinterpret_cast<uint16_t *>(k_tile), L.ring_k + static_cast<size_t>(bh) * L.R * D,
-                          L.R, tile, nt);
-            stage_ring<D>(reinterpret_cast<uint16_t *>(v_tile), L.ring_v + static_cast<size_t>(bh) * L.R * D,
-                          L.R, tile, nt);
+            stage_ring<D, 4>(reinterpret_cast<uint16_t *>(k_tile),
+                             L.ring_k + static_cast<size_t>(bh) * L.R * D, L.R, tile, nt);
+            stage_ring<D, 4>(reinterpret_cast<uint16_t *>(v_tile),
+                             L.ring_v + static_cast<size_t>(bh) * L.R * D, L.R, tile, nt);
         }
         // per-thread metadata while the tile lands
         const int ti = tid / P, part = tid % P, c0 = part * CPT;
@@ -307,10 +372,10 @@ __device__ void valu_range(const AttnArgs &a, int bh, int t_beg, int t_end, int 
     for (int k = 0; k < GM; ++k) {
         const int h = oh0 + k * hstep;
         if (h < g) {
-            part[h * ps + oc] = o[k];
+            part_store(part + h * ps + oc, o[k]);
             if (oc == 0) {
-                part[h * ps + D] = m[h];
-                part[h * ps + D + 1] = l[h];
+                part_store(part + h * ps + D, m[h]);
+                part_store(part + h * ps + D + 1, l[h]);
             }
         }
     }
@@ -319,44 +384,210 @@ __device__ void valu_range(const AttnArgs &a, int bh, int t_beg, int t_end, int 
 #undef red
 }
 
+// Dynamic LDS bytes of residual_range<D>(): q[g][D], scores/weights[g][TT],
+// K and V tiles (16 KB each), per-head state.
+__host__ __device__ inline int residual_lds_bytes(int g, int D)
+{
+    const int TT = 8192 / D;
+    return (g * D + g * TT + 4 * kMaxG) * 4 + 2 * 16384;
+}
+
+// Vector-ALU attention of one workgroup over recent (16-bit) tokens
+// [t_beg, t_end) of stream bh, for any g <= 16 with few registers: tiles of TT
+// tokens staged in LDS; P threads per token for the scores; per-head softmax
+// bookkeeping by one thread per head; P.V by one thread per (channel, head).
+template <int D>
+__device__ void residual_range(const AttnArgs &a, int bh, int t_beg, int t_end, int slot, float *smem)
+{
+    constexpr int TT = valu_tile<D>();
+    constexpr int P = kAttnThreads / TT;
+    constexpr int CPT = D / P;  // 32
+    constexpr int OS = (kMaxG * D + kAttnThreads - 1) / kAttnThreads;  // output slots per thread
+    const int tid = threadIdx.x;
+    const int g = a.g;
+    float *q_l = smem;                       // [g][D]
+    float *s_l = smem + g * D;               // [g][TT] scores, then weights
+    float *st = s_l + g * TT;                // [4][kMaxG]: m, l, alpha
+    uint16_t *k_tile = reinterpret_cast<uint16_t *>(st + 4 * kMaxG);
+    uint16_t *v_tile = k_tile + 8192;
+    const int b = bh / a.Hkv, kvh = bh % a.Hkv;
+    const LayerDev &L = a.L;
+    const int bf = a.kv_bf16;
+
+    stage_q(a, b, kvh, q_l);
+    if (tid < g) {
+        st[tid] = -INFINITY;        // m
+        st[kMaxG + tid] = 0.0f;     // l
+    }
+    float o[OS];
+#pragma unroll
+    for (int k = 0; k < OS; ++k)
+        o[k] = 0.0f;
+
+    for (int tile = t_beg; tile < t_end; tile += TT) {
+        const int nt = min(TT, t_end - tile);
+        __syncthreads();
+        stage_ring<D, 4>(k_tile, L.ring_k + static_cast<size_t>(bh) * L.R * D, L.R, tile, nt);
+        stage_ring<D, 4>(v_tile, L.ring_v + static_cast<size_t>(bh) * L.R * D, L.R, tile, nt);
+        __syncthreads();
+        // scores, four heads at a time
+        const int ti = tid / P, part = tid % P, c0 = part * CPT;
+        for (int h0 = 0; h0 < g; h0 += 4) {
+            float sc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (ti < nt) {
+                const uint16_t *row = k_tile + ti * D + c0;
+#pragma unroll 8
+                for (int i = 0; i < CPT; ++i) {
+                    const float x = widen16(row[i], bf);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        if (h0 + k < g)
+                            sc[k] = __builtin_fmaf(q_l[(h0 + k) * D + c0 + i], x, sc[k]);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                for (int off = 1; off < P; off <<= 1)
+                    sc[k] += __shfl_xor(sc[k], off, 64);
+            if (ti < nt && part == 0)
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    if (h0 + k < g)
+                        s_l[(h0 + k) * TT + ti] = sc[k];
+        }
+        __syncthreads();
+        // per head (one wave each, lanes over the tile's tokens): max, weights, normalizer
+        {
+            const int lane = tid & 63, wave = tid >> 6;
+            for (int h = wave; h < g; h += kAttnThreads / 64) {
+                float tm = -INFINITY;
+                for (int i = lane; i < nt; i += 64)
+                    tm = fmaxf(tm, s_l[h * TT + i]);
+                tm = wave_max(tm);
+                const float m_old = st[h], m_new = fmaxf(m_old, tm);
+                float ls = 0.0f;
+                for (int i = lane; i < TT; i += 64) {
+                    const float p = i < nt ? exp2f(s_l[h * TT + i] - m_new) : 0.0f;
+                    s_l[h * TT + i] = p;
+                    ls += p;
+                }
+                ls = wave_sum(ls);
+                if (lane == 0) {
+                    const float alpha = exp2f(m_old - m_new);
+                    st[h] = m_new;
+                    st[kMaxG + h] = st[kMaxG + h] * alpha + ls;
+                    st[2 * kMaxG + h] = alpha;
+                }
+            }
+        }
+        __syncthreads();
+        // P.V: all TT tokens (weights of the tile's missing tokens are 0)
+#pragma unroll
+        for (int k = 0; k < OS; ++k) {
+            const int idx = tid + k * kAttnThreads;
+            if (idx < g * D) {
+                const int h = idx / D, c = idx % D;
+                float acc[4] = {o[k] * st[2 * kMaxG + h], 0.0f, 0.0f, 0.0f};
+#pragma unroll 16
+                for (int i = 0; i < TT; ++i) {
+                    const float x = i < nt ? widen16(v_tile[i * D + c], bf) : 0.0f;
+                    acc[i & 3] = __builtin_fmaf(s_l[h * TT + i], x, acc[i & 3]);
+                }
+                o[k] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+            }
+        }
+    }
+    __syncthreads();
+    const int ps = part_stride(D);
+    float *part = a.part + (static_cast<size_t>(bh) * a.n_part + slot) * g * ps;
+#pragma unroll
+    for (int k = 0; k < OS; ++k) {
+        const int idx = tid + k * kAttnThreads;
+        if (idx < g * D) {
+            const int h = idx / D, c = idx % D;
+            part_store(part + h * ps + c, o[k]);
+            if (c == 0) {
+                part_store(part + h * ps + D, st[h]);
+                part_store(part + h * ps + D + 1, st[kMaxG + h]);
+            }
+        }
+    }
+}
+
 // Called by every workgroup at its end: the last one of stream bh to arrive
 // merges the n_part partial entries, out = sum_s 2^(m_s - M) o_s /
 // sum_s 2^(m_s - M) l_s, M = max_s m_s, and re-arms the stream's counter.
+// The merge first gathers every (m, l) into LDS with one batch of loads, then
+// reads the o values with all loads of a thread issued together.
+constexpr int kMergeMax = 2048;  // (entry, head) pairs the merge stages in LDS
+
 __device__ __forceinline__ void arrive_and_merge(const AttnArgs &a, int bh, unsigned n_wgs)
 {
     __shared__ int s_last;
-    __threadfence();
+    __shared__ float s_w[kMergeMax];  // m, then weight 2^(m_s - M_h), of entry s, head h
+    __shared__ float s_l[kMergeMax];  // l of entry s, head h
+    __shared__ float s_inv[kMaxG];    // 1 / sum_s w l
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are complete
     __syncthreads();
     if (threadIdx.x == 0) {
-        const unsigned prev = atomicAdd(a.counters + bh, 1u);
+        const unsigned prev =
+            __hip_atomic_fetch_add(a.counters + bh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = (prev == n_wgs - 1);
     }
     __syncthreads();
     if (!s_last)
         return;
-    __threadfence();
     const int D = a.D, g = a.g, P = a.n_part, ps = part_stride(D);
     const int b = bh / a.Hkv, kvh = bh % a.Hkv;
     const float *part = a.part + static_cast<size_t>(bh) * P * g * ps;
-    for (int i = threadIdx.x; i < g * D; i += kAttnThreads) {
-        const int h = i / D, c = i % D;
-        float M = -INFINITY;
-#pragma unroll 8
-        for (int s = 0; s < P; ++s)
-            M = fmaxf(M, part[(s * g + h) * ps + D]);
-        float num = 0.0f, den = 0.0f;
-#pragma unroll 8
-        for (int s = 0; s < P; ++s) {
-            const float *e = part + (s * g + h) * ps;
-            const float ms = e[D];
-            const float w = (ms == -INFINITY) ? 0.0f : exp2f(ms - M);
-            num = __builtin_fmaf(w, e[c], num);
-            den = __builtin_fmaf(w, e[D + 1], den);
-        }
-        a.out[(static_cast<size_t>(b) * a.Hkv * g + kvh * g + h) * D + c] = num / den;
+    const int tid = threadIdx.x;
+    // (1) m and l of every (entry, head) into LDS
+    for (int i = tid; i < P * g; i += kAttnThreads) {
+        s_w[i] = part_load(part + i * ps + D);
+        s_l[i] = part_load(part + i * ps + D + 1);
     }
-    if (threadIdx.x == 0)
-        a.counters[bh] = 0u;
+    __syncthreads();
+    // (2) per head (one wave each, lanes over entries): M, weights, normalizer
+    {
+        const int lane = tid & 63, wave = tid >> 6;
+        for (int h = wave; h < g; h += kAttnThreads / 64) {
+            float M = -INFINITY;
+            for (int s2 = lane; s2 < P; s2 += 64)
+                M = fmaxf(M, s_w[s2 * g + h]);
+            M = wave_max(M);
+            float den = 0.0f;
+            for (int s2 = lane; s2 < P; s2 += 64) {
+                const float ms = s_w[s2 * g + h];
+                const float w = (ms == -INFINITY) ? 0.0f : exp2f(ms - M);
+                s_w[s2 * g + h] = w;
+                den = __builtin_fmaf(w, s_l[s2 * g + h], den);
+            }
+            den = wave_sum(den);
+            if (lane == 0)
+                s_inv[h] = 1.0f / den;
+        }
+    }
+    __syncthreads();
+    // (3) outputs: each thread's loads for one (head, channel) are issued together
+    for (int i = tid; i < g * D; i += kAttnThreads) {
+        const int h = i / D, c = i % D;
+        float num = 0.0f;
+        int s2 = 0;
+        for (; s2 + 8 <= P; s2 += 8) {
+            float v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                v[k] = part_load(part + ((s2 + k) * g + h) * ps + c);
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                num = __builtin_fmaf(s_w[(s2 + k) * g + h], v[k], num);
+        }
+        for (; s2 < P; ++s2)
+            num = __builtin_fmaf(s_w[s2 * g + h], part_load(part + (s2 * g + h) * ps + c), num);
+        a.out[(static_cast<size_t>(b) * a.Hkv * g + kvh * g + h) * D + c] = num * s_inv[h];
+    }
+    if (tid == 0)
+        __hip_atomic_store(a.counters + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace kvq

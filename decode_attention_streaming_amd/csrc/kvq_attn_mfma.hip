@@ -33,11 +33,13 @@ namespace kvq {
 namespace {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 
 union Frag {
     uint32_t u[4];
     half8_t h;
+    bf16x8_t b;
 };
 
 // Lazy rescale threshold (log2 units): the running max only moves when a score
@@ -52,6 +54,24 @@ constexpr int kWShift = 7;
 __device__ __forceinline__ f4_t mfma(const Frag &a, const Frag &b, f4_t c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a.h, b.h, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f4_t mfma_bf16(const Frag &a, const Frag &b, f4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.b, b.b, c, 0, 0, 0);
+}
+
+// fp32 pair -> three bfloat16 pairs with x ~= p1 + p2 + p3 (truncations; about
+// 24 significant bits)
+__device__ __forceinline__ void split3_bf16(float x0, float x1, uint32_t &p1, uint32_t &p2, uint32_t &p3)
+{
+    const uint32_t u0 = __float_as_uint(x0) & 0xFFFF0000u, u1 = __float_as_uint(x1) & 0xFFFF0000u;
+    const float r0 = x0 - __uint_as_float(u0), r1 = x1 - __uint_as_float(u1);
+    const uint32_t v0 = __float_as_uint(r0) & 0xFFFF0000u, v1 = __float_as_uint(r1) & 0xFFFF0000u;
+    const float s0 = r0 - __uint_as_float(v0), s1 = r1 - __uint_as_float(v1);
+    p1 = (u0 >> 16) | u1;
+    p2 = (v0 >> 16) | v1;
+    p3 = (__float_as_uint(s0) >> 16) | (__float_as_uint(s1) & 0xFFFF0000u);
 }
 
 // fp32 pair -> (hi, lo) fp16 pairs with x ~= hi + lo
@@ -90,16 +110,73 @@ __device__ __forceinline__ void load_words(const uint32_t *p, uint32_t (&r)[N])
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
-// Register R of an unpacked code run: codes of 2 channels (or slots) as fp16
-// integers in the two halves.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c)
+{
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(m), "s"(c));
+    return r;
+}
+
+// Operand register R of a run of b-bit codes (P = 16 / b registers per word):
+// the codes in bits b*j and 16 + b*j of word R / P, j = R % P.  A code sitting
+// at bit offset e = (b * j) % 8 of its 16-bit half (after a shift by 8 when
+// b * j >= 8) is masked into the mantissa of 1024.0 and 1024 is subtracted, both
+// exact, leaving the fp16 integer code * 2^e.  The matching factor 2^-e is
+// applied to the other operand (class_exp()).
+template <int B>
+__device__ __forceinline__ constexpr int class_exp(int R)
+{
+    return (B * (R % (16 / B))) % 8;
+}
+
 template <int B, int N>
-__device__ __forceinline__ uint32_t code_reg(const uint32_t (&w)[N], int R)
+__device__ __forceinline__ uint32_t code_reg(const uint32_t (&w)[N], const uint32_t (&w8)[N], int R)
 {
     constexpr int P = 16 / B;
-    constexpr uint32_t M = ((1u << B) - 1u) * 0x00010001u;
-    const uint32_t biased = ((w[R / P] >> (B * (R % P))) & M) | 0x64006400u;  // 1024 + k
+    const int j = R % P;
+    const uint32_t src = (B * j >= 8) ? w8[R / P] : w[R / P];
+    const uint32_t mask = (((1u << B) - 1u) << class_exp<B>(R)) * 0x00010001u;
+    const uint32_t biased = and_or(src, mask, 0x64006400u);  // 1024 + code * 2^e
     const half2_t k = __builtin_bit_cast(half2_t, biased) - half2_t{1024.0f16, 1024.0f16};
     return __builtin_bit_cast(uint32_t, k);
+}
+
+template <int N>
+__device__ __forceinline__ void shift8(const uint32_t (&w)[N], uint32_t (&w8)[N])
+{
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        w8[i] = w[i] >> 8;
+}
+
+// n consecutive q values (fp32, fp16 or bf16) from a 16-byte aligned run.
+template <int N>
+__device__ __forceinline__ void load_q_run(const void *q, int dtype, size_t i0, float (&r)[N])
+{
+    if (dtype == 0) {
+        const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(q) + i0);
+#pragma unroll
+        for (int i = 0; i < N / 4; ++i) {
+            const float4 v = p[i];
+            r[4 * i] = v.x;
+            r[4 * i + 1] = v.y;
+            r[4 * i + 2] = v.z;
+            r[4 * i + 3] = v.w;
+        }
+    } else {
+        const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(q) + i0);
+        const int bf = dtype == 2;
+#pragma unroll
+        for (int i = 0; i < N / 8; ++i) {
+            const uint4 v = p[i];
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                r[8 * i + 2 * k] = widen16(static_cast<uint16_t>(w[k] & 0xFFFFu), bf);
+                r[8 * i + 2 * k + 1] = widen16(static_cast<uint16_t>(w[k] >> 16), bf);
+            }
+        }
+    }
 }
 
 __device__ __forceinline__ float xor_sum(float v)
@@ -115,6 +192,14 @@ __device__ __forceinline__ float xor_max(float v)
     v = fmaxf(v, __shfl_xor(v, 32, 64));
     return v;
 }
+
+// Block data of 32 tokens: K rows of both 16-token tiles, the V fragment and
+// the V meta (s, z) of this lane's 8 k-slot tokens.
+template <int KW, int FW>
+struct BlockData {
+    uint32_t k0[KW], k1[KW], v[FW];
+    float4 vm[4];
+};
 
 template <int KB, int VB, int D>
 __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane)
@@ -148,21 +233,17 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane)
     const uint32_t *vw_base = L.v_words + static_cast<size_t>(bh) * L.capq * L.wv + lane * FW;
     const float *vm_base = L.v_meta + static_cast<size_t>(bh) * L.capq * 2;
 
-    // block data: K rows of both 16-token tiles, V fragment, V meta of 8 tokens
-    uint32_t kr0[KW], kr1[KW], vf[FW];
-    float4 vm[4];
-    auto load_block = [&](int t0) {
-        load_words(kw_base + static_cast<size_t>(t0 + col) * L.wk, kr0);
-        load_words(kw_base + static_cast<size_t>(t0 + 16 + col) * L.wk, kr1);
-        load_words(vw_base + static_cast<size_t>(t0) * L.wv, vf);
+    auto load_block = [&](BlockData<KW, FW> &d, int t0) {
+        load_words(kw_base + static_cast<size_t>(t0 + col) * L.wk, d.k0);
+        load_words(kw_base + static_cast<size_t>(t0 + 16 + col) * L.wk, d.k1);
+        load_words(vw_base + static_cast<size_t>(t0) * L.wv, d.v);
         const float4 *m0 = reinterpret_cast<const float4 *>(vm_base + static_cast<size_t>(t0 + 4 * q) * 2);
         const float4 *m1 = reinterpret_cast<const float4 *>(vm_base + static_cast<size_t>(t0 + 16 + 4 * q) * 2);
-        vm[0] = m0[0];
-        vm[1] = m0[1];
-        vm[2] = m1[0];
-        vm[3] = m1[1];
+        d.vm[0] = m0[0];
+        d.vm[1] = m0[1];
+        d.vm[2] = m1[0];
+        d.vm[3] = m1[1];
     };
-    load_block(t_unit);
 
     float m_run = -INFINITY, l_run = 0.0f, zb_run = 0.0f;
     int E = -1000;  // running V-scale exponent: all weights are scaled by 2^-E
@@ -172,13 +253,11 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane)
         O[m] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
     Frag bhi[NC], blo[NC];
-    float bias = 0.0f;
-    int kexp = 0;
-    int w_first = t_unit;  // first token of the current window
+    float bias = 0.0f, kscale = 0.0f;
+    int w_first = t_unit;
     bool act_win = false;
 
-    for (int bi = 0; bi < nblk; ++bi) {
-        const int t0 = t_unit + bi * 32;
+    auto process = [&](const BlockData<KW, FW> &d, int t0) {
         if ((t0 - t_unit) % win_tokens == 0) {
             // ---- new window: B operand of q.K for this lane's column, q * s as hi/lo fp16 ----
             w_first = t0;
@@ -188,7 +267,9 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane)
             const int gi = w0 + (act_win ? jslot : 0);
             const float *sp = km_base + static_cast<size_t>(gi) * 2 * D;
             const float *zp = sp + D;
-            float qs[QC];
+            float qs[QC], qv[QC];
+            load_q_run<QC>(a.q, a.q_dtype, q_base, qv);
+            const float qscale = act_win ? a.scale_log2 : 0.0f;
             float amax = 0.0f;
             bias = 0.0f;
 #pragma unroll
@@ -199,7 +280,7 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane)
                 const float zv[4] = {z4.x, z4.y, z4.z, z4.w};
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    const float qq = act_win ? load_q(a.q, a.q_dtype, q_base + i + k) * a.scale_log2 : 0.0f;
+                    const float qq = qv[i + k] * qscale;
                     qs[i + k] = qq * sv[k];
                     bias = __builtin_fmaf(qq, zv[k], bias);
                     amax = fmaxf(amax, fabsf(qs[i + k]));
@@ -215,62 +296,51 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane)
                 for (int p = 0; p < 4; ++p) {
                     const int R = 4 * k + p;
                     const int clo = (R / PK) * CW + (R % PK), chi = clo + PK;
-                    split_pair(ldexpf(qs[clo], sh), ldexpf(qs[chi], sh), bhi[k].u[p], blo[k].u[p]);
+                    const int e = sh - class_exp<KB>(R);
+                    split_pair(ldexpf(qs[clo], e), ldexpf(qs[chi], e), bhi[k].u[p], blo[k].u[p]);
                 }
             }
-            kexp = -sh;  // acc * 2^-sh
+            kscale = ldexpf(1.0f, -sh);  // acc * 2^-sh
         }
         const int slot = (t0 - w_first) / G;
         const bool act = act_win && jslot == slot;
 
-        // take this block's data, then start loading the next block
-        uint32_t k0[KW], k1[KW], v[FW];
-#pragma unroll
-        for (int i = 0; i < KW; ++i) {
-            k0[i] = kr0[i];
-            k1[i] = kr1[i];
-        }
-#pragma unroll
-        for (int i = 0; i < FW; ++i)
-            v[i] = vf[i];
-        const float vs[8] = {vm[0].x, vm[0].z, vm[1].x, vm[1].z, vm[2].x, vm[2].z, vm[3].x, vm[3].z};
-        const float vz[8] = {vm[0].y, vm[0].w, vm[1].y, vm[1].w, vm[2].y, vm[2].w, vm[3].y, vm[3].w};
-        if (bi + 1 < nblk)
-            load_block(t0 + 32);
-
         // q.K for tokens t0 + 4q + j (acc0) and t0 + 16 + 4q + j (acc1)
+        uint32_t k08[KW], k18[KW];
+        shift8(d.k0, k08);
+        shift8(d.k1, k18);
         f4_t acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int k = 0; k < NC; ++k) {
             Frag a0, a1;
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
-                a0.u[p] = code_reg<KB>(k0, 4 * k + p);
-                a1.u[p] = code_reg<KB>(k1, 4 * k + p);
+                a0.u[p] = code_reg<KB>(d.k0, k08, 4 * k + p);
+                a1.u[p] = code_reg<KB>(d.k1, k18, 4 * k + p);
             }
             acc0 = mfma(a0, bhi[k], acc0);
             acc0 = mfma(a0, blo[k], acc0);
             acc1 = mfma(a1, bhi[k], acc1);
             acc1 = mfma(a1, blo[k], acc1);
         }
+        const float vs[8] = {d.vm[0].x, d.vm[0].z, d.vm[1].x, d.vm[1].z,
+                             d.vm[2].x, d.vm[2].z, d.vm[3].x, d.vm[3].z};
+        const float vz[8] = {d.vm[0].y, d.vm[0].w, d.vm[1].y, d.vm[1].w,
+                             d.vm[2].y, d.vm[2].w, d.vm[3].y, d.vm[3].w};
         float sc[8];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            sc[j] = ldexpf(acc0[j], kexp) + bias;
-            sc[4 + j] = ldexpf(acc1[j], kexp) + bias;
+            sc[j] = __builtin_fmaf(acc0[j], kscale, bias);
+            sc[4 + j] = __builtin_fmaf(acc1[j], kscale, bias);
         }
-        float tmax = sc[0];
-#pragma unroll
-        for (int j = 1; j < 8; ++j)
-            tmax = fmaxf(tmax, sc[j]);
+        float tmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                           fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
         tmax = xor_max(tmax);
-        int eb = -1000;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (vs[j] > 0.0f)
-                eb = max(eb, __builtin_amdgcn_frexp_expf(vs[j]));
-        eb = max(eb, __shfl_xor(eb, 16, 64));
-        eb = max(eb, __shfl_xor(eb, 32, 64));
+        // V-scale exponent of the block: s < 2^eb for every token
+        float vmax = fmaxf(fmaxf(fmaxf(vs[0], vs[1]), fmaxf(vs[2], vs[3])),
+                           fmaxf(fmaxf(vs[4], vs[5]), fmaxf(vs[6], vs[7])));
+        vmax = xor_max(vmax);
+        int eb = vmax > 0.0f ? __builtin_amdgcn_frexp_expf(vmax) : -1000;
         eb = __builtin_amdgcn_readfirstlane(eb);
         const bool need = act && (tmax > m_run + kTau);
         if (__builtin_amdgcn_ballot_w64(need) != 0 || eb > E) {
@@ -286,32 +356,52 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane)
             m_run = m_new;
             E = E_new;
         }
+        const float mo = act ? m_run : INFINITY;  // inactive columns: weights 0
         float p[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            p[j] = act ? exp2f(sc[j] - m_run) : 0.0f;
+            p[j] = exp2f(sc[j] - mo);
             l_run += p[j];
             zb_run = __builtin_fmaf(p[j], vz[j], zb_run);
         }
-        // B operand of P.V: weights p s 2^(kWShift - E), k-slot pairs (0,1) (2,3) (4,5) (6,7)
+        // B operand of P.V: weights p s 2^(kWShift - E), k-slot pairs (0,1) (2,3)
+        // (4,5) (6,7), each divided by its code class factor
         Frag whi, wlo;
         const int wsh = kWShift - E;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            split_pair(ldexpf(p[2 * r] * vs[2 * r], wsh), ldexpf(p[2 * r + 1] * vs[2 * r + 1], wsh),
-                       whi.u[r], wlo.u[r]);
+        for (int r = 0; r < 4; ++r) {
+            const int e = wsh - class_exp<VB>(r);
+            split_pair(ldexpf(p[2 * r] * vs[2 * r], e), ldexpf(p[2 * r + 1] * vs[2 * r + 1], e), whi.u[r],
+                       wlo.u[r]);
+        }
+        uint32_t v8[FW];
+        shift8(d.v, v8);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             Frag av;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                av.u[r] = code_reg<VB>(v, 4 * m + r);
+                av.u[r] = code_reg<VB>(d.v, v8, 4 * m + r);
             O[m] = mfma(av, whi, O[m]);
             O[m] = mfma(av, wlo, O[m]);
         }
+    };
+
+    // ping-pong over the unit's blocks: the next block loads while this one computes
+    BlockData<KW, FW> bufA, bufB;
+    load_block(bufA, t_unit);
+    for (int bi = 0; bi < nblk; bi += 2) {
+        const int t0 = t_unit + bi * 32;
+        if (bi + 1 < nblk)
+            load_block(bufB, t0 + 32);
+        process(bufA, t0);
+        if (bi + 1 >= nblk)
+            break;
+        if (bi + 2 < nblk)
+            load_block(bufA, t0 + 64);
+        process(bufB, t0 + 32);
     }
 
-    // ---- finish: per column totals, then merge the NG columns of each head ----
     // this lane's column: l, z-term and o (weights carry 2^(kWShift - E))
     const float Lcol = xor_sum(l_run);
     const float ZB = xor_sum(zb_run);
@@ -351,34 +441,212 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane)
         float *part = a.part + ((static_cast<size_t>(bh) * a.n_part + unit) * g + col) * ps;
 #pragma unroll
         for (int m = 0; m < MT; ++m)
-            *reinterpret_cast<float4 *>(part + 16 * m + 4 * q) =
-                make_float4(oc[m][0], oc[m][1], oc[m][2], oc[m][3]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                part_store(part + 16 * m + 4 * q + j, oc[m][j]);
         if (q == 0) {
-            part[D] = M;
-            part[D + 1] = Lc;
+            part_store(part + D, M);
+            part_store(part + D + 1, Lc);
         }
     }
 }
 
+// Recent (16-bit) tokens [Tq + runit * res_tokens, ...) of one stream on the
+// matrix core, one wave.  Column h < g carries head h.  q.K reads the K rows as
+// fp16 or bf16 operands directly (q split into hi/lo fp16, or three bfloat16
+// parts); P.V reads V through a per-wave LDS tile written transposed
+// ([channel][token]) so that each lane's operand (eight tokens of one channel)
+// is two 8-byte LDS reads.
+template <int D>
+__device__ void mfma_residual_unit(const AttnArgs &a, int bh, int runit, int lane, uint16_t *vt)
+{
+    constexpr int NC = D / 32;
+    constexpr int MT = D / 16;
+    const LayerDev &L = a.L;
+    const int g = a.g;
+    const int col = lane & 15, q = lane >> 4;
+    const bool act = col < g;
+    const int h = act ? col : 0;
+    const int b = bh / a.Hkv, kvh = bh % a.Hkv;
+    const int bf = a.kv_bf16;
+    const int t_beg = a.Tq + runit * a.res_tokens;
+    const int t_end = min(a.N, t_beg + a.res_tokens);
+    const uint16_t *rk = L.ring_k + static_cast<size_t>(bh) * L.R * D;
+    const uint16_t *rv = L.ring_v + static_cast<size_t>(bh) * L.R * D;
+
+    // B operand of q.K: q of head h, chunk k, quad q -> channels 32k + 8q + i
+    Frag b1[NC], b2[NC], b3[NC];
+    int sh;
+    {
+        float qv[NC][8];
+        const size_t base = (static_cast<size_t>(b) * a.Hkv * g + kvh * g + h) * D;
+        float amax = 0.0f;
+#pragma unroll
+        for (int k = 0; k < NC; ++k) {
+            float r[8];
+            load_q_run<8>(a.q, a.q_dtype, base + 32 * k + 8 * q, r);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                qv[k][i] = act ? r[i] * a.scale_log2 : 0.0f;
+                amax = fmaxf(amax, fabsf(qv[k][i]));
+            }
+        }
+        amax = xor_max(amax);
+        const int qexp = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) : 0;
+        sh = bf ? 0 : 14 - qexp;  // fp16 operands need the fp16 range
+#pragma unroll
+        for (int k = 0; k < NC; ++k)
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const float x0 = ldexpf(qv[k][2 * p], sh), x1 = ldexpf(qv[k][2 * p + 1], sh);
+                if (bf)
+                    split3_bf16(x0, x1, b1[k].u[p], b2[k].u[p], b3[k].u[p]);
+                else
+                    split_pair(x0, x1, b1[k].u[p], b2[k].u[p]);
+            }
+    }
+    const float kscale = ldexpf(1.0f, -sh);
+
+    float m_run = -INFINITY, l_run = 0.0f;
+    f4_t O[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+        O[m] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    for (int t0 = t_beg; t0 < t_end; t0 += 32) {
+        // K rows of the two 16-token tiles (rows past the end repeat the last token)
+        const int ta = min(t0 + col, t_end - 1), tb = min(t0 + 16 + col, t_end - 1);
+        uint4 ka[NC], kb2[NC];
+#pragma unroll
+        for (int k = 0; k < NC; ++k) {
+            ka[k] = *reinterpret_cast<const uint4 *>(rk + static_cast<size_t>(ta % L.R) * D + 32 * k + 8 * q);
+            kb2[k] = *reinterpret_cast<const uint4 *>(rk + static_cast<size_t>(tb % L.R) * D + 32 * k + 8 * q);
+        }
+        // V rows -> LDS [channel][token]: lane handles token (lane & 31), half of the row
+        {
+            const int tt = lane & 31, half = lane >> 5;
+            const int tv = min(t0 + tt, t_end - 1);
+            const uint4 *src = reinterpret_cast<const uint4 *>(rv + static_cast<size_t>(tv % L.R) * D + half * (D / 2));
+            uint4 v[D / 16];
+#pragma unroll
+            for (int i = 0; i < D / 16; ++i)
+                v[i] = src[i];
+#pragma unroll
+            for (int i = 0; i < D / 16; ++i) {
+                const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int c = half * (D / 2) + 8 * i + e;
+                    vt[c * 32 + tt] = static_cast<uint16_t>((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu));
+                }
+            }
+        }
+        f4_t acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int k = 0; k < NC; ++k) {
+            Frag a0, a1;
+            a0.u[0] = ka[k].x; a0.u[1] = ka[k].y; a0.u[2] = ka[k].z; a0.u[3] = ka[k].w;
+            a1.u[0] = kb2[k].x; a1.u[1] = kb2[k].y; a1.u[2] = kb2[k].z; a1.u[3] = kb2[k].w;
+            if (bf) {
+                acc0 = mfma_bf16(a0, b1[k], acc0);
+                acc0 = mfma_bf16(a0, b2[k], acc0);
+                acc0 = mfma_bf16(a0, b3[k], acc0);
+                acc1 = mfma_bf16(a1, b1[k], acc1);
+                acc1 = mfma_bf16(a1, b2[k], acc1);
+                acc1 = mfma_bf16(a1, b3[k], acc1);
+            } else {
+                acc0 = mfma(a0, b1[k], acc0);
+                acc0 = mfma(a0, b2[k], acc0);
+                acc1 = mfma(a1, b1[k], acc1);
+                acc1 = mfma(a1, b2[k], acc1);
+            }
+        }
+        float sc[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            sc[j] = (t0 + 4 * q + j < t_end) ? acc0[j] * kscale : -INFINITY;
+            sc[4 + j] = (t0 + 16 + 4 * q + j < t_end) ? acc1[j] * kscale : -INFINITY;
+        }
+        float tmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                           fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+        tmax = xor_max(tmax);
+        const bool need = act && (tmax > m_run + kTau);
+        if (__builtin_amdgcn_ballot_w64(need) != 0) {
+            const float m_new = need ? tmax : m_run;
+            const float alpha = (m_new == m_run) ? 1.0f : exp2f(m_run - m_new);
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                O[m] *= alpha;
+            l_run *= alpha;
+            m_run = m_new;
+        }
+        const float mo = act ? m_run : INFINITY;
+        float p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            p[j] = exp2f(sc[j] - mo);
+            l_run += p[j];
+        }
+        // weights p 2^kWShift (below 2^15) as hi/lo fp16 or three bfloat16 parts
+        Frag w1, w2, w3;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float x0 = ldexpf(p[2 * r], kWShift), x1 = ldexpf(p[2 * r + 1], kWShift);
+            if (bf)
+                split3_bf16(x0, x1, w1.u[r], w2.u[r], w3.u[r]);
+            else
+                split_pair(x0, x1, w1.u[r], w2.u[r]);
+        }
+        // V^T operand of tile m: channel 16m + col, tokens 4q..4q+3 and 16+4q..16+4q+3
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const uint16_t *row = vt + (16 * m + col) * 32;
+            const uint2 lo = *reinterpret_cast<const uint2 *>(row + 4 * q);
+            const uint2 hi = *reinterpret_cast<const uint2 *>(row + 16 + 4 * q);
+            Frag av;
+            av.u[0] = lo.x; av.u[1] = lo.y; av.u[2] = hi.x; av.u[3] = hi.y;
+            if (bf) {
+                O[m] = mfma_bf16(av, w1, O[m]);
+                O[m] = mfma_bf16(av, w2, O[m]);
+                O[m] = mfma_bf16(av, w3, O[m]);
+            } else {
+                O[m] = mfma(av, w1, O[m]);
+                O[m] = mfma(av, w2, O[m]);
+            }
+        }
+    }
+    const float Lc = xor_sum(l_run);
+    if (act) {
+        const int ps = part_stride(D);
+        float *part = a.part + ((static_cast<size_t>(bh) * a.n_part + a.units_q + runit) * g + col) * ps;
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                part_store(part + 16 * m + 4 * q + j, ldexpf(O[m][j], -kWShift));
+        if (q == 0) {
+            part_store(part + D, m_run);
+            part_store(part + D + 1, Lc);
+        }
+    }
+}
+
+// Waves per SIMD the register allocation must allow: three for the narrow
+// pairs (a few bytes of spill at most), two for the wider ones.
+template <int KB, int VB>
+constexpr int mfma_waves_per_simd() { return 2; }
+
 template <int KB, int VB, int D>
-__global__ __launch_bounds__(kAttnThreads) void attn_mfma_kernel(AttnArgs a)
+__global__ __launch_bounds__(kAttnThreads, (mfma_waves_per_simd<KB, VB>())) void attn_mfma_kernel(AttnArgs a)
 {
     const int bh = blockIdx.y, wg = blockIdx.x;
-    if (wg < a.mfma_wgs) {
-        const int unit = wg * 4 + (threadIdx.x >> 6);
-        if (unit < a.units_q)
-            mfma_unit<KB, VB, D>(a, bh, unit, threadIdx.x & 63);
-    } else {
-        const int r = wg - a.mfma_wgs;
-        const int t_beg = a.valu_beg + r * a.valu_tps;
-        const int t_end = min(a.N, t_beg + a.valu_tps);
-        extern __shared__ float smem[];
-        if (a.g <= 4)
-            valu_range<D, 4>(a, bh, t_beg, t_end, a.units_q + r, smem);
-        else if (a.g <= 8)
-            valu_range<D, 8>(a, bh, t_beg, t_end, a.units_q + r, smem);
-        else
-            valu_range<D, 16>(a, bh, t_beg, t_end, a.units_q + r, smem);
+    const int unit = wg * 4 + (threadIdx.x >> 6);
+    if (unit < a.units_q) {
+        mfma_unit<KB, VB, D>(a, bh, unit, threadIdx.x & 63);
+    } else if (unit < a.units_q + a.units_r) {
+        extern __shared__ uint16_t vt_lds[];  // 32 x D per wave
+        mfma_residual_unit<D>(a, bh, unit - a.units_q, threadIdx.x & 63,
+                              vt_lds + (threadIdx.x >> 6) * 32 * D);
     }
     arrive_and_merge(a, bh, gridDim.x);
 }
@@ -386,8 +654,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_mfma_kernel(AttnArgs a)
 template <int KB, int VB>
 hipError_t launch_pair(const AttnArgs &a, hipStream_t st)
 {
-    dim3 grid(a.mfma_wgs + a.valu_wgs, a.BH);
-    const size_t lds = a.valu_wgs > 0 ? valu_lds_bytes(a.g, a.D) : 0;
+    dim3 grid(a.mfma_wgs, a.BH);
+    const size_t lds = a.units_r > 0 ? 4 * 32 * a.D * sizeof(uint16_t) : 0;
     hipLaunchKernelGGL((attn_mfma_kernel<KB, VB, KVQ_D>), grid, dim3(kAttnThreads), lds, st, a);
     return hipGetLastError();
 }

@@ -64,8 +64,10 @@ struct AttnArgs {
     // vector-ALU ranges: wg_valu workgroups per stream cover tokens [valu_beg, N)
     int valu_beg, valu_wgs, valu_tps;
     // matrix-core units: units_q waves per stream cover groups [0, Tq / G),
-    // unit_groups groups each; mfma_wgs = ceil(units_q / 4) workgroups
-    int units_q, unit_groups, mfma_wgs;
+    // unit_groups groups each; then units_r waves cover the recent tokens
+    // [Tq, N), res_tokens each (a multiple of 32); mfma_wgs = ceil((units_q +
+    // units_r) / 4) workgroups
+    int units_q, unit_groups, units_r, res_tokens, mfma_wgs;
     float scale_log2;     // log2(e) / sqrt(D)
 };
 

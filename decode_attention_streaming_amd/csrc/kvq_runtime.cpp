@@ -20,7 +20,7 @@ namespace {
 
 thread_local std::string g_create_error = "no error";
 
-constexpr int kMaxPart = 256;  // partial entries per stream (splits + units)
+constexpr int kMaxPart = 128;  // partial entries per stream (splits + units); P * g <= 2048
 constexpr int kMaxG = 16;
 constexpr int kMaxTileElems = 16384;  // group_size * head_dim staged by the flush kernel
 
@@ -363,31 +363,47 @@ int kvq_decode_attention(kvq_handle *h, int layer, const void *q, float *out)
     a.BH = BH;
     a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D)));
     const char *force_valu = getenv("KVQ_FORCE_VALU");
-    const bool use_mfma = d.v_tiled && d.kb != 16 && kvq::mfma_supported(d.kb, d.vb, D) && s.Tq > 0 &&
+    const bool use_mfma = (d.kb == 16 || (d.v_tiled && kvq::mfma_supported(d.kb, d.vb, D))) &&
                           !(force_valu && atoi(force_valu) > 0);
     int S = 0;
     if (use_mfma) {
-        // matrix-core units over whole groups, vector-ALU workgroups over the
-        // recent tokens (256 per workgroup)
+        // matrix-core units over whole groups, then over the recent tokens
         const int n_groups = s.Tq / d.G;
         const int Tr = s.N - s.Tq;
-        a.valu_beg = s.Tq;
-        a.valu_tps = 256;
-        a.valu_wgs = (Tr + 255) / 256;
-        long ug = static_cast<long>(n_groups) * BH / (8L * h->cu_count);
-        const char *env = getenv("KVQ_UNIT_GROUPS");
-        if (env && atoi(env) > 0)
-            ug = atoi(env);
-        if (ug < 1)
-            ug = 1;
-        if (ug > n_groups)
-            ug = n_groups;
-        while ((n_groups + ug - 1) / ug + a.valu_wgs > kMaxPart)
-            ++ug;
+        long ug = 1;
+        if (n_groups > 0) {
+            // about one unit (wave) per SIMD over the whole launch
+            ug = (static_cast<long>(n_groups) * BH + 4L * h->cu_count - 1) / (4L * h->cu_count);
+            const char *env = getenv("KVQ_UNIT_GROUPS");
+            if (env && atoi(env) > 0)
+                ug = atoi(env);
+            if (ug < 1)
+                ug = 1;
+            if (ug > n_groups)
+                ug = n_groups;
+        }
+        // recent tokens: 32-token blocks, about as many per unit as a quantized unit holds
+        int rt = static_cast<int>(ug * d.G);
+        rt = (rt + 31) / 32 * 32;
+        if (rt < 64)
+            rt = 64;
+        for (;;) {
+            const int uq = n_groups > 0 ? static_cast<int>((n_groups + ug - 1) / ug) : 0;
+            const int ur = (Tr + rt - 1) / rt;
+            if (uq + ur <= kMaxPart)
+                break;
+            if (uq > ur)
+                ++ug;
+            else
+                rt += 32;
+        }
         a.unit_groups = static_cast<int>(ug);
-        a.units_q = static_cast<int>((n_groups + ug - 1) / ug);
-        a.mfma_wgs = (a.units_q + 3) / 4;
-        S = a.units_q;
+        a.units_q = n_groups > 0 ? static_cast<int>((n_groups + ug - 1) / ug) : 0;
+        a.res_tokens = rt;
+        a.units_r = (Tr + rt - 1) / rt;
+        a.mfma_wgs = (a.units_q + a.units_r + 3) / 4;
+        a.valu_beg = a.valu_tps = a.valu_wgs = 0;
+        S = a.units_q + a.units_r;
     } else {
         // splits: about two workgroups per compute unit, >= 64 tokens each
         S = (2 * h->cu_count + BH - 1) / BH;
@@ -407,9 +423,9 @@ int kvq_decode_attention(kvq_handle *h, int layer, const void *q, float *out)
         a.valu_beg = 0;
         a.valu_tps = tps;
         a.valu_wgs = S;
-        a.units_q = a.unit_groups = a.mfma_wgs = 0;
+        a.units_q = a.unit_groups = a.units_r = a.res_tokens = a.mfma_wgs = 0;
     }
-    a.n_part = a.units_q + a.valu_wgs;
+    a.n_part = a.units_q + a.units_r + a.valu_wgs;
     e = kvq::launch_attention(a, use_mfma, h->stream);
     if (e != hipSuccess)
         return h->dev_fail(e, "attention launch");
