@@ -1,6 +1,7 @@
 // kvq_attn_common.h -- device code shared by the decode-attention kernels:
-// the vector-ALU pass over a token range, and the log-sum-exp merge of split
-// partials done by the last workgroup of each stream to finish.
+// the vector-ALU pass over a token range, the hand-off of per-workgroup
+// partial results, and their log-sum-exp merge by the last workgroup of each
+// stream to finish.
 //
 // Attention o = softmax(q K^T / sqrt(D)) V over one query token per sequence
 // (KVTuner summary, A3 attention equation), in the log2 domain: q is
@@ -20,22 +21,50 @@ namespace kvq {
 constexpr int kAttnThreads = 256;
 constexpr int kMaxG = 16;
 
-// Partial entry of one (stream, split, head): o[D], m, l, 2 pad floats.
+// Partial entry of one (stream, workgroup, head): o[D], then m (log2 domain),
+// l and two unused floats.  16-byte aligned (D is a multiple of 4).
 __device__ __forceinline__ int part_stride(int D) { return D + 4; }
 
 // Partials pass between workgroups of one launch, which may run on different
-// XCDs with separate L2 caches.  They are written and read with agent-scope
-// atomic accesses, which are coherent at the device level, so the hand-off
-// needs no whole-cache write-back or invalidation.
+// XCDs with separate L2 caches.  They are written and read with device-coherent
+// accesses (write-through stores, loads that bypass a possibly stale L2), so
+// the hand-off needs no whole-cache write-back or invalidation.
 __device__ __forceinline__ void part_store(float *p, float v)
 {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ float part_load(const float *p)
-{
-    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+typedef float f4_t __attribute__((ext_vector_type(4)));
+
+// Cache-policy bit of a buffer access that makes it coherent across the
+// device (the agent-scope bit; the accesses skip or write through L2).
+constexpr int kDeviceCoherent = 16;
+
+// Buffer view of the partial entries of one stream, with 16-byte coherent
+// accesses (hardware range-checked against the stream's entries).
+struct PartBuf {
+    __amdgpu_buffer_rsrc_t r;
+
+    __device__ PartBuf(const AttnArgs &a, int bh)
+    {
+        const size_t n = static_cast<size_t>(a.n_part) * a.g * part_stride(a.D);
+        r = __builtin_amdgcn_make_buffer_rsrc(a.part + static_cast<size_t>(bh) * n, 0,
+                                              static_cast<int>(n * 4), 0x00020000);
+    }
+    // float offset of (entry, head, channel)
+    __device__ int off(const AttnArgs &a, int entry, int h, int c) const
+    {
+        return (entry * a.g + h) * part_stride(a.D) + c;
+    }
+    __device__ void store4(int off_f, f4_t v) const
+    {
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, off_f * 4, 0, kDeviceCoherent);
+    }
+    __device__ f4_t load4(int off_f) const
+    {
+        return __builtin_amdgcn_raw_buffer_load_b128(r, off_f * 4, 0, kDeviceCoherent);
+    }
+};
 
 __device__ __forceinline__ float widen16(uint16_t x, int bf16)
 {
@@ -63,6 +92,26 @@ __device__ __forceinline__ float wave_sum(float v)
     for (int off = 32; off > 0; off >>= 1)
         v += __shfl_xor(v, off, 64);
     return v;
+}
+
+// Reductions over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one column of a
+// 16-row matrix-core tile), with two VALU lane swaps instead of LDS shuffles:
+// the 16-lane swap exchanges rows 0 <-> 1 and 2 <-> 3 of two copies of v, the
+// 32-lane swap the two halves.
+__device__ __forceinline__ float col_max(float v)
+{
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+    const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+
+__device__ __forceinline__ float col_sum(float v)
+{
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+    const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(t[0]) + __uint_as_float(t[1]);
 }
 
 // K code of channel c in a token-major packed row.
@@ -384,149 +433,49 @@ __device__ void valu_range(const AttnArgs &a, int bh, int t_beg, int t_end, int 
 #undef red
 }
 
-// Dynamic LDS bytes of residual_range<D>(): q[g][D], scores/weights[g][TT],
-// K and V tiles (16 KB each), per-head state.
-__host__ __device__ inline int residual_lds_bytes(int g, int D)
+// Workgroup-level merge: the waves of one workgroup have left their per-head
+// results in LDS (o[g][D] at wave * region floats, m and l in pm / pl; m =
+// -inf marks an empty one); the workgroup writes one partial entry per head,
+// o = sum_w 2^(m_w - M) o_w, l = sum_w 2^(m_w - M) l_w, M = max_w m_w.
+__device__ __forceinline__ void wg_merge_store(const AttnArgs &a, int bh, int entry, const float *lds,
+                                               int region, const float (*pm)[kMaxG], const float (*pl)[kMaxG])
 {
-    const int TT = 8192 / D;
-    return (g * D + g * TT + 4 * kMaxG) * 4 + 2 * 16384;
-}
-
-// Vector-ALU attention of one workgroup over recent (16-bit) tokens
-// [t_beg, t_end) of stream bh, for any g <= 16 with few registers: tiles of TT
-// tokens staged in LDS; P threads per token for the scores; per-head softmax
-// bookkeeping by one thread per head; P.V by one thread per (channel, head).
-template <int D>
-__device__ void residual_range(const AttnArgs &a, int bh, int t_beg, int t_end, int slot, float *smem)
-{
-    constexpr int TT = valu_tile<D>();
-    constexpr int P = kAttnThreads / TT;
-    constexpr int CPT = D / P;  // 32
-    constexpr int OS = (kMaxG * D + kAttnThreads - 1) / kAttnThreads;  // output slots per thread
-    const int tid = threadIdx.x;
-    const int g = a.g;
-    float *q_l = smem;                       // [g][D]
-    float *s_l = smem + g * D;               // [g][TT] scores, then weights
-    float *st = s_l + g * TT;                // [4][kMaxG]: m, l, alpha
-    uint16_t *k_tile = reinterpret_cast<uint16_t *>(st + 4 * kMaxG);
-    uint16_t *v_tile = k_tile + 8192;
-    const int b = bh / a.Hkv, kvh = bh % a.Hkv;
-    const LayerDev &L = a.L;
-    const int bf = a.kv_bf16;
-
-    stage_q(a, b, kvh, q_l);
-    if (tid < g) {
-        st[tid] = -INFINITY;        // m
-        st[kMaxG + tid] = 0.0f;     // l
-    }
-    float o[OS];
+    const int D = a.D, nc4 = D / 4;
+    const PartBuf pb(a, bh);
+    for (int it = threadIdx.x; it < a.g * nc4; it += kAttnThreads) {
+        const int h = it / nc4, c4 = it % nc4;
+        float M = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < OS; ++k)
-        o[k] = 0.0f;
-
-    for (int tile = t_beg; tile < t_end; tile += TT) {
-        const int nt = min(TT, t_end - tile);
-        __syncthreads();
-        stage_ring<D, 4>(k_tile, L.ring_k + static_cast<size_t>(bh) * L.R * D, L.R, tile, nt);
-        stage_ring<D, 4>(v_tile, L.ring_v + static_cast<size_t>(bh) * L.R * D, L.R, tile, nt);
-        __syncthreads();
-        // scores, four heads at a time
-        const int ti = tid / P, part = tid % P, c0 = part * CPT;
-        for (int h0 = 0; h0 < g; h0 += 4) {
-            float sc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (ti < nt) {
-                const uint16_t *row = k_tile + ti * D + c0;
-#pragma unroll 8
-                for (int i = 0; i < CPT; ++i) {
-                    const float x = widen16(row[i], bf);
+        for (int w = 0; w < kAttnThreads / 64; ++w)
+            M = fmaxf(M, pm[w][h]);
+        f4_t o = {0.0f, 0.0f, 0.0f, 0.0f};
+        float l = 0.0f;
+        if (M != -INFINITY) {
 #pragma unroll
-                    for (int k = 0; k < 4; ++k)
-                        if (h0 + k < g)
-                            sc[k] = __builtin_fmaf(q_l[(h0 + k) * D + c0 + i], x, sc[k]);
-                }
-            }
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                for (int off = 1; off < P; off <<= 1)
-                    sc[k] += __shfl_xor(sc[k], off, 64);
-            if (ti < nt && part == 0)
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    if (h0 + k < g)
-                        s_l[(h0 + k) * TT + ti] = sc[k];
-        }
-        __syncthreads();
-        // per head (one wave each, lanes over the tile's tokens): max, weights, normalizer
-        {
-            const int lane = tid & 63, wave = tid >> 6;
-            for (int h = wave; h < g; h += kAttnThreads / 64) {
-                float tm = -INFINITY;
-                for (int i = lane; i < nt; i += 64)
-                    tm = fmaxf(tm, s_l[h * TT + i]);
-                tm = wave_max(tm);
-                const float m_old = st[h], m_new = fmaxf(m_old, tm);
-                float ls = 0.0f;
-                for (int i = lane; i < TT; i += 64) {
-                    const float p = i < nt ? exp2f(s_l[h * TT + i] - m_new) : 0.0f;
-                    s_l[h * TT + i] = p;
-                    ls += p;
-                }
-                ls = wave_sum(ls);
-                if (lane == 0) {
-                    const float alpha = exp2f(m_old - m_new);
-                    st[h] = m_new;
-                    st[kMaxG + h] = st[kMaxG + h] * alpha + ls;
-                    st[2 * kMaxG + h] = alpha;
-                }
+            for (int w = 0; w < kAttnThreads / 64; ++w) {
+                if (pm[w][h] == -INFINITY)
+                    continue;
+                const float f = exp2f(pm[w][h] - M);
+                const f4_t v = *reinterpret_cast<const f4_t *>(lds + w * region + h * D + 4 * c4);
+                o += f * v;
+                l = __builtin_fmaf(f, pl[w][h], l);
             }
         }
-        __syncthreads();
-        // P.V: all TT tokens (weights of the tile's missing tokens are 0)
-#pragma unroll
-        for (int k = 0; k < OS; ++k) {
-            const int idx = tid + k * kAttnThreads;
-            if (idx < g * D) {
-                const int h = idx / D, c = idx % D;
-                float acc[4] = {o[k] * st[2 * kMaxG + h], 0.0f, 0.0f, 0.0f};
-#pragma unroll 16
-                for (int i = 0; i < TT; ++i) {
-                    const float x = i < nt ? widen16(v_tile[i * D + c], bf) : 0.0f;
-                    acc[i & 3] = __builtin_fmaf(s_l[h * TT + i], x, acc[i & 3]);
-                }
-                o[k] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-            }
-        }
-    }
-    __syncthreads();
-    const int ps = part_stride(D);
-    float *part = a.part + (static_cast<size_t>(bh) * a.n_part + slot) * g * ps;
-#pragma unroll
-    for (int k = 0; k < OS; ++k) {
-        const int idx = tid + k * kAttnThreads;
-        if (idx < g * D) {
-            const int h = idx / D, c = idx % D;
-            part_store(part + h * ps + c, o[k]);
-            if (c == 0) {
-                part_store(part + h * ps + D, st[h]);
-                part_store(part + h * ps + D + 1, st[kMaxG + h]);
-            }
-        }
+        pb.store4(pb.off(a, entry, h, 4 * c4), o);
+        if (c4 == 0)
+            pb.store4(pb.off(a, entry, h, D), f4_t{M, l, 0.0f, 0.0f});
     }
 }
 
 // Called by every workgroup at its end: the last one of stream bh to arrive
 // merges the n_part partial entries, out = sum_s 2^(m_s - M) o_s /
 // sum_s 2^(m_s - M) l_s, M = max_s m_s, and re-arms the stream's counter.
-// The merge first gathers every (m, l) into LDS with one batch of loads, then
-// reads the o values with all loads of a thread issued together.
-constexpr int kMergeMax = 2048;  // (entry, head) pairs the merge stages in LDS
-
+// Each thread owns four channels of one head and issues the (m, l) and o loads
+// of up to eight entries together: one memory round trip for up to eight
+// entries.
 __device__ __forceinline__ void arrive_and_merge(const AttnArgs &a, int bh, unsigned n_wgs)
 {
     __shared__ int s_last;
-    __shared__ float s_w[kMergeMax];  // m, then weight 2^(m_s - M_h), of entry s, head h
-    __shared__ float s_l[kMergeMax];  // l of entry s, head h
-    __shared__ float s_inv[kMaxG];    // 1 / sum_s w l
     __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are complete
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -537,56 +486,50 @@ __device__ __forceinline__ void arrive_and_merge(const AttnArgs &a, int bh, unsi
     __syncthreads();
     if (!s_last)
         return;
-    const int D = a.D, g = a.g, P = a.n_part, ps = part_stride(D);
+    const int D = a.D, g = a.g, P = a.n_part, nc4 = D / 4;
     const int b = bh / a.Hkv, kvh = bh % a.Hkv;
-    const float *part = a.part + static_cast<size_t>(bh) * P * g * ps;
-    const int tid = threadIdx.x;
-    // (1) m and l of every (entry, head) into LDS
-    for (int i = tid; i < P * g; i += kAttnThreads) {
-        s_w[i] = part_load(part + i * ps + D);
-        s_l[i] = part_load(part + i * ps + D + 1);
-    }
-    __syncthreads();
-    // (2) per head (one wave each, lanes over entries): M, weights, normalizer
-    {
-        const int lane = tid & 63, wave = tid >> 6;
-        for (int h = wave; h < g; h += kAttnThreads / 64) {
-            float M = -INFINITY;
-            for (int s2 = lane; s2 < P; s2 += 64)
-                M = fmaxf(M, s_w[s2 * g + h]);
-            M = wave_max(M);
-            float den = 0.0f;
-            for (int s2 = lane; s2 < P; s2 += 64) {
-                const float ms = s_w[s2 * g + h];
-                const float w = (ms == -INFINITY) ? 0.0f : exp2f(ms - M);
-                s_w[s2 * g + h] = w;
-                den = __builtin_fmaf(w, s_l[s2 * g + h], den);
+    const PartBuf pb(a, bh);
+    constexpr int kChunk = 8;
+    for (int it = threadIdx.x; it < g * nc4; it += kAttnThreads) {
+        const int h = it / nc4, c4 = it % nc4;
+        float M = -INFINITY, den = 0.0f;
+        f4_t num = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int s0 = 0; s0 < P; s0 += kChunk) {
+            f4_t ml[kChunk], ov[kChunk];
+#pragma unroll
+            for (int k = 0; k < kChunk; ++k) {
+                if (s0 + k < P) {
+                    ml[k] = pb.load4(pb.off(a, s0 + k, h, D));
+                    ov[k] = pb.load4(pb.off(a, s0 + k, h, 4 * c4));
+                }
             }
-            den = wave_sum(den);
-            if (lane == 0)
-                s_inv[h] = 1.0f / den;
-        }
-    }
-    __syncthreads();
-    // (3) outputs: each thread's loads for one (head, channel) are issued together
-    for (int i = tid; i < g * D; i += kAttnThreads) {
-        const int h = i / D, c = i % D;
-        float num = 0.0f;
-        int s2 = 0;
-        for (; s2 + 8 <= P; s2 += 8) {
-            float v[8];
+            float Mc = M;
 #pragma unroll
-            for (int k = 0; k < 8; ++k)
-                v[k] = part_load(part + ((s2 + k) * g + h) * ps + c);
+            for (int k = 0; k < kChunk; ++k)
+                if (s0 + k < P)
+                    Mc = fmaxf(Mc, ml[k][0]);
+            if (Mc == -INFINITY)
+                continue;
+            if (Mc != M) {
+                const float r = (M == -INFINITY) ? 0.0f : exp2f(M - Mc);
+                num *= r;
+                den *= r;
+                M = Mc;
+            }
 #pragma unroll
-            for (int k = 0; k < 8; ++k)
-                num = __builtin_fmaf(s_w[(s2 + k) * g + h], v[k], num);
+            for (int k = 0; k < kChunk; ++k) {
+                if (s0 + k < P && ml[k][0] != -INFINITY) {
+                    const float w = exp2f(ml[k][0] - M);
+                    num += w * ov[k];
+                    den = __builtin_fmaf(w, ml[k][1], den);
+                }
+            }
         }
-        for (; s2 < P; ++s2)
-            num = __builtin_fmaf(s_w[s2 * g + h], part_load(part + (s2 * g + h) * ps + c), num);
-        a.out[(static_cast<size_t>(b) * a.Hkv * g + kvh * g + h) * D + c] = num * s_inv[h];
+        const float inv = 1.0f / den;
+        *reinterpret_cast<f4_t *>(a.out + (static_cast<size_t>(b) * a.Hkv * g + kvh * g + h) * D + 4 * c4) =
+            num * inv;
     }
-    if (tid == 0)
+    if (threadIdx.x == 0)
         __hip_atomic_store(a.counters + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 

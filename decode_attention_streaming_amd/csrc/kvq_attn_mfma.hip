@@ -17,12 +17,14 @@
 //
 // One wave processes one unit (a run of whole K groups of one stream).  The 16
 // columns of each product are (head, group-slot) pairs: with g query heads per
-// kv-head, NG = 16 / g consecutive groups are processed per window, column
-// j*g + h carrying head h over the tokens of group j.  Every column keeps its
-// own online-softmax state, so each lane's B operand is useful and no data
-// moves between the two products; the NG columns of a head are merged at the
-// end of the unit.  Query heads of a GQA group share every K/V read (KIVI
-// notes, section 7.2).
+// kv-head, NG (the largest power of two <= 16 / g) consecutive groups are
+// processed per window, column j*S + h (S = 16 / NG) carrying head h over the
+// tokens of group j.  Every column keeps its own online-softmax state, so each
+// lane's B operand is useful and no data moves between the two products; the
+// NG columns of a head are merged at the end of the unit by row rotations.
+// The four waves of a workgroup then merge their results through LDS into one
+// partial entry per head.  Query heads of a GQA group share every K/V read
+// (KIVI notes, section 7.2).
 #include "kvq_attn_common.h"
 
 #ifndef KVQ_D
@@ -34,8 +36,6 @@ namespace {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f4_t __attribute__((ext_vector_type(4)));
-
 union Frag {
     uint32_t u[4];
     half8_t h;
@@ -179,17 +179,48 @@ __device__ __forceinline__ void load_q_run(const void *q, int dtype, size_t i0, 
     }
 }
 
-__device__ __forceinline__ float xor_sum(float v)
+// v of the lane R columns away in the same 16-lane row (row rotation)
+template <int R>
+__device__ __forceinline__ float row_ror(float v)
 {
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + R, 0xF, 0xF, true));
+}
+
+// Columns per group slot (S) for g query heads: 16 / NG, NG the largest power
+// of two with NG * g <= 16.
+__device__ __forceinline__ int slot_stride(int g)
+{
+    int ng = 16;
+    while (ng * g > 16)
+        ng >>= 1;
+    return 16 / ng;
+}
+
+// Sum (or max) over the columns h, h + S, h + 2S, ... of each row, left in
+// every one of them.
+__device__ __forceinline__ float coset_sum(float v, int S)
+{
+    if (S <= 8)
+        v += row_ror<8>(v);
+    if (S <= 4)
+        v += row_ror<4>(v);
+    if (S <= 2)
+        v += row_ror<2>(v);
+    if (S <= 1)
+        v += row_ror<1>(v);
     return v;
 }
 
-__device__ __forceinline__ float xor_max(float v)
+__device__ __forceinline__ float coset_max(float v, int S)
 {
-    v = fmaxf(v, __shfl_xor(v, 16, 64));
-    v = fmaxf(v, __shfl_xor(v, 32, 64));
+    if (S <= 8)
+        v = fmaxf(v, row_ror<8>(v));
+    if (S <= 4)
+        v = fmaxf(v, row_ror<4>(v));
+    if (S <= 2)
+        v = fmaxf(v, row_ror<2>(v));
+    if (S <= 1)
+        v = fmaxf(v, row_ror<1>(v));
     return v;
 }
 
@@ -201,8 +232,9 @@ struct BlockData {
     float4 vm[4];
 };
 
+// Results of one unit for head h < g go to po[h * D + c], pm[h], pl[h] (LDS).
 template <int KB, int VB, int D>
-__device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane)
+__device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *po, float *pm, float *pl)
 {
     constexpr int NC = D / 32;          // 32-channel chunks of q.K
     constexpr int QC = D / 4;           // channels owned by one lane quad
@@ -215,10 +247,10 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane)
     const LayerDev &L = a.L;
     const int G = L.G, g = a.g;
     const int col = lane & 15, q = lane >> 4;
-    const int NG = 16 / g;
-    const bool used = col < NG * g;
-    const int h = used ? col % g : 0;
-    const int jslot = used ? col / g : NG;
+    const int S = slot_stride(g), NG = 16 / S;
+    const bool used = (col % S) < g;
+    const int h = used ? col % S : 0;
+    const int jslot = used ? col / S : NG;
     const int b = bh / a.Hkv, kvh = bh % a.Hkv;
     const int n_groups = a.Tq / G;
     const int g_beg = unit * a.unit_groups;
@@ -286,8 +318,8 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane)
                     amax = fmaxf(amax, fabsf(qs[i + k]));
                 }
             }
-            bias = xor_sum(bias);
-            amax = xor_max(amax);
+            bias = col_sum(bias);
+            amax = col_max(amax);
             const int sexp = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) : 0;
             const int sh = 14 - sexp;  // |q s| * 2^sh < 2^14
 #pragma unroll
@@ -335,11 +367,11 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane)
         }
         float tmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
                            fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-        tmax = xor_max(tmax);
+        tmax = col_max(tmax);
         // V-scale exponent of the block: s < 2^eb for every token
         float vmax = fmaxf(fmaxf(fmaxf(vs[0], vs[1]), fmaxf(vs[2], vs[3])),
                            fmaxf(fmaxf(vs[4], vs[5]), fmaxf(vs[6], vs[7])));
-        vmax = xor_max(vmax);
+        vmax = col_max(vmax);
         int eb = vmax > 0.0f ? __builtin_amdgcn_frexp_expf(vmax) : -1000;
         eb = __builtin_amdgcn_readfirstlane(eb);
         const bool need = act && (tmax > m_run + kTau);
@@ -402,51 +434,27 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane)
         process(bufB, t0 + 32);
     }
 
-    // this lane's column: l, z-term and o (weights carry 2^(kWShift - E))
-    const float Lcol = xor_sum(l_run);
-    const float ZB = xor_sum(zb_run);
-    float ocol[MT][4];
+    // this lane's column: l, z-term and o (weights carry 2^(kWShift - E)); the
+    // columns of one head are rescaled to their common max and summed
+    const float Lcol = col_sum(l_run);
+    const float ZB = col_sum(zb_run);
+    const float M = coset_max(m_run, S);
+    const float alpha = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - M);
+    const float fo = ldexpf(alpha, E - kWShift), fz = alpha * ZB;
+    const float Lh = coset_sum(alpha * Lcol, S);
+    float o[MT][4];
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            ocol[m][j] = ldexpf(O[m][j], E - kWShift) + ZB;
-    // head h = col (col < g) gathers the unmerged columns j*g + h, j = 1..NG-1
-    float M = m_run, Lc = Lcol;
-    float oc[MT][4];
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            oc[m][j] = ocol[m][j];
-    for (int jn = 1; jn < NG; ++jn) {
-        const int src = ((col + jn * g) & 15) + 16 * q;
-        const float m2 = __shfl(m_run, src, 64);
-        const float L2 = __shfl(Lcol, src, 64);
-        const float Mn = fmaxf(M, m2);
-        const float a1 = (M == Mn) ? 1.0f : exp2f(M - Mn);
-        const float a2 = (m2 == Mn) ? 1.0f : exp2f(m2 - Mn);
-        Lc = Lc * a1 + L2 * a2;
+            o[m][j] = coset_sum(__builtin_fmaf(O[m][j], fo, fz), S);
+    if (col < g) {  // slot 0 of head col
 #pragma unroll
         for (int m = 0; m < MT; ++m)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float o2 = __shfl(ocol[m][j], src, 64);
-                oc[m][j] = oc[m][j] * a1 + o2 * a2;
-            }
-        M = Mn;
-    }
-    if (col < g) {
-        const int ps = part_stride(D);
-        float *part = a.part + ((static_cast<size_t>(bh) * a.n_part + unit) * g + col) * ps;
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                part_store(part + 16 * m + 4 * q + j, oc[m][j]);
+            *reinterpret_cast<f4_t *>(po + col * D + 16 * m + 4 * q) = f4_t{o[m][0], o[m][1], o[m][2], o[m][3]};
         if (q == 0) {
-            part_store(part + D, M);
-            part_store(part + D + 1, Lc);
+            pm[col] = M;
+            pl[col] = Lh;
         }
     }
 }
@@ -458,7 +466,8 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane)
 // ([channel][token]) so that each lane's operand (eight tokens of one channel)
 // is two 8-byte LDS reads.
 template <int D>
-__device__ void mfma_residual_unit(const AttnArgs &a, int bh, int runit, int lane, uint16_t *vt)
+__device__ void mfma_residual_unit(const AttnArgs &a, int bh, int runit, int lane, float *po, float *pm,
+                                   float *pl)
 {
     constexpr int NC = D / 32;
     constexpr int MT = D / 16;
@@ -471,6 +480,7 @@ __device__ void mfma_residual_unit(const AttnArgs &a, int bh, int runit, int lan
     const int bf = a.kv_bf16;
     const int t_beg = a.Tq + runit * a.res_tokens;
     const int t_end = min(a.N, t_beg + a.res_tokens);
+    uint16_t *vt = reinterpret_cast<uint16_t *>(po);  // [D][32] tile, then the results
     const uint16_t *rk = L.ring_k + static_cast<size_t>(bh) * L.R * D;
     const uint16_t *rv = L.ring_v + static_cast<size_t>(bh) * L.R * D;
 
@@ -491,7 +501,7 @@ __device__ void mfma_residual_unit(const AttnArgs &a, int bh, int runit, int lan
                 amax = fmaxf(amax, fabsf(qv[k][i]));
             }
         }
-        amax = xor_max(amax);
+        amax = col_max(amax);
         const int qexp = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) : 0;
         sh = bf ? 0 : 14 - qexp;  // fp16 operands need the fp16 range
 #pragma unroll
@@ -569,7 +579,7 @@ __device__ void mfma_residual_unit(const AttnArgs &a, int bh, int runit, int lan
         }
         float tmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
                            fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-        tmax = xor_max(tmax);
+        tmax = col_max(tmax);
         const bool need = act && (tmax > m_run + kTau);
         if (__builtin_amdgcn_ballot_w64(need) != 0) {
             const float m_new = need ? tmax : m_run;
@@ -615,18 +625,17 @@ __device__ void mfma_residual_unit(const AttnArgs &a, int bh, int runit, int lan
             }
         }
     }
-    const float Lc = xor_sum(l_run);
+    const float Lc = col_sum(l_run);
+    asm volatile("" ::: "memory");  // the V tile's last reads stay before the result writes
     if (act) {
-        const int ps = part_stride(D);
-        float *part = a.part + ((static_cast<size_t>(bh) * a.n_part + a.units_q + runit) * g + col) * ps;
 #pragma unroll
         for (int m = 0; m < MT; ++m)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                part_store(part + 16 * m + 4 * q + j, ldexpf(O[m][j], -kWShift));
+            *reinterpret_cast<f4_t *>(po + col * D + 16 * m + 4 * q) =
+                f4_t{ldexpf(O[m][0], -kWShift), ldexpf(O[m][1], -kWShift), ldexpf(O[m][2], -kWShift),
+                     ldexpf(O[m][3], -kWShift)};
         if (q == 0) {
-            part_store(part + D, m_run);
-            part_store(part + D + 1, Lc);
+            pm[col] = m_run;
+            pl[col] = Lc;
         }
     }
 }
@@ -636,18 +645,33 @@ __device__ void mfma_residual_unit(const AttnArgs &a, int bh, int runit, int lan
 template <int KB, int VB>
 constexpr int mfma_waves_per_simd() { return 2; }
 
+// LDS floats per wave: the recent-token V tile (32 x D 16-bit values) when
+// the launch has recent-token units, and the wave's results o[g][D].
+__host__ __device__ inline int wave_region(const AttnArgs &a)
+{
+    const int vt = a.units_r > 0 ? 16 * a.D : 0;
+    return vt > a.g * a.D ? vt : a.g * a.D;
+}
+
 template <int KB, int VB, int D>
 __global__ __launch_bounds__(kAttnThreads, (mfma_waves_per_simd<KB, VB>())) void attn_mfma_kernel(AttnArgs a)
 {
-    const int bh = blockIdx.y, wg = blockIdx.x;
-    const int unit = wg * 4 + (threadIdx.x >> 6);
+    extern __shared__ float lds[];
+    __shared__ float s_pm[kAttnThreads / 64][kMaxG], s_pl[kAttnThreads / 64][kMaxG];
+    const int bh = blockIdx.y, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int unit = blockIdx.x * 4 + wave;
+    const int region = wave_region(a);
+    float *po = lds + wave * region;
     if (unit < a.units_q) {
-        mfma_unit<KB, VB, D>(a, bh, unit, threadIdx.x & 63);
+        mfma_unit<KB, VB, D>(a, bh, unit, lane, po, s_pm[wave], s_pl[wave]);
     } else if (unit < a.units_q + a.units_r) {
-        extern __shared__ uint16_t vt_lds[];  // 32 x D per wave
-        mfma_residual_unit<D>(a, bh, unit - a.units_q, threadIdx.x & 63,
-                              vt_lds + (threadIdx.x >> 6) * 32 * D);
+        mfma_residual_unit<D>(a, bh, unit - a.units_q, lane, po, s_pm[wave], s_pl[wave]);
+    } else if (lane < a.g) {
+        s_pm[wave][lane] = -INFINITY;
+        s_pl[wave][lane] = 0.0f;
     }
+    __syncthreads();
+    wg_merge_store(a, bh, blockIdx.x, lds, region, s_pm, s_pl);
     arrive_and_merge(a, bh, gridDim.x);
 }
 
@@ -655,7 +679,7 @@ template <int KB, int VB>
 hipError_t launch_pair(const AttnArgs &a, hipStream_t st)
 {
     dim3 grid(a.mfma_wgs, a.BH);
-    const size_t lds = a.units_r > 0 ? 4 * 32 * a.D * sizeof(uint16_t) : 0;
+    const size_t lds = (kAttnThreads / 64) * wave_region(a) * sizeof(float);
     hipLaunchKernelGGL((attn_mfma_kernel<KB, VB, KVQ_D>), grid, dim3(kAttnThreads), lds, st, a);
     return hipGetLastError();
 }

@@ -56,11 +56,11 @@ struct AttnArgs {
     LayerDev L;
     const void *q;        // [B][Hq][D] in q_dtype
     float *out;           // [B][Hq][D]
-    float *part;          // [BH][n_part][g][D + 2]: o[D], m (log2 domain), l
+    float *part;          // [BH][n_part][g][D + 4]: o[D], m (log2 domain), l, 2 unused
     unsigned *counters;   // [BH] arrival counters, zero between calls
     int q_dtype, kv_bf16;
     int D, g, Hkv, N, Tq, BH;
-    int n_part;           // partial entries per stream
+    int n_part;           // partial entries per stream (one per workgroup)
     // vector-ALU ranges: wg_valu workgroups per stream cover tokens [valu_beg, N)
     int valu_beg, valu_wgs, valu_tps;
     // matrix-core units: units_q waves per stream cover groups [0, Tq / G),

@@ -425,7 +425,8 @@ int kvq_decode_attention(kvq_handle *h, int layer, const void *q, float *out)
         a.valu_wgs = S;
         a.units_q = a.unit_groups = a.units_r = a.res_tokens = a.mfma_wgs = 0;
     }
-    a.n_part = a.units_q + a.units_r + a.valu_wgs;
+    // one partial entry per workgroup
+    a.n_part = use_mfma ? a.mfma_wgs : a.valu_wgs;
     e = kvq::launch_attention(a, use_mfma, h->stream);
     if (e != hipSuccess)
         return h->dev_fail(e, "attention launch");
