@@ -256,8 +256,6 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *
     const int g_beg = unit * a.unit_groups;
     const int g_end = min(g_beg + a.unit_groups, n_groups);
     const int t_unit = g_beg * G;
-    const int nblk = (g_end - g_beg) * G / 32;
-    const int win_tokens = NG * G;
 
     const size_t q_base = (static_cast<size_t>(b) * a.Hkv * g + kvh * g + h) * D + q * QC;
     const uint32_t *kw_base = L.k_words + static_cast<size_t>(bh) * L.capq * L.wk + q * KW;
@@ -289,11 +287,11 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *
     int w_first = t_unit;
     bool act_win = false;
 
-    auto process = [&](const BlockData<KW, FW> &d, int t0) {
-        if ((t0 - t_unit) % win_tokens == 0) {
-            // ---- new window: B operand of q.K for this lane's column, q * s as hi/lo fp16 ----
-            w_first = t0;
-            const int w0 = t0 / G;
+    // ---- new window of groups [w0, w0 + NG): B operand of q.K for this lane's
+    // column, q * s as hi/lo fp16 ----
+    auto setup_window = [&](int w0) {
+        {
+            w_first = w0 * G;
             const int nwin = min(NG, g_end - w0);
             act_win = jslot < nwin;
             const int gi = w0 + (act_win ? jslot : 0);
@@ -334,6 +332,9 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *
             }
             kscale = ldexpf(1.0f, -sh);  // acc * 2^-sh
         }
+    };
+
+    auto process = [&](const BlockData<KW, FW> &d, int t0) {
         const int slot = (t0 - w_first) / G;
         const bool act = act_win && jslot == slot;
 
@@ -419,19 +420,25 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *
         }
     };
 
-    // ping-pong over the unit's blocks: the next block loads while this one computes
+    // windows of NG groups; inside, ping-pong over the blocks: the next block
+    // loads while this one computes
     BlockData<KW, FW> bufA, bufB;
-    load_block(bufA, t_unit);
-    for (int bi = 0; bi < nblk; bi += 2) {
-        const int t0 = t_unit + bi * 32;
-        if (bi + 1 < nblk)
-            load_block(bufB, t0 + 32);
-        process(bufA, t0);
-        if (bi + 1 >= nblk)
-            break;
-        if (bi + 2 < nblk)
-            load_block(bufA, t0 + 64);
-        process(bufB, t0 + 32);
+    for (int w0 = g_beg; w0 < g_end; w0 += NG) {
+        const int wt0 = w0 * G;
+        const int wblk = min(NG, g_end - w0) * G / 32;
+        load_block(bufA, wt0);
+        setup_window(w0);
+        for (int bi = 0; bi < wblk; bi += 2) {
+            const int t0 = wt0 + bi * 32;
+            if (bi + 1 < wblk)
+                load_block(bufB, t0 + 32);
+            process(bufA, t0);
+            if (bi + 1 >= wblk)
+                break;
+            if (bi + 2 < wblk)
+                load_block(bufA, t0 + 64);
+            process(bufB, t0 + 32);
+        }
     }
 
     // this lane's column: l, z-term and o (weights carry 2^(kWShift - E)); the
@@ -658,7 +665,9 @@ __global__ __launch_bounds__(kAttnThreads, (mfma_waves_per_simd<KB, VB>())) void
 {
     extern __shared__ float lds[];
     __shared__ float s_pm[kAttnThreads / 64][kMaxG], s_pl[kAttnThreads / 64][kMaxG];
-    const int bh = blockIdx.y, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // the wave index is uniform across the wave: keep it (and everything derived
+    // from it) in scalar registers, so that unit bounds and branches are scalar
+    const int bh = blockIdx.y, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int unit = blockIdx.x * 4 + wave;
     const int region = wave_region(a);
     float *po = lds + wave * region;

@@ -20,7 +20,8 @@ namespace {
 
 thread_local std::string g_create_error = "no error";
 
-constexpr int kMaxPart = 128;  // partial entries per stream (splits + units); P * g <= 2048
+constexpr int kMaxPart = 128;  // partial entries per stream (one per workgroup), as the merge supports
+constexpr int kMaxUnits = 4 * kMaxPart;  // matrix-core units per stream (four per workgroup)
 constexpr int kMaxG = 16;
 constexpr int kMaxTileElems = 16384;  // group_size * head_dim staged by the flush kernel
 
@@ -370,27 +371,34 @@ int kvq_decode_attention(kvq_handle *h, int layer, const void *q, float *out)
         // matrix-core units over whole groups, then over the recent tokens
         const int n_groups = s.Tq / d.G;
         const int Tr = s.N - s.Tq;
+        // recent tokens: 32-token blocks, about as many per unit as a quantized unit holds
+        auto res_len = [&](long ug_) {
+            int r = static_cast<int>(ug_ * d.G);
+            r = (r + 31) / 32 * 32;
+            return r < 64 ? 64 : r;
+        };
         long ug = 1;
         if (n_groups > 0) {
-            // about one unit (wave) per SIMD over the whole launch
-            ug = (static_cast<long>(n_groups) * BH + 4L * h->cu_count - 1) / (4L * h->cu_count);
+            // as many units (waves) as the register allocation keeps resident at
+            // once, two per SIMD: no second, partly filled round of waves
+            const long cap = 8L * h->cu_count;
+            ug = (static_cast<long>(n_groups) * BH + cap - 1) / cap;
+            if (ug < 1)
+                ug = 1;
+            while (ug < n_groups &&
+                   BH * ((n_groups + ug - 1) / ug + (Tr + res_len(ug) - 1) / res_len(ug)) > cap)
+                ++ug;
             const char *env = getenv("KVQ_UNIT_GROUPS");
             if (env && atoi(env) > 0)
                 ug = atoi(env);
-            if (ug < 1)
-                ug = 1;
             if (ug > n_groups)
                 ug = n_groups;
         }
-        // recent tokens: 32-token blocks, about as many per unit as a quantized unit holds
-        int rt = static_cast<int>(ug * d.G);
-        rt = (rt + 31) / 32 * 32;
-        if (rt < 64)
-            rt = 64;
+        int rt = res_len(ug);
         for (;;) {
             const int uq = n_groups > 0 ? static_cast<int>((n_groups + ug - 1) / ug) : 0;
             const int ur = (Tr + rt - 1) / rt;
-            if (uq + ur <= kMaxPart)
+            if (uq + ur <= kMaxUnits)
                 break;
             if (uq > ur)
                 ++ug;
@@ -427,6 +435,8 @@ int kvq_decode_attention(kvq_handle *h, int layer, const void *q, float *out)
     }
     // one partial entry per workgroup
     a.n_part = use_mfma ? a.mfma_wgs : a.valu_wgs;
+    if (a.n_part < 1 || a.n_part > kMaxPart)
+        return h->fail(KVQ_EINVAL, "internal: %d partial entries per stream", a.n_part);
     e = kvq::launch_attention(a, use_mfma, h->stream);
     if (e != hipSuccess)
         return h->dev_fail(e, "attention launch");
