@@ -224,15 +224,31 @@ __device__ __forceinline__ float coset_max(float v, int S)
     return v;
 }
 
-// Block data of 32 tokens: K rows of both 16-token tiles, the V fragment and
-// the V meta (s, z) of this lane's 8 k-slot tokens.
-template <int KW, int FW>
-struct BlockData {
-    uint32_t k0[KW], k1[KW], v[FW];
+// Blocks (32 tokens each, one per group slot) processed together in one
+// round: four, or fewer when a block's operands take many registers.
+template <int KB, int VB, int D>
+constexpr int round_blocks()
+{
+    constexpr int regs = 2 * (D * KB / 128) + D * VB / 64;  // K rows of two tiles + V fragment
+    return regs >= 48 ? 1 : (regs >= 24 ? 2 : 4);
+}
+
+// Data of one round: for each of its blocks the K rows of both 16-token tiles
+// and the V fragment; the V meta (s, z) of this lane's eight k-slot tokens in
+// its own block.
+template <int NB, int KW, int FW>
+struct RoundData {
+    uint32_t k0[NB][KW], k1[NB][KW], v[NB][FW];
     float4 vm[4];
 };
 
-// Results of one unit for head h < g go to po[h * D + c], pm[h], pl[h] (LDS).
+// One unit: groups [g_beg, g_end) of stream bh, in windows of NG groups (one
+// per column slot).  Inside a window, round (r, u) takes block r of the groups
+// in slots u .. u + nb - 1: every block's q.K product is computed for all 16
+// columns, and each lane keeps the scores of the block of its own slot, so the
+// softmax work of one round serves nb blocks.  In the P.V products a lane's
+// weights enter only its own block's product (zeros elsewhere).
+// Results for head h < g go to po[h * D + c], pm[h], pl[h] (LDS).
 template <int KB, int VB, int D>
 __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *po, float *pm, float *pl)
 {
@@ -243,6 +259,7 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *
     constexpr int CW = 32 / KB;         // K channels per word
     constexpr int FW = D * VB / 64;     // V words per lane per 32-token block
     constexpr int MT = D / 16;          // 16-channel tiles of P.V
+    constexpr int NB = round_blocks<KB, VB, D>();
 
     const LayerDev &L = a.L;
     const int G = L.G, g = a.g;
@@ -255,7 +272,7 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *
     const int n_groups = a.Tq / G;
     const int g_beg = unit * a.unit_groups;
     const int g_end = min(g_beg + a.unit_groups, n_groups);
-    const int t_unit = g_beg * G;
+    const int bpg = G / 32;  // blocks per group
 
     const size_t q_base = (static_cast<size_t>(b) * a.Hkv * g + kvh * g + h) * D + q * QC;
     const uint32_t *kw_base = L.k_words + static_cast<size_t>(bh) * L.capq * L.wk + q * KW;
@@ -263,20 +280,8 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *
     const uint32_t *vw_base = L.v_words + static_cast<size_t>(bh) * L.capq * L.wv + lane * FW;
     const float *vm_base = L.v_meta + static_cast<size_t>(bh) * L.capq * 2;
 
-    auto load_block = [&](BlockData<KW, FW> &d, int t0) {
-        load_words(kw_base + static_cast<size_t>(t0 + col) * L.wk, d.k0);
-        load_words(kw_base + static_cast<size_t>(t0 + 16 + col) * L.wk, d.k1);
-        load_words(vw_base + static_cast<size_t>(t0) * L.wv, d.v);
-        const float4 *m0 = reinterpret_cast<const float4 *>(vm_base + static_cast<size_t>(t0 + 4 * q) * 2);
-        const float4 *m1 = reinterpret_cast<const float4 *>(vm_base + static_cast<size_t>(t0 + 16 + 4 * q) * 2);
-        d.vm[0] = m0[0];
-        d.vm[1] = m0[1];
-        d.vm[2] = m1[0];
-        d.vm[3] = m1[1];
-    };
-
     float m_run = -INFINITY, l_run = 0.0f, zb_run = 0.0f;
-    int E = -1000;  // running V-scale exponent: all weights are scaled by 2^-E
+    int E = -1000;  // running V-scale exponent of this column: its weights carry 2^-E
     f4_t O[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m)
@@ -284,101 +289,123 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *
 
     Frag bhi[NC], blo[NC];
     float bias = 0.0f, kscale = 0.0f;
-    int w_first = t_unit;
-    bool act_win = false;
 
-    // ---- new window of groups [w0, w0 + NG): B operand of q.K for this lane's
+    // ---- window of groups [w0, w0 + nwin): B operand of q.K for this lane's
     // column, q * s as hi/lo fp16 ----
-    auto setup_window = [&](int w0) {
-        {
-            w_first = w0 * G;
-            const int nwin = min(NG, g_end - w0);
-            act_win = jslot < nwin;
-            const int gi = w0 + (act_win ? jslot : 0);
-            const float *sp = km_base + static_cast<size_t>(gi) * 2 * D;
-            const float *zp = sp + D;
-            float qs[QC], qv[QC];
-            load_q_run<QC>(a.q, a.q_dtype, q_base, qv);
-            const float qscale = act_win ? a.scale_log2 : 0.0f;
-            float amax = 0.0f;
-            bias = 0.0f;
+    auto setup_window = [&](int w0, int nwin) {
+        const bool act_win = jslot < nwin;
+        const int gi = w0 + (act_win ? jslot : 0);
+        const float *sp = km_base + static_cast<size_t>(gi) * 2 * D;
+        const float *zp = sp + D;
+        float qs[QC], qv[QC];
+        load_q_run<QC>(a.q, a.q_dtype, q_base, qv);
+        const float qscale = act_win ? a.scale_log2 : 0.0f;
+        float amax = 0.0f;
+        bias = 0.0f;
 #pragma unroll
-            for (int i = 0; i < QC; i += 4) {
-                const float4 s4 = *reinterpret_cast<const float4 *>(sp + i);
-                const float4 z4 = *reinterpret_cast<const float4 *>(zp + i);
-                const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
-                const float zv[4] = {z4.x, z4.y, z4.z, z4.w};
+        for (int i = 0; i < QC; i += 4) {
+            const float4 s4 = *reinterpret_cast<const float4 *>(sp + i);
+            const float4 z4 = *reinterpret_cast<const float4 *>(zp + i);
+            const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+            const float zv[4] = {z4.x, z4.y, z4.z, z4.w};
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const float qq = qv[i + k] * qscale;
-                    qs[i + k] = qq * sv[k];
-                    bias = __builtin_fmaf(qq, zv[k], bias);
-                    amax = fmaxf(amax, fabsf(qs[i + k]));
-                }
+            for (int k = 0; k < 4; ++k) {
+                const float qq = qv[i + k] * qscale;
+                qs[i + k] = qq * sv[k];
+                bias = __builtin_fmaf(qq, zv[k], bias);
+                amax = fmaxf(amax, fabsf(qs[i + k]));
             }
-            bias = col_sum(bias);
-            amax = col_max(amax);
-            const int sexp = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) : 0;
-            const int sh = 14 - sexp;  // |q s| * 2^sh < 2^14
-#pragma unroll
-            for (int k = 0; k < NC; ++k) {
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const int R = 4 * k + p;
-                    const int clo = (R / PK) * CW + (R % PK), chi = clo + PK;
-                    const int e = sh - class_exp<KB>(R);
-                    split_pair(ldexpf(qs[clo], e), ldexpf(qs[chi], e), bhi[k].u[p], blo[k].u[p]);
-                }
-            }
-            kscale = ldexpf(1.0f, -sh);  // acc * 2^-sh
         }
-    };
-
-    auto process = [&](const BlockData<KW, FW> &d, int t0) {
-        const int slot = (t0 - w_first) / G;
-        const bool act = act_win && jslot == slot;
-
-        // q.K for tokens t0 + 4q + j (acc0) and t0 + 16 + 4q + j (acc1)
-        uint32_t k08[KW], k18[KW];
-        shift8(d.k0, k08);
-        shift8(d.k1, k18);
-        f4_t acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+        bias = col_sum(bias);
+        amax = col_max(amax);
+        const int sexp = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) : 0;
+        const int sh = 14 - sexp;  // |q s| * 2^sh < 2^14
 #pragma unroll
         for (int k = 0; k < NC; ++k) {
-            Frag a0, a1;
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
-                a0.u[p] = code_reg<KB>(d.k0, k08, 4 * k + p);
-                a1.u[p] = code_reg<KB>(d.k1, k18, 4 * k + p);
+                const int R = 4 * k + p;
+                const int clo = (R / PK) * CW + (R % PK), chi = clo + PK;
+                const int e = sh - class_exp<KB>(R);
+                split_pair(ldexpf(qs[clo], e), ldexpf(qs[chi], e), bhi[k].u[p], blo[k].u[p]);
             }
-            acc0 = mfma(a0, bhi[k], acc0);
-            acc0 = mfma(a0, blo[k], acc0);
-            acc1 = mfma(a1, bhi[k], acc1);
-            acc1 = mfma(a1, blo[k], acc1);
         }
+        kscale = ldexpf(1.0f, -sh);  // acc * 2^-sh
+    };
+
+    // ---- one round: nb blocks starting at tokens t_first + i * G ----
+    auto load_round = [&](RoundData<NB, KW, FW> &d, int t_first, int nb, int my_b) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            if (i < nb) {
+                const int t0 = t_first + i * G;
+                load_words(kw_base + static_cast<size_t>(t0 + col) * L.wk, d.k0[i]);
+                load_words(kw_base + static_cast<size_t>(t0 + 16 + col) * L.wk, d.k1[i]);
+                load_words(vw_base + static_cast<size_t>(t0) * L.wv, d.v[i]);
+            }
+        }
+        const int tm = t_first + my_b * G;
+        const float4 *m0 = reinterpret_cast<const float4 *>(vm_base + static_cast<size_t>(tm + 4 * q) * 2);
+        const float4 *m1 = reinterpret_cast<const float4 *>(vm_base + static_cast<size_t>(tm + 16 + 4 * q) * 2);
+        d.vm[0] = m0[0];
+        d.vm[1] = m0[1];
+        d.vm[2] = m1[0];
+        d.vm[3] = m1[1];
+    };
+
+    auto process_round = [&](const RoundData<NB, KW, FW> &d, int nb, bool mine, int my_b) {
+        // q.K for tokens 4q + j (acc0) and 16 + 4q + j (acc1) of each block;
+        // this lane keeps its own block's scores
+        float sc[8];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            if (i < nb) {
+                uint32_t k08[KW], k18[KW];
+                shift8(d.k0[i], k08);
+                shift8(d.k1[i], k18);
+                f4_t acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int k = 0; k < NC; ++k) {
+                    Frag a0, a1;
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        a0.u[p] = code_reg<KB>(d.k0[i], k08, 4 * k + p);
+                        a1.u[p] = code_reg<KB>(d.k1[i], k18, 4 * k + p);
+                    }
+                    acc0 = mfma(a0, bhi[k], acc0);
+                    acc0 = mfma(a0, blo[k], acc0);
+                    acc1 = mfma(a1, bhi[k], acc1);
+                    acc1 = mfma(a1, blo[k], acc1);
+                }
+                if (i == 0 || my_b == i) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        sc[j] = acc0[j];
+                        sc[4 + j] = acc1[j];
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            sc[j] = __builtin_fmaf(sc[j], kscale, bias);
         const float vs[8] = {d.vm[0].x, d.vm[0].z, d.vm[1].x, d.vm[1].z,
                              d.vm[2].x, d.vm[2].z, d.vm[3].x, d.vm[3].z};
         const float vz[8] = {d.vm[0].y, d.vm[0].w, d.vm[1].y, d.vm[1].w,
                              d.vm[2].y, d.vm[2].w, d.vm[3].y, d.vm[3].w};
-        float sc[8];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            sc[j] = __builtin_fmaf(acc0[j], kscale, bias);
-            sc[4 + j] = __builtin_fmaf(acc1[j], kscale, bias);
-        }
         float tmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
                            fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
         tmax = col_max(tmax);
-        // V-scale exponent of the block: s < 2^eb for every token
+        // V-scale exponent of this column's block: s < 2^eb for every token
         float vmax = fmaxf(fmaxf(fmaxf(vs[0], vs[1]), fmaxf(vs[2], vs[3])),
                            fmaxf(fmaxf(vs[4], vs[5]), fmaxf(vs[6], vs[7])));
         vmax = col_max(vmax);
-        int eb = vmax > 0.0f ? __builtin_amdgcn_frexp_expf(vmax) : -1000;
-        eb = __builtin_amdgcn_readfirstlane(eb);
-        const bool need = act && (tmax > m_run + kTau);
-        if (__builtin_amdgcn_ballot_w64(need) != 0 || eb > E) {
-            const float m_new = need ? tmax : m_run;
-            const int E_new = max(E, eb);
+        const int eb = vmax > 0.0f ? __builtin_amdgcn_frexp_expf(vmax) : -1000;
+        const bool need_m = mine && (tmax > m_run + kTau);
+        const bool need_e = mine && (eb > E);
+        if (__builtin_amdgcn_ballot_w64(need_m || need_e) != 0) {
+            const float m_new = need_m ? tmax : m_run;
+            const int E_new = need_e ? eb : E;
             const float alpha = (m_new == m_run) ? 1.0f : exp2f(m_run - m_new);
             const float f = ldexpf(alpha, E - E_new);
 #pragma unroll
@@ -389,7 +416,7 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *
             m_run = m_new;
             E = E_new;
         }
-        const float mo = act ? m_run : INFINITY;  // inactive columns: weights 0
+        const float mo = mine ? m_run : INFINITY;  // columns without a block here: weights 0
         float p[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -407,37 +434,43 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *
             split_pair(ldexpf(p[2 * r] * vs[2 * r], e), ldexpf(p[2 * r + 1] * vs[2 * r + 1], e), whi.u[r],
                        wlo.u[r]);
         }
-        uint32_t v8[FW];
-        shift8(d.v, v8);
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            Frag av;
+        for (int i = 0; i < NB; ++i) {
+            if (i < nb) {
+                Frag bh_, bl_;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                av.u[r] = code_reg<VB>(d.v, v8, 4 * m + r);
-            O[m] = mfma(av, whi, O[m]);
-            O[m] = mfma(av, wlo, O[m]);
+                for (int r = 0; r < 4; ++r) {
+                    bh_.u[r] = (my_b == i) ? whi.u[r] : 0u;
+                    bl_.u[r] = (my_b == i) ? wlo.u[r] : 0u;
+                }
+                uint32_t v8[FW];
+                shift8(d.v[i], v8);
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    Frag av;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        av.u[r] = code_reg<VB>(d.v[i], v8, 4 * m + r);
+                    O[m] = mfma(av, bh_, O[m]);
+                    O[m] = mfma(av, bl_, O[m]);
+                }
+            }
         }
     };
 
-    // windows of NG groups; inside, ping-pong over the blocks: the next block
-    // loads while this one computes
-    BlockData<KW, FW> bufA, bufB;
     for (int w0 = g_beg; w0 < g_end; w0 += NG) {
-        const int wt0 = w0 * G;
-        const int wblk = min(NG, g_end - w0) * G / 32;
-        load_block(bufA, wt0);
-        setup_window(w0);
-        for (int bi = 0; bi < wblk; bi += 2) {
-            const int t0 = wt0 + bi * 32;
-            if (bi + 1 < wblk)
-                load_block(bufB, t0 + 32);
-            process(bufA, t0);
-            if (bi + 1 >= wblk)
-                break;
-            if (bi + 2 < wblk)
-                load_block(bufA, t0 + 64);
-            process(bufB, t0 + 32);
+        const int nwin = min(NG, g_end - w0);
+        const bool in_win = jslot < nwin;
+        setup_window(w0, nwin);
+        for (int r = 0; r < bpg; ++r) {
+            for (int u = 0; u < nwin; u += NB) {
+                const int nb = min(NB, nwin - u);
+                const bool mine = in_win && jslot >= u && jslot < u + nb;
+                const int my_b = mine ? jslot - u : 0;
+                RoundData<NB, KW, FW> d;
+                load_round(d, (w0 + u) * G + r * 32, nb, my_b);
+                process_round(d, nb, mine, my_b);
+            }
         }
     }
 

@@ -379,15 +379,20 @@ int kvq_decode_attention(kvq_handle *h, int layer, const void *q, float *out)
         };
         long ug = 1;
         if (n_groups > 0) {
-            // as many units (waves) as the register allocation keeps resident at
-            // once, two per SIMD: no second, partly filled round of waves
+            // units of whole windows (the kernel's ng groups, one per column slot
+            // of the matrix products), as many units (waves) as the register
+            // allocation keeps resident at once, two per SIMD: no second, partly
+            // filled round of waves
+            const int g = h->cfg.n_q_heads / h->cfg.n_kv_heads;
+            long ng = 16;
+            while (ng * g > 16)
+                ng >>= 1;
             const long cap = 8L * h->cu_count;
             ug = (static_cast<long>(n_groups) * BH + cap - 1) / cap;
-            if (ug < 1)
-                ug = 1;
+            ug = (ug + ng - 1) / ng * ng;
             while (ug < n_groups &&
                    BH * ((n_groups + ug - 1) / ug + (Tr + res_len(ug) - 1) / res_len(ug)) > cap)
-                ++ug;
+                ug += ng;
             const char *env = getenv("KVQ_UNIT_GROUPS");
             if (env && atoi(env) > 0)
                 ug = atoi(env);
