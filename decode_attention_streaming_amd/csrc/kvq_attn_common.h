@@ -467,24 +467,18 @@ __device__ __forceinline__ void wg_merge_store(const AttnArgs &a, int bh, int en
     }
 }
 
-// Partial entries per stream the merge supports (one per workgroup).
-constexpr int kMaxEntries = 128;
-
 // Called by every workgroup at its end: the last one of stream bh to arrive
 // merges the n_part partial entries, out = sum_s 2^(m_s - M) o_s /
 // sum_s 2^(m_s - M) l_s, M = max_s m_s, and re-arms the stream's counter.
 // Thread t owns four channels of one head (item t % n_items) and the entries
-// sub, sub + n_sub, ... (sub = t / n_items): its o loads are issued together
-// with the (m, l) loads of all entries, so that up to kLoads entries per
-// thread cost one memory round trip; the per-entry weights come from LDS and
-// the n_sub partial sums are added through LDS.
+// sub, sub + n_sub, ... (sub = t / n_items).  It issues the (m, l) and o loads
+// of up to kChunk of its entries together (one memory round trip), merges them
+// online, and the n_sub partial states of an item are merged through LDS.
 __device__ __forceinline__ void arrive_and_merge(const AttnArgs &a, int bh, unsigned n_wgs)
 {
-    constexpr int kLoads = 16;
+    constexpr int kChunk = 16;
     __shared__ int s_last;
-    __shared__ float s_w[kMaxEntries * kMaxG];  // m, then the weight 2^(m - M), of (entry, head)
-    __shared__ float s_l[kMaxEntries * kMaxG];
-    __shared__ float s_den[kMaxG];
+    __shared__ float s_m[kAttnThreads], s_d[kAttnThreads];
     __shared__ f4_t s_acc[kAttnThreads];
     __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are complete
     __syncthreads();
@@ -502,77 +496,69 @@ __device__ __forceinline__ void arrive_and_merge(const AttnArgs &a, int bh, unsi
     const int n_sub = n_items >= kAttnThreads ? 1 : kAttnThreads / n_items;
     const int b = bh / a.Hkv, kvh = bh % a.Hkv;
     const PartBuf pb(a, bh);
-    // (1) issue the (m, l) loads of every (entry, head), then the first o loads
-    f4_t ml[kMaxEntries * kMaxG / kAttnThreads];
-#pragma unroll
-    for (int k = 0; k < kMaxEntries * kMaxG / kAttnThreads; ++k) {
-        const int i = tid + k * kAttnThreads;
-        if (i < P * g)
-            ml[k] = pb.load4(pb.off(a, i / g, i % g, D));
-    }
     for (int it0 = 0; it0 < n_items; it0 += kAttnThreads) {
         const int item = it0 + (n_sub > 1 ? tid % n_items : tid);
         const int sub = n_sub > 1 ? tid / n_items : 0;
         const bool own = item < n_items && sub < n_sub;
         const int h = own ? item / nc4 : 0, c4 = own ? item % nc4 : 0;
+        float M = -INFINITY, den = 0.0f;
         f4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int e0 = 0; e0 < P; e0 += kLoads * n_sub) {
-            f4_t ov[kLoads];
+        for (int e0 = sub; e0 < P; e0 += kChunk * n_sub) {
+            f4_t ml[kChunk], ov[kChunk];
 #pragma unroll
-            for (int k = 0; k < kLoads; ++k) {
-                const int e = e0 + sub + k * n_sub;
-                if (own && e < P)
+            for (int k = 0; k < kChunk; ++k) {
+                const int e = e0 + k * n_sub;
+                if (own && e < P) {
+                    ml[k] = pb.load4(pb.off(a, e, h, D));
                     ov[k] = pb.load4(pb.off(a, e, h, 4 * c4));
-            }
-            if (it0 == 0 && e0 == 0) {
-                // (2) per head: M, weights, normalizer (one wave per head, lanes over entries)
-#pragma unroll
-                for (int k = 0; k < kMaxEntries * kMaxG / kAttnThreads; ++k) {
-                    const int i = tid + k * kAttnThreads;
-                    if (i < P * g) {
-                        s_w[i] = ml[k][0];
-                        s_l[i] = ml[k][1];
-                    }
                 }
-                __syncthreads();
-                const int lane = tid & 63, wave = tid >> 6;
-                for (int hh = wave; hh < g; hh += kAttnThreads / 64) {
-                    float M = -INFINITY;
-                    for (int e = lane; e < P; e += 64)
-                        M = fmaxf(M, s_w[e * g + hh]);
-                    M = wave_max(M);
-                    float den = 0.0f;
-                    for (int e = lane; e < P; e += 64) {
-                        const float me = s_w[e * g + hh];
-                        const float w = (me == -INFINITY) ? 0.0f : exp2f(me - M);
-                        s_w[e * g + hh] = w;
-                        den = __builtin_fmaf(w, s_l[e * g + hh], den);
-                    }
-                    den = wave_sum(den);
-                    if (lane == 0)
-                        s_den[hh] = den;
-                }
-                __syncthreads();
             }
+            float Mc = M;
 #pragma unroll
-            for (int k = 0; k < kLoads; ++k) {
-                const int e = e0 + sub + k * n_sub;
-                if (own && e < P)
-                    acc += s_w[e * g + h] * ov[k];
+            for (int k = 0; k < kChunk; ++k)
+                if (own && e0 + k * n_sub < P)
+                    Mc = fmaxf(Mc, ml[k][0]);
+            if (Mc == -INFINITY)
+                continue;
+            const float r = (M == -INFINITY) ? 0.0f : exp2f(M - Mc);
+            acc *= r;
+            den *= r;
+            M = Mc;
+#pragma unroll
+            for (int k = 0; k < kChunk; ++k) {
+                if (own && e0 + k * n_sub < P && ml[k][0] != -INFINITY) {
+                    const float w = exp2f(ml[k][0] - M);
+                    acc += w * ov[k];
+                    den = __builtin_fmaf(w, ml[k][1], den);
+                }
             }
         }
-        // (3) add the n_sub partial sums of each item and write the output
         if (n_sub > 1) {
+            // merge the n_sub states of each item (entry sets of its threads)
+            s_m[tid] = M;
+            s_d[tid] = den;
             s_acc[tid] = acc;
             __syncthreads();
             if (own && sub == 0) {
+                float Mt = M;
                 for (int j = 1; j < n_sub; ++j)
-                    acc += s_acc[tid + j * n_items];
+                    Mt = fmaxf(Mt, s_m[tid + j * n_items]);
+                const float r0 = (M == -INFINITY) ? 0.0f : exp2f(M - Mt);
+                acc *= r0;
+                den *= r0;
+                for (int j = 1; j < n_sub; ++j) {
+                    const float mj = s_m[tid + j * n_items];
+                    if (mj == -INFINITY)
+                        continue;
+                    const float rj = exp2f(mj - Mt);
+                    acc += rj * s_acc[tid + j * n_items];
+                    den = __builtin_fmaf(rj, s_d[tid + j * n_items], den);
+                }
             }
         }
         if (own && sub == 0)
             *reinterpret_cast<f4_t *>(a.out + (static_cast<size_t>(b) * a.Hkv * g + kvh * g + h) * D + 4 * c4) =
-                acc * (1.0f / s_den[h]);
+                acc * (1.0f / den);
     }
     if (tid == 0)
         __hip_atomic_store(a.counters + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
