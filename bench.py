@@ -2,7 +2,8 @@
 
 One step = for every layer: append one token per sequence (K and V, with a
 group flush whenever the recent-token buffer is full), then decode attention
-of one query token per sequence over the layer's whole cache.  Inputs are
+of one query token per sequence over the layer's whole cache, issued as one
+kvq_append_decode_attention call (one launch when no flush is due).  Inputs are
 seeded synthetic tensors already resident in HBM.
 
 Default workload: Llama-3.1-8B-shaped decode (32 layers, 32 query / 8 KV heads,
@@ -182,9 +183,9 @@ def main():
     torch.cuda.synchronize()
 
     def step(s):
+        # one call per layer: append one token per sequence, then attend
         for l in range(L):
-            cache.append(l, knew[l][s], vnew[l][s])
-            cache.decode_attention(l, qs[l][s], outs[l])
+            cache.append_decode_attention(l, knew[l][s], vnew[l][s], qs[l][s], outs[l])
 
     for s in range(args.warmup):
         step(s)

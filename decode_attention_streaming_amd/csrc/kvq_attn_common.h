@@ -189,22 +189,32 @@ __device__ __forceinline__ void stage_words(uint32_t *dst, const uint32_t *src, 
 }
 
 // Ring rows of tokens [t0, t0 + n) into LDS [n][D] (n * D / 8 <= MAXI * 256).
+// Token new_t, when in range, is read from new_row instead of the ring and
+// also stored into its ring slot.
 template <int D, int MAXI>
-__device__ __forceinline__ void stage_ring(uint16_t *dst, const uint16_t *ring, int R, int t0, int n)
+__device__ __forceinline__ void stage_ring(uint16_t *dst, uint16_t *ring, int R, int t0, int n,
+                                           const uint16_t *new_row, int new_t)
 {
     constexpr int CH = D / 8;  // 16-byte chunks per row
     uint4 v[MAXI];
 #pragma unroll
     for (int k = 0; k < MAXI; ++k) {
         const int it = threadIdx.x + k * kAttnThreads;
-        if (it < n * CH)
-            v[k] = reinterpret_cast<const uint4 *>(ring + static_cast<size_t>((t0 + it / CH) % R) * D)[it % CH];
+        if (it < n * CH) {
+            const int t = t0 + it / CH;
+            const uint16_t *row = (t == new_t) ? new_row : ring + static_cast<size_t>(t % R) * D;
+            v[k] = reinterpret_cast<const uint4 *>(row)[it % CH];
+        }
     }
 #pragma unroll
     for (int k = 0; k < MAXI; ++k) {
         const int it = threadIdx.x + k * kAttnThreads;
-        if (it < n * CH)
+        if (it < n * CH) {
             reinterpret_cast<uint4 *>(dst + (it / CH) * D)[it % CH] = v[k];
+            const int t = t0 + it / CH;
+            if (t == new_t)
+                reinterpret_cast<uint4 *>(ring + static_cast<size_t>(t % R) * D)[it % CH] = v[k];
+        }
     }
 }
 
@@ -278,10 +288,10 @@ __device__ void valu_range(const AttnArgs &a, int bh, int t_beg, int t_end, int 
             stage_words<4>(k_tile, L.k_words + (row0 + tile) * L.wk, nt * L.wk);
             stage_words<4>(v_tile, L.v_words + (row0 + tile) * L.wv, nt * L.wv);
         } else {
-            stage_ring<D, 4>(reinterpret_cast<uint16_t *>(k_tile),
-                             L.ring_k + static_cast<size_t>(bh) * L.R * D, L.R, tile, nt);
-            stage_ring<D, 4>(reinterpret_cast<uint16_t *>(v_tile),
-                             L.ring_v + static_cast<size_t>(bh) * L.R * D, L.R, tile, nt);
+            stage_ring<D, 4>(reinterpret_cast<uint16_t *>(k_tile), L.ring_k + static_cast<size_t>(bh) * L.R * D,
+                             L.R, tile, nt, a.new_k + static_cast<size_t>(bh) * D, a.new_t);
+            stage_ring<D, 4>(reinterpret_cast<uint16_t *>(v_tile), L.ring_v + static_cast<size_t>(bh) * L.R * D,
+                             L.R, tile, nt, a.new_v + static_cast<size_t>(bh) * D, a.new_t);
         }
         // per-thread metadata while the tile lands
         const int ti = tid / P, part = tid % P, c0 = part * CPT;

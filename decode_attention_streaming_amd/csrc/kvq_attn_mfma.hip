@@ -521,8 +521,16 @@ __device__ void mfma_residual_unit(const AttnArgs &a, int bh, int runit, int lan
     const int t_beg = a.Tq + runit * a.res_tokens;
     const int t_end = min(a.N, t_beg + a.res_tokens);
     uint16_t *vt = reinterpret_cast<uint16_t *>(po);  // [D][32] tile, then the results
-    const uint16_t *rk = L.ring_k + static_cast<size_t>(bh) * L.R * D;
-    const uint16_t *rv = L.ring_v + static_cast<size_t>(bh) * L.R * D;
+    uint16_t *rk = L.ring_k + static_cast<size_t>(bh) * L.R * D;
+    uint16_t *rv = L.ring_v + static_cast<size_t>(bh) * L.R * D;
+    // row of token t: the ring, or the just-appended token's own row
+    const int new_t = a.new_t;
+    auto k_row = [&](int t) {
+        return (t == new_t) ? a.new_k + static_cast<size_t>(bh) * D : rk + static_cast<size_t>(t % L.R) * D;
+    };
+    auto v_row = [&](int t) {
+        return (t == new_t) ? a.new_v + static_cast<size_t>(bh) * D : rv + static_cast<size_t>(t % L.R) * D;
+    };
 
     // B operand of q.K: q of head h, chunk k, quad q -> channels 32k + 8q + i
     Frag b1[NC], b2[NC], b3[NC];
@@ -567,20 +575,34 @@ __device__ void mfma_residual_unit(const AttnArgs &a, int bh, int runit, int lan
         // K rows of the two 16-token tiles (rows past the end repeat the last token)
         const int ta = min(t0 + col, t_end - 1), tb = min(t0 + 16 + col, t_end - 1);
         uint4 ka[NC], kb2[NC];
+        const uint16_t *ra = k_row(ta), *rb = k_row(tb);
 #pragma unroll
         for (int k = 0; k < NC; ++k) {
-            ka[k] = *reinterpret_cast<const uint4 *>(rk + static_cast<size_t>(ta % L.R) * D + 32 * k + 8 * q);
-            kb2[k] = *reinterpret_cast<const uint4 *>(rk + static_cast<size_t>(tb % L.R) * D + 32 * k + 8 * q);
+            ka[k] = *reinterpret_cast<const uint4 *>(ra + 32 * k + 8 * q);
+            kb2[k] = *reinterpret_cast<const uint4 *>(rb + 32 * k + 8 * q);
+        }
+        // the just-appended token's K row goes to its ring slot
+        if (t0 + col == new_t || t0 + 16 + col == new_t) {
+            uint16_t *dst = rk + static_cast<size_t>(new_t % L.R) * D;
+#pragma unroll
+            for (int k = 0; k < NC; ++k)
+                *reinterpret_cast<uint4 *>(dst + 32 * k + 8 * q) = (t0 + col == new_t) ? ka[k] : kb2[k];
         }
         // V rows -> LDS [channel][token]: lane handles token (lane & 31), half of the row
         {
             const int tt = lane & 31, half = lane >> 5;
             const int tv = min(t0 + tt, t_end - 1);
-            const uint4 *src = reinterpret_cast<const uint4 *>(rv + static_cast<size_t>(tv % L.R) * D + half * (D / 2));
+            const uint4 *src = reinterpret_cast<const uint4 *>(v_row(tv) + half * (D / 2));
             uint4 v[D / 16];
 #pragma unroll
             for (int i = 0; i < D / 16; ++i)
                 v[i] = src[i];
+            if (t0 + tt == new_t) {  // the just-appended token's V row goes to its ring slot
+                uint4 *dst = reinterpret_cast<uint4 *>(rv + static_cast<size_t>(new_t % L.R) * D + half * (D / 2));
+#pragma unroll
+                for (int i = 0; i < D / 16; ++i)
+                    dst[i] = v[i];
+            }
 #pragma unroll
             for (int i = 0; i < D / 16; ++i) {
                 const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};

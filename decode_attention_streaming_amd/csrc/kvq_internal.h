@@ -69,6 +69,11 @@ struct AttnArgs {
     // units_r) / 4) workgroups
     int units_q, unit_groups, units_r, res_tokens, mfma_wgs;
     float scale_log2;     // log2(e) / sqrt(D)
+    // token new_t (>= 0) has just been appended and is not in the ring yet: it
+    // is read from new_k / new_v ([BH][D]) and written to its ring slot by the
+    // workgroup that attends to it; new_t = -1 when there is none
+    const uint16_t *new_k, *new_v;
+    int new_t;
 };
 
 hipError_t launch_flush(const FlushArgs &a, hipStream_t st);

@@ -318,17 +318,72 @@ int kvq_append(kvq_handle *h, int layer, const void *k_new, const void *v_new, i
     return KVQ_OK;
 }
 
-int kvq_decode_attention(kvq_handle *h, int layer, const void *q, float *out)
+// Arguments of a decode-attention call, checked before any state changes.
+static int check_attention_args(kvq_handle *h, int layer, const void *q, const float *out)
 {
-    if (!h)
-        return KVQ_EINVAL;
     if (layer < 0 || layer >= h->cfg.n_layers)
         return h->fail(KVQ_EINVAL, "layer %d out of range [0, %d)", layer, h->cfg.n_layers);
     if (!q || !out)
         return h->fail(KVQ_EINVAL, "q or out is NULL");
-    LayerState &s = h->plan.layers[layer];
-    if (s.N == 0)
+    if (reinterpret_cast<uintptr_t>(q) % 16 || reinterpret_cast<uintptr_t>(out) % 16)
+        return h->fail(KVQ_EINVAL, "q and out must be 16-byte aligned");
+    return KVQ_OK;
+}
+
+// One attention launch over the layer's current state.  new_t >= 0: token
+// new_t was appended but is not in the ring yet (its rows are new_k / new_v);
+// the launch also stores it there.
+static int attention_launch(kvq_handle *h, int layer, const void *q, float *out, const void *new_k,
+                            const void *new_v, int new_t);
+
+int kvq_decode_attention(kvq_handle *h, int layer, const void *q, float *out)
+{
+    if (!h)
+        return KVQ_EINVAL;
+    const int rc = check_attention_args(h, layer, q, out);
+    if (rc != KVQ_OK)
+        return rc;
+    if (h->plan.layers[layer].N == 0)
         return h->fail(KVQ_EINVAL, "layer %d holds no tokens", layer);
+    return attention_launch(h, layer, q, out, nullptr, nullptr, -1);
+}
+
+int kvq_append_decode_attention(kvq_handle *h, int layer, const void *k_new, const void *v_new, const void *q,
+                                float *out)
+{
+    if (!h)
+        return KVQ_EINVAL;
+    int rc = check_attention_args(h, layer, q, out);
+    if (rc != KVQ_OK)
+        return rc;
+    if (!k_new || !v_new)
+        return h->fail(KVQ_EINVAL, "k_new or v_new is NULL");
+    if (reinterpret_cast<uintptr_t>(k_new) % 16 || reinterpret_cast<uintptr_t>(v_new) % 16)
+        return h->fail(KVQ_EINVAL, "k_new and v_new must be 16-byte aligned");
+    LayerState &s = h->plan.layers[layer];
+    const kvq::LayerDev &d = s.dev;
+    if (static_cast<long>(s.N) + 1 > h->cfg.max_context)
+        return h->fail(KVQ_ECAPACITY, "layer %d: %d + 1 tokens exceed max_context %d", layer, s.N,
+                       h->cfg.max_context);
+    const bool flush = d.kb != 16 && s.N - s.Tq == d.R;  // the recent buffer is full
+    if (flush) {
+        rc = kvq_append(h, layer, k_new, v_new, 1);
+        if (rc != KVQ_OK)
+            return rc;
+        return attention_launch(h, layer, q, out, nullptr, nullptr, -1);
+    }
+    const int t = s.N;
+    s.N = t + 1;
+    rc = attention_launch(h, layer, q, out, k_new, v_new, t);
+    if (rc != KVQ_OK)
+        s.N = t;
+    return rc;
+}
+
+static int attention_launch(kvq_handle *h, int layer, const void *q, float *out, const void *new_k,
+                            const void *new_v, int new_t)
+{
+    LayerState &s = h->plan.layers[layer];
     if (h->cu_count == 0) {
         int dev = 0, n = 0;
         hipError_t e = hipGetDevice(&dev);
@@ -363,6 +418,9 @@ int kvq_decode_attention(kvq_handle *h, int layer, const void *q, float *out)
     a.Tq = s.Tq;
     a.BH = BH;
     a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D)));
+    a.new_t = new_t;
+    a.new_k = new_t >= 0 ? static_cast<const uint16_t *>(new_k) : d.ring_k;
+    a.new_v = new_t >= 0 ? static_cast<const uint16_t *>(new_v) : d.ring_v;
     const char *force_valu = getenv("KVQ_FORCE_VALU");
     const bool use_mfma = (d.kb == 16 || (d.v_tiled && kvq::mfma_supported(d.kb, d.vb, D))) &&
                           !(force_valu && atoi(force_valu) > 0);

@@ -18,9 +18,9 @@ KVQ_F32, KVQ_F16, KVQ_BF16 = 0, 1, 2
 KVQ_WORKSPACE_ALIGN = 256
 _DT = {"f32": KVQ_F32, "f16": KVQ_F16, "bf16": KVQ_BF16}
 
-EXPORTED = ["kvq_workspace_bytes", "kvq_create", "kvq_append", "kvq_decode_attention", "kvq_bytes",
-            "kvq_bytes_layer", "kvq_export_layer", "kvq_sync", "kvq_set_stream", "kvq_last_error",
-            "kvq_destroy", "kvq_last_launch"]
+EXPORTED = ["kvq_workspace_bytes", "kvq_create", "kvq_append", "kvq_decode_attention",
+            "kvq_append_decode_attention", "kvq_bytes", "kvq_bytes_layer", "kvq_export_layer", "kvq_sync",
+            "kvq_set_stream", "kvq_last_error", "kvq_destroy", "kvq_last_launch"]
 
 
 class kvq_layer_cfg(ctypes.Structure):
@@ -65,6 +65,7 @@ def lib():
         "kvq_create": (I, [P, P, ctypes.c_size_t, P]),
         "kvq_append": (I, [P, I, P, P, I]),
         "kvq_decode_attention": (I, [P, I, P, P]),
+        "kvq_append_decode_attention": (I, [P, I, P, P, P, P]),
         "kvq_bytes": (ctypes.c_int64, [P]),
         "kvq_bytes_layer": (I, [P, I, P]),
         "kvq_export_layer": (I, [P, I] + [P] * 8),
@@ -119,6 +120,10 @@ def kvq_append(h, layer, k_ptr, v_ptr, n_new):
 
 def kvq_decode_attention(h, layer, q_ptr, out_ptr):
     return _check(lib().kvq_decode_attention(h, layer, q_ptr, out_ptr), h)
+
+
+def kvq_append_decode_attention(h, layer, k_ptr, v_ptr, q_ptr, out_ptr):
+    return _check(lib().kvq_append_decode_attention(h, layer, k_ptr, v_ptr, q_ptr, out_ptr), h)
 
 
 def kvq_bytes(h):
@@ -210,7 +215,7 @@ class Cache:
         kvq_append(self.h, layer, ctypes.c_void_p(k_new.data_ptr()),
                    ctypes.c_void_p(v_new.data_ptr()), k_new.shape[2])
 
-    def decode_attention(self, layer, q, out=None):
+    def _q_check(self, q, out):
         s = self.shape
         torch = self.torch
         want = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[self.q_dtype]
@@ -219,8 +224,24 @@ class Cache:
             raise ValueError("q must be contiguous [B, Hq, d] %s" % want)
         if out is None:
             out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        return out
+
+    def decode_attention(self, layer, q, out=None):
+        out = self._q_check(q, out)
         kvq_decode_attention(self.h, layer, ctypes.c_void_p(q.data_ptr()),
                              ctypes.c_void_p(out.data_ptr()))
+        return out
+
+    def append_decode_attention(self, layer, k_new, v_new, q, out=None):
+        """One token per sequence appended, then decode attention (one call)."""
+        self._kv_check(k_new)
+        self._kv_check(v_new)
+        if k_new.shape[2] != 1 or v_new.shape[2] != 1:
+            raise ValueError("one token per sequence")
+        out = self._q_check(q, out)
+        kvq_append_decode_attention(self.h, layer, ctypes.c_void_p(k_new.data_ptr()),
+                                    ctypes.c_void_p(v_new.data_ptr()), ctypes.c_void_p(q.data_ptr()),
+                                    ctypes.c_void_p(out.data_ptr()))
         return out
 
     def bytes(self):

@@ -121,10 +121,21 @@ int kvq_append(kvq_handle *h, int layer, const void *k_new, const void *v_new, i
 /* Decode attention of one query token per sequence over every token of `layer`
  * (quantized tokens dequantized on the fly, recent tokens in 16 bits), scale
  * 1/sqrt(head_dim).
- *   q:   device pointer, [batch][n_q_heads][head_dim] in q_dtype.
- *   out: device pointer, [batch][n_q_heads][head_dim] fp32.
- * Errors: KVQ_EINVAL (bad layer, null pointer, empty layer), KVQ_EDEVICE. */
+ *   q:   device pointer, [batch][n_q_heads][head_dim] in q_dtype, 16-byte aligned.
+ *   out: device pointer, [batch][n_q_heads][head_dim] fp32, 16-byte aligned.
+ * Errors: KVQ_EINVAL (bad layer, null or misaligned pointer, empty layer),
+ * KVQ_EDEVICE. */
 int kvq_decode_attention(kvq_handle *h, int layer, const void *q, float *out);
+
+/* One decode step of one layer: kvq_append of one token per sequence
+ * (k_new, v_new: [batch][n_kv_heads][1][head_dim]) followed by
+ * kvq_decode_attention, with results identical to those two calls (state,
+ * export and output).  When the append needs no flush, the new token reaches
+ * the recent-token buffer inside the attention launch (one launch instead of
+ * two); the streaming rule is the one of the KIVI notes, section 6.2.
+ * Errors: those of the two calls; on error the layer is unchanged. */
+int kvq_append_decode_attention(kvq_handle *h, int layer, const void *k_new, const void *v_new, const void *q,
+                                float *out);
 
 /* Live bytes of the cache state over all layers, host arithmetic only: per
  * (sequence, kv-head): Tq rows of packed K and V codes (4 bytes per word), one

@@ -190,3 +190,37 @@ def test_unit_sizes_and_column_merge(ug, monkeypatch):
         w = ad_hoc_workload(400 + Hq + kb, 2, Hq, Hkv, 128, kb, vb, G, G, 1700, "bf16", "bf16")
         print("unit groups", ug, "g", Hq // Hkv, "pair", (kb, vb), flush=True)
         _run_case(w, [1650, 1])
+
+
+@pytest.mark.parametrize("kind", ["mfma_k4v2", "valu_k3v4", "plain16", "valu_g16"])
+def test_append_decode_attention_equals_two_calls(kind):
+    """The one-call decode step (append one token, then attend) gives the same
+    outputs, bit for bit, and the same state as kvq_append + kvq_decode_attention,
+    across flushes of the recent-token buffer."""
+    spec = {  # (B, Hq, Hkv, d, kb, vb, G, R, ctx, kv, q)
+        "mfma_k4v2": (2, 8, 2, 128, 4, 2, 32, 32, 200, "bf16", "bf16"),
+        "valu_k3v4": (2, 2, 2, 128, 3, 4, 32, 50, 200, "f16", "f32"),
+        "plain16": (1, 4, 1, 128, 16, 16, 32, 32, 160, "bf16", "bf16"),
+        "valu_g16": (1, 8, 2, 64, 8, 4, 16, 24, 160, "f16", "f16"),
+    }[kind]
+    w = ad_hoc_workload(500 + sorted(["mfma_k4v2", "valu_k3v4", "plain16", "valu_g16"]).index(kind), *spec)
+    print("fused step", kind, flush=True)
+    st = synth.LayerStats(w, 0)
+    n0 = 70
+    k, v = synth.layer_tokens(w, 0, 0, n0 + 80, DEV, stats=st)
+    two, one = make_cache(w), make_cache(w)
+    two.append(0, k[:, :, :n0].contiguous(), v[:, :, :n0].contiguous())
+    one.append(0, k[:, :, :n0].contiguous(), v[:, :, :n0].contiguous())
+    for i in range(80):
+        kt = k[:, :, n0 + i:n0 + i + 1].contiguous()
+        vt = v[:, :, n0 + i:n0 + i + 1].contiguous()
+        q = synth.query(w, 0, i, DEV)
+        two.append(0, kt, vt)
+        oa = two.decode_attention(0, q)
+        ob = one.append_decode_attention(0, kt, vt, q)
+        torch.cuda.synchronize()
+        assert torch.equal(oa, ob), "step %d: outputs differ" % i
+    compare_export(one.export(0), two.export(0))
+    orc = make_oracle(w, w.layers[0], w.context)
+    orc.append(stream_view(k), stream_view(v))
+    compare_export(one.export(0), orc.export())
