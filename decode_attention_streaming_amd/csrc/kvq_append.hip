@@ -9,10 +9,10 @@
 // (KVmix notes, key design 2).  Quantizing straight into the packed history
 // follows KVmix key design 4.
 //
-// One workgroup quantizes one group of one stream.  The group's 16-bit K tile
-// is staged in LDS with 16-byte loads, reduced per channel (min/max over the G
-// tokens), encoded and packed; then the V tile is staged in the same LDS and
-// reduced per token with wavefront min/max.
+// One workgroup quantizes the K half, another the V half of one group of one
+// stream.  The group's 16-bit tile is staged in LDS with 16-byte loads; K is
+// reduced per channel (min/max over the G tokens), V per token (min/max over
+// head_dim, a few threads per token); then the codes are packed.
 //
 // Bit-exactness with a serial CPU evaluation: min/max are exact in any order;
 // the subtraction and the IEEE fp32 division are correctly rounded (no fast
@@ -54,20 +54,6 @@ __device__ __forceinline__ uint32_t code_of(float x, float mn, float s, int qmax
     return static_cast<uint32_t>(r);
 }
 
-__device__ __forceinline__ float wave_min(float v)
-{
-    for (int off = 32; off > 0; off >>= 1)
-        v = fminf(v, __shfl_xor(v, off, 64));
-    return v;
-}
-
-__device__ __forceinline__ float wave_max(float v)
-{
-    for (int off = 32; off > 0; off >>= 1)
-        v = fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
-}
-
 __device__ __forceinline__ const uint16_t *src_row(const FlushArgs &a, const uint16_t *ring,
                                                    const uint16_t *fresh, int bh, int t)
 {
@@ -99,11 +85,12 @@ __device__ __forceinline__ void stage(const FlushArgs &a, const uint16_t *ring, 
     }
 }
 
+// One workgroup per (group, stream, K or V): the K and V halves of a group
+// are independent and run side by side.
 __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a)
 {
 #pragma clang fp contract(off)
-    const int j = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int j = blockIdx.x, bh = blockIdx.y, is_v = blockIdx.z, tid = threadIdx.x;
     const int D = a.D, G = a.L.G;
     const int t0 = a.Tq0 + j * G;
     const int gi = t0 / G;
@@ -113,132 +100,139 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a)
     __shared__ float red_mn[kThreads], red_mx[kThreads];
     __shared__ float s_c[256], mn_c[256];
 
-    // ---- Key: min / max per channel over the G tokens ----
-    stage(a, a.L.ring_k, a.k_new, bh, t0, tile);
-    __syncthreads();
-    const int parts = kThreads / D;  // threads per channel (D divides 256)
-    const int c = tid % D, p = tid / D;
-    float mn = INFINITY, mx = -INFINITY;
-    for (int i = p; i < G; i += parts) {
-        const float x = widen16(tile[i * D + c], bf);
-        mn = fminf(mn, x);
-        mx = fmaxf(mx, x);
-    }
-    red_mn[tid] = mn;
-    red_mx[tid] = mx;
-    __syncthreads();
-    if (p == 0) {
-        for (int r = 1; r < parts; ++r) {
-            mn = fminf(mn, red_mn[r * D + c]);
-            mx = fmaxf(mx, red_mx[r * D + c]);
+    if (!is_v) {
+        // ---- Key: min / max per channel over the G tokens ----
+        stage(a, a.L.ring_k, a.k_new, bh, t0, tile);
+        __syncthreads();
+        const int parts = kThreads / D;  // threads per channel (D divides 256)
+        const int c = tid % D, p = tid / D;
+        float mn = INFINITY, mx = -INFINITY;
+        for (int i = p; i < G; i += parts) {
+            const float x = widen16(tile[i * D + c], bf);
+            mn = fminf(mn, x);
+            mx = fmaxf(mx, x);
         }
-        const float s = (mx - mn) / static_cast<float>(qmax_of(a.L.kb, c));
-        s_c[c] = s;
-        mn_c[c] = mn;
-        float *meta = a.L.k_meta + (static_cast<size_t>(bh) * (a.L.capq / G) + gi) * 2 * D;
-        meta[c] = (s == 0.0f) ? 0.0f : s;
-        meta[D + c] = (mn == 0.0f) ? 0.0f : mn;
-    }
-    __syncthreads();
-
-    // ---- Key codes: one packed word per work item (token i, word w) ----
-    const int wk = a.L.wk, kb = a.L.kb;
-    for (int it = tid; it < G * wk; it += kThreads) {
-        const int i = it / wk, w = it % wk;
-        const uint16_t *row = tile + i * D;
-        uint32_t word = 0;
-        if (kb == 3) {
-            for (int sl = 0; sl < 11; ++sl) {
-                const int cc = w * 11 + sl;
-                if (cc < D)
-                    word |= code_of(widen16(row[cc], bf), mn_c[cc], s_c[cc], qmax_of(3, cc)) << (3 * sl);
+        red_mn[tid] = mn;
+        red_mx[tid] = mx;
+        __syncthreads();
+        if (p == 0) {
+            for (int r = 1; r < parts; ++r) {
+                mn = fminf(mn, red_mn[r * D + c]);
+                mx = fmaxf(mx, red_mx[r * D + c]);
             }
-        } else {
-            const int epw = 32 / kb, qm = (1 << kb) - 1;
-            for (int sl = 0; sl < epw; ++sl) {
-                const int cc = w * epw + sl;
-                word |= code_of(widen16(row[cc], bf), mn_c[cc], s_c[cc], qm) << (kb * sl);
-            }
+            const float s = (mx - mn) / static_cast<float>(qmax_of(a.L.kb, c));
+            s_c[c] = s;
+            mn_c[c] = mn;
+            float *meta = a.L.k_meta + (static_cast<size_t>(bh) * (a.L.capq / G) + gi) * 2 * D;
+            meta[c] = (s == 0.0f) ? 0.0f : s;
+            meta[D + c] = (mn == 0.0f) ? 0.0f : mn;
         }
-        a.L.k_words[(static_cast<size_t>(bh) * a.L.capq + t0 + i) * wk + w] = word;
-    }
-    __syncthreads();
+        __syncthreads();
 
-    // ---- Value: one wave per token, min / max over the D channels ----
-    stage(a, a.L.ring_v, a.v_new, bh, t0, tile);
-    __syncthreads();
-    const int vb = a.L.vb, vq = (1 << vb) - 1;
-    for (int i = wave; i < G; i += kThreads / 64) {
-        float vmn = INFINITY, vmx = -INFINITY;
-        for (int cc = lane; cc < D; cc += 64) {
-            const float x = widen16(tile[i * D + cc], bf);
-            vmn = fminf(vmn, x);
-            vmx = fmaxf(vmx, x);
-        }
-        vmn = wave_min(vmn);
-        vmx = wave_max(vmx);
-        if (lane == 0) {
-            const float s = (vmx - vmn) / static_cast<float>(vq);
-            red_mn[i] = vmn;  // reuse: per-token minimum and scale
-            red_mx[i] = s;
-            float *vm = a.L.v_meta + (static_cast<size_t>(bh) * a.L.capq + t0 + i) * 2;
-            vm[0] = (s == 0.0f) ? 0.0f : s;
-            vm[1] = (vmn == 0.0f) ? 0.0f : vmn;
-        }
-    }
-    __syncthreads();
-
-    const int wv = a.L.wv;
-    uint32_t *vrow0 = a.L.v_words + (static_cast<size_t>(bh) * a.L.capq + t0) * wv;
-    if (a.L.v_tiled) {
-        // 32-token blocks of operand fragments (layout in kvq_layout.h)
-        const int fw = D * vb / 64, P = 16 / vb, blk_words = D * vb;
-        for (int it = tid; it < G * wv; it += kThreads) {
-            const int blk = it / blk_words, wi = it % blk_words;
-            const int frag = wi / fw, u = wi % fw;
-            const int q = frag >> 4, c16 = frag & 15;
+        // ---- Key codes: one packed word per work item (token i, word w) ----
+        const int wk = a.L.wk, kb = a.L.kb;
+        for (int it = tid; it < G * wk; it += kThreads) {
+            const int i = it / wk, w = it % wk;
+            const uint16_t *row = tile + i * D;
             uint32_t word = 0;
-            for (int jj = 0; jj < P; ++jj) {
-                const int R = u * P + jj, m = R >> 2;
-                for (int half = 0; half < 2; ++half) {
-                    const int s = 2 * (R & 3) + half;
-                    const int tb = (s >> 2) * 16 + 4 * q + (s & 3);
-                    const int i = blk * 32 + tb, cc = 16 * m + c16;
-                    word |= code_of(widen16(tile[i * D + cc], bf), red_mn[i], red_mx[i], vq)
-                            << (vb * jj + 16 * half);
+            if (kb == 3) {
+                for (int sl = 0; sl < 11; ++sl) {
+                    const int cc = w * 11 + sl;
+                    if (cc < D)
+                        word |= code_of(widen16(row[cc], bf), mn_c[cc], s_c[cc], qmax_of(3, cc)) << (3 * sl);
+                }
+            } else {
+                const int epw = 32 / kb, qm = (1 << kb) - 1;
+                for (int sl = 0; sl < epw; ++sl) {
+                    const int cc = w * epw + sl;
+                    word |= code_of(widen16(row[cc], bf), mn_c[cc], s_c[cc], qm) << (kb * sl);
                 }
             }
-            vrow0[it] = word;
+            a.L.k_words[(static_cast<size_t>(bh) * a.L.capq + t0 + i) * wk + w] = word;
         }
     } else {
-        const int epw = 32 / vb;
-        for (int it = tid; it < G * wv; it += kThreads) {
-            const int i = it / wv, w = it % wv;
-            uint32_t word = 0;
-            for (int sl = 0; sl < epw; ++sl) {
-                const int cc = w * epw + sl;
-                word |= code_of(widen16(tile[i * D + cc], bf), red_mn[i], red_mx[i], vq) << (vb * sl);
+        // ---- Value: min / max per token over the D channels, tpt threads per token ----
+        stage(a, a.L.ring_v, a.v_new, bh, t0, tile);
+        __syncthreads();
+        const int vb = a.L.vb, vq = (1 << vb) - 1;
+        const int tpt = G <= kThreads ? kThreads / G : 1;  // threads per token
+        for (int i0 = 0; i0 < G; i0 += kThreads / tpt) {
+            const int i = i0 + tid / tpt, sub = tid % tpt;
+            float vmn = INFINITY, vmx = -INFINITY;
+            if (i < G && tid / tpt < kThreads / tpt) {
+                for (int cc = sub; cc < D; cc += tpt) {
+                    const float x = widen16(tile[i * D + cc], bf);
+                    vmn = fminf(vmn, x);
+                    vmx = fmaxf(vmx, x);
+                }
             }
-            vrow0[it] = word;
+            __syncthreads();  // red_* of the previous pass are consumed
+            red_mn[tid] = vmn;
+            red_mx[tid] = vmx;
+            __syncthreads();
+            if (i < G && sub == 0 && tid / tpt < kThreads / tpt) {
+                for (int r = 1; r < tpt; ++r) {
+                    vmn = fminf(vmn, red_mn[tid + r]);
+                    vmx = fmaxf(vmx, red_mx[tid + r]);
+                }
+                const float s = (vmx - vmn) / static_cast<float>(vq);
+                s_c[i % 256] = s;  // per-token scale and minimum (G <= 256 per pass)
+                mn_c[i % 256] = vmn;
+                float *vm = a.L.v_meta + (static_cast<size_t>(bh) * a.L.capq + t0 + i) * 2;
+                vm[0] = (s == 0.0f) ? 0.0f : s;
+                vm[1] = (vmn == 0.0f) ? 0.0f : vmn;
+            }
+        }
+        __syncthreads();
+
+        const int wv = a.L.wv;
+        uint32_t *vrow0 = a.L.v_words + (static_cast<size_t>(bh) * a.L.capq + t0) * wv;
+        if (a.L.v_tiled) {
+            // 32-token blocks of operand fragments (layout in kvq_layout.h)
+            const int fw = D * vb / 64, P = 16 / vb, blk_words = D * vb;
+            for (int it = tid; it < G * wv; it += kThreads) {
+                const int blk = it / blk_words, wi = it % blk_words;
+                const int frag = wi / fw, u = wi % fw;
+                const int q = frag >> 4, c16 = frag & 15;
+                uint32_t word = 0;
+                for (int jj = 0; jj < P; ++jj) {
+                    const int R = u * P + jj, m = R >> 2;
+                    for (int half = 0; half < 2; ++half) {
+                        const int s = 2 * (R & 3) + half;
+                        const int tb = (s >> 2) * 16 + 4 * q + (s & 3);
+                        const int i = blk * 32 + tb, cc = 16 * m + c16;
+                        word |= code_of(widen16(tile[i * D + cc], bf), mn_c[i], s_c[i], vq) << (vb * jj + 16 * half);
+                    }
+                }
+                vrow0[it] = word;
+            }
+        } else {
+            const int epw = 32 / vb;
+            for (int it = tid; it < G * wv; it += kThreads) {
+                const int i = it / wv, w = it % wv;
+                uint32_t word = 0;
+                for (int sl = 0; sl < epw; ++sl) {
+                    const int cc = w * epw + sl;
+                    word |= code_of(widen16(tile[i * D + cc], bf), mn_c[i], s_c[i], vq) << (vb * sl);
+                }
+                vrow0[it] = word;
+            }
         }
     }
 
     if (a.ring_after && j == 0) {
         // single-token append: the new token takes the slot of the oldest
-        // flushed token, which was staged above
+        // flushed token, which was staged above (K by the K workgroup, V by the V one)
         __syncthreads();
         const size_t dst = (static_cast<size_t>(bh) * a.L.R + (a.N0 % a.L.R)) * D;
         const size_t src = static_cast<size_t>(bh) * D;
-        for (int ch = tid; ch < D / 8; ch += kThreads) {
-            *reinterpret_cast<uint4 *>(a.L.ring_k + dst + ch * 8) =
-                *reinterpret_cast<const uint4 *>(a.k_new + src + ch * 8);
-            *reinterpret_cast<uint4 *>(a.L.ring_v + dst + ch * 8) =
-                *reinterpret_cast<const uint4 *>(a.v_new + src + ch * 8);
-        }
+        uint16_t *ring = is_v ? a.L.ring_v : a.L.ring_k;
+        const uint16_t *fresh = is_v ? a.v_new : a.k_new;
+        for (int ch = tid; ch < D / 8; ch += kThreads)
+            *reinterpret_cast<uint4 *>(ring + dst + ch * 8) = *reinterpret_cast<const uint4 *>(fresh + src + ch * 8);
     }
 }
 
-// Copy the new tokens that stay recent into their ring slots, 16 bytes per item.
 __global__ __launch_bounds__(kThreads) void ring_write_kernel(RingArgs a)
 {
     const int chunks = a.D / 8;  // 8 16-bit values per 16-byte chunk
@@ -268,7 +262,7 @@ __global__ void zero_kernel(unsigned *p, int n)
 
 hipError_t launch_flush(const FlushArgs &a, hipStream_t st)
 {
-    dim3 grid(a.n_groups, a.BH);
+    dim3 grid(a.n_groups, a.BH, 2);
     hipLaunchKernelGGL(flush_kernel, grid, dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
