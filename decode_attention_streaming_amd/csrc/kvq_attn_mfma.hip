@@ -250,7 +250,8 @@ struct RoundData {
 // weights enter only its own block's product (zeros elsewhere).
 // Results for head h < g go to po[h * D + c], pm[h], pl[h] (LDS).
 template <int KB, int VB, int D>
-__device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *po, float *pm, float *pl)
+__device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *po, float *pm, float *pl,
+                          float *meta_lds)
 {
     constexpr int NC = D / 32;          // 32-channel chunks of q.K
     constexpr int QC = D / 4;           // channels owned by one lane quad
@@ -290,15 +291,55 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *
     Frag bhi[NC], blo[NC];
     float bias = 0.0f, kscale = 0.0f;
 
-    // ---- window of groups [w0, w0 + nwin): B operand of q.K for this lane's
-    // column, q * s as hi/lo fp16 ----
-    auto setup_window = [&](int w0, int nwin) {
+    // ---- window of groups [w0, w0 + nwin): its K scales and zeros go to this
+    // wave's LDS with direct-to-LDS loads (no registers held while they fly), so
+    // that the window's first round can load at the same time ----
+    // The stream's q (g heads, fp32 or 16-bit) follows them, loaded the same way.
+    const int qbytes = a.q_dtype == 0 ? 4 : 2;
+    float *q_lds = meta_lds + NG * 2 * D;
+    auto setup_issue = [&](int w0, int nwin) {
+        const float *src = L.k_meta + (static_cast<size_t>(bh) * (L.capq / G) + w0) * 2 * D;
+        const int n16 = nwin * D / 2;  // 16-byte pieces of nwin groups' [2][D] floats
+        for (int i0 = 0; i0 < n16; i0 += 64) {
+            if (i0 + lane < n16)
+                __builtin_amdgcn_global_load_lds(src + 4 * (i0 + lane), meta_lds + 4 * i0, 16, 0, 0);
+        }
+        const char *qsrc = static_cast<const char *>(a.q) + (static_cast<size_t>(b) * a.Hkv + kvh) * g * D * qbytes;
+        const int nq16 = g * D * qbytes / 16;
+        for (int i0 = 0; i0 < nq16; i0 += 64) {
+            if (i0 + lane < nq16)
+                __builtin_amdgcn_global_load_lds(qsrc + 16 * (i0 + lane), q_lds + 4 * i0, 16, 0, 0);
+        }
+    };
+    // ---- B operand of q.K for this lane's column, q * s as hi/lo fp16; waits
+    // for every load issued so far ----
+    auto setup_compute = [&](int nwin) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         const bool act_win = jslot < nwin;
-        const int gi = w0 + (act_win ? jslot : 0);
-        const float *sp = km_base + static_cast<size_t>(gi) * 2 * D;
+        const float *sp = meta_lds + (act_win ? jslot : 0) * 2 * D + q * QC;
         const float *zp = sp + D;
         float qs[QC], qv[QC];
-        load_q_run<QC>(a.q, a.q_dtype, q_base, qv);
+        if (a.q_dtype == 0) {
+            const float4 *qp = reinterpret_cast<const float4 *>(q_lds + h * D + q * QC);
+#pragma unroll
+            for (int i = 0; i < QC / 4; ++i) {
+                const float4 v = qp[i];
+                qv[4 * i] = v.x; qv[4 * i + 1] = v.y; qv[4 * i + 2] = v.z; qv[4 * i + 3] = v.w;
+            }
+        } else {
+            const int bf = a.q_dtype == 2;
+            const uint4 *qp = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(q_lds) + h * D + q * QC);
+#pragma unroll
+            for (int i = 0; i < QC / 8; ++i) {
+                const uint4 v = qp[i];
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    qv[8 * i + 2 * k] = widen16(static_cast<uint16_t>(w[k] & 0xFFFFu), bf);
+                    qv[8 * i + 2 * k + 1] = widen16(static_cast<uint16_t>(w[k] >> 16), bf);
+                }
+            }
+        }
         const float qscale = act_win ? a.scale_log2 : 0.0f;
         float amax = 0.0f;
         bias = 0.0f;
@@ -331,6 +372,8 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *
             }
         }
         kscale = ldexpf(1.0f, -sh);  // acc * 2^-sh
+        // the next window's meta may overwrite this one only after these reads
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     };
 
     // ---- one round: nb blocks starting at tokens t_first + i * G ----
@@ -461,7 +504,7 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *
     for (int w0 = g_beg; w0 < g_end; w0 += NG) {
         const int nwin = min(NG, g_end - w0);
         const bool in_win = jslot < nwin;
-        setup_window(w0, nwin);
+        setup_issue(w0, nwin);
         for (int r = 0; r < bpg; ++r) {
             for (int u = 0; u < nwin; u += NB) {
                 const int nb = min(NB, nwin - u);
@@ -469,6 +512,8 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *
                 const int my_b = mine ? jslot - u : 0;
                 RoundData<NB, KW, FW> d;
                 load_round(d, (w0 + u) * G + r * 32, nb, my_b);
+                if (r == 0 && u == 0)  // one memory round trip for the set-up and the first round
+                    setup_compute(nwin);
                 process_round(d, nb, mine, my_b);
             }
         }
@@ -582,11 +627,17 @@ __device__ void mfma_residual_unit(const AttnArgs &a, int bh, int runit, int lan
             kb2[k] = *reinterpret_cast<const uint4 *>(rb + 32 * k + 8 * q);
         }
         // the just-appended token's K row goes to its ring slot
-        if (t0 + col == new_t || t0 + 16 + col == new_t) {
+        if (t0 + col == new_t) {
             uint16_t *dst = rk + static_cast<size_t>(new_t % L.R) * D;
 #pragma unroll
             for (int k = 0; k < NC; ++k)
-                *reinterpret_cast<uint4 *>(dst + 32 * k + 8 * q) = (t0 + col == new_t) ? ka[k] : kb2[k];
+                *reinterpret_cast<uint4 *>(dst + 32 * k + 8 * q) = ka[k];
+        }
+        if (t0 + 16 + col == new_t) {
+            uint16_t *dst = rk + static_cast<size_t>(new_t % L.R) * D;
+#pragma unroll
+            for (int k = 0; k < NC; ++k)
+                *reinterpret_cast<uint4 *>(dst + 32 * k + 8 * q) = kb2[k];
         }
         // V rows -> LDS [channel][token]: lane handles token (lane & 31), half of the row
         {
@@ -715,6 +766,16 @@ __host__ __device__ inline int wave_region(const AttnArgs &a)
     return vt > a.g * a.D ? vt : a.g * a.D;
 }
 
+// LDS floats per wave for the K scales and zeros of one window (ng groups of
+// [2][D] floats) of the quantized units, and the stream's q.
+__host__ __device__ inline int meta_region(const AttnArgs &a)
+{
+    int ng = 16;
+    while (ng * a.g > 16)
+        ng >>= 1;
+    return a.units_q > 0 ? ng * 2 * a.D + a.g * a.D : 0;  // + the stream's q (up to fp32)
+}
+
 template <int KB, int VB, int D>
 __global__ __launch_bounds__(kAttnThreads, (mfma_waves_per_simd<KB, VB>())) void attn_mfma_kernel(AttnArgs a)
 {
@@ -727,7 +788,8 @@ __global__ __launch_bounds__(kAttnThreads, (mfma_waves_per_simd<KB, VB>())) void
     const int region = wave_region(a);
     float *po = lds + wave * region;
     if (unit < a.units_q) {
-        mfma_unit<KB, VB, D>(a, bh, unit, lane, po, s_pm[wave], s_pl[wave]);
+        mfma_unit<KB, VB, D>(a, bh, unit, lane, po, s_pm[wave], s_pl[wave],
+                             lds + (kAttnThreads / 64) * region + wave * meta_region(a));
     } else if (unit < a.units_q + a.units_r) {
         mfma_residual_unit<D>(a, bh, unit - a.units_q, lane, po, s_pm[wave], s_pl[wave]);
     } else if (lane < a.g) {
@@ -743,7 +805,7 @@ template <int KB, int VB>
 hipError_t launch_pair(const AttnArgs &a, hipStream_t st)
 {
     dim3 grid(a.mfma_wgs, a.BH);
-    const size_t lds = (kAttnThreads / 64) * wave_region(a) * sizeof(float);
+    const size_t lds = (kAttnThreads / 64) * (wave_region(a) + meta_region(a)) * sizeof(float);
     hipLaunchKernelGGL((attn_mfma_kernel<KB, VB, KVQ_D>), grid, dim3(kAttnThreads), lds, st, a);
     return hipGetLastError();
 }
