@@ -758,22 +758,9 @@ __device__ void mfma_residual_unit(const AttnArgs &a, int bh, int runit, int lan
 template <int KB, int VB>
 constexpr int mfma_waves_per_simd() { return 2; }
 
-// LDS floats per wave: the recent-token V tile (32 x D 16-bit values) when
-// the launch has recent-token units, and the wave's results o[g][D].
 __host__ __device__ inline int wave_region(const AttnArgs &a)
 {
-    const int vt = a.units_r > 0 ? 16 * a.D : 0;
-    return vt > a.g * a.D ? vt : a.g * a.D;
-}
-
-// LDS floats per wave for the K scales and zeros of one window (ng groups of
-// [2][D] floats) of the quantized units, and the stream's q.
-__host__ __device__ inline int meta_region(const AttnArgs &a)
-{
-    int ng = 16;
-    while (ng * a.g > 16)
-        ng >>= 1;
-    return a.units_q > 0 ? ng * 2 * a.D + a.g * a.D : 0;  // + the stream's q (up to fp32)
+    return mfma_wave_region(a.D, a.g, a.units_q > 0, a.units_r > 0);
 }
 
 template <int KB, int VB, int D>
@@ -788,8 +775,7 @@ __global__ __launch_bounds__(kAttnThreads, (mfma_waves_per_simd<KB, VB>())) void
     const int region = wave_region(a);
     float *po = lds + wave * region;
     if (unit < a.units_q) {
-        mfma_unit<KB, VB, D>(a, bh, unit, lane, po, s_pm[wave], s_pl[wave],
-                             lds + (kAttnThreads / 64) * region + wave * meta_region(a));
+        mfma_unit<KB, VB, D>(a, bh, unit, lane, po, s_pm[wave], s_pl[wave], po);
     } else if (unit < a.units_q + a.units_r) {
         mfma_residual_unit<D>(a, bh, unit - a.units_q, lane, po, s_pm[wave], s_pl[wave]);
     } else if (lane < a.g) {
@@ -805,7 +791,7 @@ template <int KB, int VB>
 hipError_t launch_pair(const AttnArgs &a, hipStream_t st)
 {
     dim3 grid(a.mfma_wgs, a.BH);
-    const size_t lds = (kAttnThreads / 64) * (wave_region(a) + meta_region(a)) * sizeof(float);
+    const size_t lds = (kAttnThreads / 64) * wave_region(a) * sizeof(float);
     hipLaunchKernelGGL((attn_mfma_kernel<KB, VB, KVQ_D>), grid, dim3(kAttnThreads), lds, st, a);
     return hipGetLastError();
 }

@@ -76,6 +76,23 @@ struct AttnArgs {
     int new_t;
 };
 
+// LDS floats per wave of the matrix-core kernel, one region used three ways:
+// a quantized unit's K scales and zeros of one window (ng groups of [2][D]
+// floats, ng = the largest power of two with ng * g <= 16) followed by the
+// stream's q; a recent-token unit's V tile (32 x D 16-bit values); and, at the
+// end of either, the wave's results o[g][D].
+__host__ __device__ inline int mfma_wave_region(int D, int g, bool has_q_units, bool has_r_units)
+{
+    int ng = 16;
+    while (ng * g > 16)
+        ng >>= 1;
+    const int vt = has_r_units ? 16 * D : 0;
+    const int meta = has_q_units ? ng * 2 * D + g * D : 0;  // + q (up to fp32)
+    int r = g * D;
+    r = vt > r ? vt : r;
+    return meta > r ? meta : r;
+}
+
 hipError_t launch_flush(const FlushArgs &a, hipStream_t st);
 hipError_t launch_ring_write(const RingArgs &a, hipStream_t st);
 // True when the matrix-core kernel is built for this (k_bits, v_bits, D).

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -435,29 +436,68 @@ static int attention_launch(kvq_handle *h, int layer, const void *q, float *out,
             r = (r + 31) / 32 * 32;
             return r < 64 ? 64 : r;
         };
+        const int g = h->cfg.n_q_heads / h->cfg.n_kv_heads;
+        // workgroups resident at once: two per CU by the register allocation
+        // (two waves per SIMD), fewer when the LDS of four wave regions and the
+        // merge's own arrays do not fit twice in a CU's 160 KiB
+        const long wg_lds = 4L * kvq::mfma_wave_region(D, g, n_groups > 0, Tr > 0) * 4 + 8192;
+        const long per_cu = std::max(1L, std::min(2L, (160L * 1024) / wg_lds));
+        const long res_wgs = per_cu * h->cu_count;
         long ug = 1;
-        if (n_groups > 0) {
+        int rt = 0;
+        if (BH * 2 > res_wgs && !getenv("KVQ_UNIT_GROUPS")) {
+            // Many streams: each stream's work splits into U units (U a
+            // multiple of four: whole workgroups), the recent tokens into as
+            // many units as their share of the work, chosen to minimise
+            // (workgroup generations) x (unit duration) under a rough cost
+            // model in microseconds: per unit 5, per quantized 32-token block
+            // 0.8 (1.3 for K8V8/K8V4-wide rounds), per recent block 2.5.
+            const double c_blk = (d.kb + d.vb > 12) ? 1.3 : 0.8;
+            const double wq = static_cast<double>(n_groups) * (d.G / 32) * c_blk;
+            const double wr = ((Tr + 31) / 32) * 2.5;
+            int best_u = 4;
+            double best = 1e300;
+            for (int U = 4; U <= 64; U += 4) {
+                const double gens = std::ceil(static_cast<double>(BH) * (U / 4) / res_wgs);
+                const double cost = gens * (5.0 + (wq + wr) / U);
+                if (cost < best * 0.999) {
+                    best = cost;
+                    best_u = U;
+                }
+            }
+            int ur = Tr > 0 ? static_cast<int>(std::lround(best_u * wr / (wq + wr))) : 0;
+            if (Tr > 0 && ur < 1)
+                ur = 1;
+            if (n_groups > 0 && ur > best_u - 1)
+                ur = best_u - 1;
+            const int uq = best_u - ur;
+            ug = n_groups > 0 ? (n_groups + uq - 1) / uq : 1;
+            if (ur > 0)
+                rt = ((Tr + ur - 1) / ur + 31) / 32 * 32;
+        } else if (n_groups > 0) {
             // units of whole windows (the kernel's ng groups, one per column slot
-            // of the matrix products), as many units (waves) as the register
-            // allocation keeps resident at once, two per SIMD: no second, partly
-            // filled round of waves
-            const int g = h->cfg.n_q_heads / h->cfg.n_kv_heads;
+            // of the matrix products), as many units (waves) as stay resident at
+            // once: no second, partly filled generation of waves
             long ng = 16;
             while (ng * g > 16)
                 ng >>= 1;
-            const long cap = 8L * h->cu_count;
+            const long cap = 4 * res_wgs;
             ug = (static_cast<long>(n_groups) * BH + cap - 1) / cap;
             ug = (ug + ng - 1) / ng * ng;
             while (ug < n_groups &&
                    BH * ((n_groups + ug - 1) / ug + (Tr + res_len(ug) - 1) / res_len(ug)) > cap)
                 ug += ng;
-            const char *env = getenv("KVQ_UNIT_GROUPS");
-            if (env && atoi(env) > 0)
-                ug = atoi(env);
-            if (ug > n_groups)
-                ug = n_groups;
         }
-        int rt = res_len(ug);
+        if (const char *env = getenv("KVQ_UNIT_GROUPS"))
+            if (atoi(env) > 0)
+                ug = atoi(env);
+        if (ug > n_groups)
+            ug = n_groups > 0 ? n_groups : 1;
+        if (rt == 0)
+            rt = res_len(ug);
+        if (const char *env = getenv("KVQ_RES_TOKENS"))
+            if (atoi(env) > 0)
+                rt = (atoi(env) + 31) / 32 * 32;
         for (;;) {
             const int uq = n_groups > 0 ? static_cast<int>((n_groups + ug - 1) / ug) : 0;
             const int ur = (Tr + rt - 1) / rt;

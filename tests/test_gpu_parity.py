@@ -59,6 +59,10 @@ CASES = {
     "mfma_k4v4_g8_G128": (1, 8, 1, 128, 4, 4, 128, 128, 700, "bf16", "bf16", [600, 3]),
     "mfma_k2v4_g5_d64": (2, 10, 2, 64, 2, 4, 64, 70, 500, "f16", "f32", [400, 30]),
     "mfma_k8v8_g4_long": (1, 4, 1, 128, 8, 8, 32, 32, 2100, "bf16", "bf16", [2050, 1]),
+    # more streams than resident workgroups: units sized per stream, the recent
+    # tokens split over several units
+    "mfma_k2v2_many_streams": (8, 40, 40, 128, 2, 2, 32, 256, 640, "f16", "f16", [600, 1]),
+    "mfma_k8v4_g2_many_streams": (16, 48, 24, 128, 8, 4, 32, 96, 420, "bf16", "bf16", [400, 1]),
 }
 
 
