@@ -42,8 +42,10 @@ void launch_valu(const AttnArgs &a, dim3 grid, size_t lds, hipStream_t st)
 
 bool mfma_supported(int kb, int vb, int D)
 {
-    const bool bits = (kb == 2 || kb == 4 || kb == 8) && (vb == 2 || vb == 4 || vb == 8);
-    return bits && (D == 64 || D == 128 || D == 256);
+    const bool vbits = vb == 2 || vb == 4 || vb == 8;
+    if (kb == 3)  // twelve words per row, three per lane quad
+        return vbits && D == 128;
+    return vbits && (kb == 2 || kb == 4 || kb == 8) && (D == 64 || D == 128 || D == 256);
 }
 
 // a 16-bit layer runs only recent-token units: any instantiation serves

@@ -149,6 +149,48 @@ __device__ __forceinline__ void shift8(const uint32_t (&w)[N], uint32_t (&w8)[N]
         w8[i] = w[i] >> 8;
 }
 
+// 3-bit K rows (KVmix notes, key design 2): each word holds channels 11w + j,
+// j < 10 as 3-bit codes at bits 3j, and j = 10 as a 2-bit code at bits 30-31.
+// Six operand registers per word, each taking one code from each 16-bit half
+// at bit offset e <= 7 of that half (registers 3-5 read the word shifted right
+// by 8, so that slots 3-5 and 8-10 sit low enough):
+//   register  source  lo half (slot, e)  hi half (slot, e)
+//   0         w       (0, 0)             (6, 2)
+//   1         w       (1, 3)             (7, 5)
+//   2         w       (2, 6)             none
+//   3         w >> 8  (3, 1)             (8, 0)
+//   4         w >> 8  (4, 4)             (9, 3)
+//   5         w >> 8  (5, 7)             (10, 6), two bits
+__host__ __device__ constexpr int k3_lo_e(int r)
+{
+    return r == 0 ? 0 : r == 1 ? 3 : r == 2 ? 6 : r == 3 ? 1 : r == 4 ? 4 : 7;
+}
+__host__ __device__ constexpr int k3_hi_slot(int r)
+{
+    return r == 0 ? 6 : r == 1 ? 7 : r == 2 ? -1 : r == 3 ? 8 : r == 4 ? 9 : 10;
+}
+__host__ __device__ constexpr int k3_hi_e(int r)
+{
+    return r == 0 ? 2 : r == 1 ? 5 : r == 2 ? 0 : r == 3 ? 0 : r == 4 ? 3 : 6;
+}
+__host__ __device__ constexpr uint32_t k3_mask(int r)
+{
+    return (7u << k3_lo_e(r)) |
+           (k3_hi_slot(r) < 0 ? 0u : ((k3_hi_slot(r) == 10 ? 3u : 7u) << (16 + k3_hi_e(r))));
+}
+
+// Operand register R (word R / 6, register R % 6 of the table above) of a
+// run of 3-bit K words: fp16 integers code * 2^e in both halves.
+template <int N>
+__device__ __forceinline__ uint32_t code_reg3(const uint32_t (&w)[N], const uint32_t (&w8)[N], int R)
+{
+    const int r = R % 6;
+    const uint32_t src = r >= 3 ? w8[R / 6] : w[R / 6];
+    const uint32_t biased = and_or(src, k3_mask(r), 0x64006400u);
+    const half2_t k = __builtin_bit_cast(half2_t, biased) - half2_t{1024.0f16, 1024.0f16};
+    return __builtin_bit_cast(uint32_t, k);
+}
+
 // n consecutive q values (fp32, fp16 or bf16) from a 16-byte aligned run.
 template <int N>
 __device__ __forceinline__ void load_q_run(const void *q, int dtype, size_t i0, float (&r)[N])
@@ -229,7 +271,8 @@ __device__ __forceinline__ float coset_max(float v, int S)
 template <int KB, int VB, int D>
 constexpr int round_blocks()
 {
-    constexpr int regs = 2 * (D * KB / 128) + D * VB / 64;  // K rows of two tiles + V fragment
+    // K rows of two tiles + V fragment (+ the 3-bit path's extra q.K operand chunk)
+    constexpr int regs = 2 * (D * KB / 128) + D * VB / 64 + (KB == 3 ? 4 : 0);
     return regs >= 48 ? 1 : (regs >= 24 ? 2 : 4);
 }
 
@@ -253,11 +296,14 @@ template <int KB, int VB, int D>
 __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *po, float *pm, float *pl,
                           float *meta_lds)
 {
-    constexpr int NC = D / 32;          // 32-channel chunks of q.K
-    constexpr int QC = D / 4;           // channels owned by one lane quad
-    constexpr int KW = D * KB / 128;    // K words per lane per token
-    constexpr int PK = 16 / KB;         // K code pairs per word
-    constexpr int CW = 32 / KB;         // K channels per word
+    constexpr int QC = D / 4;           // channels owned by one lane quad (2, 4, 8 bits)
+    constexpr int KW = D * KB / 128;    // K words per lane per token (3 bits: D / 11 rounded up, / 4)
+    constexpr int PK = KB == 3 ? 1 : 16 / KB;  // K code pairs per word
+    constexpr int CW = KB == 3 ? 11 : 32 / KB; // K channels per word
+    // 32-position chunks of q.K: D / 32, or six registers per 3-bit word
+    // (padded with zero registers to whole chunks)
+    constexpr int NC = KB == 3 ? (6 * KW + 3) / 4 : D / 32;
+    constexpr int QK = KB == 3 ? 11 * KW : QC;  // channels of a quad's K words (3 bits: some past D)
     constexpr int FW = D * VB / 64;     // V words per lane per 32-token block
     constexpr int MT = D / 16;          // 16-channel tiles of P.V
     constexpr int NB = round_blocks<KB, VB, D>();
@@ -275,9 +321,7 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *
     const int g_end = min(g_beg + a.unit_groups, n_groups);
     const int bpg = G / 32;  // blocks per group
 
-    const size_t q_base = (static_cast<size_t>(b) * a.Hkv * g + kvh * g + h) * D + q * QC;
     const uint32_t *kw_base = L.k_words + static_cast<size_t>(bh) * L.capq * L.wk + q * KW;
-    const float *km_base = L.k_meta + static_cast<size_t>(bh) * (L.capq / G) * 2 * D + q * QC;
     const uint32_t *vw_base = L.v_words + static_cast<size_t>(bh) * L.capq * L.wv + lane * FW;
     const float *vm_base = L.v_meta + static_cast<size_t>(bh) * L.capq * 2;
 
@@ -316,45 +360,66 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *
     auto setup_compute = [&](int nwin) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         const bool act_win = jslot < nwin;
-        const float *sp = meta_lds + (act_win ? jslot : 0) * 2 * D + q * QC;
-        const float *zp = sp + D;
-        float qs[QC], qv[QC];
-        if (a.q_dtype == 0) {
-            const float4 *qp = reinterpret_cast<const float4 *>(q_lds + h * D + q * QC);
-#pragma unroll
-            for (int i = 0; i < QC / 4; ++i) {
-                const float4 v = qp[i];
-                qv[4 * i] = v.x; qv[4 * i + 1] = v.y; qv[4 * i + 2] = v.z; qv[4 * i + 3] = v.w;
-            }
-        } else {
-            const int bf = a.q_dtype == 2;
-            const uint4 *qp = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(q_lds) + h * D + q * QC);
-#pragma unroll
-            for (int i = 0; i < QC / 8; ++i) {
-                const uint4 v = qp[i];
-                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    qv[8 * i + 2 * k] = widen16(static_cast<uint16_t>(w[k] & 0xFFFFu), bf);
-                    qv[8 * i + 2 * k + 1] = widen16(static_cast<uint16_t>(w[k] >> 16), bf);
-                }
-            }
-        }
         const float qscale = act_win ? a.scale_log2 : 0.0f;
+        float qs[QK];
         float amax = 0.0f;
         bias = 0.0f;
+        if constexpr (KB == 3) {
+            // the quad's 11 * KW channels from c0 (those past D weigh 0)
+            const int c0 = QK * q;
+            const float *sp = meta_lds + (act_win ? jslot : 0) * 2 * D;
+            const float *zp = sp + D;
+            const int bf = a.q_dtype == 2;
 #pragma unroll
-        for (int i = 0; i < QC; i += 4) {
-            const float4 s4 = *reinterpret_cast<const float4 *>(sp + i);
-            const float4 z4 = *reinterpret_cast<const float4 *>(zp + i);
-            const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
-            const float zv[4] = {z4.x, z4.y, z4.z, z4.w};
+            for (int i = 0; i < QK; ++i) {
+                const int c = c0 + i;
+                const bool ok = c < D;
+                const int cc = ok ? c : 0;
+                const float qv = a.q_dtype == 0 ? q_lds[h * D + cc]
+                                                : widen16(reinterpret_cast<const uint16_t *>(q_lds)[h * D + cc], bf);
+                const float qq = ok ? qv * qscale : 0.0f;
+                qs[i] = qq * sp[cc];
+                bias = __builtin_fmaf(qq, zp[cc], bias);
+                amax = fmaxf(amax, fabsf(qs[i]));
+            }
+        } else {
+            const float *sp = meta_lds + (act_win ? jslot : 0) * 2 * D + q * QC;
+            const float *zp = sp + D;
+            float qv[QC];
+            if (a.q_dtype == 0) {
+                const float4 *qp = reinterpret_cast<const float4 *>(q_lds + h * D + q * QC);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float qq = qv[i + k] * qscale;
-                qs[i + k] = qq * sv[k];
-                bias = __builtin_fmaf(qq, zv[k], bias);
-                amax = fmaxf(amax, fabsf(qs[i + k]));
+                for (int i = 0; i < QC / 4; ++i) {
+                    const float4 v = qp[i];
+                    qv[4 * i] = v.x; qv[4 * i + 1] = v.y; qv[4 * i + 2] = v.z; qv[4 * i + 3] = v.w;
+                }
+            } else {
+                const int bf = a.q_dtype == 2;
+                const uint4 *qp = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(q_lds) + h * D + q * QC);
+#pragma unroll
+                for (int i = 0; i < QC / 8; ++i) {
+                    const uint4 v = qp[i];
+                    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        qv[8 * i + 2 * k] = widen16(static_cast<uint16_t>(w[k] & 0xFFFFu), bf);
+                        qv[8 * i + 2 * k + 1] = widen16(static_cast<uint16_t>(w[k] >> 16), bf);
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < QC; i += 4) {
+                const float4 s4 = *reinterpret_cast<const float4 *>(sp + i);
+                const float4 z4 = *reinterpret_cast<const float4 *>(zp + i);
+                const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+                const float zv[4] = {z4.x, z4.y, z4.z, z4.w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const float qq = qv[i + k] * qscale;
+                    qs[i + k] = qq * sv[k];
+                    bias = __builtin_fmaf(qq, zv[k], bias);
+                    amax = fmaxf(amax, fabsf(qs[i + k]));
+                }
             }
         }
         bias = col_sum(bias);
@@ -366,9 +431,22 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
                 const int R = 4 * k + p;
-                const int clo = (R / PK) * CW + (R % PK), chi = clo + PK;
-                const int e = sh - class_exp<KB>(R);
-                split_pair(ldexpf(qs[clo], e), ldexpf(qs[chi], e), bhi[k].u[p], blo[k].u[p]);
+                if constexpr (KB == 3) {
+                    if (R < 6 * KW) {
+                        const int w = R / 6, r = R % 6;
+                        const float xlo = ldexpf(qs[11 * w + r], sh - k3_lo_e(r));
+                        const float xhi = k3_hi_slot(r) < 0 ? 0.0f
+                                                            : ldexpf(qs[11 * w + k3_hi_slot(r)], sh - k3_hi_e(r));
+                        split_pair(xlo, xhi, bhi[k].u[p], blo[k].u[p]);
+                    } else {
+                        bhi[k].u[p] = 0u;
+                        blo[k].u[p] = 0u;
+                    }
+                } else {
+                    const int clo = (R / PK) * CW + (R % PK), chi = clo + PK;
+                    const int e = sh - class_exp<KB>(R);
+                    split_pair(ldexpf(qs[clo], e), ldexpf(qs[chi], e), bhi[k].u[p], blo[k].u[p]);
+                }
             }
         }
         kscale = ldexpf(1.0f, -sh);  // acc * 2^-sh
@@ -412,8 +490,14 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *
                     Frag a0, a1;
 #pragma unroll
                     for (int p = 0; p < 4; ++p) {
-                        a0.u[p] = code_reg<KB>(d.k0[i], k08, 4 * k + p);
-                        a1.u[p] = code_reg<KB>(d.k1[i], k18, 4 * k + p);
+                        const int R = 4 * k + p;
+                        if constexpr (KB == 3) {
+                            a0.u[p] = R < 6 * KW ? code_reg3(d.k0[i], k08, R) : 0u;
+                            a1.u[p] = R < 6 * KW ? code_reg3(d.k1[i], k18, R) : 0u;
+                        } else {
+                            a0.u[p] = code_reg<KB>(d.k0[i], k08, R);
+                            a1.u[p] = code_reg<KB>(d.k1[i], k18, R);
+                        }
                     }
                     acc0 = mfma(a0, bhi[k], acc0);
                     acc0 = mfma(a0, blo[k], acc0);
@@ -810,6 +894,11 @@ hipError_t KVQ_CAT(launch_mfma_d, KVQ_D)(const AttnArgs &a, hipStream_t st)
     KVQ_PAIR(2, 2) KVQ_PAIR(2, 4) KVQ_PAIR(2, 8)
     KVQ_PAIR(4, 2) KVQ_PAIR(4, 4) KVQ_PAIR(4, 8)
     KVQ_PAIR(8, 2) KVQ_PAIR(8, 4) KVQ_PAIR(8, 8)
+#if KVQ_D == 128
+    // 3-bit rows: twelve words, three per lane quad (head_dim 256 would need
+    // more registers than two waves per SIMD leave)
+    KVQ_PAIR(3, 2) KVQ_PAIR(3, 4) KVQ_PAIR(3, 8)
+#endif
 #undef KVQ_PAIR
     return hipErrorInvalidValue;
 }

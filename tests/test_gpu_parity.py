@@ -47,6 +47,11 @@ CASES = {
     "cfg1_k4v2_d64": (1, 1, 1, 64, 4, 2, 32, 32, 288, "f16", "f32", [288]),
     "k8v4_g4_ragged": (2, 8, 2, 128, 8, 4, 32, 40, 320, "bf16", "bf16", [300, 1, 1, 7]),
     "k3v4_mha_R50": (2, 2, 2, 128, 3, 4, 32, 50, 400, "f16", "f16", [333, 2]),
+    "k3v2_g4_bf16": (2, 8, 2, 128, 3, 2, 32, 32, 700, "bf16", "bf16", [650, 1, 20]),
+    "k3v8_g2_G64": (1, 4, 2, 128, 3, 8, 64, 70, 600, "f16", "f32", [520, 3]),
+    # 3-bit K outside the matrix-core path: head_dim 64, groups of 16
+    "valu_k3v4_d64": (2, 4, 2, 64, 3, 4, 32, 40, 300, "f16", "f16", [260, 1]),
+    "valu_k3v2_G16": (1, 2, 1, 128, 3, 2, 16, 20, 200, "bf16", "f32", [150, 2]),
     "k2v2_d256_g16": (1, 16, 1, 256, 2, 2, 16, 16, 300, "bf16", "f32", [250, 3]),
     "k4v4_d64_g7_tiles": (2, 14, 2, 64, 4, 4, 64, 64, 1100, "bf16", "bf16", [1000, 1, 50]),
     "plain16_g4": (2, 8, 2, 128, 16, 16, 32, 32, 600, "bf16", "f32", [513, 1]),
@@ -190,24 +195,25 @@ def test_unit_sizes_and_column_merge(ug, monkeypatch):
     """Matrix-core units of 1, 3 and 40 groups: windows holding up to 16 / g
     groups per column set, merged per head at the end of each unit."""
     monkeypatch.setenv("KVQ_UNIT_GROUPS", ug)
-    for (Hq, Hkv, kb, vb, G) in [(2, 2, 2, 2, 32), (16, 4, 4, 2, 32), (16, 2, 8, 4, 64)]:
+    for (Hq, Hkv, kb, vb, G) in [(2, 2, 2, 2, 32), (16, 4, 4, 2, 32), (16, 2, 8, 4, 64), (2, 2, 3, 4, 32)]:
         w = ad_hoc_workload(400 + Hq + kb, 2, Hq, Hkv, 128, kb, vb, G, G, 1700, "bf16", "bf16")
         print("unit groups", ug, "g", Hq // Hkv, "pair", (kb, vb), flush=True)
         _run_case(w, [1650, 1])
 
 
-@pytest.mark.parametrize("kind", ["mfma_k4v2", "valu_k3v4", "plain16", "valu_g16"])
+@pytest.mark.parametrize("kind", ["mfma_k4v2", "mfma_k3v4", "valu_k3v4", "plain16", "valu_g16"])
 def test_append_decode_attention_equals_two_calls(kind):
     """The one-call decode step (append one token, then attend) gives the same
     outputs, bit for bit, and the same state as kvq_append + kvq_decode_attention,
     across flushes of the recent-token buffer."""
     spec = {  # (B, Hq, Hkv, d, kb, vb, G, R, ctx, kv, q)
         "mfma_k4v2": (2, 8, 2, 128, 4, 2, 32, 32, 200, "bf16", "bf16"),
-        "valu_k3v4": (2, 2, 2, 128, 3, 4, 32, 50, 200, "f16", "f32"),
+        "mfma_k3v4": (2, 2, 2, 128, 3, 4, 32, 50, 200, "f16", "f32"),
+        "valu_k3v4": (2, 2, 2, 128, 3, 4, 16, 50, 200, "f16", "f32"),
         "plain16": (1, 4, 1, 128, 16, 16, 32, 32, 160, "bf16", "bf16"),
         "valu_g16": (1, 8, 2, 64, 8, 4, 16, 24, 160, "f16", "f16"),
     }[kind]
-    w = ad_hoc_workload(500 + sorted(["mfma_k4v2", "valu_k3v4", "plain16", "valu_g16"]).index(kind), *spec)
+    w = ad_hoc_workload(500 + sorted(["mfma_k4v2", "mfma_k3v4", "valu_k3v4", "plain16", "valu_g16"]).index(kind), *spec)
     print("fused step", kind, flush=True)
     st = synth.LayerStats(w, 0)
     n0 = 70
@@ -228,3 +234,21 @@ def test_append_decode_attention_equals_two_calls(kind):
     orc = make_oracle(w, w.layers[0], w.context)
     orc.append(stream_view(k), stream_view(v))
     compare_export(one.export(0), orc.export())
+
+
+@pytest.mark.parametrize("d,G,variant", [(128, 32, 1), (64, 32, 0), (128, 16, 0)])
+def test_k3_path_choice(d, G, variant):
+    """3-bit K layers run on the matrix core at head_dim 128 with 32-token
+    multiples for G (variant 1), on the vector ALU otherwise (variant 0)."""
+    w = ad_hoc_workload(600 + d + G, 1, 2, 1, d, 3, 4, G, G, 200, "f16", "f32")
+    cache = make_cache(w)
+    orc = make_oracle(w, w.layers[0], w.context)
+    k, v = synth.layer_tokens(w, 0, 0, 150, DEV)
+    cache.append(0, k, v)
+    orc.append(stream_view(k), stream_view(v))
+    q = synth.query(w, 0, 0, DEV)
+    out = cache.decode_attention(0, q)
+    torch.cuda.synchronize()
+    assert kvq.kvq_last_launch(cache.h)[1] == variant
+    check_attention(out, orc.attention(q_streams(q, w.g)), w.g)
+    cache.close()
