@@ -266,16 +266,6 @@ __device__ __forceinline__ float coset_max(float v, int S)
     return v;
 }
 
-// Blocks (32 tokens each, one per group slot) processed together in one
-// round: four, or fewer when a block's operands take many registers.
-template <int KB, int VB, int D>
-constexpr int round_blocks()
-{
-    // K rows of two tiles + V fragment (+ the 3-bit path's extra q.K operand chunk)
-    constexpr int regs = 2 * (D * KB / 128) + D * VB / 64 + (KB == 3 ? 4 : 0);
-    return regs >= 48 ? 1 : (regs >= 24 ? 2 : 4);
-}
-
 // Data of one round: for each of its blocks the K rows of both 16-token tiles
 // and the V fragment; the V meta (s, z) of this lane's eight k-slot tokens in
 // its own block.
@@ -306,7 +296,7 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *
     constexpr int QK = KB == 3 ? 11 * KW : QC;  // channels of a quad's K words (3 bits: some past D)
     constexpr int FW = D * VB / 64;     // V words per lane per 32-token block
     constexpr int MT = D / 16;          // 16-channel tiles of P.V
-    constexpr int NB = round_blocks<KB, VB, D>();
+    constexpr int NB = mfma_round_blocks(KB, VB, D);
 
     const LayerDev &L = a.L;
     const int G = L.G, g = a.g;
@@ -317,8 +307,8 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *
     const int jslot = used ? col / S : NG;
     const int b = bh / a.Hkv, kvh = bh % a.Hkv;
     const int n_groups = a.Tq / G;
-    const int g_beg = unit * a.unit_groups;
-    const int g_end = min(g_beg + a.unit_groups, n_groups);
+    const int g_beg = unit * a.unit_groups + min(unit, a.unit_extra);
+    const int g_end = g_beg + a.unit_groups + (unit < a.unit_extra ? 1 : 0);
     const int bpg = G / 32;  // blocks per group
 
     const uint32_t *kw_base = L.k_words + static_cast<size_t>(bh) * L.capq * L.wk + q * KW;

@@ -64,10 +64,11 @@ struct AttnArgs {
     // vector-ALU ranges: wg_valu workgroups per stream cover tokens [valu_beg, N)
     int valu_beg, valu_wgs, valu_tps;
     // matrix-core units: units_q waves per stream cover groups [0, Tq / G),
-    // unit_groups groups each; then units_r waves cover the recent tokens
+    // unit u taking unit_groups groups, plus one more for u < unit_extra
+    // (the remainder); then units_r waves cover the recent tokens
     // [Tq, N), res_tokens each (a multiple of 32); mfma_wgs = ceil((units_q +
     // units_r) / 4) workgroups
-    int units_q, unit_groups, units_r, res_tokens, mfma_wgs;
+    int units_q, unit_groups, unit_extra, units_r, res_tokens, mfma_wgs;
     float scale_log2;     // log2(e) / sqrt(D)
     // token new_t (>= 0) has just been appended and is not in the ring yet: it
     // is read from new_k / new_v ([BH][D]) and written to its ring slot by the
@@ -91,6 +92,16 @@ __host__ __device__ inline int mfma_wave_region(int D, int g, bool has_q_units, 
     int r = g * D;
     r = vt > r ? vt : r;
     return meta > r ? meta : r;
+}
+
+// 32-token blocks (one per group slot) the matrix-core kernel processes
+// together in one round: four, or fewer when a block's operands take many
+// registers (K rows of two 16-token tiles + the V fragment, + the 3-bit
+// path's extra q.K operand chunk).
+__host__ __device__ constexpr int mfma_round_blocks(int kb, int vb, int D)
+{
+    const int regs = 2 * (D * kb / 128) + D * vb / 64 + (kb == 3 ? 4 : 0);
+    return regs >= 48 ? 1 : (regs >= 24 ? 2 : 4);
 }
 
 hipError_t launch_flush(const FlushArgs &a, hipStream_t st);

@@ -443,9 +443,12 @@ static int attention_launch(kvq_handle *h, int layer, const void *q, float *out,
         const long wg_lds = 4L * kvq::mfma_wave_region(D, g, n_groups > 0, Tr > 0) * 4 + 8192;
         const long per_cu = std::max(1L, std::min(2L, (160L * 1024) / wg_lds));
         const long res_wgs = per_cu * h->cu_count;
-        long ug = 1;
+        // quantized units: uq per stream, groups split as evenly as possible;
+        // recent-token units: ceil(Tr / rt) per stream, rt tokens each
+        long uq = 0;
         int rt = 0;
-        if (BH * 2 > res_wgs && !getenv("KVQ_UNIT_GROUPS")) {
+        const char *env_ug = getenv("KVQ_UNIT_GROUPS");
+        if (BH * 2 > res_wgs && !(env_ug && atoi(env_ug) > 0)) {
             // Many streams: each stream's work splits into U units (U a
             // multiple of four: whole workgroups), the recent tokens into as
             // many units as their share of the work, chosen to minimise
@@ -470,8 +473,7 @@ static int attention_launch(kvq_handle *h, int layer, const void *q, float *out,
                 ur = 1;
             if (n_groups > 0 && ur > best_u - 1)
                 ur = best_u - 1;
-            const int uq = best_u - ur;
-            ug = n_groups > 0 ? (n_groups + uq - 1) / uq : 1;
+            uq = best_u - ur;
             if (ur > 0)
                 rt = ((Tr + ur - 1) / ur + 31) / 32 * 32;
         } else if (n_groups > 0) {
@@ -482,34 +484,43 @@ static int attention_launch(kvq_handle *h, int layer, const void *q, float *out,
             while (ng * g > 16)
                 ng >>= 1;
             const long cap = 4 * res_wgs;
-            ug = (static_cast<long>(n_groups) * BH + cap - 1) / cap;
+            long ug = (static_cast<long>(n_groups) * BH + cap - 1) / cap;
             ug = (ug + ng - 1) / ng * ng;
             while (ug < n_groups &&
                    BH * ((n_groups + ug - 1) / ug + (Tr + res_len(ug) - 1) / res_len(ug)) > cap)
                 ug += ng;
-        }
-        if (const char *env = getenv("KVQ_UNIT_GROUPS"))
-            if (atoi(env) > 0)
-                ug = atoi(env);
-        if (ug > n_groups)
-            ug = n_groups > 0 ? n_groups : 1;
-        if (rt == 0)
+            if (env_ug && atoi(env_ug) > 0)
+                ug = atoi(env_ug);
+            if (ug > n_groups)
+                ug = n_groups;
+            uq = (n_groups + ug - 1) / ug;
             rt = res_len(ug);
+            // whole workgroups: when the units leave the last workgroup of each
+            // stream partly idle, more (smaller) quantized units fill it if that
+            // takes a group off the longest unit
+            const long ur = (Tr + rt - 1) / rt;
+            const long U4 = (uq + ur + 3) / 4 * 4, uq4 = U4 - ur;
+            if (!(env_ug && atoi(env_ug) > 0) && BH * U4 <= cap && uq4 <= n_groups &&
+                (n_groups + uq4 - 1) / uq4 < (n_groups + uq - 1) / uq)
+                uq = uq4;
+        }
+        if (rt == 0)
+            rt = res_len(uq > 0 ? (n_groups + uq - 1) / uq : 1);
         if (const char *env = getenv("KVQ_RES_TOKENS"))
             if (atoi(env) > 0)
                 rt = (atoi(env) + 31) / 32 * 32;
-        for (;;) {
-            const int uq = n_groups > 0 ? static_cast<int>((n_groups + ug - 1) / ug) : 0;
-            const int ur = (Tr + rt - 1) / rt;
-            if (uq + ur <= kMaxUnits)
-                break;
-            if (uq > ur)
-                ++ug;
+        if (uq > n_groups)
+            uq = n_groups;
+        // the merge takes at most kMaxUnits / 4 workgroups per stream
+        while (uq + (Tr + rt - 1) / rt > kMaxUnits) {
+            if (uq > (Tr + rt - 1) / rt)
+                --uq;
             else
                 rt += 32;
         }
-        a.unit_groups = static_cast<int>(ug);
-        a.units_q = n_groups > 0 ? static_cast<int>((n_groups + ug - 1) / ug) : 0;
+        a.units_q = static_cast<int>(uq);
+        a.unit_groups = uq > 0 ? static_cast<int>(n_groups / uq) : 0;
+        a.unit_extra = uq > 0 ? static_cast<int>(n_groups % uq) : 0;
         a.res_tokens = rt;
         a.units_r = (Tr + rt - 1) / rt;
         a.mfma_wgs = (a.units_q + a.units_r + 3) / 4;
@@ -534,7 +545,7 @@ static int attention_launch(kvq_handle *h, int layer, const void *q, float *out,
         a.valu_beg = 0;
         a.valu_tps = tps;
         a.valu_wgs = S;
-        a.units_q = a.unit_groups = a.units_r = a.res_tokens = a.mfma_wgs = 0;
+        a.units_q = a.unit_groups = a.unit_extra = a.units_r = a.res_tokens = a.mfma_wgs = 0;
     }
     // one partial entry per workgroup
     a.n_part = use_mfma ? a.mfma_wgs : a.valu_wgs;
