@@ -20,7 +20,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_valu_kernel(AttnArgs a)
     const int t_end = min(a.N, t_beg + a.valu_tps);
     extern __shared__ float smem[];
     valu_range<D, GM>(a, bh, t_beg, t_end, split, smem);
-    arrive_and_merge(a, bh, gridDim.x);
+    arrive_and_merge<D>(a, bh, gridDim.x);
 }
 
 template <int D>

@@ -447,10 +447,11 @@ __device__ void valu_range(const AttnArgs &a, int bh, int t_beg, int t_end, int 
 // results in LDS (o[g][D] at wave * region floats, m and l in pm / pl; m =
 // -inf marks an empty one); the workgroup writes one partial entry per head,
 // o = sum_w 2^(m_w - M) o_w, l = sum_w 2^(m_w - M) l_w, M = max_w m_w.
+template <int D>
 __device__ __forceinline__ void wg_merge_store(const AttnArgs &a, int bh, int entry, const float *lds,
                                                int region, const float (*pm)[kMaxG], const float (*pl)[kMaxG])
 {
-    const int D = a.D, nc4 = D / 4;
+    constexpr int nc4 = D / 4;
     const PartBuf pb(a, bh);
     for (int it = threadIdx.x; it < a.g * nc4; it += kAttnThreads) {
         const int h = it / nc4, c4 = it % nc4;
@@ -484,6 +485,7 @@ __device__ __forceinline__ void wg_merge_store(const AttnArgs &a, int bh, int en
 // sub, sub + n_sub, ... (sub = t / n_items).  It issues the (m, l) and o loads
 // of up to kChunk of its entries together (one memory round trip), merges them
 // online, and the n_sub partial states of an item are merged through LDS.
+template <int D>
 __device__ __forceinline__ void arrive_and_merge(const AttnArgs &a, int bh, unsigned n_wgs)
 {
     constexpr int kChunk = 16;
@@ -501,14 +503,24 @@ __device__ __forceinline__ void arrive_and_merge(const AttnArgs &a, int bh, unsi
     if (!s_last)
         return;
     const int tid = threadIdx.x;
-    const int D = a.D, g = a.g, P = a.n_part, nc4 = D / 4;
+    constexpr int nc4 = D / 4;
+    const int g = a.g, P = a.n_part;
     const int n_items = g * nc4;  // <= 1024
-    const int n_sub = n_items >= kAttnThreads ? 1 : kAttnThreads / n_items;
-    const int b = bh / a.Hkv, kvh = bh % a.Hkv;
+    // n_sub = kAttnThreads / n_items threads per item (when items are fewer
+    // than threads); thread tid = sub * n_items + item, found by subtraction
+    int n_sub = 1, tid_item = tid, tid_sub = 0;
+    if (n_items < kAttnThreads) {
+        while ((n_sub + 1) * n_items <= kAttnThreads)
+            ++n_sub;
+        while (tid_item >= n_items) {
+            tid_item -= n_items;
+            ++tid_sub;
+        }
+    }
     const PartBuf pb(a, bh);
     for (int it0 = 0; it0 < n_items; it0 += kAttnThreads) {
-        const int item = it0 + (n_sub > 1 ? tid % n_items : tid);
-        const int sub = n_sub > 1 ? tid / n_items : 0;
+        const int item = it0 + tid_item;
+        const int sub = tid_sub;
         const bool own = item < n_items && sub < n_sub;
         const int h = own ? item / nc4 : 0, c4 = own ? item % nc4 : 0;
         float M = -INFINITY, den = 0.0f;
@@ -567,7 +579,7 @@ __device__ __forceinline__ void arrive_and_merge(const AttnArgs &a, int bh, unsi
             }
         }
         if (own && sub == 0)
-            *reinterpret_cast<f4_t *>(a.out + (static_cast<size_t>(b) * a.Hkv * g + kvh * g + h) * D + 4 * c4) =
+            *reinterpret_cast<f4_t *>(a.out + (static_cast<size_t>(bh) * g + h) * D + 4 * c4) =
                 acc * (1.0f / den);
     }
     if (tid == 0)

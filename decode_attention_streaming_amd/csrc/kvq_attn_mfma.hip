@@ -228,16 +228,6 @@ __device__ __forceinline__ float row_ror(float v)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + R, 0xF, 0xF, true));
 }
 
-// Columns per group slot (S) for g query heads: 16 / NG, NG the largest power
-// of two with NG * g <= 16.
-__device__ __forceinline__ int slot_stride(int g)
-{
-    int ng = 16;
-    while (ng * g > 16)
-        ng >>= 1;
-    return 16 / ng;
-}
-
 // Sum (or max) over the columns h, h + S, h + 2S, ... of each row, left in
 // every one of them.
 __device__ __forceinline__ float coset_sum(float v, int S)
@@ -301,12 +291,13 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *
     const LayerDev &L = a.L;
     const int G = L.G, g = a.g;
     const int col = lane & 15, q = lane >> 4;
-    const int S = slot_stride(g), NG = 16 / S;
-    const bool used = (col % S) < g;
-    const int h = used ? col % S : 0;
-    const int jslot = used ? col / S : NG;
-    const int b = bh / a.Hkv, kvh = bh % a.Hkv;
-    const int n_groups = a.Tq / G;
+    // S = 2^s_log2 columns per group slot, NG = 16 / S slots (host-computed:
+    // no division before the first loads)
+    const int S = 1 << a.s_log2, NG = 16 >> a.s_log2;
+    const bool used = (col & (S - 1)) < g;
+    const int h = used ? (col & (S - 1)) : 0;
+    const int jslot = used ? (col >> a.s_log2) : NG;
+    const int n_groups = a.n_groups;
     const int g_beg = unit * a.unit_groups + min(unit, a.unit_extra);
     const int g_end = g_beg + a.unit_groups + (unit < a.unit_extra ? 1 : 0);
     const int bpg = G / 32;  // blocks per group
@@ -332,13 +323,13 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *
     const int qbytes = a.q_dtype == 0 ? 4 : 2;
     float *q_lds = meta_lds + NG * 2 * D;
     auto setup_issue = [&](int w0, int nwin) {
-        const float *src = L.k_meta + (static_cast<size_t>(bh) * (L.capq / G) + w0) * 2 * D;
+        const float *src = L.k_meta + (static_cast<size_t>(bh) * a.ngcap + w0) * 2 * D;
         const int n16 = nwin * D / 2;  // 16-byte pieces of nwin groups' [2][D] floats
         for (int i0 = 0; i0 < n16; i0 += 64) {
             if (i0 + lane < n16)
                 __builtin_amdgcn_global_load_lds(src + 4 * (i0 + lane), meta_lds + 4 * i0, 16, 0, 0);
         }
-        const char *qsrc = static_cast<const char *>(a.q) + (static_cast<size_t>(b) * a.Hkv + kvh) * g * D * qbytes;
+        const char *qsrc = static_cast<const char *>(a.q) + static_cast<size_t>(bh) * g * D * qbytes;
         const int nq16 = g * D * qbytes / 16;
         for (int i0 = 0; i0 < nq16; i0 += 64) {
             if (i0 + lane < nq16)
@@ -635,7 +626,6 @@ __device__ void mfma_residual_unit(const AttnArgs &a, int bh, int runit, int lan
     const int col = lane & 15, q = lane >> 4;
     const bool act = col < g;
     const int h = act ? col : 0;
-    const int b = bh / a.Hkv, kvh = bh % a.Hkv;
     const int bf = a.kv_bf16;
     const int t_beg = a.Tq + runit * a.res_tokens;
     const int t_end = min(a.N, t_beg + a.res_tokens);
@@ -656,7 +646,7 @@ __device__ void mfma_residual_unit(const AttnArgs &a, int bh, int runit, int lan
     int sh;
     {
         float qv[NC][8];
-        const size_t base = (static_cast<size_t>(b) * a.Hkv * g + kvh * g + h) * D;
+        const size_t base = (static_cast<size_t>(bh) * g + h) * D;  // stream bh = (b, kv head)
         float amax = 0.0f;
 #pragma unroll
         for (int k = 0; k < NC; ++k) {
@@ -857,8 +847,8 @@ __global__ __launch_bounds__(kAttnThreads, (mfma_waves_per_simd<KB, VB>())) void
         s_pl[wave][lane] = 0.0f;
     }
     __syncthreads();
-    wg_merge_store(a, bh, blockIdx.x, lds, region, s_pm, s_pl);
-    arrive_and_merge(a, bh, gridDim.x);
+    wg_merge_store<D>(a, bh, blockIdx.x, lds, region, s_pm, s_pl);
+    arrive_and_merge<D>(a, bh, gridDim.x);
 }
 
 template <int KB, int VB>

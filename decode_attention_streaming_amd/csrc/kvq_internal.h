@@ -69,6 +69,10 @@ struct AttnArgs {
     // [Tq, N), res_tokens each (a multiple of 32); mfma_wgs = ceil((units_q +
     // units_r) / 4) workgroups
     int units_q, unit_groups, unit_extra, units_r, res_tokens, mfma_wgs;
+    // Tq / G, capq / G, and log2 of the columns per group slot of the
+    // matrix-core products (S = 16 / NG, NG the largest power of two with
+    // NG * g <= 16)
+    int n_groups, ngcap, s_log2;
     float scale_log2;     // log2(e) / sqrt(D)
     // token new_t (>= 0) has just been appended and is not in the ring yet: it
     // is read from new_k / new_v ([BH][D]) and written to its ring slot by the

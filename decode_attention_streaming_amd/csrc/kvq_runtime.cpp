@@ -519,6 +519,11 @@ static int attention_launch(kvq_handle *h, int layer, const void *q, float *out,
                 rt += 32;
         }
         a.units_q = static_cast<int>(uq);
+        a.n_groups = n_groups;
+        a.ngcap = d.capq / d.G;
+        a.s_log2 = 0;
+        while ((16 >> a.s_log2) * g > 16)
+            ++a.s_log2;
         a.unit_groups = uq > 0 ? static_cast<int>(n_groups / uq) : 0;
         a.unit_extra = uq > 0 ? static_cast<int>(n_groups % uq) : 0;
         a.res_tokens = rt;
@@ -546,6 +551,7 @@ static int attention_launch(kvq_handle *h, int layer, const void *q, float *out,
         a.valu_tps = tps;
         a.valu_wgs = S;
         a.units_q = a.unit_groups = a.unit_extra = a.units_r = a.res_tokens = a.mfma_wgs = 0;
+        a.n_groups = a.ngcap = a.s_log2 = 0;
     }
     // one partial entry per workgroup
     a.n_part = use_mfma ? a.mfma_wgs : a.valu_wgs;
