@@ -191,31 +191,37 @@ __device__ __forceinline__ uint32_t code_reg3(const uint32_t (&w)[N], const uint
     return __builtin_bit_cast(uint32_t, k);
 }
 
-// n consecutive q values (fp32, fp16 or bf16) from a 16-byte aligned run.
-template <int N>
-__device__ __forceinline__ void load_q_run(const void *q, int dtype, size_t i0, float (&r)[N])
+// q values of runs i0 + stride * k, k < K, of 8 consecutive elements (fp32,
+// fp16 or bf16; 16-byte aligned): every load is issued before any is used.
+template <int K>
+__device__ __forceinline__ void load_q_runs(const void *q, int dtype, size_t i0, int stride, float (&r)[K][8])
 {
     if (dtype == 0) {
-        const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(q) + i0);
+        float4 v[K][2];
 #pragma unroll
-        for (int i = 0; i < N / 4; ++i) {
-            const float4 v = p[i];
-            r[4 * i] = v.x;
-            r[4 * i + 1] = v.y;
-            r[4 * i + 2] = v.z;
-            r[4 * i + 3] = v.w;
+        for (int k = 0; k < K; ++k) {
+            const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(q) + i0 + stride * k);
+            v[k][0] = p[0];
+            v[k][1] = p[1];
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            r[k][0] = v[k][0].x; r[k][1] = v[k][0].y; r[k][2] = v[k][0].z; r[k][3] = v[k][0].w;
+            r[k][4] = v[k][1].x; r[k][5] = v[k][1].y; r[k][6] = v[k][1].z; r[k][7] = v[k][1].w;
         }
     } else {
-        const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(q) + i0);
         const int bf = dtype == 2;
+        uint4 v[K];
 #pragma unroll
-        for (int i = 0; i < N / 8; ++i) {
-            const uint4 v = p[i];
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        for (int k = 0; k < K; ++k)
+            v[k] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(q) + i0 + stride * k);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                r[8 * i + 2 * k] = widen16(static_cast<uint16_t>(w[k] & 0xFFFFu), bf);
-                r[8 * i + 2 * k + 1] = widen16(static_cast<uint16_t>(w[k] >> 16), bf);
+        for (int k = 0; k < K; ++k) {
+            const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                r[k][2 * j] = widen16(static_cast<uint16_t>(w[j] & 0xFFFFu), bf);
+                r[k][2 * j + 1] = widen16(static_cast<uint16_t>(w[j] >> 16), bf);
             }
         }
     }
@@ -648,13 +654,12 @@ __device__ void mfma_residual_unit(const AttnArgs &a, int bh, int runit, int lan
         float qv[NC][8];
         const size_t base = (static_cast<size_t>(bh) * g + h) * D;  // stream bh = (b, kv head)
         float amax = 0.0f;
+        load_q_runs<NC>(a.q, a.q_dtype, base + 8 * q, 32, qv);
 #pragma unroll
         for (int k = 0; k < NC; ++k) {
-            float r[8];
-            load_q_run<8>(a.q, a.q_dtype, base + 32 * k + 8 * q, r);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                qv[k][i] = act ? r[i] * a.scale_log2 : 0.0f;
+                qv[k][i] = act ? qv[k][i] * a.scale_log2 : 0.0f;
                 amax = fmaxf(amax, fabsf(qv[k][i]));
             }
         }

@@ -503,12 +503,20 @@ static int attention_launch(kvq_handle *h, int layer, const void *q, float *out,
             if (!(env_ug && atoi(env_ug) > 0) && BH * U4 <= cap && uq4 <= n_groups &&
                 (n_groups + uq4 - 1) / uq4 < (n_groups + uq - 1) / uq)
                 uq = uq4;
+            // few streams: while there are more SIMDs than waves, shorter units
+            // (one wave per SIMD, whole workgroups) shorten the critical path
+            const long u_simd = (4L * h->cu_count / BH) / 4 * 4;
+            if (!(env_ug && atoi(env_ug) > 0) && u_simd > uq + ur)
+                uq = std::min<long>(n_groups, u_simd - ur);
         }
         if (rt == 0)
             rt = res_len(uq > 0 ? (n_groups + uq - 1) / uq : 1);
         if (const char *env = getenv("KVQ_RES_TOKENS"))
             if (atoi(env) > 0)
                 rt = (atoi(env) + 31) / 32 * 32;
+        if (const char *env = getenv("KVQ_UNITS_Q"))
+            if (atoi(env) > 0)
+                uq = atoi(env);
         if (uq > n_groups)
             uq = n_groups;
         // the merge takes at most kMaxUnits / 4 workgroups per stream
