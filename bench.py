@@ -278,7 +278,7 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "kernel": "decode attention (one launch per call: split units + in-kernel merge), "
-                      "variant %d (1 = matrix core), %d partials per stream" % (variant, splits),
+                      "variant %d (1 = matrix core), %d work units per stream" % (variant, splits),
             "avg_call_us": round(avg_call_us, 3),
             "bytes_per_call": int(avg_att_bytes),
         },
