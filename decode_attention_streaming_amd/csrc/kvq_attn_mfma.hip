@@ -235,31 +235,64 @@ __device__ __forceinline__ float row_ror(float v)
 }
 
 // Sum (or max) over the columns h, h + S, h + 2S, ... of each row, left in
-// every one of them.
-__device__ __forceinline__ float coset_sum(float v, int S)
+// every one of them (S a compile-time power of two: no branches).
+template <int S>
+__device__ __forceinline__ float coset_sum(float v)
 {
-    if (S <= 8)
+    if constexpr (S <= 8)
         v += row_ror<8>(v);
-    if (S <= 4)
+    if constexpr (S <= 4)
         v += row_ror<4>(v);
-    if (S <= 2)
+    if constexpr (S <= 2)
         v += row_ror<2>(v);
-    if (S <= 1)
+    if constexpr (S <= 1)
         v += row_ror<1>(v);
     return v;
 }
 
-__device__ __forceinline__ float coset_max(float v, int S)
+template <int S>
+__device__ __forceinline__ float coset_max(float v)
 {
-    if (S <= 8)
+    if constexpr (S <= 8)
         v = fmaxf(v, row_ror<8>(v));
-    if (S <= 4)
+    if constexpr (S <= 4)
         v = fmaxf(v, row_ror<4>(v));
-    if (S <= 2)
+    if constexpr (S <= 2)
         v = fmaxf(v, row_ror<2>(v));
-    if (S <= 1)
+    if constexpr (S <= 1)
         v = fmaxf(v, row_ror<1>(v));
     return v;
+}
+
+// End of a quantized unit: this lane's column state (l, z-term, o; weights
+// carry 2^(kWShift - E)); the S-strided columns of one head are rescaled to
+// their common max and summed, and slot 0 of head h < g writes o[h][D], m, l
+// to LDS.
+template <int S, int D, int MT>
+__device__ __forceinline__ void finish_unit(float m_run, float l_run, float zb_run, int E, const f4_t (&O)[MT],
+                                            int col, int q, int g, float *po, float *pm, float *pl)
+{
+    const float Lcol = col_sum(l_run);
+    const float ZB = col_sum(zb_run);
+    const float M = coset_max<S>(m_run);
+    const float alpha = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - M);
+    const float fo = ldexpf(alpha, E - kWShift), fz = alpha * ZB;
+    const float Lh = coset_sum<S>(alpha * Lcol);
+    float o[MT][4];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            o[m][j] = coset_sum<S>(__builtin_fmaf(O[m][j], fo, fz));
+    if (col < g) {  // slot 0 of head col
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+            *reinterpret_cast<f4_t *>(po + col * D + 16 * m + 4 * q) = f4_t{o[m][0], o[m][1], o[m][2], o[m][3]};
+        if (q == 0) {
+            pm[col] = M;
+            pl[col] = Lh;
+        }
+    }
 }
 
 // Data of one round: for each of its blocks the K rows of both 16-token tiles
@@ -590,28 +623,12 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *
         }
     }
 
-    // this lane's column: l, z-term and o (weights carry 2^(kWShift - E)); the
-    // columns of one head are rescaled to their common max and summed
-    const float Lcol = col_sum(l_run);
-    const float ZB = col_sum(zb_run);
-    const float M = coset_max(m_run, S);
-    const float alpha = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - M);
-    const float fo = ldexpf(alpha, E - kWShift), fz = alpha * ZB;
-    const float Lh = coset_sum(alpha * Lcol, S);
-    float o[MT][4];
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            o[m][j] = coset_sum(__builtin_fmaf(O[m][j], fo, fz), S);
-    if (col < g) {  // slot 0 of head col
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-            *reinterpret_cast<f4_t *>(po + col * D + 16 * m + 4 * q) = f4_t{o[m][0], o[m][1], o[m][2], o[m][3]};
-        if (q == 0) {
-            pm[col] = M;
-            pl[col] = Lh;
-        }
+    switch (a.s_log2) {
+    case 0: finish_unit<1, D>(m_run, l_run, zb_run, E, O, col, q, g, po, pm, pl); break;
+    case 1: finish_unit<2, D>(m_run, l_run, zb_run, E, O, col, q, g, po, pm, pl); break;
+    case 2: finish_unit<4, D>(m_run, l_run, zb_run, E, O, col, q, g, po, pm, pl); break;
+    case 3: finish_unit<8, D>(m_run, l_run, zb_run, E, O, col, q, g, po, pm, pl); break;
+    default: finish_unit<16, D>(m_run, l_run, zb_run, E, O, col, q, g, po, pm, pl); break;
     }
 }
 
