@@ -524,12 +524,11 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *
                     acc1 = mfma(a1, bhi[k], acc1);
                     acc1 = mfma(a1, blo[k], acc1);
                 }
-                if (i == 0 || my_b == i) {
+                const bool take = (i == 0) | (my_b == i);  // selects, not a branch
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        sc[j] = acc0[j];
-                        sc[4 + j] = acc1[j];
-                    }
+                for (int j = 0; j < 4; ++j) {
+                    sc[j] = take ? acc0[j] : sc[j];
+                    sc[4 + j] = take ? acc1[j] : sc[4 + j];
                 }
             }
         }
@@ -606,12 +605,12 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *
     };
 
     for (int w0 = g_beg; w0 < g_end; w0 += NG) {
-        const int nwin = min(NG, g_end - w0);
+        const int nwin = __builtin_amdgcn_readfirstlane(min(NG, g_end - w0));  // uniform
         const bool in_win = jslot < nwin;
         setup_issue(w0, nwin);
         for (int r = 0; r < bpg; ++r) {
             for (int u = 0; u < nwin; u += NB) {
-                const int nb = min(NB, nwin - u);
+                const int nb = __builtin_amdgcn_readfirstlane(min(NB, nwin - u));
                 const bool mine = in_win && jslot >= u && jslot < u + nb;
                 const int my_b = mine ? jslot - u : 0;
                 RoundData<NB, KW, FW> d;
@@ -638,7 +637,7 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *
 // parts); P.V reads V through a per-wave LDS tile written transposed
 // ([channel][token]) so that each lane's operand (eight tokens of one channel)
 // is two 8-byte LDS reads.
-template <int D>
+template <int D, bool BF>
 __device__ void mfma_residual_unit(const AttnArgs &a, int bh, int runit, int lane, float *po, float *pm,
                                    float *pl)
 {
@@ -649,7 +648,7 @@ __device__ void mfma_residual_unit(const AttnArgs &a, int bh, int runit, int lan
     const int col = lane & 15, q = lane >> 4;
     const bool act = col < g;
     const int h = act ? col : 0;
-    const int bf = a.kv_bf16;
+    constexpr bool bf = BF;  // bfloat16 recent tokens (instantiated per dtype: no branches)
     const int t_beg = a.Tq + runit * a.res_tokens;
     const int t_end = min(a.N, t_beg + a.res_tokens);
     uint16_t *vt = reinterpret_cast<uint16_t *>(po);  // [D][32] tile, then the results
@@ -688,7 +687,7 @@ __device__ void mfma_residual_unit(const AttnArgs &a, int bh, int runit, int lan
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
                 const float x0 = ldexpf(qv[k][2 * p], sh), x1 = ldexpf(qv[k][2 * p + 1], sh);
-                if (bf)
+                if constexpr (bf)
                     split3_bf16(x0, x1, b1[k].u[p], b2[k].u[p], b3[k].u[p]);
                 else
                     split_pair(x0, x1, b1[k].u[p], b2[k].u[p]);
@@ -756,7 +755,7 @@ __device__ void mfma_residual_unit(const AttnArgs &a, int bh, int runit, int lan
             Frag a0, a1;
             a0.u[0] = ka[k].x; a0.u[1] = ka[k].y; a0.u[2] = ka[k].z; a0.u[3] = ka[k].w;
             a1.u[0] = kb2[k].x; a1.u[1] = kb2[k].y; a1.u[2] = kb2[k].z; a1.u[3] = kb2[k].w;
-            if (bf) {
+            if constexpr (bf) {
                 acc0 = mfma_bf16(a0, b1[k], acc0);
                 acc0 = mfma_bf16(a0, b2[k], acc0);
                 acc0 = mfma_bf16(a0, b3[k], acc0);
@@ -801,7 +800,7 @@ __device__ void mfma_residual_unit(const AttnArgs &a, int bh, int runit, int lan
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const float x0 = ldexpf(p[2 * r], kWShift), x1 = ldexpf(p[2 * r + 1], kWShift);
-            if (bf)
+            if constexpr (bf)
                 split3_bf16(x0, x1, w1.u[r], w2.u[r], w3.u[r]);
             else
                 split_pair(x0, x1, w1.u[r], w2.u[r]);
@@ -814,7 +813,7 @@ __device__ void mfma_residual_unit(const AttnArgs &a, int bh, int runit, int lan
             const uint2 hi = *reinterpret_cast<const uint2 *>(row + 16 + 4 * q);
             Frag av;
             av.u[0] = lo.x; av.u[1] = lo.y; av.u[2] = hi.x; av.u[3] = hi.y;
-            if (bf) {
+            if constexpr (bf) {
                 O[m] = mfma_bf16(av, w1, O[m]);
                 O[m] = mfma_bf16(av, w2, O[m]);
                 O[m] = mfma_bf16(av, w3, O[m]);
@@ -863,7 +862,10 @@ __global__ __launch_bounds__(kAttnThreads, (mfma_waves_per_simd<KB, VB>())) void
     if (unit < a.units_q) {
         mfma_unit<KB, VB, D>(a, bh, unit, lane, po, s_pm[wave], s_pl[wave], po);
     } else if (unit < a.units_q + a.units_r) {
-        mfma_residual_unit<D>(a, bh, unit - a.units_q, lane, po, s_pm[wave], s_pl[wave]);
+        if (a.kv_bf16)
+            mfma_residual_unit<D, true>(a, bh, unit - a.units_q, lane, po, s_pm[wave], s_pl[wave]);
+        else
+            mfma_residual_unit<D, false>(a, bh, unit - a.units_q, lane, po, s_pm[wave], s_pl[wave]);
     } else if (lane < a.g) {
         s_pm[wave][lane] = -INFINITY;
         s_pl[wave][lane] = 0.0f;
