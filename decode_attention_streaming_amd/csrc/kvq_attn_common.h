@@ -478,45 +478,22 @@ __device__ __forceinline__ void wg_merge_store(const AttnArgs &a, int bh, int en
     }
 }
 
-// Called by every workgroup at its end: the last one of stream bh to arrive
-// merges the n_part partial entries, out = sum_s 2^(m_s - M) o_s /
-// sum_s 2^(m_s - M) l_s, M = max_s m_s, and re-arms the stream's counter.
-// Thread t owns four channels of one head (item t % n_items) and the entries
-// sub, sub + n_sub, ... (sub = t / n_items).  It issues the (m, l) and o loads
-// of up to kChunk of its entries together (one memory round trip), merges them
-// online, and the n_sub partial states of an item are merged through LDS.
-template <int D>
-__device__ __forceinline__ void arrive_and_merge(const AttnArgs &a, int bh, unsigned n_wgs)
+// Merge of the n_part partial entries of stream bh by its last workgroup:
+// out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, M = max_s m_s.
+// Thread t owns four channels of one head (item tid_item) and the entries
+// tid_sub, tid_sub + n_sub, ...  It issues the (m, l) and o loads of up to KC
+// of its entries together (one memory round trip), merges them online, and
+// the n_sub partial states of an item are merged through LDS (s_m, s_d,
+// s_acc).  KC is instantiated to the entries a thread actually has, so that
+// no masked-off entry slots are executed.
+template <int D, int KC>
+__device__ __forceinline__ void merge_stream(const AttnArgs &a, int bh, int n_sub, int tid_item, int tid_sub,
+                                             float *s_m, float *s_d, f4_t *s_acc)
 {
-    constexpr int kChunk = 16;
-    __shared__ int s_last;
-    __shared__ float s_m[kAttnThreads], s_d[kAttnThreads];
-    __shared__ f4_t s_acc[kAttnThreads];
-    __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are complete
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned prev =
-            __hip_atomic_fetch_add(a.counters + bh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (prev == n_wgs - 1);
-    }
-    __syncthreads();
-    if (!s_last)
-        return;
     const int tid = threadIdx.x;
     constexpr int nc4 = D / 4;
     const int g = a.g, P = a.n_part;
     const int n_items = g * nc4;  // <= 1024
-    // n_sub = kAttnThreads / n_items threads per item (when items are fewer
-    // than threads); thread tid = sub * n_items + item, found by subtraction
-    int n_sub = 1, tid_item = tid, tid_sub = 0;
-    if (n_items < kAttnThreads) {
-        while ((n_sub + 1) * n_items <= kAttnThreads)
-            ++n_sub;
-        while (tid_item >= n_items) {
-            tid_item -= n_items;
-            ++tid_sub;
-        }
-    }
     const PartBuf pb(a, bh);
     for (int it0 = 0; it0 < n_items; it0 += kAttnThreads) {
         const int item = it0 + tid_item;
@@ -525,10 +502,10 @@ __device__ __forceinline__ void arrive_and_merge(const AttnArgs &a, int bh, unsi
         const int h = own ? item / nc4 : 0, c4 = own ? item % nc4 : 0;
         float M = -INFINITY, den = 0.0f;
         f4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int e0 = sub; e0 < P; e0 += kChunk * n_sub) {
-            f4_t ml[kChunk], ov[kChunk];
+        for (int e0 = sub; e0 < P; e0 += KC * n_sub) {
+            f4_t ml[KC], ov[KC];
 #pragma unroll
-            for (int k = 0; k < kChunk; ++k) {
+            for (int k = 0; k < KC; ++k) {
                 const int e = e0 + k * n_sub;
                 if (own && e < P) {
                     ml[k] = pb.load4(pb.off(a, e, h, D));
@@ -537,7 +514,7 @@ __device__ __forceinline__ void arrive_and_merge(const AttnArgs &a, int bh, unsi
             }
             float Mc = M;
 #pragma unroll
-            for (int k = 0; k < kChunk; ++k)
+            for (int k = 0; k < KC; ++k)
                 if (own && e0 + k * n_sub < P)
                     Mc = fmaxf(Mc, ml[k][0]);
             if (Mc == -INFINITY)
@@ -547,7 +524,7 @@ __device__ __forceinline__ void arrive_and_merge(const AttnArgs &a, int bh, unsi
             den *= r;
             M = Mc;
 #pragma unroll
-            for (int k = 0; k < kChunk; ++k) {
+            for (int k = 0; k < KC; ++k) {
                 if (own && e0 + k * n_sub < P && ml[k][0] != -INFINITY) {
                     const float w = exp2f(ml[k][0] - M);
                     acc += w * ov[k];
@@ -582,6 +559,49 @@ __device__ __forceinline__ void arrive_and_merge(const AttnArgs &a, int bh, unsi
             *reinterpret_cast<f4_t *>(a.out + (static_cast<size_t>(bh) * g + h) * D + 4 * c4) =
                 acc * (1.0f / den);
     }
+}
+
+// Called by every workgroup at its end: the last one of stream bh to arrive
+// merges the n_part partial entries (merge_stream) and re-arms the stream's
+// counter.
+template <int D>
+__device__ __forceinline__ void arrive_and_merge(const AttnArgs &a, int bh, unsigned n_wgs)
+{
+    __shared__ int s_last;
+    __shared__ float s_m[kAttnThreads], s_d[kAttnThreads];
+    __shared__ f4_t s_acc[kAttnThreads];
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are complete
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned prev =
+            __hip_atomic_fetch_add(a.counters + bh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (prev == n_wgs - 1);
+    }
+    __syncthreads();
+    if (!s_last)
+        return;
+    const int tid = threadIdx.x;
+    const int n_items = a.g * (D / 4);  // <= 1024
+    // n_sub = kAttnThreads / n_items threads per item (when items are fewer
+    // than threads); thread tid = sub * n_items + item, found by subtraction
+    int n_sub = 1, tid_item = tid, tid_sub = 0;
+    if (n_items < kAttnThreads) {
+        while ((n_sub + 1) * n_items <= kAttnThreads)
+            ++n_sub;
+        while (tid_item >= n_items) {
+            tid_item -= n_items;
+            ++tid_sub;
+        }
+    }
+    const int P = a.n_part;  // entries per thread: ceil(P / n_sub)
+    if (P <= 2 * n_sub)
+        merge_stream<D, 2>(a, bh, n_sub, tid_item, tid_sub, s_m, s_d, s_acc);
+    else if (P <= 4 * n_sub)
+        merge_stream<D, 4>(a, bh, n_sub, tid_item, tid_sub, s_m, s_d, s_acc);
+    else if (P <= 8 * n_sub)
+        merge_stream<D, 8>(a, bh, n_sub, tid_item, tid_sub, s_m, s_d, s_acc);
+    else
+        merge_stream<D, 16>(a, bh, n_sub, tid_item, tid_sub, s_m, s_d, s_acc);
     if (tid == 0)
         __hip_atomic_store(a.counters + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
