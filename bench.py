@@ -26,13 +26,20 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 
 
-def stream_state_bytes(d, kb, vb, G, N, Tq):
-    """Live bytes of one (sequence, kv-head) stream, as kvq_bytes documents."""
+def stream_state_bytes(d, kb, vb, G, N, Tq, k_tok=False):
+    """Live bytes of one (sequence, kv-head) stream, as kvq_bytes documents
+    (k_tok: per-token Key, one scale and zero per Key token)."""
     if kb == 16:
         return N * 4 * d
     wk = (d + 10) // 11 if kb == 3 else d * kb // 32
     wv = d * vb // 32
-    return Tq * 4 * (wk + wv) + (Tq // G) * 8 * d + Tq * 8 + (N - Tq) * 4 * d
+    kmeta = Tq * 8 if k_tok else (Tq // G) * 8 * d
+    return Tq * 4 * (wk + wv) + kmeta + Tq * 8 + (N - Tq) * 4 * d
+
+
+def layer_row(lc):
+    """(kb, vb, R, per-token Key) of a layer-table row (kb, vb, R[, k_mode])."""
+    return lc[0], lc[1], lc[2], len(lc) > 3 and lc[3] == 1
 
 
 def quantized_count(N, R, G, kb):
@@ -46,15 +53,16 @@ def step_bytes(w, N_before, qbytes):
     B, Hkv, Hq, d, G = w.batch, w.n_kv_heads, w.n_q_heads, w.head_dim, w.G
     BH = B * Hkv
     att = app = 0
-    for (kb, vb, R) in w.layers:
+    for lc in w.layers:
+        kb, vb, R, kt = layer_row(lc)
         N1 = N_before + 1
         Tq0 = quantized_count(N_before, R, G, kb)
         Tq1 = quantized_count(N1, R, G, kb)
-        att += BH * stream_state_bytes(d, kb, vb, G, N1, Tq1) + B * Hq * d * (qbytes + 4)
+        att += BH * stream_state_bytes(d, kb, vb, G, N1, Tq1, kt) + B * Hq * d * (qbytes + 4)
         app += BH * 2 * d * 2 * 2  # read new K and V, write them to the ring
         if Tq1 > Tq0:  # flush: read G 16-bit K/V rows, write codes and metadata
             wk = (d + 10) // 11 if kb == 3 else d * kb // 32
-            app += BH * (G * 4 * d + G * 4 * (wk + d * vb // 32) + 8 * d + 8 * G)
+            app += BH * (G * 4 * d + G * 4 * (wk + d * vb // 32) + (8 * G if kt else 8 * d) + 8 * G)
     return att, app
 
 
@@ -99,8 +107,8 @@ def cpu_baseline(w, seconds, layers_sample):
     cap = w.context + 4096
     layers = []
     for l in layers_sample:
-        kb, vb, R = w.layers[l]
-        o = ora.Layer(BH, g, d, kb, vb, w.G, R, cap, w.kv_dtype == "bf16")
+        kb, vb, R, kt = layer_row(w.layers[l])
+        o = ora.Layer(BH, g, d, kb, vb, w.G, R, cap, w.kv_dtype == "bf16", k_tok=kt)
         k, v = synth.layer_tokens(w, l, 0, w.context, "cpu")
         o.append(synth.bits16(k.reshape(BH, w.context, d)), synth.bits16(v.reshape(BH, w.context, d)))
         layers.append((l, o))
@@ -117,7 +125,7 @@ def cpu_baseline(w, seconds, layers_sample):
             o.append(kb16, vb16)
             o.attention(q)
             el += time.perf_counter() - t0
-            nbytes += BH * stream_state_bytes(d, o.k_bits, o.v_bits, o.G, o.N, o.Tq) + \
+            nbytes += BH * stream_state_bytes(d, o.k_bits, o.v_bits, o.G, o.N, o.Tq, o.k_tok) + \
                 B * w.n_q_heads * d * (qb + 4) + BH * 2 * d * 2 * 2
         steps += 1
     layer_steps = steps * len(layers)
@@ -140,7 +148,10 @@ def main():
     ap.add_argument("--steps", type=int, default=128)
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--workload", type=int, default=2)
-    ap.add_argument("--table", default="default", choices=["default", "k8v8"])
+    ap.add_argument("--table", default="default", choices=["default", "k8v8", "k4v4"],
+                    help="layer table: the workload's mixed table, or uniform KV8 / KV4 baselines")
+    ap.add_argument("--k-mode", default="per-channel", choices=["per-channel", "per-token"],
+                    help="Key quantization: per channel over G tokens (KIVI) or per token")
     ap.add_argument("--kernel-rounds", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -160,8 +171,14 @@ def main():
 
     dev = "cuda"
     w = synth.workload(args.workload)
-    if args.table == "k8v8":
-        w.layers = [(8, 8, r) for (_, _, r) in w.layers]
+    if args.table in ("k8v8", "k4v4"):
+        b = int(args.table[1])
+        w.layers = [(b, b, r) for (_, _, r) in w.layers]
+    if args.k_mode == "per-token":
+        if any(lc[0] == 3 for lc in w.layers):
+            print("per-token Key needs 2, 4 or 8 Key bits; this table has 3-bit layers", file=sys.stderr)
+            sys.exit(2)
+        w.layers = [(kb, vb, r, 1) for (kb, vb, r) in w.layers]
     L, B, Hq, Hkv, d = w.n_layers, w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim
     total = args.warmup + args.steps
     qbytes = 4 if w.q_dtype == "f32" else 2
@@ -206,11 +223,12 @@ def main():
 
     # the state the library reports agrees with the byte model used above
     N_end = w.context + total
-    for l, (kb, vb, R) in enumerate(w.layers):
+    for l, lc in enumerate(w.layers):
+        kb, vb, R, kt = layer_row(lc)
         info = cache.bytes_layer(l)
         assert info.n_tokens == N_end
         assert info.total == B * Hkv * stream_state_bytes(d, kb, vb, w.G, N_end,
-                                                         quantized_count(N_end, R, w.G, kb))
+                                                         quantized_count(N_end, R, w.G, kb), kt)
 
     # dominant kernel: decode attention (one launch per call).  HIP events on
     # the stream the library launches on bracket back-to-back calls over every
@@ -227,14 +245,15 @@ def main():
     torch.cuda.synchronize()
     avg_call_us = ev0.elapsed_time(ev1) * 1e3 / (rounds * L)
     att_per_layer = []
-    for l, (kb, vb, R) in enumerate(w.layers):
+    for l, lc in enumerate(w.layers):
+        kb, vb, R, kt = layer_row(lc)
         Tq = quantized_count(N_end, R, w.G, kb)
-        att_per_layer.append(B * Hkv * stream_state_bytes(d, kb, vb, w.G, N_end, Tq) +
+        att_per_layer.append(B * Hkv * stream_state_bytes(d, kb, vb, w.G, N_end, Tq, kt) +
                              B * Hq * d * (qbytes + 4))
     avg_att_bytes = sum(att_per_layer) / L
     achieved = avg_att_bytes / (avg_call_us * 1e-6) / 1e9
     splits, variant = kvq.kvq_last_launch(cache.h)
-    traffic = stored_traffic(args.workload, args.table)
+    traffic = stored_traffic(args.workload, args.table) if args.k_mode == "per-channel" else None
 
     if args.copy_mb > 0:  # a plain copy of known size, for scaling memory counters
         n = args.copy_mb * (1 << 20)
@@ -266,7 +285,8 @@ def main():
             "layers": L, "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": d,
             "context_start": w.context, "G": w.G, "R": w.R,
             "kv_dtype": w.kv_dtype, "q_dtype": w.q_dtype,
-            "table": "".join("K%dV%d " % (kb, vb) for kb, vb, _ in w.layers).strip(),
+            "table": "".join("K%dV%d " % tuple(lc[:2]) for lc in w.layers).strip(),
+            "k_mode": args.k_mode,
             "equiv_bits": w.equiv_bits()["kv"],
             "parallelism": "single GPU",
         },

@@ -11,8 +11,10 @@
 //
 // One workgroup quantizes the K half, another the V half of one group of one
 // stream.  The group's 16-bit tile is staged in LDS with 16-byte loads; K is
-// reduced per channel (min/max over the G tokens), V per token (min/max over
-// head_dim, a few threads per token); then the codes are packed.
+// reduced per channel (min/max over the G tokens), or per token in the
+// per-token-asym Key mode (KVTuner summary: the KIVI and per-token-asym
+// modes), V per token (min/max over head_dim, a few threads per token); then
+// the codes are packed.
 //
 // Bit-exactness with a serial CPU evaluation: min/max are exact in any order;
 // the subtraction and the IEEE fp32 division are correctly rounded (no fast
@@ -85,6 +87,44 @@ __device__ __forceinline__ void stage(const FlushArgs &a, const uint16_t *ring, 
     }
 }
 
+// Per-token min / max over the D channels of the G staged tokens, tpt threads
+// per token; scale s = (max - min) / qmax and minimum of token i go to s_c[i]
+// and mn_c[i] (G <= 256) and, as the pair (scale, zero), to meta[2 i].
+__device__ __forceinline__ void token_scales(const uint16_t *tile, int G, int D, int bf, int qmax, float *meta,
+                                             float *s_c, float *mn_c, float *red_mn, float *red_mx)
+{
+#pragma clang fp contract(off)
+    const int tid = threadIdx.x;
+    const int tpt = G <= kThreads ? kThreads / G : 1;  // threads per token
+    for (int i0 = 0; i0 < G; i0 += kThreads / tpt) {
+        const int i = i0 + tid / tpt, sub = tid % tpt;
+        float vmn = INFINITY, vmx = -INFINITY;
+        if (i < G && tid / tpt < kThreads / tpt) {
+            for (int cc = sub; cc < D; cc += tpt) {
+                const float x = widen16(tile[i * D + cc], bf);
+                vmn = fminf(vmn, x);
+                vmx = fmaxf(vmx, x);
+            }
+        }
+        __syncthreads();  // red_* of the previous pass are consumed
+        red_mn[tid] = vmn;
+        red_mx[tid] = vmx;
+        __syncthreads();
+        if (i < G && sub == 0 && tid / tpt < kThreads / tpt) {
+            for (int r = 1; r < tpt; ++r) {
+                vmn = fminf(vmn, red_mn[tid + r]);
+                vmx = fmaxf(vmx, red_mx[tid + r]);
+            }
+            const float s = (vmx - vmn) / static_cast<float>(qmax);
+            s_c[i % 256] = s;
+            mn_c[i % 256] = vmn;
+            meta[2 * i] = (s == 0.0f) ? 0.0f : s;
+            meta[2 * i + 1] = (vmn == 0.0f) ? 0.0f : vmn;
+        }
+    }
+    __syncthreads();
+}
+
 // One workgroup per (group, stream, K or V): the K and V halves of a group
 // are independent and run side by side.
 __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a)
@@ -100,7 +140,24 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a)
     __shared__ float red_mn[kThreads], red_mx[kThreads];
     __shared__ float s_c[256], mn_c[256];
 
-    if (!is_v) {
+    if (!is_v && a.L.k_tok) {
+        // ---- Key, per-token asymmetric: one scale and zero per token ----
+        stage(a, a.L.ring_k, a.k_new, bh, t0, tile);
+        __syncthreads();
+        const int kb = a.L.kb, kq = (1 << kb) - 1, wk = a.L.wk;
+        token_scales(tile, G, D, bf, kq, a.L.k_meta + (static_cast<size_t>(bh) * a.L.capq + t0) * 2, s_c, mn_c,
+                     red_mn, red_mx);
+        const int epw = 32 / kb;
+        for (int it = tid; it < G * wk; it += kThreads) {
+            const int i = it / wk, w = it % wk;
+            uint32_t word = 0;
+            for (int sl = 0; sl < epw; ++sl) {
+                const int cc = w * epw + sl;
+                word |= code_of(widen16(tile[i * D + cc], bf), mn_c[i], s_c[i], kq) << (kb * sl);
+            }
+            a.L.k_words[(static_cast<size_t>(bh) * a.L.capq + t0 + i) * wk + w] = word;
+        }
+    } else if (!is_v) {
         // ---- Key: min / max per channel over the G tokens ----
         stage(a, a.L.ring_k, a.k_new, bh, t0, tile);
         __syncthreads();
@@ -155,35 +212,8 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a)
         stage(a, a.L.ring_v, a.v_new, bh, t0, tile);
         __syncthreads();
         const int vb = a.L.vb, vq = (1 << vb) - 1;
-        const int tpt = G <= kThreads ? kThreads / G : 1;  // threads per token
-        for (int i0 = 0; i0 < G; i0 += kThreads / tpt) {
-            const int i = i0 + tid / tpt, sub = tid % tpt;
-            float vmn = INFINITY, vmx = -INFINITY;
-            if (i < G && tid / tpt < kThreads / tpt) {
-                for (int cc = sub; cc < D; cc += tpt) {
-                    const float x = widen16(tile[i * D + cc], bf);
-                    vmn = fminf(vmn, x);
-                    vmx = fmaxf(vmx, x);
-                }
-            }
-            __syncthreads();  // red_* of the previous pass are consumed
-            red_mn[tid] = vmn;
-            red_mx[tid] = vmx;
-            __syncthreads();
-            if (i < G && sub == 0 && tid / tpt < kThreads / tpt) {
-                for (int r = 1; r < tpt; ++r) {
-                    vmn = fminf(vmn, red_mn[tid + r]);
-                    vmx = fmaxf(vmx, red_mx[tid + r]);
-                }
-                const float s = (vmx - vmn) / static_cast<float>(vq);
-                s_c[i % 256] = s;  // per-token scale and minimum (G <= 256 per pass)
-                mn_c[i % 256] = vmn;
-                float *vm = a.L.v_meta + (static_cast<size_t>(bh) * a.L.capq + t0 + i) * 2;
-                vm[0] = (s == 0.0f) ? 0.0f : s;
-                vm[1] = (vmn == 0.0f) ? 0.0f : vmn;
-            }
-        }
-        __syncthreads();
+        token_scales(tile, G, D, bf, vq, a.L.v_meta + (static_cast<size_t>(bh) * a.L.capq + t0) * 2, s_c, mn_c,
+                     red_mn, red_mx);
 
         const int wv = a.L.wv;
         uint32_t *vrow0 = a.L.v_words + (static_cast<size_t>(bh) * a.L.capq + t0) * wv;

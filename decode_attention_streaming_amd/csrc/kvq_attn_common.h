@@ -299,7 +299,15 @@ __device__ void valu_range(const AttnArgs &a, int bh, int t_beg, int t_end, int 
         const bool valid = ti < nt;
         float ks[CPT], kz[CPT];
         float vs = 1.0f, vz = 0.0f;
-        if (quant && valid) {
+        if (quant && valid && L.k_tok) {
+            // per-token Key: one scale and zero for the whole row
+            const float2 k2 = *reinterpret_cast<const float2 *>(L.k_meta + (row0 + t) * 2);
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                ks[i] = k2.x;
+                kz[i] = k2.y;
+            }
+        } else if (quant && valid) {
             const float *km = L.k_meta + (static_cast<size_t>(bh) * ngcap + t / L.G) * 2 * D + c0;
 #pragma unroll
             for (int i = 0; i < CPT; i += 4) {
@@ -308,6 +316,8 @@ __device__ void valu_range(const AttnArgs &a, int bh, int t_beg, int t_end, int 
                 ks[i] = s4.x; ks[i + 1] = s4.y; ks[i + 2] = s4.z; ks[i + 3] = s4.w;
                 kz[i] = z4.x; kz[i + 1] = z4.y; kz[i + 2] = z4.z; kz[i + 3] = z4.w;
             }
+        }
+        if (quant && valid) {
             const float2 vm = *reinterpret_cast<const float2 *>(L.v_meta + (row0 + t) * 2);
             vs = vm.x;
             vz = vm.y;

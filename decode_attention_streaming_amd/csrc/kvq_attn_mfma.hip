@@ -302,6 +302,7 @@ template <int NB, int KW, int FW>
 struct RoundData {
     uint32_t k0[NB][KW], k1[NB][KW], v[NB][FW];
     float4 vm[4];
+    float4 km[4];  // per-token Key: (scale, zero) of the same eight tokens
 };
 
 // One unit: groups [g_beg, g_end) of stream bh, in windows of NG groups (one
@@ -311,7 +312,7 @@ struct RoundData {
 // softmax work of one round serves nb blocks.  In the P.V products a lane's
 // weights enter only its own block's product (zeros elsewhere).
 // Results for head h < g go to po[h * D + c], pm[h], pl[h] (LDS).
-template <int KB, int VB, int D>
+template <int KB, int VB, int D, bool KT>
 __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *po, float *pm, float *pl,
                           float *meta_lds)
 {
@@ -344,6 +345,8 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *
     const uint32_t *kw_base = L.k_words + static_cast<size_t>(bh) * L.capq * L.wk + q * KW;
     const uint32_t *vw_base = L.v_words + static_cast<size_t>(bh) * L.capq * L.wv + lane * FW;
     const float *vm_base = L.v_meta + static_cast<size_t>(bh) * L.capq * 2;
+    constexpr bool ktok = KT;  // per-token Key
+    const float *km_tok = L.k_meta + static_cast<size_t>(bh) * L.capq * 2;  // its [capq][2] meta
 
     float m_run = -INFINITY, l_run = 0.0f, zb_run = 0.0f;
     int E = -1000;  // running V-scale exponent of this column: its weights carry 2^-E
@@ -363,7 +366,7 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *
     float *q_lds = meta_lds + NG * 2 * D;
     auto setup_issue = [&](int w0, int nwin) {
         const float *src = L.k_meta + (static_cast<size_t>(bh) * a.ngcap + w0) * 2 * D;
-        const int n16 = nwin * D / 2;  // 16-byte pieces of nwin groups' [2][D] floats
+        const int n16 = ktok ? 0 : nwin * D / 2;  // 16-byte pieces of nwin groups' [2][D] floats
         for (int i0 = 0; i0 < n16; i0 += 64) {
             if (i0 + lane < n16)
                 __builtin_amdgcn_global_load_lds(src + 4 * (i0 + lane), meta_lds + 4 * i0, 16, 0, 0);
@@ -429,8 +432,12 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *
             }
 #pragma unroll
             for (int i = 0; i < QC; i += 4) {
-                const float4 s4 = *reinterpret_cast<const float4 *>(sp + i);
-                const float4 z4 = *reinterpret_cast<const float4 *>(zp + i);
+                // per-token Key: no per-channel factors here (s = z = 1: bias is
+                // then sum_c q_c, the z-term's factor); the token's scale and
+                // zero apply to the scores
+                const float4 one = {1.0f, 1.0f, 1.0f, 1.0f};
+                const float4 s4 = ktok ? one : *reinterpret_cast<const float4 *>(sp + i);
+                const float4 z4 = ktok ? one : *reinterpret_cast<const float4 *>(zp + i);
                 const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
                 const float zv[4] = {z4.x, z4.y, z4.z, z4.w};
 #pragma unroll
@@ -492,6 +499,17 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *
         d.vm[1] = m0[1];
         d.vm[2] = m1[0];
         d.vm[3] = m1[1];
+        if constexpr (KT) {
+            {
+                const float4 *k0 = reinterpret_cast<const float4 *>(km_tok + static_cast<size_t>(tm + 4 * q) * 2);
+                const float4 *k1 =
+                    reinterpret_cast<const float4 *>(km_tok + static_cast<size_t>(tm + 16 + 4 * q) * 2);
+                d.km[0] = k0[0];
+                d.km[1] = k0[1];
+                d.km[2] = k1[0];
+                d.km[3] = k1[1];
+            }
+        }
     };
 
     auto process_round = [&](const RoundData<NB, KW, FW> &d, int nb, bool mine, int my_b) {
@@ -532,9 +550,20 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *
                 }
             }
         }
+        if constexpr (KT) {
+            // score_t = s_t sum_c q_c code_tc + z_t sum_c q_c
+            const float ks[8] = {d.km[0].x, d.km[0].z, d.km[1].x, d.km[1].z,
+                                 d.km[2].x, d.km[2].z, d.km[3].x, d.km[3].z};
+            const float kz[8] = {d.km[0].y, d.km[0].w, d.km[1].y, d.km[1].w,
+                                 d.km[2].y, d.km[2].w, d.km[3].y, d.km[3].w};
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            sc[j] = __builtin_fmaf(sc[j], kscale, bias);
+            for (int j = 0; j < 8; ++j)
+                sc[j] = __builtin_fmaf(sc[j] * kscale, ks[j], kz[j] * bias);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                sc[j] = __builtin_fmaf(sc[j], kscale, bias);
+        }
         const float vs[8] = {d.vm[0].x, d.vm[0].z, d.vm[1].x, d.vm[1].z,
                              d.vm[2].x, d.vm[2].z, d.vm[3].x, d.vm[3].z};
         const float vz[8] = {d.vm[0].y, d.vm[0].w, d.vm[1].y, d.vm[1].w,
@@ -848,7 +877,7 @@ __host__ __device__ inline int wave_region(const AttnArgs &a)
     return mfma_wave_region(a.D, a.g, a.units_q > 0, a.units_r > 0);
 }
 
-template <int KB, int VB, int D>
+template <int KB, int VB, int D, bool KT>
 __global__ __launch_bounds__(kAttnThreads, (mfma_waves_per_simd<KB, VB>())) void attn_mfma_kernel(AttnArgs a)
 {
     extern __shared__ float lds[];
@@ -860,7 +889,7 @@ __global__ __launch_bounds__(kAttnThreads, (mfma_waves_per_simd<KB, VB>())) void
     const int region = wave_region(a);
     float *po = lds + wave * region;
     if (unit < a.units_q) {
-        mfma_unit<KB, VB, D>(a, bh, unit, lane, po, s_pm[wave], s_pl[wave], po);
+        mfma_unit<KB, VB, D, KT>(a, bh, unit, lane, po, s_pm[wave], s_pl[wave], po);
     } else if (unit < a.units_q + a.units_r) {
         if (a.kv_bf16)
             mfma_residual_unit<D, true>(a, bh, unit - a.units_q, lane, po, s_pm[wave], s_pl[wave]);
@@ -875,12 +904,12 @@ __global__ __launch_bounds__(kAttnThreads, (mfma_waves_per_simd<KB, VB>())) void
     arrive_and_merge<D>(a, bh, gridDim.x);
 }
 
-template <int KB, int VB>
+template <int KB, int VB, bool KT>
 hipError_t launch_pair(const AttnArgs &a, hipStream_t st)
 {
     dim3 grid(a.mfma_wgs, a.BH);
     const size_t lds = (kAttnThreads / 64) * wave_region(a) * sizeof(float);
-    hipLaunchKernelGGL((attn_mfma_kernel<KB, VB, KVQ_D>), grid, dim3(kAttnThreads), lds, st, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<KB, VB, KVQ_D, KT>), grid, dim3(kAttnThreads), lds, st, a);
     return hipGetLastError();
 }
 
@@ -892,16 +921,18 @@ hipError_t launch_pair(const AttnArgs &a, hipStream_t st)
 hipError_t KVQ_CAT(launch_mfma_d, KVQ_D)(const AttnArgs &a, hipStream_t st)
 {
     const int kb = a.L.kb, vb = a.L.vb;
-#define KVQ_PAIR(K, V)                 \
-    if (kb == K && vb == V)            \
-        return launch_pair<K, V>(a, st);
+#define KVQ_PAIR(K, V)                                                        \
+    if (kb == K && vb == V)                                                   \
+        return a.L.k_tok ? launch_pair<K, V, true>(a, st) : launch_pair<K, V, false>(a, st);
     KVQ_PAIR(2, 2) KVQ_PAIR(2, 4) KVQ_PAIR(2, 8)
     KVQ_PAIR(4, 2) KVQ_PAIR(4, 4) KVQ_PAIR(4, 8)
     KVQ_PAIR(8, 2) KVQ_PAIR(8, 4) KVQ_PAIR(8, 8)
 #if KVQ_D == 128
     // 3-bit rows: twelve words, three per lane quad (head_dim 256 would need
     // more registers than two waves per SIMD leave)
-    KVQ_PAIR(3, 2) KVQ_PAIR(3, 4) KVQ_PAIR(3, 8)
+    if (kb == 3 && vb == 2) return launch_pair<3, 2, false>(a, st);
+    if (kb == 3 && vb == 4) return launch_pair<3, 4, false>(a, st);
+    if (kb == 3 && vb == 8) return launch_pair<3, 8, false>(a, st);
 #endif
 #undef KVQ_PAIR
     return hipErrorInvalidValue;

@@ -22,6 +22,7 @@ namespace kvq {
 struct LayerDev {
     uint32_t *k_words;  // [BH][capq][wk]
     float *k_meta;      // [BH][capq / G][2][D]   per group: D scales, then D zeros
+                        // (per-token Key: [BH][capq][2], scale and zero per token)
     uint32_t *v_words;  // [BH][capq][wv] (row-major or 32-token tiles, same size)
     float *v_meta;      // [BH][capq][2]          per token: scale, zero
     uint16_t *ring_k;   // [BH][R][D]             recent tokens, slot = t % R
@@ -32,6 +33,7 @@ struct LayerDev {
     int G;              // tokens per K group
     int capq;           // quantized-token capacity per stream (multiple of G and 32)
     int v_tiled;        // V code layout, see above
+    int k_tok;          // 1: Key quantized per token (k_meta per token), 0: per channel
 };
 
 // Quantize and pack groups [Tq0 + j*G, Tq0 + (j+1)*G), j < n_groups, for every

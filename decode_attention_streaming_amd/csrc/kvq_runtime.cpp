@@ -106,12 +106,18 @@ int plan_layout(const kvq_config *cfg, Plan *plan, std::string *err)
         if (!valid_pair(lc.k_bits, lc.v_bits))
             return fail(KVQ_EINVAL, "layer %d: (k_bits, v_bits) = (%d, %d) not supported", l, lc.k_bits,
                         lc.v_bits);
+        if (lc.k_mode != KVQ_K_PER_CHANNEL && lc.k_mode != KVQ_K_PER_TOKEN)
+            return fail(KVQ_EINVAL, "layer %d: k_mode %d is neither per-channel (0) nor per-token (1)", l,
+                        lc.k_mode);
+        if (lc.k_mode == KVQ_K_PER_TOKEN && lc.k_bits == 3)
+            return fail(KVQ_EUNSUPPORTED, "layer %d: per-token Key needs k_bits 2, 4 or 8", l);
         LayerState &s = plan->layers[l];
         kvq::LayerDev &d = s.dev;
         d.kb = lc.k_bits;
         d.vb = lc.v_bits;
         d.G = G;
         d.v_tiled = plan->v_tiled;
+        d.k_tok = (lc.k_mode == KVQ_K_PER_TOKEN && lc.k_bits != 16) ? 1 : 0;
         if (d.kb == 16) {
             d.R = cfg->max_context;
             d.capq = G;  // unused
@@ -130,7 +136,7 @@ int plan_layout(const kvq_config *cfg, Plan *plan, std::string *err)
             s.off_kw = off;
             off = align_up(off + BH * d.capq * d.wk * 4, A);
             s.off_km = off;
-            off = align_up(off + BH * (d.capq / G) * 2 * D * 4, A);
+            off = align_up(off + (d.k_tok ? BH * d.capq * 2 * 4 : BH * (d.capq / G) * 2 * D * 4), A);
             s.off_vw = off;
             off = align_up(off + BH * d.capq * d.wv * 4, A);
             s.off_vm = off;
@@ -585,6 +591,7 @@ static void layer_bytes(const kvq_handle *h, const LayerState &s, kvq_bytes_info
     info->k_bits = d.kb;
     info->v_bits = d.vb;
     info->residual_len = d.R;
+    info->k_mode = d.k_tok ? KVQ_K_PER_TOKEN : KVQ_K_PER_CHANNEL;
     if (d.kb == 16) {
         info->residual = BH * s.N * 4 * D;
     } else {
@@ -592,7 +599,7 @@ static void layer_bytes(const kvq_handle *h, const LayerState &s, kvq_bytes_info
         info->v_words = d.wv;
         info->k_codes = BH * s.Tq * 4 * d.wk;
         info->v_codes = BH * s.Tq * 4 * d.wv;
-        info->k_meta = BH * (s.Tq / d.G) * 8 * D;
+        info->k_meta = d.k_tok ? BH * s.Tq * 8 : BH * (s.Tq / d.G) * 8 * D;
         info->v_meta = BH * s.Tq * 8;
         info->residual = BH * (s.N - s.Tq) * 4 * D;
     }
@@ -667,7 +674,18 @@ int kvq_export_layer(kvq_handle *h, int layer, uint32_t *k_words, float *k_scale
                     return h->dev_fail(e, "export v_words");
                 }
             }
-            if (k_scale || k_zero) {
+            if ((k_scale || k_zero) && d.k_tok) {
+                std::vector<float> m(static_cast<size_t>(Tq) * 2);
+                if ((e = hipMemcpy(m.data(), d.k_meta + row0 * 2, m.size() * 4, hipMemcpyDeviceToHost)) !=
+                    hipSuccess)
+                    return h->dev_fail(e, "export k_meta");
+                for (int t = 0; t < Tq; ++t) {
+                    if (k_scale)
+                        k_scale[static_cast<size_t>(bh) * Tq + t] = m[2 * t];
+                    if (k_zero)
+                        k_zero[static_cast<size_t>(bh) * Tq + t] = m[2 * t + 1];
+                }
+            } else if (k_scale || k_zero) {
                 std::vector<float> m(static_cast<size_t>(ng) * 2 * D);
                 if ((e = hipMemcpy(m.data(), d.k_meta + static_cast<size_t>(bh) * ngcap * 2 * D,
                                    m.size() * 4, hipMemcpyDeviceToHost)) != hipSuccess)

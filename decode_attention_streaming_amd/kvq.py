@@ -23,9 +23,12 @@ EXPORTED = ["kvq_workspace_bytes", "kvq_create", "kvq_append", "kvq_decode_atten
             "kvq_set_stream", "kvq_last_error", "kvq_destroy", "kvq_last_launch"]
 
 
+KVQ_K_PER_CHANNEL, KVQ_K_PER_TOKEN = 0, 1
+
+
 class kvq_layer_cfg(ctypes.Structure):
     _fields_ = [("k_bits", ctypes.c_int32), ("v_bits", ctypes.c_int32),
-                ("residual_len", ctypes.c_int32)]
+                ("residual_len", ctypes.c_int32), ("k_mode", ctypes.c_int32)]
 
 
 class kvq_config(ctypes.Structure):
@@ -39,7 +42,7 @@ class kvq_bytes_info(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in
                 ("k_codes", "k_meta", "v_codes", "v_meta", "residual", "total")] + [
         (n, ctypes.c_int32) for n in ("n_tokens", "n_quantized", "n_residual", "k_words",
-                                      "v_words", "k_bits", "v_bits", "residual_len")]
+                                      "v_words", "k_bits", "v_bits", "residual_len", "k_mode")]
 
 
 class KvqError(RuntimeError):
@@ -260,8 +263,8 @@ class Cache:
         out = dict(
             N=info.n_tokens, Tq=Tq,
             k_words=np.zeros((B * H, Tq, wk), np.uint32),
-            k_scale=np.zeros((B * H, Tq // G, d), np.float32),
-            k_zero=np.zeros((B * H, Tq // G, d), np.float32),
+            k_scale=np.zeros((B * H, Tq) if info.k_mode else (B * H, Tq // G, d), np.float32),
+            k_zero=np.zeros((B * H, Tq) if info.k_mode else (B * H, Tq // G, d), np.float32),
             v_words=np.zeros((B * H, Tq, wv), np.uint32),
             v_scale=np.zeros((B * H, Tq), np.float32),
             v_zero=np.zeros((B * H, Tq), np.float32),

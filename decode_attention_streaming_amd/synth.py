@@ -48,7 +48,7 @@ class Workload:
     q_dtype: str           # "f32" | "f16" | "bf16"
     G: int
     R: int
-    layers: List[Tuple[int, int, int]] = field(default_factory=list)  # (kb, vb, R_l)
+    layers: List[Tuple[int, ...]] = field(default_factory=list)  # (kb, vb, R_l[, k_mode])
     k_outliers: Tuple[int, float] = (2, 10.0)
     v_kind: str = "normal"  # "normal" | "walk512" | "half_shift"
 

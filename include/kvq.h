@@ -64,15 +64,27 @@ extern "C" {
 /* Required alignment of the device workspace, in bytes. */
 #define KVQ_WORKSPACE_ALIGN 256
 
+/* Key quantization modes (KVTuner summary, A3 and the evaluation of the
+ * KIVI and per-token-asym modes): KIVI's per-channel Key (one scale and zero
+ * per channel over a group of G tokens) or per-token asymmetric Key (one scale
+ * and zero per token over its head_dim channels, like Value). */
+#define KVQ_K_PER_CHANNEL 0
+#define KVQ_K_PER_TOKEN 1
+
 /* One row of the per-layer precision table.
  *   k_bits in {2, 3, 4, 8, 16}; v_bits in {2, 4, 8, 16}; 16 means the layer is
  *   not quantized and must be given as the pair (16, 16).
  *   residual_len: recent-token buffer length R_l for this layer; 0 selects the
- *   config's residual_len.  Must be >= group_size.  Ignored for (16, 16). */
+ *   config's residual_len.  Must be >= group_size.  Ignored for (16, 16).
+ *   k_mode: KVQ_K_PER_CHANNEL (0) or KVQ_K_PER_TOKEN (1); per-token Key needs
+ *   k_bits in {2, 4, 8} (the 3-bit layout's 2-bit slot is a per-channel
+ *   format).  Ignored for (16, 16).  Both modes keep the same recent-token
+ *   buffer and flush G tokens at a time. */
 typedef struct kvq_layer_cfg {
     int32_t k_bits;
     int32_t v_bits;
     int32_t residual_len;
+    int32_t k_mode;
 } kvq_layer_cfg;
 
 /* Cache geometry.  All counts are >= 1.
@@ -139,8 +151,9 @@ int kvq_append_decode_attention(kvq_handle *h, int layer, const void *k_new, con
 
 /* Live bytes of the cache state over all layers, host arithmetic only: per
  * (sequence, kv-head): Tq rows of packed K and V codes (4 bytes per word), one
- * fp32 scale and zero per channel per K group, one fp32 scale and zero per V
- * token, and 2 bytes per element for the recent K and V tokens; a (16, 16)
+ * fp32 scale and zero per channel per K group (per-token Key: per K token),
+ * one fp32 scale and zero per V token, and 2 bytes per element for the recent
+ * K and V tokens; a (16, 16)
  * layer counts all its tokens at 2 bytes per element.  (KIVI notes, section 2.1
  * for the 16-bit case.)  Returns -1 for a NULL handle. */
 int64_t kvq_bytes(const kvq_handle *h);
@@ -153,6 +166,7 @@ typedef struct kvq_bytes_info {
     int32_t k_words;      /* 32-bit words per packed K row */
     int32_t v_words;      /* 32-bit words per packed V row */
     int32_t k_bits, v_bits, residual_len;
+    int32_t k_mode;       /* KVQ_K_PER_CHANNEL or KVQ_K_PER_TOKEN */
 } kvq_bytes_info;
 
 /* Byte breakdown and token counts of one layer (host only). */
@@ -165,7 +179,8 @@ int kvq_bytes_layer(const kvq_handle *h, int layer, kvq_bytes_info *info);
  *   k_words  uint32 [B][H][Tq][k_words]   row t = channels 0..d-1 of token t,
  *            codes least-significant bits first (3-bit: channel c in word c/11,
  *            bits 3(c%11), 2 bits wide in slot 10; unused slots 0)
- *   k_scale, k_zero  float [B][H][Tq/G][d]
+ *   k_scale, k_zero  float [B][H][Tq/G][d] (per-channel Key) or
+ *            float [B][H][Tq] (per-token Key)
  *   v_words  uint32 [B][H][Tq][v_words]
  *   v_scale, v_zero  float [B][H][Tq]
  *   res_k, res_v     kv_dtype [B][H][Tr][d], oldest token first

@@ -22,6 +22,9 @@
  *              (Key per channel, Value per token, q = round((x - min)/s),
  *              s = (max - min)/q_max, results packed into int32; the 3-bit
  *              layout of eleven elements per word: ten at 3 bits, one at 2).
+ *   [KVTuner]  also: the two Key quantization modes it evaluates, KIVI
+ *              (per-channel Key) and per-token-asym (each token's Key
+ *              quantized over its channels, like Value).
  *   [KIVI]     "LLM quantization notes 08: KV cache quantization and KIVI",
  *              section 6.1 (one scale + zero-point per head per channel for K,
  *              per token for V), section 6.2 (streaming: recent tokens kept in
@@ -192,18 +195,31 @@ static void flush_group(kvqo_layer *L)
     for (int s = 0; s < L->n_streams; ++s) {
         const uint16_t *hk = L->hist_k + ((size_t)s * L->cap + t0) * d;
         const uint16_t *hv = L->hist_v + ((size_t)s * L->cap + t0) * d;
-        /* Key: one (scale, zero) per channel over the G tokens of the group. */
-        for (int i = 0; i < G; ++i)
+        if (L->k_tok) {
+            /* Key, per-token-asym mode: one (scale, zero) per token over its
+             * d channels, as for Value. */
+            for (int i = 0; i < G; ++i) {
+                for (int c = 0; c < d; ++c)
+                    x[c] = widen(hk[(size_t)i * d + c], L->is_bf16);
+                size_t t = (size_t)s * L->cap + t0 + i;
+                kvqo_quantize(x, d, 1, (1 << L->k_bits) - 1, codes, 1,
+                              &L->k_scale[t], &L->k_zero[t]);
+                kvqo_pack_row(codes, d, L->k_bits, L->k_words + t * wk);
+            }
+        } else {
+            /* Key: one (scale, zero) per channel over the G tokens of the group. */
+            for (int i = 0; i < G; ++i)
+                for (int c = 0; c < d; ++c)
+                    x[(size_t)i * d + c] = widen(hk[(size_t)i * d + c], L->is_bf16);
+            float *ks = L->k_scale + ((size_t)s * (L->cap / G) + gi) * d;
+            float *kz = L->k_zero + ((size_t)s * (L->cap / G) + gi) * d;
             for (int c = 0; c < d; ++c)
-                x[(size_t)i * d + c] = widen(hk[(size_t)i * d + c], L->is_bf16);
-        float *ks = L->k_scale + ((size_t)s * (L->cap / G) + gi) * d;
-        float *kz = L->k_zero + ((size_t)s * (L->cap / G) + gi) * d;
-        for (int c = 0; c < d; ++c)
-            kvqo_quantize(x + c, G, d, kvqo_qmax(L->k_bits, c), codes + c, d,
-                          &ks[c], &kz[c]);
-        for (int i = 0; i < G; ++i)
-            kvqo_pack_row(codes + (size_t)i * d, d, L->k_bits,
-                          L->k_words + ((size_t)s * L->cap + t0 + i) * wk);
+                kvqo_quantize(x + c, G, d, kvqo_qmax(L->k_bits, c), codes + c, d,
+                              &ks[c], &kz[c]);
+            for (int i = 0; i < G; ++i)
+                kvqo_pack_row(codes + (size_t)i * d, d, L->k_bits,
+                              L->k_words + ((size_t)s * L->cap + t0 + i) * wk);
+        }
         /* Value: one (scale, zero) per token over its d channels. */
         for (int i = 0; i < G; ++i) {
             for (int c = 0; c < d; ++c)
@@ -242,6 +258,10 @@ int kvqo_append(kvqo_layer *L, const uint16_t *k_new, const uint16_t *v_new, int
 /* Dequantized Key of token t of stream s, channel c, in fp64. */
 static double key_hat(const kvqo_layer *L, int s, int t, int c, const uint8_t *row_codes)
 {
+    if (t < L->Tq && L->k_tok) {
+        size_t tt = (size_t)s * L->cap + t;
+        return (double)row_codes[c] * (double)L->k_scale[tt] + (double)L->k_zero[tt];
+    }
     if (t < L->Tq) {
         size_t g = (size_t)s * (L->cap / L->G) + t / L->G;
         return (double)row_codes[c] * (double)L->k_scale[g * L->d + c] +
@@ -321,13 +341,13 @@ void kvqo_attention(const kvqo_layer *L, const double *q, double *out)
  * per token.  Recent tokens: K and V at 2 bytes per element.  A (16,16) layer
  * holds N tokens at 2 bytes per element for K and V.
  * [KIVI] 2.1: the 16-bit case is 2 * head_dim * 2 bytes per token per head. */
-long long kvqo_stream_bytes(int d, int k_bits, int v_bits, int G, long long N, long long Tq)
+long long kvqo_stream_bytes(int d, int k_bits, int v_bits, int G, long long N, long long Tq, int k_tok)
 {
     if (k_bits == 16)
         return N * 4LL * d;
     long long Tr = N - Tq;
     long long code_bytes = Tq * 4LL * (kvqo_words_per_row(d, k_bits) + kvqo_words_per_row(d, v_bits));
-    long long kmeta = (Tq / G) * 8LL * d;
+    long long kmeta = k_tok ? Tq * 8LL : (Tq / G) * 8LL * d; /* per token or per group and channel */
     long long vmeta = Tq * 8LL;
     return code_bytes + kmeta + vmeta + Tr * 4LL * d;
 }

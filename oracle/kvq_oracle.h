@@ -7,6 +7,7 @@
  *   hist_k, hist_v   uint16 [n_streams][cap][d]   every appended token, raw
  *   k_words          uint32 [n_streams][cap][W(k_bits)]   rows 0..Tq-1 valid
  *   k_scale, k_zero  float  [n_streams][cap/G][d]         groups 0..Tq/G-1
+ *                    (per-token Key, k_tok = 1: float [n_streams][cap])
  *   v_words          uint32 [n_streams][cap][W(v_bits)]
  *   v_scale, v_zero  float  [n_streams][cap]
  * Tokens [0, Tq) are quantized; tokens [Tq, N) are the recent 16-bit tokens.
@@ -22,6 +23,7 @@ typedef struct kvqo_layer {
     int cap;              /* token capacity */
     int is_bf16;          /* 16-bit inputs: 0 = IEEE binary16, 1 = bfloat16 */
     int N, Tq;            /* tokens appended, tokens quantized */
+    int k_tok;            /* 1: Key per token (like Value), 0: per channel over G tokens */
     uint16_t *hist_k, *hist_v;
     uint32_t *k_words;
     float *k_scale, *k_zero;
@@ -41,6 +43,6 @@ void kvqo_quantize(const float *x, int n, long stride, int qmax,
 int kvqo_append(kvqo_layer *L, const uint16_t *k_new, const uint16_t *v_new, int n);
 /* q, out: double [n_streams][g][d]. */
 void kvqo_attention(const kvqo_layer *L, const double *q, double *out);
-long long kvqo_stream_bytes(int d, int k_bits, int v_bits, int G, long long N, long long Tq);
+long long kvqo_stream_bytes(int d, int k_bits, int v_bits, int G, long long N, long long Tq, int k_tok);
 
 #endif

@@ -68,7 +68,7 @@ def _bind(L):
     L.kvqo_attention.restype = None
     L.kvqo_attention.argtypes = [P, P, P]
     L.kvqo_stream_bytes.restype = ctypes.c_longlong
-    L.kvqo_stream_bytes.argtypes = [ctypes.c_int] * 4 + [ctypes.c_longlong] * 2
+    L.kvqo_stream_bytes.argtypes = [ctypes.c_int] * 4 + [ctypes.c_longlong] * 2 + [ctypes.c_int]
     _lib = L
     return L
 
@@ -122,8 +122,8 @@ def quantize(x, qmax_):
     return codes, s[0], z[0]
 
 
-def stream_bytes(d, k_bits, v_bits, G, N, Tq):
-    return lib().kvqo_stream_bytes(d, k_bits, v_bits, G, N, Tq)
+def stream_bytes(d, k_bits, v_bits, G, N, Tq, k_tok=False):
+    return lib().kvqo_stream_bytes(d, k_bits, v_bits, G, N, Tq, int(bool(k_tok)))
 
 
 # ---------------------------------------------------------------------------
@@ -133,7 +133,7 @@ def stream_bytes(d, k_bits, v_bits, G, N, Tq):
 class _LayerStruct(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in
                 ("n_streams", "g", "d", "k_bits", "v_bits", "G", "R", "cap", "is_bf16",
-                 "N", "Tq")] + [(n, ctypes.c_void_p) for n in
+                 "N", "Tq", "k_tok")] + [(n, ctypes.c_void_p) for n in
                                 ("hist_k", "hist_v", "k_words", "k_scale", "k_zero",
                                  "v_words", "v_scale", "v_zero")]
 
@@ -143,9 +143,11 @@ class Layer:
 
     k_bits/v_bits in {2,3(K only),4,8}, or 16/16 for a layer kept in 16 bits.
     Inputs are 16-bit bit patterns (numpy uint16), fp16 or bf16 per ``is_bf16``.
+    ``k_tok``: Key quantized per token (KVTuner's per-token-asym mode) instead
+    of per channel over G tokens (KIVI).
     """
 
-    def __init__(self, n_streams, g, d, k_bits, v_bits, G, R, cap, is_bf16):
+    def __init__(self, n_streams, g, d, k_bits, v_bits, G, R, cap, is_bf16, k_tok=False):
         cap = -(-cap // G) * G
         if k_bits == 16 or v_bits == 16:
             assert k_bits == v_bits == 16
@@ -153,6 +155,8 @@ class Layer:
         self.n_streams, self.g, self.d = n_streams, g, d
         self.k_bits, self.v_bits, self.G, self.R, self.cap = k_bits, v_bits, G, R, cap
         self.is_bf16 = bool(is_bf16)
+        self.k_tok = bool(k_tok) and k_bits != 16
+        assert not (self.k_tok and k_bits == 3), "per-token Key: 2, 4 or 8 bits"
         for b in (k_bits, v_bits):
             assert b == 3 or (d * b) % 32 == 0, "a row must fill whole 32-bit words"
         wk, wv = words_per_row(d, k_bits), words_per_row(d, v_bits)
@@ -160,8 +164,9 @@ class Layer:
         self.hist_k = np.zeros((S, cap, d), np.uint16)
         self.hist_v = np.zeros((S, cap, d), np.uint16)
         self.k_words = np.zeros((S, cap, wk), np.uint32)
-        self.k_scale = np.zeros((S, cap // G, d), np.float32)
-        self.k_zero = np.zeros((S, cap // G, d), np.float32)
+        kshape = (S, cap) if self.k_tok else (S, cap // G, d)
+        self.k_scale = np.zeros(kshape, np.float32)
+        self.k_zero = np.zeros(kshape, np.float32)
         self.v_words = np.zeros((S, cap, wv), np.uint32)
         self.v_scale = np.zeros((S, cap), np.float32)
         self.v_zero = np.zeros((S, cap), np.float32)
@@ -169,6 +174,7 @@ class Layer:
         for f in ("n_streams", "g", "d", "k_bits", "v_bits", "G", "R", "cap"):
             setattr(st, f, getattr(self, f))
         st.is_bf16 = int(self.is_bf16)
+        st.k_tok = int(self.k_tok)
         st.N = 0
         st.Tq = 0
         for f in ("hist_k", "hist_v", "k_words", "k_scale", "k_zero", "v_words", "v_scale",
@@ -208,8 +214,8 @@ class Layer:
         return dict(
             N=N, Tq=Tq,
             k_words=self.k_words[:, :Tq].copy(),
-            k_scale=self.k_scale[:, :Tq // G].copy(),
-            k_zero=self.k_zero[:, :Tq // G].copy(),
+            k_scale=self.k_scale[:, :(Tq if self.k_tok else Tq // G)].copy(),
+            k_zero=self.k_zero[:, :(Tq if self.k_tok else Tq // G)].copy(),
             v_words=self.v_words[:, :Tq].copy(),
             v_scale=self.v_scale[:, :Tq].copy(),
             v_zero=self.v_zero[:, :Tq].copy(),
@@ -219,4 +225,4 @@ class Layer:
 
     def bytes(self):
         return self.n_streams * stream_bytes(self.d, self.k_bits, self.v_bits, self.G, self.N,
-                                             self.Tq)
+                                             self.Tq, self.k_tok)

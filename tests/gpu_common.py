@@ -13,9 +13,11 @@ MAX_ABS = 5e-3
 
 
 def ad_hoc_workload(cid, B, Hq, Hkv, d, kb, vb, G, R, ctx, kv="bf16", q="f32",
-                    k_outliers=(2, 10.0), v_kind="normal"):
+                    k_outliers=(2, 10.0), v_kind="normal", k_mode=0):
+    """k_mode 1: per-token Key (the layer row gets a fourth element)."""
+    lc = (kb, vb, R, k_mode) if k_mode else (kb, vb, R)
     w = synth.Workload(cid, "case%d" % cid, 1, B, Hq, Hkv, d, ctx, kv, q, G, R,
-                       layers=[(kb, vb, R)], k_outliers=k_outliers, v_kind=v_kind)
+                       layers=[lc], k_outliers=k_outliers, v_kind=v_kind)
     return w
 
 
@@ -26,9 +28,11 @@ def make_cache(w, layers=None, max_context=None):
 
 
 def make_oracle(w, layer_cfg, cap, streams=None):
-    kb, vb, R = layer_cfg
+    kb, vb, R = layer_cfg[:3]
+    k_tok = len(layer_cfg) > 3 and layer_cfg[3] == 1
     S = w.batch * w.n_kv_heads if streams is None else len(streams)
-    return ora.Layer(S, w.g, w.head_dim, kb, vb, w.G, R if R else w.R, cap, w.kv_dtype == "bf16")
+    return ora.Layer(S, w.g, w.head_dim, kb, vb, w.G, R if R else w.R, cap, w.kv_dtype == "bf16",
+                     k_tok=k_tok)
 
 
 def stream_view(t, streams=None):

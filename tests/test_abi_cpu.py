@@ -108,3 +108,14 @@ def test_handle_validation_leaves_state_unchanged():
         kvq.kvq_destroy(h)
     kvq.kvq_destroy(None)
     assert kvq.lib().kvq_bytes(None) == -1
+
+
+def test_key_mode_validation():
+    """k_mode must be 0 (per channel) or 1 (per token); per-token Key needs 2, 4
+    or 8 bits; a per-token table is otherwise accepted."""
+    assert kvq.kvq_workspace_bytes(_cfg(layers=[(4, 2, 0, 2), (4, 2, 0)])) == 0
+    assert "k_mode" in kvq.kvq_last_error()
+    assert kvq.kvq_workspace_bytes(_cfg(layers=[(3, 4, 0, 1), (4, 2, 0)])) == 0
+    assert "per-token" in kvq.kvq_last_error()
+    assert kvq.kvq_workspace_bytes(_cfg(layers=[(4, 2, 0, 1), (8, 8, 0, 1)])) > 0
+    assert kvq.kvq_workspace_bytes(_cfg(layers=[(16, 16, 0, 1), (2, 2, 0, 1)])) > 0

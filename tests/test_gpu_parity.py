@@ -68,13 +68,24 @@ CASES = {
     # tokens split over several units
     "mfma_k2v2_many_streams": (8, 40, 40, 128, 2, 2, 32, 256, 640, "f16", "f16", [600, 1]),
     "mfma_k8v4_g2_many_streams": (16, 48, 24, 128, 8, 4, 32, 96, 420, "bf16", "bf16", [400, 1]),
+    # per-token-asym Key (13th element: k_mode 1)
+    "tok_mfma_k4v2_g4": (2, 8, 2, 128, 4, 2, 32, 32, 420, "bf16", "bf16", [350, 1, 30], 1),
+    "tok_mfma_k8v4_mha": (2, 2, 2, 128, 8, 4, 32, 48, 400, "f16", "f16", [330, 5], 1),
+    "tok_mfma_k2v8_g16_d256": (1, 16, 1, 256, 2, 8, 32, 32, 300, "bf16", "f32", [290, 1], 1),
+    "tok_mfma_k2v2_d64_G64": (2, 10, 2, 64, 2, 2, 64, 70, 500, "f16", "f32", [400, 30], 1),
+    "tok_mfma_k8v8_long": (1, 4, 1, 128, 8, 8, 32, 32, 2100, "bf16", "bf16", [2050, 1], 1),
+    "tok_mfma_k4v4_many_streams": (8, 40, 40, 128, 4, 4, 32, 256, 640, "f16", "f16", [600, 1], 1),
+    "tok_valu_k4v4_G16": (2, 8, 2, 128, 4, 4, 16, 20, 300, "bf16", "f32", [250, 1, 7], 1),
+    "tok_valu_k8v2_G8_d64": (1, 4, 1, 64, 8, 2, 8, 9, 120, "f16", "f16", [1] * 40, 1),
 }
 
 
 @pytest.mark.parametrize("name", sorted(CASES))
 def test_small_parity(name):
-    B, Hq, Hkv, d, kb, vb, G, R, ctx, kv, q, chunks = CASES[name]
-    w = ad_hoc_workload(200 + sorted(CASES).index(name), B, Hq, Hkv, d, kb, vb, G, R, ctx, kv, q)
+    B, Hq, Hkv, d, kb, vb, G, R, ctx, kv, q, chunks = CASES[name][:12]
+    k_mode = CASES[name][12] if len(CASES[name]) > 12 else 0
+    w = ad_hoc_workload(200 + sorted(CASES).index(name), B, Hq, Hkv, d, kb, vb, G, R, ctx, kv, q,
+                        k_mode=k_mode)
     print("case", name, flush=True)
     _run_case(w, chunks, decode_checks=set(range(len(chunks))))
 
@@ -201,7 +212,10 @@ def test_unit_sizes_and_column_merge(ug, monkeypatch):
         _run_case(w, [1650, 1])
 
 
-@pytest.mark.parametrize("kind", ["mfma_k4v2", "mfma_k3v4", "valu_k3v4", "plain16", "valu_g16"])
+FUSED_KINDS = ["mfma_k4v2", "mfma_k3v4", "valu_k3v4", "plain16", "valu_g16", "tok_mfma_k4v4", "tok_valu_k2v4"]
+
+
+@pytest.mark.parametrize("kind", FUSED_KINDS)
 def test_append_decode_attention_equals_two_calls(kind):
     """The one-call decode step (append one token, then attend) gives the same
     outputs, bit for bit, and the same state as kvq_append + kvq_decode_attention,
@@ -212,8 +226,10 @@ def test_append_decode_attention_equals_two_calls(kind):
         "valu_k3v4": (2, 2, 2, 128, 3, 4, 16, 50, 200, "f16", "f32"),
         "plain16": (1, 4, 1, 128, 16, 16, 32, 32, 160, "bf16", "bf16"),
         "valu_g16": (1, 8, 2, 64, 8, 4, 16, 24, 160, "f16", "f16"),
+        "tok_mfma_k4v4": (2, 8, 2, 128, 4, 4, 32, 32, 200, "bf16", "bf16"),
+        "tok_valu_k2v4": (1, 4, 1, 128, 2, 4, 16, 20, 200, "f16", "f32"),
     }[kind]
-    w = ad_hoc_workload(500 + sorted(["mfma_k4v2", "mfma_k3v4", "valu_k3v4", "plain16", "valu_g16"]).index(kind), *spec)
+    w = ad_hoc_workload(500 + sorted(FUSED_KINDS).index(kind), *spec, k_mode=1 if kind.startswith("tok") else 0)
     print("fused step", kind, flush=True)
     st = synth.LayerStats(w, 0)
     n0 = 70
@@ -236,11 +252,13 @@ def test_append_decode_attention_equals_two_calls(kind):
     compare_export(one.export(0), orc.export())
 
 
-@pytest.mark.parametrize("d,G,variant", [(128, 32, 1), (64, 32, 0), (128, 16, 0)])
-def test_k3_path_choice(d, G, variant):
+@pytest.mark.parametrize("d,G,kb,k_mode,variant", [(128, 32, 3, 0, 1), (64, 32, 3, 0, 0), (128, 16, 3, 0, 0),
+                                                  (64, 32, 4, 1, 1), (128, 16, 4, 1, 0)])
+def test_path_choice(d, G, kb, k_mode, variant):
     """3-bit K layers run on the matrix core at head_dim 128 with 32-token
-    multiples for G (variant 1), on the vector ALU otherwise (variant 0)."""
-    w = ad_hoc_workload(600 + d + G, 1, 2, 1, d, 3, 4, G, G, 200, "f16", "f32")
+    multiples for G (variant 1), on the vector ALU otherwise (variant 0);
+    per-token Key takes the matrix core whenever G is a multiple of 32."""
+    w = ad_hoc_workload(600 + d + G + kb, 1, 2, 1, d, kb, 4, G, G, 200, "f16", "f32", k_mode=k_mode)
     cache = make_cache(w)
     orc = make_oracle(w, w.layers[0], w.context)
     k, v = synth.layer_tokens(w, 0, 0, 150, DEV)
