@@ -190,6 +190,11 @@ class Cache:
         self.h = kvq_create(self.cfg, ctypes.c_void_p(aligned), nbytes)
         self.device = device
 
+    def set_stream(self, stream):
+        """Enqueue later calls on `stream` (a torch stream), e.g. a capturing one."""
+        kvq_set_stream(self.h, ctypes.c_void_p(stream.cuda_stream))
+        self.stream = stream
+
     def close(self):
         if self.h is not None:
             kvq_destroy(self.h)
