@@ -166,6 +166,10 @@ struct kvq_handle {
     hipStream_t stream = nullptr;
     int cu_count = 0;
     int last_splits = 0, last_variant = -1;
+    // launch-shape overrides for tests and tuning, read once at create from
+    // KVQ_FORCE_VALU, KVQ_UNIT_GROUPS, KVQ_UNITS_Q, KVQ_RES_TOKENS, KVQ_SPLITS
+    // (0 = not set)
+    int env_force_valu = 0, env_unit_groups = 0, env_units_q = 0, env_res_tokens = 0, env_splits = 0;
     bool touched = false;  // device work was enqueued
     bool counters_ready = false;
     std::string err = "no error";
@@ -236,6 +240,16 @@ int kvq_create(const kvq_config *cfg, void *workspace, size_t ws_bytes, kvq_hand
     h->ws = static_cast<char *>(workspace);
     h->ws_bytes = ws_bytes;
     h->stream = static_cast<hipStream_t>(cfg->stream);
+    auto env_int = [](const char *name) {
+        const char *v = getenv(name);
+        const int x = v ? atoi(v) : 0;
+        return x > 0 ? x : 0;
+    };
+    h->env_force_valu = env_int("KVQ_FORCE_VALU");
+    h->env_unit_groups = env_int("KVQ_UNIT_GROUPS");
+    h->env_units_q = env_int("KVQ_UNITS_Q");
+    h->env_res_tokens = env_int("KVQ_RES_TOKENS");
+    h->env_splits = env_int("KVQ_SPLITS");
     const size_t BH = static_cast<size_t>(h->BH());
     for (LayerState &s : h->plan.layers) {
         kvq::LayerDev &d = s.dev;
@@ -428,9 +442,8 @@ static int attention_launch(kvq_handle *h, int layer, const void *q, float *out,
     a.new_t = new_t;
     a.new_k = new_t >= 0 ? static_cast<const uint16_t *>(new_k) : d.ring_k;
     a.new_v = new_t >= 0 ? static_cast<const uint16_t *>(new_v) : d.ring_v;
-    const char *force_valu = getenv("KVQ_FORCE_VALU");
     const bool use_mfma = (d.kb == 16 || (d.v_tiled && kvq::mfma_supported(d.kb, d.vb, D))) &&
-                          !(force_valu && atoi(force_valu) > 0);
+                          h->env_force_valu == 0;
     int S = 0;
     if (use_mfma) {
         // matrix-core units over whole groups, then over the recent tokens
@@ -453,8 +466,8 @@ static int attention_launch(kvq_handle *h, int layer, const void *q, float *out,
         // recent-token units: ceil(Tr / rt) per stream, rt tokens each
         long uq = 0;
         int rt = 0;
-        const char *env_ug = getenv("KVQ_UNIT_GROUPS");
-        if (BH * 2 > res_wgs && !(env_ug && atoi(env_ug) > 0)) {
+        const int env_ug = h->env_unit_groups;
+        if (BH * 2 > res_wgs && env_ug == 0) {
             // Many streams: each stream's work splits into U units (U a
             // multiple of four: whole workgroups), the recent tokens into as
             // many units as their share of the work, chosen to minimise
@@ -495,8 +508,8 @@ static int attention_launch(kvq_handle *h, int layer, const void *q, float *out,
             while (ug < n_groups &&
                    BH * ((n_groups + ug - 1) / ug + (Tr + res_len(ug) - 1) / res_len(ug)) > cap)
                 ug += ng;
-            if (env_ug && atoi(env_ug) > 0)
-                ug = atoi(env_ug);
+            if (env_ug > 0)
+                ug = env_ug;
             if (ug > n_groups)
                 ug = n_groups;
             uq = (n_groups + ug - 1) / ug;
@@ -506,23 +519,21 @@ static int attention_launch(kvq_handle *h, int layer, const void *q, float *out,
             // takes a group off the longest unit
             const long ur = (Tr + rt - 1) / rt;
             const long U4 = (uq + ur + 3) / 4 * 4, uq4 = U4 - ur;
-            if (!(env_ug && atoi(env_ug) > 0) && BH * U4 <= cap && uq4 <= n_groups &&
+            if (env_ug == 0 && BH * U4 <= cap && uq4 <= n_groups &&
                 (n_groups + uq4 - 1) / uq4 < (n_groups + uq - 1) / uq)
                 uq = uq4;
             // few streams: while there are more SIMDs than waves, shorter units
             // (one wave per SIMD, whole workgroups) shorten the critical path
             const long u_simd = (4L * h->cu_count / BH) / 4 * 4;
-            if (!(env_ug && atoi(env_ug) > 0) && u_simd > uq + ur)
+            if (env_ug == 0 && u_simd > uq + ur)
                 uq = std::min<long>(n_groups, u_simd - ur);
         }
         if (rt == 0)
             rt = res_len(uq > 0 ? (n_groups + uq - 1) / uq : 1);
-        if (const char *env = getenv("KVQ_RES_TOKENS"))
-            if (atoi(env) > 0)
-                rt = (atoi(env) + 31) / 32 * 32;
-        if (const char *env = getenv("KVQ_UNITS_Q"))
-            if (atoi(env) > 0)
-                uq = atoi(env);
+        if (h->env_res_tokens > 0)
+            rt = (h->env_res_tokens + 31) / 32 * 32;
+        if (h->env_units_q > 0)
+            uq = h->env_units_q;
         if (uq > n_groups)
             uq = n_groups;
         // the merge takes at most kMaxUnits / 4 workgroups per stream
@@ -548,9 +559,8 @@ static int attention_launch(kvq_handle *h, int layer, const void *q, float *out,
     } else {
         // splits: about two workgroups per compute unit, >= 64 tokens each
         S = (2 * h->cu_count + BH - 1) / BH;
-        const char *env = getenv("KVQ_SPLITS");
-        if (env && atoi(env) > 0)
-            S = atoi(env);
+        if (h->env_splits > 0)
+            S = h->env_splits;
         const int max_by_len = (s.N + 63) / 64;
         if (S > max_by_len)
             S = max_by_len;
