@@ -335,6 +335,70 @@ void kvqo_attention(const kvqo_layer *L, const double *q, double *out)
     free(e);
 }
 
+/* Attention of the last n_q appended tokens' queries over the cache, in fp64:
+ * the prefill form of the same equation.  [KVTuner] A3: the query of step i
+ * attends to the keys and values of steps up to and including i
+ * (K = concat(K_{:i-1}, k_i)); [KVTuner] A2 (calibration): prefill attention
+ * runs on the dequantized cache.  Query j (0 <= j < n_q) sits at position
+ * p = N - n_q + j and attends to tokens 0..p as the cache holds them (codes
+ * dequantized for t < Tq, the 16-bit values for the recent tokens).
+ * q and out: [n_streams][g][n_q][d]. */
+void kvqo_prefill_attention(const kvqo_layer *L, const double *q, int n_q, double *out)
+{
+    const int d = L->d, N = L->N, g = L->g;
+    const int wk = kvqo_words_per_row(d, L->k_bits);
+    const int wv = kvqo_words_per_row(d, L->v_bits);
+    const size_t n1 = (size_t)(N > 0 ? N : 1);
+    double *e = (double *)malloc(sizeof(double) * n1);
+    double *kh = (double *)malloc(sizeof(double) * n1 * d);
+    double *vh = (double *)malloc(sizeof(double) * n1 * d);
+    uint8_t *codes = (uint8_t *)malloc((size_t)d);
+    const double scale = 1.0 / sqrt((double)d);
+    for (int s = 0; s < L->n_streams; ++s) {
+        for (int t = 0; t < N; ++t) {
+            if (t < L->Tq)
+                kvqo_unpack_row(L->k_words + ((size_t)s * L->cap + t) * wk, d, L->k_bits, codes);
+            for (int c = 0; c < d; ++c)
+                kh[(size_t)t * d + c] = key_hat(L, s, t, c, codes);
+            if (t < L->Tq)
+                kvqo_unpack_row(L->v_words + ((size_t)s * L->cap + t) * wv, d, L->v_bits, codes);
+            for (int c = 0; c < d; ++c)
+                vh[(size_t)t * d + c] = value_hat(L, s, t, c, codes);
+        }
+        for (int h = 0; h < g; ++h) {
+            for (int j = 0; j < n_q; ++j) {
+                const int p = N - n_q + j; /* this query's position: keys 0..p */
+                const double *qv = q + (((size_t)s * g + h) * n_q + j) * d;
+                double *o = out + (((size_t)s * g + h) * n_q + j) * d;
+                double m = -INFINITY;
+                for (int t = 0; t <= p; ++t) {
+                    double acc = 0.0;
+                    for (int c = 0; c < d; ++c)
+                        acc += qv[c] * kh[(size_t)t * d + c];
+                    e[t] = acc * scale;
+                    if (e[t] > m)
+                        m = e[t];
+                }
+                double l = 0.0;
+                for (int t = 0; t <= p; ++t) {
+                    e[t] = exp(e[t] - m);
+                    l += e[t];
+                }
+                for (int c = 0; c < d; ++c) {
+                    double acc = 0.0;
+                    for (int t = 0; t <= p; ++t)
+                        acc += e[t] * vh[(size_t)t * d + c];
+                    o[c] = acc / l;
+                }
+            }
+        }
+    }
+    free(codes);
+    free(vh);
+    free(kh);
+    free(e);
+}
+
 /* Live bytes of one stream with N tokens of which Tq are quantized.
  * Codes: Tq rows of K words and V words (4 bytes each).  K metadata: one fp32
  * scale and zero per channel per group.  V metadata: one fp32 scale and zero

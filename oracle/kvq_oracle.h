@@ -43,6 +43,9 @@ void kvqo_quantize(const float *x, int n, long stride, int qmax,
 int kvqo_append(kvqo_layer *L, const uint16_t *k_new, const uint16_t *v_new, int n);
 /* q, out: double [n_streams][g][d]. */
 void kvqo_attention(const kvqo_layer *L, const double *q, double *out);
+/* Causal attention of the queries of the last n_q appended tokens (1 <= n_q <= N):
+ * q, out: double [n_streams][g][n_q][d]; query j attends to tokens 0..N-n_q+j. */
+void kvqo_prefill_attention(const kvqo_layer *L, const double *q, int n_q, double *out);
 long long kvqo_stream_bytes(int d, int k_bits, int v_bits, int G, long long N, long long Tq, int k_tok);
 
 #endif

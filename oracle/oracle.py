@@ -7,8 +7,10 @@ What it computes, with the pages it follows, is documented in ``kvq_oracle.c``:
 asymmetric uniform quantization (KVTuner summary, A3 "KV cache quantization
 basics"; KVmix notes, key design 2), K per channel over a token group and V per
 token with a 16-bit recent-token buffer (KIVI notes, sections 6.1-6.2), int32
-packing including the 11-per-word 3-bit layout (KVmix notes, key design 2), and
-fp64 decode attention (KVTuner summary, A3 attention equation).
+packing including the 11-per-word 3-bit layout (KVmix notes, key design 2),
+fp64 decode attention (KVTuner summary, A3 attention equation), and fp64 causal
+attention of a prefill chunk over the dequantized cache (the same equation;
+KVTuner summary, A2 calibration on dequantized KV).
 """
 import ctypes
 import os
@@ -67,6 +69,8 @@ def _bind(L):
     L.kvqo_append.argtypes = [P, P, P, ctypes.c_int]
     L.kvqo_attention.restype = None
     L.kvqo_attention.argtypes = [P, P, P]
+    L.kvqo_prefill_attention.restype = None
+    L.kvqo_prefill_attention.argtypes = [P, P, ctypes.c_int, P]
     L.kvqo_stream_bytes.restype = ctypes.c_longlong
     L.kvqo_stream_bytes.argtypes = [ctypes.c_int] * 4 + [ctypes.c_longlong] * 2 + [ctypes.c_int]
     _lib = L
@@ -206,6 +210,17 @@ class Layer:
         assert q.shape == (self.n_streams, self.g, self.d)
         out = np.zeros_like(q)
         lib().kvqo_attention(ctypes.byref(self._st), _ptr(q), _ptr(out))
+        return out
+
+    def prefill_attention(self, q):
+        """Causal attention of the last n_q tokens' queries (chunked prefill):
+        q float64 [n_streams, g, n_q, d]; query j attends to tokens
+        0 .. N - n_q + j.  Returns float64 [n_streams, g, n_q, d]."""
+        q = np.ascontiguousarray(q, dtype=np.float64)
+        S, g, n_q, d = q.shape
+        assert (S, g, d) == (self.n_streams, self.g, self.d) and 1 <= n_q <= self.N
+        out = np.zeros_like(q)
+        lib().kvqo_prefill_attention(ctypes.byref(self._st), _ptr(q), n_q, _ptr(out))
         return out
 
     def export(self):

@@ -22,6 +22,10 @@ MUTANTS = {
     "v_zero_from_scale": ("(double)L->v_zero[tt];", "(double)L->v_scale[tt];"),
     "reversed_offset": ("float t = (x[(long)i * stride] - mn) / s;",
                         "float t = (mx - x[(long)i * stride]) / s;"),
+    "prefill_causal_off_by_one": ("const int p = N - n_q + j;", "const int p = N - n_q + j - 1;"),
+    "prefill_no_causal_mask": ("const int p = N - n_q + j;", "const int p = N - 1;"),
+    "prefill_query_of_wrong_head": ("const double *qv = q + (((size_t)s * g + h) * n_q + j) * d;",
+                                    "const double *qv = q + (((size_t)s * g) * n_q + j) * d;"),
     "pack_msb_first": ("*shift = bits * (c % per_word);",
                        "*shift = 32 - bits * (1 + c % per_word);"),
 }

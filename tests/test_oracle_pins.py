@@ -413,3 +413,91 @@ def test_attention_softmax_shift_invariance():
     q = rng.standard_normal((S, 2, d))
     np.testing.assert_allclose(a.attention(q), b.attention(q), rtol=1e-12, atol=1e-12)
     assert np.array_equal(a.export()["k_words"], b.export()["k_words"])
+
+
+# ---------------------------------------------------------------------------
+# Chunked-prefill attention (KVTuner summary, A3 attention equation: the query
+# of step i attends to the keys up to and including step i; A2 calibration:
+# prefill attention runs on the dequantized cache)
+# ---------------------------------------------------------------------------
+
+def _sdpa64_causal(q, K, V):
+    """q [S,g,n_q,d], K/V [S,N,d] (fp64); query j attends to tokens
+    0 .. N - n_q + j.  torch's fp64 SDPA with an explicit boolean mask."""
+    S, g, n_q, d = q.shape
+    N = K.shape[1]
+    mask = torch.arange(N)[None, :] <= (N - n_q + torch.arange(n_q))[:, None]  # [n_q, N]
+    kt = torch.from_numpy(K)[:, None].expand(-1, g, -1, -1).contiguous()
+    vt = torch.from_numpy(V)[:, None].expand(-1, g, -1, -1).contiguous()
+    o = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(q), kt, vt, attn_mask=mask)
+    return o.numpy()
+
+
+@pytest.mark.parametrize("g,d,N,n_q,bf16", [(1, 16, 1, 1, False), (4, 32, 37, 37, True),
+                                           (2, 64, 50, 9, False), (7, 32, 70, 1, True)])
+def test_prefill_unquantized_matches_causal_sdpa(g, d, N, n_q, bf16):
+    rng = np.random.default_rng(g * 1000 + N + n_q)
+    S = 2
+    k = _rand_tokens(rng, S, N, d, bf16)
+    v = _rand_tokens(rng, S, N, d, bf16)
+    lay = ora.Layer(S, g, d, 16, 16, 8, 8, N, bf16)
+    lay.append(k, v)
+    q = rng.standard_normal((S, g, n_q, d))
+    ref = _sdpa64_causal(q, _widen(k, bf16), _widen(v, bf16))
+    np.testing.assert_allclose(lay.prefill_attention(q), ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("kb,vb,G,R,N,n_q,g,bf16", [
+    (4, 2, 8, 8, 40, 40, 2, False),   # whole sequence: the mask cuts through every group
+    (2, 4, 4, 6, 33, 20, 1, True),    # chunk longer than the recent buffer
+    (8, 8, 16, 16, 64, 5, 4, False),  # chunk inside the recent buffer
+    (3, 4, 8, 8, 45, 17, 3, False),
+])
+def test_prefill_on_grid_matches_causal_sdpa(kb, vb, G, R, N, n_q, g, bf16):
+    """Lossless quantization: causal attention over the quantized cache equals
+    fp64 causal attention over the raw tokens, whichever tokens the chunk's
+    queries see in codes and which in 16 bits."""
+    rng = np.random.default_rng(kb * 77 + N + n_q)
+    S, d = 2, 32 if kb != 3 else 64
+    kbits, vbits, K, V = grid_tokens(rng, S, N, d, G, kb, vb, bf16)
+    lay = ora.Layer(S, g, d, kb, vb, G, R, N, bf16)
+    lay.append(kbits[:, :N - n_q], vbits[:, :N - n_q])
+    lay.append(kbits[:, N - n_q:], vbits[:, N - n_q:])
+    assert lay.Tq == _expected_tq(N, R, G) and lay.Tq > 0
+    q = rng.standard_normal((S, g, n_q, d))
+    np.testing.assert_allclose(lay.prefill_attention(q), _sdpa64_causal(q, K, V), rtol=1e-11, atol=1e-12)
+
+
+def _np_unpack(words, d, bits):
+    """LSB-first codes of 2/4/8-bit rows, written independently of the oracle."""
+    per = 32 // bits
+    c = np.arange(d)
+    return (words[..., c // per] >> np.uint32(bits) * (c % per).astype(np.uint32)) & np.uint32((1 << bits) - 1)
+
+
+def test_prefill_first_query_and_zero_query_closed_forms():
+    """Off-grid data.  With n_q = N the first query sees token 0 alone, so its
+    output is that token's dequantized value; a zero query weighs its visible
+    tokens equally, so query j's output is the mean of the dequantized values
+    of tokens 0 .. N - n_q + j (values rebuilt here from the canonical export)."""
+    rng = np.random.default_rng(21)
+    S, g, d, G, R, N = 2, 2, 32, 8, 12, 41
+    k = _rand_tokens(rng, S, N, d, False)
+    v = _rand_tokens(rng, S, N, d, False)
+    lay = ora.Layer(S, g, d, 4, 2, G, R, N, False)
+    lay.append(k, v)
+    ex = lay.export()
+    Tq = ex["Tq"]
+    vcodes = _np_unpack(ex["v_words"], d, 2).astype(np.float64)
+    vhat = np.concatenate([vcodes * ex["v_scale"][..., None].astype(np.float64)
+                           + ex["v_zero"][..., None].astype(np.float64),
+                           _widen(ex["res_v"], False)], axis=1)  # [S, N, d]
+    assert Tq > 0 and vhat.shape == (S, N, d)
+    out = lay.prefill_attention(rng.standard_normal((S, g, N, d)))
+    np.testing.assert_allclose(out[:, :, 0], np.repeat(vhat[:, None, 0], g, axis=1), rtol=0, atol=1e-12)
+    n_q = 30
+    out0 = lay.prefill_attention(np.zeros((S, g, n_q, d)))
+    for j in range(n_q):
+        p = N - n_q + j
+        np.testing.assert_allclose(out0[:, :, j], np.repeat(vhat[:, None, :p + 1].mean(axis=2), g, axis=1),
+                                   rtol=1e-12, atol=1e-12)
