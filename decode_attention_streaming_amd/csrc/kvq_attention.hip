@@ -9,6 +9,9 @@ namespace kvq {
 hipError_t launch_mfma_d64(const AttnArgs &a, hipStream_t st);
 hipError_t launch_mfma_d128(const AttnArgs &a, hipStream_t st);
 hipError_t launch_mfma_d256(const AttnArgs &a, hipStream_t st);
+hipError_t launch_prefill_d64(const PrefillArgs &a, hipStream_t st);
+hipError_t launch_prefill_d128(const PrefillArgs &a, hipStream_t st);
+hipError_t launch_prefill_d256(const PrefillArgs &a, hipStream_t st);
 
 namespace {
 
@@ -46,6 +49,25 @@ bool mfma_supported(int kb, int vb, int D)
     if (kb == 3)  // twelve words per row, three per lane quad
         return vbits && D == 128;
     return vbits && (kb == 2 || kb == 4 || kb == 8) && (D == 64 || D == 128 || D == 256);
+}
+
+bool prefill_supported(int kb, int vb, int D, int v_tiled)
+{
+    if (D != 64 && D != 128 && D != 256)
+        return false;
+    if (kb == 16)
+        return vb == 16;
+    const bool ok = (kb == 2 || kb == 4 || kb == 8) && (vb == 2 || vb == 4 || vb == 8);
+    return ok && v_tiled;  // V codes in the matrix-core tile layout (G a multiple of 32)
+}
+
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st)
+{
+    if (a.D == 64)
+        return launch_prefill_d64(a, st);
+    if (a.D == 128)
+        return launch_prefill_d128(a, st);
+    return launch_prefill_d256(a, st);
 }
 
 // a 16-bit layer runs only recent-token units: any instantiation serves

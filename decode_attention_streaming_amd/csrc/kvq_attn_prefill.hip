@@ -1,0 +1,495 @@
+// kvq_attn_prefill.hip -- matrix-core causal attention of a prefill chunk over
+// the quantized cache, for one head_dim (KVQ_D, set by the build).
+//
+// The queries of the last n_q appended tokens attend to the cache as it is
+// stored: query j, at position p = N - n_q + j, sees tokens 0..p (KVTuner
+// summary, A3 attention equation: the query of step i attends to the keys of
+// steps up to i), quantized tokens dequantized on the fly and recent tokens in
+// 16 bits (KVTuner summary, A2: calibration runs prefill attention on the
+// dequantized cache).
+//
+// One wave computes a tile of 16 / g queries of one (sequence, kv-head)
+// stream: the 16 columns of each 16x16x32 product are (query, head) pairs,
+// column jq * g + h carrying query head h of query jq.  Unlike decode, every
+// column uses the same K group, so the products are dense: the B operand of
+// q.K is (q_col * s_c) for the group's per-channel scales s (KVmix notes, key
+// design 4: scale folded into the product, codes as exact fp16 integers), the
+// z term sum_c q_c z_c stays in fp32, and P.V takes the weights p_t s_t of
+// every column against the V code fragments (z term sum_t p_t z_t in fp32).
+// Causality is a per-column mask on the scores.  The wave walks the stream's
+// tokens once, quantized blocks first, then the recent 16-bit tokens, with one
+// online softmax per column; no split and no merge.
+#include "kvq_mfma_ops.h"
+
+#ifndef KVQ_D
+#error "KVQ_D (head_dim) must be defined"
+#endif
+
+#define KVQ_CAT2(x, y) x##y
+#define KVQ_CAT(x, y) KVQ_CAT2(x, y)
+
+namespace kvq {
+namespace {
+
+// q of this lane's column, channels c0 .. c0 + QC - 1 (16-byte aligned runs),
+// widened to fp32
+template <int QC>
+__device__ __forceinline__ void load_q_slice(const void *q, int dtype, size_t i0, float (&r)[QC])
+{
+    if (dtype == 0) {
+        float4 v[QC / 4];
+#pragma unroll
+        for (int i = 0; i < QC / 4; ++i)
+            v[i] = reinterpret_cast<const float4 *>(static_cast<const float *>(q) + i0)[i];
+#pragma unroll
+        for (int i = 0; i < QC / 4; ++i) {
+            r[4 * i] = v[i].x;
+            r[4 * i + 1] = v[i].y;
+            r[4 * i + 2] = v[i].z;
+            r[4 * i + 3] = v[i].w;
+        }
+    } else {
+        const int bf = dtype == 2;
+        uint4 v[QC / 8];
+#pragma unroll
+        for (int i = 0; i < QC / 8; ++i)
+            v[i] = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(q) + i0)[i];
+#pragma unroll
+        for (int i = 0; i < QC / 8; ++i) {
+            const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                r[8 * i + 2 * k] = widen16(static_cast<uint16_t>(w[k] & 0xFFFFu), bf);
+                r[8 * i + 2 * k + 1] = widen16(static_cast<uint16_t>(w[k] >> 16), bf);
+            }
+        }
+    }
+}
+
+// Per-wave state of one tile: the column's online softmax (log2 domain) and
+// its output accumulators.
+template <int MT>
+struct ColState {
+    float m_run = -INFINITY, l_run = 0.0f;
+    f4_t O[MT];
+};
+
+// Recent 16-bit tokens [t_beg, t_end) of stream bh for the tile's columns
+// (fp16 or bfloat16 operands, as in decode); V rows staged transposed in the
+// wave's LDS tile vt ([D][32]).  O is in units of 2^kWShift on entry and exit.
+template <int D, bool BF>
+__device__ __forceinline__ void prefill_recent(const PrefillArgs &a, int bh, size_t qrow, bool act, int p_col,
+                                               int t_beg, int t_end, int lane, uint16_t *vt,
+                                               ColState<D / 16> &st)
+{
+    constexpr int NC = D / 32;
+    constexpr int MT = D / 16;
+    const LayerDev &L = a.L;
+    const int col = lane & 15, q = lane >> 4;
+    const uint16_t *rk = L.ring_k + static_cast<size_t>(bh) * L.R * D;
+    const uint16_t *rv = L.ring_v + static_cast<size_t>(bh) * L.R * D;
+
+    // B operand of q.K: this column's q, chunk k, quad q -> channels 32k + 8q + i
+    Frag b1[NC], b2[NC], b3[NC];
+    int sh;
+    {
+        float qv[NC][8];
+        float amax = 0.0f;
+        load_q_runs<NC>(a.q, a.q_dtype, qrow + 8 * q, 32, qv);
+#pragma unroll
+        for (int k = 0; k < NC; ++k)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                qv[k][i] = act ? qv[k][i] * a.scale_log2 : 0.0f;
+                amax = fmaxf(amax, fabsf(qv[k][i]));
+            }
+        amax = col_max(amax);
+        const int qexp = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) : 0;
+        sh = BF ? 0 : 14 - qexp;
+#pragma unroll
+        for (int k = 0; k < NC; ++k)
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const float x0 = ldexpf(qv[k][2 * p], sh), x1 = ldexpf(qv[k][2 * p + 1], sh);
+                if constexpr (BF)
+                    split3_bf16(x0, x1, b1[k].u[p], b2[k].u[p], b3[k].u[p]);
+                else
+                    split_pair(x0, x1, b1[k].u[p], b2[k].u[p]);
+            }
+    }
+    const float kscale = ldexpf(1.0f, -sh);
+
+    for (int t0 = t_beg; t0 < t_end; t0 += 32) {
+        const int ta = min(t0 + col, t_end - 1), tb = min(t0 + 16 + col, t_end - 1);
+        uint4 ka[NC], kb2[NC];
+        const uint16_t *ra = rk + static_cast<size_t>(ta % L.R) * D;
+        const uint16_t *rb = rk + static_cast<size_t>(tb % L.R) * D;
+#pragma unroll
+        for (int k = 0; k < NC; ++k) {
+            ka[k] = *reinterpret_cast<const uint4 *>(ra + 32 * k + 8 * q);
+            kb2[k] = *reinterpret_cast<const uint4 *>(rb + 32 * k + 8 * q);
+        }
+        // V rows -> LDS [channel][token]: lane handles token (lane & 31), half a row
+        {
+            const int tt = lane & 31, half = lane >> 5;
+            const int tv = min(t0 + tt, t_end - 1);
+            const uint4 *src = reinterpret_cast<const uint4 *>(rv + static_cast<size_t>(tv % L.R) * D + half * (D / 2));
+            uint4 v[D / 16];
+#pragma unroll
+            for (int i = 0; i < D / 16; ++i)
+                v[i] = src[i];
+#pragma unroll
+            for (int i = 0; i < D / 16; ++i) {
+                const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int c = half * (D / 2) + 8 * i + e;
+                    vt[c * 32 + tt] = static_cast<uint16_t>((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu));
+                }
+            }
+        }
+        f4_t acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int k = 0; k < NC; ++k) {
+            Frag a0, a1;
+            a0.u[0] = ka[k].x; a0.u[1] = ka[k].y; a0.u[2] = ka[k].z; a0.u[3] = ka[k].w;
+            a1.u[0] = kb2[k].x; a1.u[1] = kb2[k].y; a1.u[2] = kb2[k].z; a1.u[3] = kb2[k].w;
+            if constexpr (BF) {
+                acc0 = mfma_bf16(a0, b1[k], acc0);
+                acc0 = mfma_bf16(a0, b2[k], acc0);
+                acc0 = mfma_bf16(a0, b3[k], acc0);
+                acc1 = mfma_bf16(a1, b1[k], acc1);
+                acc1 = mfma_bf16(a1, b2[k], acc1);
+                acc1 = mfma_bf16(a1, b3[k], acc1);
+            } else {
+                acc0 = mfma(a0, b1[k], acc0);
+                acc0 = mfma(a0, b2[k], acc0);
+                acc1 = mfma(a1, b1[k], acc1);
+                acc1 = mfma(a1, b2[k], acc1);
+            }
+        }
+        // scores of tokens 4q + j and 16 + 4q + j; causal mask t <= p_col
+        float sc[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int t1 = t0 + 4 * q + j, t2 = t0 + 16 + 4 * q + j;
+            sc[j] = (t1 < t_end && t1 <= p_col) ? acc0[j] * kscale : -INFINITY;
+            sc[4 + j] = (t2 < t_end && t2 <= p_col) ? acc1[j] * kscale : -INFINITY;
+        }
+        float tmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                           fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+        tmax = col_max(tmax);
+        const bool need = act && (tmax > st.m_run + kTau);
+        if (__builtin_amdgcn_ballot_w64(need) != 0) {
+            const float m_new = need ? tmax : st.m_run;
+            const float alpha = (m_new == st.m_run) ? 1.0f : exp2f(st.m_run - m_new);
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                st.O[m] *= alpha;
+            st.l_run *= alpha;
+            st.m_run = m_new;
+        }
+        const float mo = act ? st.m_run : INFINITY;
+        float p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            p[j] = exp2f(sc[j] - mo);
+            st.l_run += p[j];
+        }
+        Frag w1, w2, w3;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float x0 = ldexpf(p[2 * r], kWShift), x1 = ldexpf(p[2 * r + 1], kWShift);
+            if constexpr (BF)
+                split3_bf16(x0, x1, w1.u[r], w2.u[r], w3.u[r]);
+            else
+                split_pair(x0, x1, w1.u[r], w2.u[r]);
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const uint16_t *row = vt + (16 * m + col) * 32;
+            const uint2 lo = *reinterpret_cast<const uint2 *>(row + 4 * q);
+            const uint2 hi = *reinterpret_cast<const uint2 *>(row + 16 + 4 * q);
+            Frag av;
+            av.u[0] = lo.x; av.u[1] = lo.y; av.u[2] = hi.x; av.u[3] = hi.y;
+            if constexpr (BF) {
+                st.O[m] = mfma_bf16(av, w1, st.O[m]);
+                st.O[m] = mfma_bf16(av, w2, st.O[m]);
+                st.O[m] = mfma_bf16(av, w3, st.O[m]);
+            } else {
+                st.O[m] = mfma(av, w1, st.O[m]);
+                st.O[m] = mfma(av, w2, st.O[m]);
+            }
+        }
+        asm volatile("" ::: "memory");  // this block's V tile reads stay before the next block's writes
+    }
+}
+
+// One tile: queries tile * QT .. tile * QT + QT - 1 of stream bh.
+template <int KB, int VB, int D, bool KT>
+__device__ void prefill_tile(const PrefillArgs &a, int bh, int tile, int lane, uint16_t *vt)
+{
+    constexpr int QC = D / 4;         // channels owned by one lane quad
+    constexpr int KW = D * KB / 128;  // K words per lane per token
+    constexpr int PK = 16 / KB;       // K code pairs per word
+    constexpr int CW = 32 / KB;       // K channels per word
+    constexpr int NC = D / 32;        // 32-position chunks of q.K
+    constexpr int FW = D * VB / 64;   // V words per lane per 32-token block
+    constexpr int MT = D / 16;        // 16-channel tiles of P.V
+
+    const LayerDev &L = a.L;
+    const int g = a.g, G = L.G;
+    const int col = lane & 15, q = lane >> 4;
+    const int jq = col / g, h = col - jq * g;
+    const int qi = tile * a.QT + jq;
+    const bool act = jq < a.QT && qi < a.n_q;
+    const int p_col = act ? a.N - a.n_q + qi : -1;  // last token this column sees
+    const size_t qrow = (static_cast<size_t>(bh * g + (act ? h : 0)) * a.n_q + (act ? qi : 0)) * D;
+    // tokens [0, t_end) cover every column of the tile (uniform)
+    const int qi_last = min(a.n_q - 1, tile * a.QT + a.QT - 1);
+    const int t_end = a.N - a.n_q + qi_last + 1;
+    const int tq_end = min(a.Tq, (t_end + 31) & ~31);  // quantized blocks to visit
+
+    ColState<MT> st;
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+        st.O[m] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    if (tq_end > 0) {
+        const uint32_t *kw_base = L.k_words + static_cast<size_t>(bh) * L.capq * L.wk + q * KW;
+        const uint32_t *vw_base = L.v_words + static_cast<size_t>(bh) * L.capq * L.wv + lane * FW;
+        const float *vm_base = L.v_meta + static_cast<size_t>(bh) * L.capq * 2;
+        const float *km_tok = L.k_meta + static_cast<size_t>(bh) * L.capq * 2;
+        float zb_run = 0.0f;
+        int E = -1000;  // running V-scale exponent: the weights carry 2^(kWShift - E)
+        Frag bhi[NC], blo[NC];
+        float bias = 0.0f, kscale = 0.0f;
+
+        // B operand of q.K for group gi (per-token Key: q alone, built once):
+        // q * s as hi/lo fp16 in the code-register order of the quad's words
+        auto build_b = [&](int gi) {
+            float qv[QC];
+            load_q_slice<QC>(a.q, a.q_dtype, qrow + q * QC, qv);
+            const float qscale = act ? a.scale_log2 : 0.0f;
+            const float *sp = L.k_meta + (static_cast<size_t>(bh) * a.ngcap + gi) * 2 * D + q * QC;
+            const float *zp = sp + D;
+            float qs[QC];
+            float amax = 0.0f;
+            bias = 0.0f;
+#pragma unroll
+            for (int i = 0; i < QC; i += 4) {
+                const float4 one = {1.0f, 1.0f, 1.0f, 1.0f};
+                const float4 s4 = KT ? one : *reinterpret_cast<const float4 *>(sp + i);
+                const float4 z4 = KT ? one : *reinterpret_cast<const float4 *>(zp + i);
+                const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+                const float zv[4] = {z4.x, z4.y, z4.z, z4.w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const float qq = qv[i + k] * qscale;
+                    qs[i + k] = qq * sv[k];
+                    bias = __builtin_fmaf(qq, zv[k], bias);
+                    amax = fmaxf(amax, fabsf(qs[i + k]));
+                }
+            }
+            bias = col_sum(bias);
+            amax = col_max(amax);
+            const int sexp = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) : 0;
+            const int sh = 14 - sexp;  // |q s| * 2^sh < 2^14
+#pragma unroll
+            for (int k = 0; k < NC; ++k)
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const int R = 4 * k + p;
+                    const int clo = (R / PK) * CW + (R % PK), chi = clo + PK;
+                    const int e = sh - class_exp<KB>(R);
+                    split_pair(ldexpf(qs[clo], e), ldexpf(qs[chi], e), bhi[k].u[p], blo[k].u[p]);
+                }
+            kscale = ldexpf(1.0f, -sh);
+        };
+        if constexpr (KT)
+            build_b(0);
+
+        for (int t0 = 0; t0 < tq_end; t0 += 32) {
+            if constexpr (!KT) {
+                if (t0 % G == 0)  // G is a multiple of 32: a group starts on a block
+                    build_b(t0 / G);
+            }
+            uint32_t k0[KW], k1[KW], vw[FW];
+            load_words(kw_base + static_cast<size_t>(t0 + col) * L.wk, k0);
+            load_words(kw_base + static_cast<size_t>(t0 + 16 + col) * L.wk, k1);
+            load_words(vw_base + static_cast<size_t>(t0) * L.wv, vw);
+            const float4 *m0 = reinterpret_cast<const float4 *>(vm_base + static_cast<size_t>(t0 + 4 * q) * 2);
+            const float4 *m1 = reinterpret_cast<const float4 *>(vm_base + static_cast<size_t>(t0 + 16 + 4 * q) * 2);
+            const float4 vm[4] = {m0[0], m0[1], m1[0], m1[1]};
+            float4 km[4];
+            if constexpr (KT) {
+                const float4 *c0 = reinterpret_cast<const float4 *>(km_tok + static_cast<size_t>(t0 + 4 * q) * 2);
+                const float4 *c1 = reinterpret_cast<const float4 *>(km_tok + static_cast<size_t>(t0 + 16 + 4 * q) * 2);
+                km[0] = c0[0];
+                km[1] = c0[1];
+                km[2] = c1[0];
+                km[3] = c1[1];
+            }
+            // q.K for tokens 4q + j (acc0) and 16 + 4q + j (acc1)
+            uint32_t k08[KW], k18[KW];
+            shift8(k0, k08);
+            shift8(k1, k18);
+            f4_t acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int k = 0; k < NC; ++k) {
+                Frag a0, a1;
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    a0.u[p] = code_reg<KB>(k0, k08, 4 * k + p);
+                    a1.u[p] = code_reg<KB>(k1, k18, 4 * k + p);
+                }
+                acc0 = mfma(a0, bhi[k], acc0);
+                acc0 = mfma(a0, blo[k], acc0);
+                acc1 = mfma(a1, bhi[k], acc1);
+                acc1 = mfma(a1, blo[k], acc1);
+            }
+            float sc[8];
+            if constexpr (KT) {
+                // score_t = s_t sum_c q_c code_tc + z_t sum_c q_c
+                const float ks[8] = {km[0].x, km[0].z, km[1].x, km[1].z, km[2].x, km[2].z, km[3].x, km[3].z};
+                const float kz[8] = {km[0].y, km[0].w, km[1].y, km[1].w, km[2].y, km[2].w, km[3].y, km[3].w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    sc[j] = __builtin_fmaf(acc0[j] * kscale, ks[j], kz[j] * bias);
+                    sc[4 + j] = __builtin_fmaf(acc1[j] * kscale, ks[4 + j], kz[4 + j] * bias);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    sc[j] = __builtin_fmaf(acc0[j], kscale, bias);
+                    sc[4 + j] = __builtin_fmaf(acc1[j], kscale, bias);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {  // causal mask
+                sc[j] = (t0 + 4 * q + j <= p_col) ? sc[j] : -INFINITY;
+                sc[4 + j] = (t0 + 16 + 4 * q + j <= p_col) ? sc[4 + j] : -INFINITY;
+            }
+            const float vs[8] = {vm[0].x, vm[0].z, vm[1].x, vm[1].z, vm[2].x, vm[2].z, vm[3].x, vm[3].z};
+            const float vz[8] = {vm[0].y, vm[0].w, vm[1].y, vm[1].w, vm[2].y, vm[2].w, vm[3].y, vm[3].w};
+            float tmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                               fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+            tmax = col_max(tmax);
+            float vmax = fmaxf(fmaxf(fmaxf(vs[0], vs[1]), fmaxf(vs[2], vs[3])),
+                               fmaxf(fmaxf(vs[4], vs[5]), fmaxf(vs[6], vs[7])));
+            vmax = col_max(vmax);
+            const int eb = vmax > 0.0f ? __builtin_amdgcn_frexp_expf(vmax) : -1000;
+            const bool need_m = act && (tmax > st.m_run + kTau);
+            const bool need_e = act && (eb > E);
+            if (__builtin_amdgcn_ballot_w64(need_m || need_e) != 0) {
+                const float m_new = need_m ? tmax : st.m_run;
+                const int E_new = need_e ? eb : E;
+                const float alpha = (m_new == st.m_run) ? 1.0f : exp2f(st.m_run - m_new);
+                const float f = ldexpf(alpha, E - E_new);
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+                    st.O[m] *= f;
+                st.l_run *= alpha;
+                zb_run *= alpha;
+                st.m_run = m_new;
+                E = E_new;
+            }
+            const float mo = act ? st.m_run : INFINITY;
+            float p[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                p[j] = exp2f(sc[j] - mo);
+                st.l_run += p[j];
+                zb_run = __builtin_fmaf(p[j], vz[j], zb_run);
+            }
+            // B operand of P.V: weights p s 2^(kWShift - E), k-slot pairs, each
+            // divided by its code class factor
+            Frag whi, wlo;
+            const int wsh = kWShift - E;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int e = wsh - class_exp<VB>(r);
+                split_pair(ldexpf(p[2 * r] * vs[2 * r], e), ldexpf(p[2 * r + 1] * vs[2 * r + 1], e), whi.u[r],
+                           wlo.u[r]);
+            }
+            uint32_t v8[FW];
+            shift8(vw, v8);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                Frag av;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    av.u[r] = code_reg<VB>(vw, v8, 4 * m + r);
+                st.O[m] = mfma(av, whi, st.O[m]);
+                st.O[m] = mfma(av, wlo, st.O[m]);
+            }
+        }
+        // into the recent-token units (2^kWShift): o = O 2^(E - kWShift) + sum_t p_t z_t
+        const float ZB = ldexpf(col_sum(zb_run), kWShift);
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                st.O[m][j] = ldexpf(st.O[m][j], E) + ZB;
+    }
+
+    if (a.Tq < t_end) {
+        if (a.kv_bf16)
+            prefill_recent<D, true>(a, bh, qrow, act, p_col, a.Tq, t_end, lane, vt, st);
+        else
+            prefill_recent<D, false>(a, bh, qrow, act, p_col, a.Tq, t_end, lane, vt, st);
+    }
+
+    const float Lc = col_sum(st.l_run);
+    if (act) {
+        const float inv = ldexpf(1.0f / Lc, -kWShift);
+        float *o = a.out + qrow + 4 * q;
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+            *reinterpret_cast<f4_t *>(o + 16 * m) = st.O[m] * inv;
+    }
+}
+
+template <int KB, int VB, int D, bool KT>
+__global__ __launch_bounds__(256, 2) void attn_prefill_kernel(PrefillArgs a)
+{
+    extern __shared__ uint16_t vt_all[];  // one [D][32] 16-bit tile per wave
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    // Workgroups are dealt to the eight XCDs in turn; number them so that
+    // consecutive slots (tiles of one stream, which read the same cache rows)
+    // land on the same XCD and share its L2.
+    const int id = blockIdx.x;
+    const int slot = (a.n_wg % 8 == 0) ? (id % 8) * (a.n_wg / 8) + id / 8 : id;
+    const int unit = slot * 4 + wave;
+    if (unit >= a.BH * a.n_tiles)
+        return;  // no workgroup barrier follows: a wave may leave alone
+    const int bh = unit / a.n_tiles, tile = unit - bh * a.n_tiles;
+    prefill_tile<KB, VB, D, KT>(a, bh, tile, lane, vt_all + wave * D * 32);
+}
+
+template <int KB, int VB, bool KT>
+hipError_t launch_prefill_pair(const PrefillArgs &a, hipStream_t st)
+{
+    const size_t lds = 4 * KVQ_D * 32 * sizeof(uint16_t);
+    hipLaunchKernelGGL((attn_prefill_kernel<KB, VB, KVQ_D, KT>), dim3(a.n_wg), dim3(256), lds, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t KVQ_CAT(launch_prefill_d, KVQ_D)(const PrefillArgs &a, hipStream_t st)
+{
+    const int kb = a.L.kb, vb = a.L.vb;
+    if (kb == 16)  // recent tokens only: any instantiation serves
+        return launch_prefill_pair<2, 2, false>(a, st);
+#define KVQ_PAIR(K, V)                                                        \
+    if (kb == K && vb == V)                                                   \
+        return a.L.k_tok ? launch_prefill_pair<K, V, true>(a, st) : launch_prefill_pair<K, V, false>(a, st);
+    KVQ_PAIR(2, 2) KVQ_PAIR(2, 4) KVQ_PAIR(2, 8)
+    KVQ_PAIR(4, 2) KVQ_PAIR(4, 4) KVQ_PAIR(4, 8)
+    KVQ_PAIR(8, 2) KVQ_PAIR(8, 4) KVQ_PAIR(8, 8)
+#undef KVQ_PAIR
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kvq

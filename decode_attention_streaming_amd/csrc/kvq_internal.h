@@ -83,6 +83,21 @@ struct AttnArgs {
     int new_t;
 };
 
+// Causal attention of the queries of the last n_q appended tokens (a prefill
+// chunk): query j (position N - n_q + j) attends to tokens 0 .. N - n_q + j.
+// One wave per tile of QT = 16 / g queries of one stream; n_wg workgroups of
+// four waves cover BH * n_tiles tiles.
+struct PrefillArgs {
+    LayerDev L;
+    const void *q;   // [B][Hq][n_q][D] in q_dtype
+    float *out;      // [B][Hq][n_q][D]
+    int q_dtype, kv_bf16;
+    int D, g, BH, N, Tq, n_q;
+    int QT, n_tiles, n_wg;
+    int ngcap;       // capq / G
+    float scale_log2;  // log2(e) / sqrt(D)
+};
+
 // LDS floats per wave of the matrix-core kernel, one region used three ways:
 // a quantized unit's K scales and zeros of one window (ng groups of [2][D]
 // floats, ng = the largest power of two with ng * g <= 16) followed by the
@@ -116,5 +131,8 @@ hipError_t launch_ring_write(const RingArgs &a, hipStream_t st);
 bool mfma_supported(int kb, int vb, int D);
 hipError_t launch_attention(const AttnArgs &a, bool use_mfma, hipStream_t st);
 hipError_t launch_zero(unsigned *p, int n, hipStream_t st);
+// True when the prefill kernel is built for this layer format.
+bool prefill_supported(int kb, int vb, int D, int v_tiled);
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st);
 
 }  // namespace kvq

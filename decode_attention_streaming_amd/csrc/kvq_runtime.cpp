@@ -401,6 +401,51 @@ int kvq_append_decode_attention(kvq_handle *h, int layer, const void *k_new, con
     return rc;
 }
 
+int kvq_prefill_attention(kvq_handle *h, int layer, const void *q, int n_q, float *out)
+{
+    if (!h)
+        return KVQ_EINVAL;
+    const int rc = check_attention_args(h, layer, q, out);
+    if (rc != KVQ_OK)
+        return rc;
+    const LayerState &s = h->plan.layers[layer];
+    const kvq::LayerDev &d = s.dev;
+    if (n_q < 1 || n_q > s.N)
+        return h->fail(KVQ_EINVAL, "n_q = %d outside [1, %d] (tokens in layer %d)", n_q, s.N, layer);
+    const int D = h->cfg.head_dim;
+    if (!kvq::prefill_supported(d.kb, d.vb, D, d.v_tiled))
+        return h->fail(KVQ_EUNSUPPORTED,
+                       "layer %d: prefill attention needs k_bits and v_bits in {2, 4, 8} with group_size a "
+                       "multiple of 32, or a (16, 16) layer (layer is K%dV%d, group_size %d)",
+                       layer, d.kb, d.vb, d.G);
+    const int g = h->cfg.n_q_heads / h->cfg.n_kv_heads;
+    kvq::PrefillArgs a;
+    a.L = d;
+    a.q = q;
+    a.out = out;
+    a.q_dtype = h->cfg.q_dtype;
+    a.kv_bf16 = h->cfg.kv_dtype == KVQ_BF16;
+    a.D = D;
+    a.g = g;
+    a.BH = h->BH();
+    a.N = s.N;
+    a.Tq = s.Tq;
+    a.n_q = n_q;
+    a.QT = 16 / g;
+    a.n_tiles = (n_q + a.QT - 1) / a.QT;
+    const long units = static_cast<long>(a.BH) * a.n_tiles;
+    if (units > 4L * INT32_MAX / 8)
+        return h->fail(KVQ_EUNSUPPORTED, "%ld query tiles exceed one launch", units);
+    a.n_wg = static_cast<int>((units + 3) / 4);
+    a.ngcap = d.capq / d.G;
+    a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D)));
+    const hipError_t e = kvq::launch_prefill(a, h->stream);
+    if (e != hipSuccess)
+        return h->dev_fail(e, "prefill attention launch");
+    h->touched = true;
+    return KVQ_OK;
+}
+
 static int attention_launch(kvq_handle *h, int layer, const void *q, float *out, const void *new_k,
                             const void *new_v, int new_t)
 {

@@ -20,7 +20,7 @@ _DT = {"f32": KVQ_F32, "f16": KVQ_F16, "bf16": KVQ_BF16}
 
 EXPORTED = ["kvq_workspace_bytes", "kvq_create", "kvq_append", "kvq_decode_attention",
             "kvq_append_decode_attention", "kvq_bytes", "kvq_bytes_layer", "kvq_export_layer", "kvq_sync",
-            "kvq_set_stream", "kvq_last_error", "kvq_destroy", "kvq_last_launch"]
+            "kvq_set_stream", "kvq_last_error", "kvq_destroy", "kvq_last_launch", "kvq_prefill_attention"]
 
 
 KVQ_K_PER_CHANNEL, KVQ_K_PER_TOKEN = 0, 1
@@ -77,6 +77,7 @@ def lib():
         "kvq_last_error": (ctypes.c_char_p, [P]),
         "kvq_destroy": (None, [P]),
         "kvq_last_launch": (I, [P, P, P]),
+        "kvq_prefill_attention": (I, [P, I, P, I, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -127,6 +128,10 @@ def kvq_decode_attention(h, layer, q_ptr, out_ptr):
 
 def kvq_append_decode_attention(h, layer, k_ptr, v_ptr, q_ptr, out_ptr):
     return _check(lib().kvq_append_decode_attention(h, layer, k_ptr, v_ptr, q_ptr, out_ptr), h)
+
+
+def kvq_prefill_attention(h, layer, q_ptr, n_q, out_ptr):
+    return _check(lib().kvq_prefill_attention(h, layer, q_ptr, n_q, out_ptr), h)
 
 
 def kvq_bytes(h):
@@ -250,6 +255,21 @@ class Cache:
         kvq_append_decode_attention(self.h, layer, ctypes.c_void_p(k_new.data_ptr()),
                                     ctypes.c_void_p(v_new.data_ptr()), ctypes.c_void_p(q.data_ptr()),
                                     ctypes.c_void_p(out.data_ptr()))
+        return out
+
+    def prefill_attention(self, layer, q, out=None):
+        """Causal attention of the last n_q appended tokens' queries:
+        q [B, Hq, n_q, d] (contiguous, q_dtype); out [B, Hq, n_q, d] fp32."""
+        s = self.shape
+        torch = self.torch
+        want = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[self.q_dtype]
+        if q.dtype != want or not q.is_contiguous() or q.dim() != 4 or (
+                q.shape[0], q.shape[1], q.shape[3]) != (s["batch"], s["n_q_heads"], s["head_dim"]):
+            raise ValueError("q must be contiguous [B, Hq, n_q, d] %s" % want)
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        kvq_prefill_attention(self.h, layer, ctypes.c_void_p(q.data_ptr()), q.shape[2],
+                              ctypes.c_void_p(out.data_ptr()))
         return out
 
     def bytes(self):

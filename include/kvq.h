@@ -149,6 +149,23 @@ int kvq_decode_attention(kvq_handle *h, int layer, const void *q, float *out);
 int kvq_append_decode_attention(kvq_handle *h, int layer, const void *k_new, const void *v_new, const void *q,
                                 float *out);
 
+/* Causal attention of a prefill chunk over the cache as stored: the queries of
+ * the last n_q tokens appended to `layer` (append the chunk's K and V first),
+ * query j (0 <= j < n_q, position p = N - n_q + j) attending to tokens 0..p,
+ * quantized tokens dequantized on the fly and recent tokens in 16 bits, scale
+ * 1/sqrt(head_dim).  (KVTuner summary, A3 attention equation: the query of step
+ * i attends to the keys of steps up to i; A2: calibration runs prefill attention
+ * on the dequantized cache.)
+ *   q:   device pointer, [batch][n_q_heads][n_q][head_dim] in q_dtype,
+ *        16-byte aligned.
+ *   out: device pointer, [batch][n_q_heads][n_q][head_dim] fp32, 16-byte aligned.
+ *   1 <= n_q <= tokens in the layer.
+ * Supported layers: k_bits and v_bits in {2, 4, 8} (either Key mode) with
+ * group_size a multiple of 32, or (16, 16) layers.
+ * Errors: KVQ_EINVAL (bad layer, pointer or n_q), KVQ_EUNSUPPORTED (layer
+ * format), KVQ_EDEVICE. */
+int kvq_prefill_attention(kvq_handle *h, int layer, const void *q, int n_q, float *out);
+
 /* Live bytes of the cache state over all layers, host arithmetic only: per
  * (sequence, kv-head): Tq rows of packed K and V codes (4 bytes per word), one
  * fp32 scale and zero per channel per K group (per-token Key: per K token),

@@ -88,6 +88,12 @@ def test_handle_validation_leaves_state_unchanged():
             (lambda: kvq.kvq_decode_attention(h, 1, None, p), kvq.KVQ_EINVAL, "NULL"),
             (lambda: kvq.kvq_decode_attention(h, 5, p, p), kvq.KVQ_EINVAL, "out of range"),
             (lambda: kvq.kvq_bytes_layer(h, 9), kvq.KVQ_EINVAL, "out of range"),
+            (lambda: kvq.kvq_prefill_attention(h, 0, p, 1, p), kvq.KVQ_EINVAL, "n_q = 1 outside"),
+            (lambda: kvq.kvq_prefill_attention(h, 0, p, 0, p), kvq.KVQ_EINVAL, "n_q = 0 outside"),
+            (lambda: kvq.kvq_prefill_attention(h, 2, p, 1, p), kvq.KVQ_EINVAL, "out of range"),
+            (lambda: kvq.kvq_prefill_attention(h, 0, p, 1, None), kvq.KVQ_EINVAL, "NULL"),
+            (lambda: kvq.kvq_prefill_attention(h, 0, ctypes.c_void_p((1 << 21) + 4), 1, p), kvq.KVQ_EINVAL,
+             "aligned"),
         ]
         for fn, code, msg in cases:
             with pytest.raises(kvq.KvqError) as e:
