@@ -142,6 +142,51 @@ def cpu_baseline(w, seconds, layers_sample):
     }
 
 
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+
+def prefill_leg(cache, w, C, N, qbytes, rounds, stream, dev):
+    """Causal attention of the last C tokens' queries over every layer's cache
+    (the chunk is already appended), timed with HIP events on the library's
+    stream over back-to-back calls.  Algorithmic flops: 2 d per visible (query
+    head, token) pair for q.K and 2 d for P.V; algorithmic bytes: the layer's
+    cache state once, q and out."""
+    import torch
+
+    from decode_attention_streaming_amd import synth
+
+    B, Hq, Hkv, d, L = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_layers
+    qs = [synth.queries(w, l, C, dev, seed=7).permute(1, 2, 0, 3).contiguous() for l in range(L)]
+    outs = [torch.empty((B, Hq, C, d), dtype=torch.float32, device=dev) for _ in range(L)]
+    for l in range(L):
+        cache.prefill_attention(l, qs[l], outs[l])
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for r in range(rounds):
+        for l in range(L):
+            cache.prefill_attention(l, qs[l], outs[l])
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    call_us = ev0.elapsed_time(ev1) * 1e3 / (rounds * L)
+    visible = C * (N - C) + C * (C + 1) // 2  # (query, token) pairs per head
+    flops = 4.0 * d * visible * B * Hq
+    nbytes = 0
+    for lc in w.layers:
+        kb, vb, R, kt = layer_row(lc)
+        nbytes += B * Hkv * stream_state_bytes(d, kb, vb, w.G, N, quantized_count(N, R, w.G, kb), kt)
+    nbytes = nbytes / L + B * Hq * C * d * (qbytes + 4)
+    tflops = flops / (call_us * 1e-6) / 1e12
+    return {
+        "chunk": C, "context": N, "avg_call_us": round(call_us, 3),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4)},
+        "gbs": round(nbytes / (call_us * 1e-6) / 1e9, 1),
+        "flops_per_call": flops, "bytes_per_call": int(nbytes),
+        "tok_per_s": round(B * C / (call_us * 1e-6 * L), 1),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -155,6 +200,9 @@ def main():
     ap.add_argument("--kernel-rounds", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-chunk", type=int, default=256,
+                    help="also time causal prefill attention of the last C tokens of every layer "
+                         "(0 = skip)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="also run a plain device copy of this size (counter scaling)")
     args = ap.parse_args()
@@ -280,6 +328,11 @@ def main():
     splits, variant = kvq.kvq_last_launch(cache.h)
     traffic = stored_traffic(args.workload, args.table) if args.k_mode == "per-channel" else None
 
+    prefill = None
+    C = min(args.prefill_chunk, N_end)
+    if C > 0 and all(lc[0] != 3 for lc in w.layers) and w.G % 32 == 0:
+        prefill = prefill_leg(cache, w, C, N_end, qbytes, rounds, stream, dev)
+
     if args.copy_mb > 0:  # a plain copy of known size, for scaling memory counters
         n = args.copy_mb * (1 << 20)
         src = torch.ones(n // 4, dtype=torch.float32, device=dev)
@@ -329,6 +382,8 @@ def main():
             "bytes_per_call": int(avg_att_bytes),
         },
     }
+    if prefill is not None:
+        res["prefill"] = prefill
     if not args.no_cpu_baseline:
         sample = [0, 1] if L >= 2 else [0]
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, sample)

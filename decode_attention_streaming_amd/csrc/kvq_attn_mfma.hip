@@ -365,7 +365,7 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *
         float p[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            p[j] = exp2f(sc[j] - mo);
+            p[j] = weight_exp2(sc[j] - mo);
             l_run += p[j];
             zb_run = __builtin_fmaf(p[j], vz[j], zb_run);
         }
@@ -591,7 +591,7 @@ __device__ void mfma_residual_unit(const AttnArgs &a, int bh, int runit, int lan
         float p[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            p[j] = exp2f(sc[j] - mo);
+            p[j] = weight_exp2(sc[j] - mo);
             l_run += p[j];
         }
         // weights p 2^kWShift (below 2^15) as hi/lo fp16 or three bfloat16 parts

@@ -193,7 +193,7 @@ __device__ __forceinline__ void prefill_recent(const PrefillArgs &a, int bh, siz
         float p[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            p[j] = exp2f(sc[j] - mo);
+            p[j] = weight_exp2(sc[j] - mo);
             st.l_run += p[j];
         }
         Frag w1, w2, w3;
@@ -227,7 +227,7 @@ __device__ __forceinline__ void prefill_recent(const PrefillArgs &a, int bh, siz
 
 // One tile: queries tile * QT .. tile * QT + QT - 1 of stream bh.
 template <int KB, int VB, int D, bool KT>
-__device__ void prefill_tile(const PrefillArgs &a, int bh, int tile, int lane, uint16_t *vt)
+__device__ void prefill_tile(const PrefillArgs &a, int bh, int tile, int lane, uint16_t *vt, float *meta_lds)
 {
     constexpr int QC = D / 4;         // channels owned by one lane quad
     constexpr int KW = D * KB / 128;  // K words per lane per token
@@ -265,13 +265,32 @@ __device__ void prefill_tile(const PrefillArgs &a, int bh, int tile, int lane, u
         Frag bhi[NC], blo[NC];
         float bias = 0.0f, kscale = 0.0f;
 
+        // this column's q over the quad's channels, times log2(e) / sqrt(D)
+        float qq[QC];
+        load_q_slice<QC>(a.q, a.q_dtype, qrow + q * QC, qq);
+        {
+            const float qscale = act ? a.scale_log2 : 0.0f;
+#pragma unroll
+            for (int i = 0; i < QC; ++i)
+                qq[i] *= qscale;
+        }
+
+        // K scales and zeros of group gi ([2][D] floats) into LDS slot gi & 1
+        // with direct-to-LDS loads: no registers held while they fly
+        auto meta_issue = [&](int gi) {
+            const float *src = L.k_meta + (static_cast<size_t>(bh) * a.ngcap + gi) * 2 * D;
+            float *dst = meta_lds + (gi & 1) * 2 * D;
+            constexpr int n16 = D / 2;  // 16-byte pieces
+#pragma unroll
+            for (int i0 = 0; i0 < n16; i0 += 64) {
+                if (i0 + lane < n16)
+                    __builtin_amdgcn_global_load_lds(src + 4 * (i0 + lane), dst + 4 * i0, 16, 0, 0);
+            }
+        };
         // B operand of q.K for group gi (per-token Key: q alone, built once):
         // q * s as hi/lo fp16 in the code-register order of the quad's words
         auto build_b = [&](int gi) {
-            float qv[QC];
-            load_q_slice<QC>(a.q, a.q_dtype, qrow + q * QC, qv);
-            const float qscale = act ? a.scale_log2 : 0.0f;
-            const float *sp = L.k_meta + (static_cast<size_t>(bh) * a.ngcap + gi) * 2 * D + q * QC;
+            const float *sp = meta_lds + (gi & 1) * 2 * D + q * QC;
             const float *zp = sp + D;
             float qs[QC];
             float amax = 0.0f;
@@ -285,12 +304,13 @@ __device__ void prefill_tile(const PrefillArgs &a, int bh, int tile, int lane, u
                 const float zv[4] = {z4.x, z4.y, z4.z, z4.w};
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    const float qq = qv[i + k] * qscale;
-                    qs[i + k] = qq * sv[k];
-                    bias = __builtin_fmaf(qq, zv[k], bias);
+                    qs[i + k] = qq[i + k] * sv[k];
+                    bias = __builtin_fmaf(qq[i + k], zv[k], bias);
                     amax = fmaxf(amax, fabsf(qs[i + k]));
                 }
             }
+            // the slot may be loaded again only after these reads
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             bias = col_sum(bias);
             amax = col_max(amax);
             const int sexp = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) : 0;
@@ -309,39 +329,64 @@ __device__ void prefill_tile(const PrefillArgs &a, int bh, int tile, int lane, u
         if constexpr (KT)
             build_b(0);
 
+        // one 32-token block: K rows of both 16-token tiles, the V fragment, the
+        // V meta of this lane's eight tokens (and their K meta, per-token Key)
+        struct Blk {
+            uint32_t k0[KW], k1[KW], vw[FW];
+            float4 vm[4], km[4];
+        };
+        auto load_blk = [&](Blk &b, int t0) {
+            load_words(kw_base + static_cast<size_t>(t0 + col) * L.wk, b.k0);
+            load_words(kw_base + static_cast<size_t>(t0 + 16 + col) * L.wk, b.k1);
+            load_words(vw_base + static_cast<size_t>(t0) * L.wv, b.vw);
+            const float4 *m0 = reinterpret_cast<const float4 *>(vm_base + static_cast<size_t>(t0 + 4 * q) * 2);
+            const float4 *m1 = reinterpret_cast<const float4 *>(vm_base + static_cast<size_t>(t0 + 16 + 4 * q) * 2);
+            b.vm[0] = m0[0];
+            b.vm[1] = m0[1];
+            b.vm[2] = m1[0];
+            b.vm[3] = m1[1];
+            if constexpr (KT) {
+                const float4 *c0 = reinterpret_cast<const float4 *>(km_tok + static_cast<size_t>(t0 + 4 * q) * 2);
+                const float4 *c1 = reinterpret_cast<const float4 *>(km_tok + static_cast<size_t>(t0 + 16 + 4 * q) * 2);
+                b.km[0] = c0[0];
+                b.km[1] = c0[1];
+                b.km[2] = c1[0];
+                b.km[3] = c1[1];
+            }
+        };
+
+        // Software pipeline, one block ahead: while block t0 is computed, the
+        // loads of block t0 + 32 (and of its group's meta when it starts a
+        // group) are in flight.  The last iteration reloads its own block
+        // (in bounds, unused) so that every iteration issues the same loads.
+        Blk cur, nxt;
+        if constexpr (!KT)
+            meta_issue(0);
+        load_blk(cur, 0);
         for (int t0 = 0; t0 < tq_end; t0 += 32) {
             if constexpr (!KT) {
                 if (t0 % G == 0)  // G is a multiple of 32: a group starts on a block
                     build_b(t0 / G);
             }
-            uint32_t k0[KW], k1[KW], vw[FW];
-            load_words(kw_base + static_cast<size_t>(t0 + col) * L.wk, k0);
-            load_words(kw_base + static_cast<size_t>(t0 + 16 + col) * L.wk, k1);
-            load_words(vw_base + static_cast<size_t>(t0) * L.wv, vw);
-            const float4 *m0 = reinterpret_cast<const float4 *>(vm_base + static_cast<size_t>(t0 + 4 * q) * 2);
-            const float4 *m1 = reinterpret_cast<const float4 *>(vm_base + static_cast<size_t>(t0 + 16 + 4 * q) * 2);
-            const float4 vm[4] = {m0[0], m0[1], m1[0], m1[1]};
-            float4 km[4];
-            if constexpr (KT) {
-                const float4 *c0 = reinterpret_cast<const float4 *>(km_tok + static_cast<size_t>(t0 + 4 * q) * 2);
-                const float4 *c1 = reinterpret_cast<const float4 *>(km_tok + static_cast<size_t>(t0 + 16 + 4 * q) * 2);
-                km[0] = c0[0];
-                km[1] = c0[1];
-                km[2] = c1[0];
-                km[3] = c1[1];
+            const int t1 = min(t0 + 32, tq_end - 32);
+            if constexpr (!KT) {
+                if (t1 > t0 && t1 % G == 0)
+                    meta_issue(t1 / G);
             }
+            load_blk(nxt, t1);
+
             // q.K for tokens 4q + j (acc0) and 16 + 4q + j (acc1)
             uint32_t k08[KW], k18[KW];
-            shift8(k0, k08);
-            shift8(k1, k18);
+            shift8(cur.k0, k08);
+            shift8(cur.k1, k18);
             f4_t acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int k = 0; k < NC; ++k) {
                 Frag a0, a1;
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
-                    a0.u[p] = code_reg<KB>(k0, k08, 4 * k + p);
-                    a1.u[p] = code_reg<KB>(k1, k18, 4 * k + p);
+                    a0.u[p] = code_reg<KB>(cur.k0, k08, 4 * k + p);
+                    a1.u[p] = code_reg<KB>(cur.k1, k18, 4 * k + p);
                 }
                 acc0 = mfma(a0, bhi[k], acc0);
                 acc0 = mfma(a0, blo[k], acc0);
@@ -351,6 +396,7 @@ __device__ void prefill_tile(const PrefillArgs &a, int bh, int tile, int lane, u
             float sc[8];
             if constexpr (KT) {
                 // score_t = s_t sum_c q_c code_tc + z_t sum_c q_c
+                const float4 *km = cur.km;
                 const float ks[8] = {km[0].x, km[0].z, km[1].x, km[1].z, km[2].x, km[2].z, km[3].x, km[3].z};
                 const float kz[8] = {km[0].y, km[0].w, km[1].y, km[1].w, km[2].y, km[2].w, km[3].y, km[3].w};
 #pragma unroll
@@ -370,6 +416,7 @@ __device__ void prefill_tile(const PrefillArgs &a, int bh, int tile, int lane, u
                 sc[j] = (t0 + 4 * q + j <= p_col) ? sc[j] : -INFINITY;
                 sc[4 + j] = (t0 + 16 + 4 * q + j <= p_col) ? sc[4 + j] : -INFINITY;
             }
+            const float4 *vm = cur.vm;
             const float vs[8] = {vm[0].x, vm[0].z, vm[1].x, vm[1].z, vm[2].x, vm[2].z, vm[3].x, vm[3].z};
             const float vz[8] = {vm[0].y, vm[0].w, vm[1].y, vm[1].w, vm[2].y, vm[2].w, vm[3].y, vm[3].w};
             float tmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
@@ -398,7 +445,7 @@ __device__ void prefill_tile(const PrefillArgs &a, int bh, int tile, int lane, u
             float p[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                p[j] = exp2f(sc[j] - mo);
+                p[j] = weight_exp2(sc[j] - mo);
                 st.l_run += p[j];
                 zb_run = __builtin_fmaf(p[j], vz[j], zb_run);
             }
@@ -413,16 +460,17 @@ __device__ void prefill_tile(const PrefillArgs &a, int bh, int tile, int lane, u
                            wlo.u[r]);
             }
             uint32_t v8[FW];
-            shift8(vw, v8);
+            shift8(cur.vw, v8);
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
                 Frag av;
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    av.u[r] = code_reg<VB>(vw, v8, 4 * m + r);
+                    av.u[r] = code_reg<VB>(cur.vw, v8, 4 * m + r);
                 st.O[m] = mfma(av, whi, st.O[m]);
                 st.O[m] = mfma(av, wlo, st.O[m]);
             }
+            cur = nxt;
         }
         // into the recent-token units (2^kWShift): o = O 2^(E - kWShift) + sum_t p_t z_t
         const float ZB = ldexpf(col_sum(zb_run), kWShift);
@@ -450,10 +498,15 @@ __device__ void prefill_tile(const PrefillArgs &a, int bh, int tile, int lane, u
     }
 }
 
+// LDS floats per wave: V tile (D * 32 halves = D * 16 floats) + 2 * 2 * D
+constexpr int kPrefillWaveFloats = KVQ_D * 16 + 4 * KVQ_D;
+
 template <int KB, int VB, int D, bool KT>
 __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(PrefillArgs a)
 {
-    extern __shared__ uint16_t vt_all[];  // one [D][32] 16-bit tile per wave
+    // per wave: a [D][32] 16-bit V tile (recent tokens), then two [2][D]
+    // float slots of K scales and zeros (quantized tokens)
+    extern __shared__ float lds_all[];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     // Workgroups are dealt to the eight XCDs in turn; number them so that
     // consecutive slots (tiles of one stream, which read the same cache rows)
@@ -464,13 +517,14 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(PrefillArgs a)
     if (unit >= a.BH * a.n_tiles)
         return;  // no workgroup barrier follows: a wave may leave alone
     const int bh = unit / a.n_tiles, tile = unit - bh * a.n_tiles;
-    prefill_tile<KB, VB, D, KT>(a, bh, tile, lane, vt_all + wave * D * 32);
+    float *region = lds_all + wave * kPrefillWaveFloats;
+    prefill_tile<KB, VB, D, KT>(a, bh, tile, lane, reinterpret_cast<uint16_t *>(region), region + D * 16);
 }
 
 template <int KB, int VB, bool KT>
 hipError_t launch_prefill_pair(const PrefillArgs &a, hipStream_t st)
 {
-    const size_t lds = 4 * KVQ_D * 32 * sizeof(uint16_t);
+    const size_t lds = 4 * kPrefillWaveFloats * sizeof(float);
     hipLaunchKernelGGL((attn_prefill_kernel<KB, VB, KVQ_D, KT>), dim3(a.n_wg), dim3(256), lds, st, a);
     return hipGetLastError();
 }

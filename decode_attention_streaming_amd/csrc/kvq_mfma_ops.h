@@ -38,6 +38,14 @@ __device__ __forceinline__ f4_t mfma_bf16(const Frag &a, const Frag &b, f4_t c)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.b, b.b, c, 0, 0, 0);
 }
 
+// Softmax weight 2^x for x <= kTau: the hardware exp2, without the library's
+// rescaling for subnormal results (weights below 2^-126 of the running
+// maximum become 0, a relative change far below fp32 rounding of the sums).
+__device__ __forceinline__ float weight_exp2(float x)
+{
+    return __builtin_amdgcn_exp2f(x);
+}
+
 // fp32 pair -> three bfloat16 pairs with x ~= p1 + p2 + p3 (truncations; about
 // 24 significant bits)
 __device__ __forceinline__ void split3_bf16(float x0, float x1, uint32_t &p1, uint32_t &p2, uint32_t &p3)
