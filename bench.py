@@ -78,10 +78,11 @@ def kernel_source_digest():
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload, table):
-    """HBM bytes per attention launch from the stored FETCH_SIZE / WRITE_SIZE
-    measurement of this workload, or None when the kernels have changed since."""
-    path = os.path.join(ROOT, "profiles", "attention_traffic_workload%d_%s.json" % (workload, table))
+def stored_traffic(workload, table, kind="attention"):
+    """HBM bytes per launch (kind: "attention" for decode, "prefill") from the
+    stored FETCH_SIZE / WRITE_SIZE measurement of this workload, or None when
+    the kernels have changed since."""
+    path = os.path.join(ROOT, "profiles", "%s_traffic_workload%d_%s.json" % (kind, workload, table))
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -332,6 +333,8 @@ def main():
     C = min(args.prefill_chunk, N_end)
     if C > 0 and all(lc[0] != 3 for lc in w.layers) and w.G % 32 == 0:
         prefill = prefill_leg(cache, w, C, N_end, qbytes, rounds, stream, dev)
+        if C == 256 and args.k_mode == "per-channel":
+            prefill["roofline"]["traffic"] = stored_traffic(args.workload, args.table, "prefill")
 
     if args.copy_mb > 0:  # a plain copy of known size, for scaling memory counters
         n = args.copy_mb * (1 << 20)
