@@ -331,7 +331,7 @@ def main():
 
     prefill = None
     C = min(args.prefill_chunk, N_end)
-    if C > 0 and all(lc[0] != 3 for lc in w.layers) and w.G % 32 == 0:
+    if C > 0 and (w.head_dim == 128 or all(lc[0] != 3 for lc in w.layers)) and w.G % 32 == 0:
         prefill = prefill_leg(cache, w, C, N_end, qbytes, rounds, stream, dev)
         if C == 256 and args.k_mode == "per-channel":
             prefill["roofline"]["traffic"] = stored_traffic(args.workload, args.table, "prefill")

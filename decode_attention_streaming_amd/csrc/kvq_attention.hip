@@ -57,8 +57,9 @@ bool prefill_supported(int kb, int vb, int D, int v_tiled)
         return false;
     if (kb == 16)
         return vb == 16;
-    const bool ok = (kb == 2 || kb == 4 || kb == 8) && (vb == 2 || vb == 4 || vb == 8);
-    return ok && v_tiled;  // V codes in the matrix-core tile layout (G a multiple of 32)
+    const bool vbits = vb == 2 || vb == 4 || vb == 8;
+    const bool kbits = kb == 2 || kb == 4 || kb == 8 || (kb == 3 && D == 128);  // 3 bits: twelve words a row
+    return kbits && vbits && v_tiled;  // V codes in the matrix-core tile layout (G a multiple of 32)
 }
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st)

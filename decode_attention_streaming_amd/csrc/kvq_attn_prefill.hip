@@ -229,11 +229,13 @@ __device__ __forceinline__ void prefill_recent(const PrefillArgs &a, int bh, siz
 template <int KB, int VB, int D, bool KT>
 __device__ void prefill_tile(const PrefillArgs &a, int bh, int tile, int lane, uint16_t *vt, float *meta_lds)
 {
-    constexpr int QC = D / 4;         // channels owned by one lane quad
-    constexpr int KW = D * KB / 128;  // K words per lane per token
-    constexpr int PK = 16 / KB;       // K code pairs per word
-    constexpr int CW = 32 / KB;       // K channels per word
-    constexpr int NC = D / 32;        // 32-position chunks of q.K
+    constexpr int KW = D * KB / 128;  // K words per lane per token (3 bits: D / 11 rounded up, / 4)
+    constexpr int PK = KB == 3 ? 1 : 16 / KB;   // K code pairs per word
+    constexpr int CW = KB == 3 ? 11 : 32 / KB;  // K channels per word
+    // channels of a quad's K words (3 bits: 11 per word, some past D), and
+    // 32-position chunks of q.K (3 bits: six registers per word, padded)
+    constexpr int QC = KB == 3 ? 11 * KW : D / 4;
+    constexpr int NC = KB == 3 ? (6 * KW + 3) / 4 : D / 32;
     constexpr int FW = D * VB / 64;   // V words per lane per 32-token block
     constexpr int MT = D / 16;        // 16-channel tiles of P.V
 
@@ -267,7 +269,16 @@ __device__ void prefill_tile(const PrefillArgs &a, int bh, int tile, int lane, u
 
         // this column's q over the quad's channels, times log2(e) / sqrt(D)
         float qq[QC];
-        load_q_slice<QC>(a.q, a.q_dtype, qrow + q * QC, qq);
+        if constexpr (KB == 3) {
+            // channels 11 * KW * q + i; those past D weigh 0
+#pragma unroll
+            for (int i = 0; i < QC; ++i) {
+                const int c = QC * q + i;
+                qq[i] = c < D ? load_q(a.q, a.q_dtype, qrow + (c < D ? c : 0)) : 0.0f;
+            }
+        } else {
+            load_q_slice<QC>(a.q, a.q_dtype, qrow + q * QC, qq);
+        }
         {
             const float qscale = act ? a.scale_log2 : 0.0f;
 #pragma unroll
@@ -290,13 +301,29 @@ __device__ void prefill_tile(const PrefillArgs &a, int bh, int tile, int lane, u
         // B operand of q.K for group gi (per-token Key: q alone, built once):
         // q * s as hi/lo fp16 in the code-register order of the quad's words
         auto build_b = [&](int gi) {
-            const float *sp = meta_lds + (gi & 1) * 2 * D + q * QC;
-            const float *zp = sp + D;
+            // the group's direct-to-LDS loads (issued one block earlier) must have
+            // landed: wait for them explicitly, the compiler does not always
+            // order LDS reads after them
+            if constexpr (!KT)
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             float qs[QC];
             float amax = 0.0f;
             bias = 0.0f;
+            if constexpr (KB == 3) {
+                const float *sp = meta_lds + (gi & 1) * 2 * D;
 #pragma unroll
-            for (int i = 0; i < QC; i += 4) {
+                for (int i = 0; i < QC; ++i) {
+                    const int c = QC * q + i;
+                    const int cc = c < D ? c : 0;  // qq is 0 past D
+                    qs[i] = qq[i] * sp[cc];
+                    bias = __builtin_fmaf(qq[i], sp[D + cc], bias);
+                    amax = fmaxf(amax, fabsf(qs[i]));
+                }
+            }
+            const float *sp = meta_lds + (gi & 1) * 2 * D + q * QC;
+            const float *zp = sp + D;
+#pragma unroll
+            for (int i = 0; i < (KB == 3 ? 0 : QC); i += 4) {
                 const float4 one = {1.0f, 1.0f, 1.0f, 1.0f};
                 const float4 s4 = KT ? one : *reinterpret_cast<const float4 *>(sp + i);
                 const float4 z4 = KT ? one : *reinterpret_cast<const float4 *>(zp + i);
@@ -320,9 +347,24 @@ __device__ void prefill_tile(const PrefillArgs &a, int bh, int tile, int lane, u
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
                     const int R = 4 * k + p;
-                    const int clo = (R / PK) * CW + (R % PK), chi = clo + PK;
-                    const int e = sh - class_exp<KB>(R);
-                    split_pair(ldexpf(qs[clo], e), ldexpf(qs[chi], e), bhi[k].u[p], blo[k].u[p]);
+                    if constexpr (KB == 3) {
+                        // register r of word w: the lo slot (and the hi slot) of the
+                        // 3-bit map, each divided by its bit offset
+                        if (R < 6 * KW) {
+                            const int w = R / 6, r = R % 6;
+                            const float xlo = ldexpf(qs[11 * w + r], sh - k3_lo_e(r));
+                            const float xhi =
+                                k3_hi_slot(r) < 0 ? 0.0f : ldexpf(qs[11 * w + k3_hi_slot(r)], sh - k3_hi_e(r));
+                            split_pair(xlo, xhi, bhi[k].u[p], blo[k].u[p]);
+                        } else {
+                            bhi[k].u[p] = 0u;
+                            blo[k].u[p] = 0u;
+                        }
+                    } else {
+                        const int clo = (R / PK) * CW + (R % PK), chi = clo + PK;
+                        const int e = sh - class_exp<KB>(R);
+                        split_pair(ldexpf(qs[clo], e), ldexpf(qs[chi], e), bhi[k].u[p], blo[k].u[p]);
+                    }
                 }
             kscale = ldexpf(1.0f, -sh);
         };
@@ -385,8 +427,14 @@ __device__ void prefill_tile(const PrefillArgs &a, int bh, int tile, int lane, u
                 Frag a0, a1;
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
-                    a0.u[p] = code_reg<KB>(cur.k0, k08, 4 * k + p);
-                    a1.u[p] = code_reg<KB>(cur.k1, k18, 4 * k + p);
+                    const int R = 4 * k + p;
+                    if constexpr (KB == 3) {
+                        a0.u[p] = R < 6 * KW ? code_reg3(cur.k0, k08, R) : 0u;
+                        a1.u[p] = R < 6 * KW ? code_reg3(cur.k1, k18, R) : 0u;
+                    } else {
+                        a0.u[p] = code_reg<KB>(cur.k0, k08, R);
+                        a1.u[p] = code_reg<KB>(cur.k1, k18, R);
+                    }
                 }
                 acc0 = mfma(a0, bhi[k], acc0);
                 acc0 = mfma(a0, blo[k], acc0);
@@ -543,6 +591,12 @@ hipError_t KVQ_CAT(launch_prefill_d, KVQ_D)(const PrefillArgs &a, hipStream_t st
     KVQ_PAIR(4, 2) KVQ_PAIR(4, 4) KVQ_PAIR(4, 8)
     KVQ_PAIR(8, 2) KVQ_PAIR(8, 4) KVQ_PAIR(8, 8)
 #undef KVQ_PAIR
+#if KVQ_D == 128
+    // 3-bit rows (per-channel Key only): twelve words, three per lane quad
+    if (kb == 3 && vb == 2) return launch_prefill_pair<3, 2, false>(a, st);
+    if (kb == 3 && vb == 4) return launch_prefill_pair<3, 4, false>(a, st);
+    if (kb == 3 && vb == 8) return launch_prefill_pair<3, 8, false>(a, st);
+#endif
     return hipErrorInvalidValue;
 }
 

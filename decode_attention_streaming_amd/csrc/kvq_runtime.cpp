@@ -415,8 +415,9 @@ int kvq_prefill_attention(kvq_handle *h, int layer, const void *q, int n_q, floa
     const int D = h->cfg.head_dim;
     if (!kvq::prefill_supported(d.kb, d.vb, D, d.v_tiled))
         return h->fail(KVQ_EUNSUPPORTED,
-                       "layer %d: prefill attention needs k_bits and v_bits in {2, 4, 8} with group_size a "
-                       "multiple of 32, or a (16, 16) layer (layer is K%dV%d, group_size %d)",
+                       "layer %d: prefill attention needs k_bits in {2, 3 (head_dim 128), 4, 8} and v_bits in "
+                       "{2, 4, 8} with group_size a multiple of 32, or a (16, 16) layer (layer is K%dV%d, "
+                       "group_size %d)",
                        layer, d.kb, d.vb, d.G);
     const int g = h->cfg.n_q_heads / h->cfg.n_kv_heads;
     kvq::PrefillArgs a;

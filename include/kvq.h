@@ -160,8 +160,8 @@ int kvq_append_decode_attention(kvq_handle *h, int layer, const void *k_new, con
  *        16-byte aligned.
  *   out: device pointer, [batch][n_q_heads][n_q][head_dim] fp32, 16-byte aligned.
  *   1 <= n_q <= tokens in the layer.
- * Supported layers: k_bits and v_bits in {2, 4, 8} (either Key mode) with
- * group_size a multiple of 32, or (16, 16) layers.
+ * Supported layers: k_bits in {2, 4, 8} (either Key mode) or 3 (head_dim 128),
+ * v_bits in {2, 4, 8}, with group_size a multiple of 32; or (16, 16) layers.
  * Errors: KVQ_EINVAL (bad layer, pointer or n_q), KVQ_EUNSUPPORTED (layer
  * format), KVQ_EDEVICE. */
 int kvq_prefill_attention(kvq_handle *h, int layer, const void *q, int n_q, float *out);

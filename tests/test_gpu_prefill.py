@@ -81,6 +81,9 @@ CASES = {
     "plain16_f16_whole": (1, 2, 1, 64, 16, 16, 32, 32, "f16", "f16", 0, 70, 0),
     "k2v4_single_query": (2, 8, 2, 128, 2, 4, 32, 32, "bf16", "bf16", 400, 1, 0),
     "k4v2_one_token_cache": (1, 4, 2, 128, 4, 2, 32, 32, "bf16", "f32", 0, 1, 0),
+    "k3v4_mha_R819_chunk": (2, 2, 2, 128, 3, 4, 32, 819, "f16", "f16", 3000, 200, 0),
+    "k3v2_g4_bf16_spans_groups": (2, 8, 2, 128, 3, 2, 32, 32, "bf16", "bf16", 300, 90, 0),
+    "k3v8_g2_G64_whole": (1, 4, 2, 128, 3, 8, 64, 64, "f16", "f32", 0, 250, 0),
 }
 
 
@@ -117,7 +120,7 @@ def test_prefill_llama31_shape_sampled_streams():
 
 
 def test_prefill_unsupported_formats():
-    w = ad_hoc_workload(3903, 1, 4, 1, 128, 3, 4, 32, 32, 64, "f16", "f32")
+    w = ad_hoc_workload(3903, 1, 4, 1, 64, 3, 4, 32, 32, 64, "f16", "f32")  # 3-bit Key at head_dim 64
     cache = make_cache(w)
     k, v = synth.layer_tokens(w, 0, 0, 40, DEV)
     cache.append(0, k, v)
