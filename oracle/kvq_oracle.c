@@ -43,6 +43,11 @@
  *     slot 10 at 2 bits; that channel's own min/max is quantized with qmax 3.
  *   - K and V share one recent-token buffer of R tokens; when an append finds
  *     it full, the oldest G tokens are quantized (flushed) first.
+ *   - [KVmix] key design 3 (dynamic RPC ratio r per layer, num_RPC =
+ *     floor(r * current_RPC)): with r > 0, an append that finds the buffer full
+ *     keeps floor(r * current) of its current tokens in 16 bits and quantizes
+ *     the older rest, rounded down to whole groups of G (at least one group).
+ *     r is given in parts per thousand so that the rule is integer arithmetic.
  *   - the softmax scale is 1/sqrt(head_dim).
  *   - a (16,16) layer keeps every token in its 16-bit input format.
  */
@@ -241,9 +246,21 @@ int kvqo_append(kvqo_layer *L, const uint16_t *k_new, const uint16_t *v_new, int
     if (n < 0 || L->N + n > L->cap)
         return -1;
     for (int i = 0; i < n; ++i) {
-        /* A full recent-token buffer is flushed before the new token enters. */
-        if (!is_plain(L) && L->N - L->Tq == L->R)
-            flush_group(L);
+        /* A full recent-token buffer is flushed before the new token enters:
+         * its oldest G tokens, or with a ratio r all but floor(r * current)
+         * of its tokens, in whole groups. */
+        if (!is_plain(L) && L->N - L->Tq == L->R) {
+            const int current = L->N - L->Tq;
+            int n_flush = L->G;
+            if (L->rpc_permille > 0) {
+                const int keep = (int)(((long long)current * L->rpc_permille) / 1000);
+                n_flush = (current - keep) / L->G * L->G;
+                if (n_flush < L->G)
+                    n_flush = L->G;
+            }
+            for (int f = 0; f < n_flush; f += L->G)
+                flush_group(L);
+        }
         for (int s = 0; s < L->n_streams; ++s) {
             memcpy(L->hist_k + ((size_t)s * L->cap + L->N) * d,
                    k_new + ((size_t)s * n + i) * d, sizeof(uint16_t) * d);

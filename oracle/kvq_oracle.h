@@ -24,6 +24,9 @@ typedef struct kvqo_layer {
     int is_bf16;          /* 16-bit inputs: 0 = IEEE binary16, 1 = bfloat16 */
     int N, Tq;            /* tokens appended, tokens quantized */
     int k_tok;            /* 1: Key per token (like Value), 0: per channel over G tokens */
+    int rpc_permille;     /* 0: a full recent buffer gives up its oldest G tokens;
+                             r > 0: it keeps floor(r * current / 1000) of its current
+                             tokens and gives up the rest, in whole groups (>= one) */
     uint16_t *hist_k, *hist_v;
     uint32_t *k_words;
     float *k_scale, *k_zero;

@@ -137,7 +137,7 @@ def stream_bytes(d, k_bits, v_bits, G, N, Tq, k_tok=False):
 class _LayerStruct(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in
                 ("n_streams", "g", "d", "k_bits", "v_bits", "G", "R", "cap", "is_bf16",
-                 "N", "Tq", "k_tok")] + [(n, ctypes.c_void_p) for n in
+                 "N", "Tq", "k_tok", "rpc_permille")] + [(n, ctypes.c_void_p) for n in
                                 ("hist_k", "hist_v", "k_words", "k_scale", "k_zero",
                                  "v_words", "v_scale", "v_zero")]
 
@@ -148,10 +148,11 @@ class Layer:
     k_bits/v_bits in {2,3(K only),4,8}, or 16/16 for a layer kept in 16 bits.
     Inputs are 16-bit bit patterns (numpy uint16), fp16 or bf16 per ``is_bf16``.
     ``k_tok``: Key quantized per token (KVTuner's per-token-asym mode) instead
-    of per channel over G tokens (KIVI).
+    of per channel over G tokens (KIVI).  ``rpc_permille``: KVmix's dynamic
+    recent-token ratio r (parts per thousand); 0 keeps KIVI's G-at-a-time rule.
     """
 
-    def __init__(self, n_streams, g, d, k_bits, v_bits, G, R, cap, is_bf16, k_tok=False):
+    def __init__(self, n_streams, g, d, k_bits, v_bits, G, R, cap, is_bf16, k_tok=False, rpc_permille=0):
         cap = -(-cap // G) * G
         if k_bits == 16 or v_bits == 16:
             assert k_bits == v_bits == 16
@@ -179,6 +180,9 @@ class Layer:
             setattr(st, f, getattr(self, f))
         st.is_bf16 = int(self.is_bf16)
         st.k_tok = int(self.k_tok)
+        self.rpc_permille = int(rpc_permille) if k_bits != 16 else 0
+        assert 0 <= self.rpc_permille < 1000
+        st.rpc_permille = self.rpc_permille
         st.N = 0
         st.Tq = 0
         for f in ("hist_k", "hist_v", "k_words", "k_scale", "k_zero", "v_words", "v_scale",

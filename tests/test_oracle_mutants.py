@@ -26,6 +26,10 @@ MUTANTS = {
     "prefill_no_causal_mask": ("const int p = N - n_q + j;", "const int p = N - 1;"),
     "prefill_query_of_wrong_head": ("const double *qv = q + (((size_t)s * g + h) * n_q + j) * d;",
                                     "const double *qv = q + (((size_t)s * g) * n_q + j) * d;"),
+    "rpc_flush_rounded_up": ("n_flush = (current - keep) / L->G * L->G;",
+                             "n_flush = (current - keep + L->G - 1) / L->G * L->G;"),
+    "rpc_ratio_inverted": ("const int keep = (int)(((long long)current * L->rpc_permille) / 1000);",
+                           "const int keep = (int)(((long long)current * (1000 - L->rpc_permille)) / 1000);"),
     "pack_msb_first": ("*shift = bits * (c % per_word);",
                        "*shift = 32 - bits * (1 + c % per_word);"),
 }

@@ -501,3 +501,64 @@ def test_prefill_first_query_and_zero_query_closed_forms():
         p = N - n_q + j
         np.testing.assert_allclose(out0[:, :, j], np.repeat(vhat[:, None, :p + 1].mean(axis=2), g, axis=1),
                                    rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Dynamic recent-token ratio (KVmix notes, key design 3: num_RPC =
+# floor(r x current_RPC), 20 % for high-precision layers, 10 % for the rest).
+# Reading: an append that finds the recent buffer full keeps floor(r * current)
+# of its tokens in 16 bits and quantizes the older rest in whole groups.
+# ---------------------------------------------------------------------------
+
+def _rpc_states(G, R, r, Ns, cap):
+    lay = ora.Layer(1, 1, 16, 4, 2, G, R, cap, False, rpc_permille=r)
+    seen = {}
+    for n in range(1, max(Ns) + 1):
+        k = np.full((1, 1, 16), 0x3C00, np.uint16)
+        lay.append(k, k)
+        assert lay.N - lay.Tq <= R and lay.Tq % G == 0
+        if n in Ns:
+            seen[n] = (lay.Tq, lay.N - lay.Tq)
+    return seen
+
+
+def test_rpc_worked_examples():
+    # G 4, R 20, r 20 %: full at N = 20; the 21st token finds 20 recent tokens,
+    # keeps floor(0.2 * 20) = 4, quantizes 16 (four groups) -> Tq 16, Tr 5; full
+    # again 15 tokens later (N = 36) -> the 37th gives Tq 32, Tr 5; and so on.
+    assert _rpc_states(4, 20, 200, [20, 21, 36, 37, 52, 53], 64) == {
+        20: (0, 20), 21: (16, 5), 36: (16, 20), 37: (32, 5), 52: (32, 20), 53: (48, 5)}
+    # G 8, R 50, r 10 %: keep floor(5.0) = 5, quantize floor(45 / 8) = 5 groups =
+    # 40 -> Tq 40, Tr 11 at N = 51; next at N = 91 -> Tq 80, Tr 11.
+    assert _rpc_states(8, 50, 100, [50, 51, 90, 91], 96) == {50: (0, 50), 51: (40, 11), 90: (40, 50),
+                                                               91: (80, 11)}
+    # Llama-2-7B-shaped MHA layers (G 32): R 819 at 20 % keeps floor(163.8) =
+    # 163 and quantizes 20 groups (640 of 656); R 409 at 10 % keeps 40 and
+    # quantizes 11 groups (352 of 369).
+    assert _rpc_states(32, 819, 200, [819, 820], 832) == {819: (0, 819), 820: (640, 180)}
+    assert _rpc_states(32, 409, 100, [409, 410], 416) == {409: (0, 409), 410: (352, 58)}
+    # a ratio that keeps more than R - G still gives up one group
+    assert _rpc_states(8, 10, 900, [10, 11], 32) == {10: (0, 10), 11: (8, 3)}
+
+
+@pytest.mark.parametrize("kb,vb,G,R,r,N,g,bf16", [
+    (4, 2, 8, 24, 200, 100, 2, False),
+    (3, 4, 8, 30, 100, 90, 1, True),
+])
+def test_rpc_prefill_token_by_token_and_attention_on_grid(kb, vb, G, R, r, N, g, bf16):
+    """One call of N tokens equals N single appends (state bit for bit), and on
+    lossless data attention over the cache equals fp64 SDPA over the raw tokens."""
+    rng = np.random.default_rng(kb * 13 + N + r)
+    S, d = 2, 32 if kb != 3 else 64
+    kbits, vbits, K, V = grid_tokens(rng, S, N, d, G, kb, vb, bf16)
+    a = ora.Layer(S, g, d, kb, vb, G, R, N, bf16, rpc_permille=r)
+    b = ora.Layer(S, g, d, kb, vb, G, R, N, bf16, rpc_permille=r)
+    a.append(kbits, vbits)
+    for t in range(N):
+        b.append(kbits[:, t:t + 1], vbits[:, t:t + 1])
+    ea, eb = a.export(), b.export()
+    assert ea["Tq"] == eb["Tq"] > 0
+    for key in ("k_words", "k_scale", "k_zero", "v_words", "v_scale", "v_zero", "res_k", "res_v"):
+        assert np.asarray(ea[key]).tobytes() == np.asarray(eb[key]).tobytes(), key
+    q = rng.standard_normal((S, g, d))
+    np.testing.assert_allclose(a.attention(q), _sdpa64(q, K, V), rtol=1e-11, atol=1e-12)
