@@ -38,14 +38,20 @@ def stream_state_bytes(d, kb, vb, G, N, Tq, k_tok=False):
 
 
 def layer_row(lc):
-    """(kb, vb, R, per-token Key) of a layer-table row (kb, vb, R[, k_mode])."""
-    return lc[0], lc[1], lc[2], len(lc) > 3 and lc[3] == 1
+    """(kb, vb, R, per-token Key, recent-token ratio in parts per thousand) of a
+    layer-table row (kb, vb, R[, k_mode[, rpc_permille]])."""
+    return lc[0], lc[1], lc[2], len(lc) > 3 and lc[3] == 1, lc[4] if len(lc) > 4 else 0
 
 
-def quantized_count(N, R, G, kb):
+def quantized_count(N, R, G, kb, rpc=0):
+    """Tokens held as codes after N appends: a full buffer (N - Tq = R before an
+    append) gives up f tokens, f = G, or with a recent-token ratio the whole
+    groups beyond floor(R * rpc / 1000); this happens before the appends of
+    tokens R, R + f, R + 2f, ..."""
     if kb == 16 or N <= R:
         return 0
-    return G * (-(-(N - R) // G))
+    f = G if rpc == 0 else max(G, (R - R * rpc // 1000) // G * G)
+    return f * ((N - 1 - R) // f + 1)
 
 
 def step_bytes(w, N_before, qbytes):
@@ -54,15 +60,16 @@ def step_bytes(w, N_before, qbytes):
     BH = B * Hkv
     att = app = 0
     for lc in w.layers:
-        kb, vb, R, kt = layer_row(lc)
+        kb, vb, R, kt, rpc = layer_row(lc)
         N1 = N_before + 1
-        Tq0 = quantized_count(N_before, R, G, kb)
-        Tq1 = quantized_count(N1, R, G, kb)
+        Tq0 = quantized_count(N_before, R, G, kb, rpc)
+        Tq1 = quantized_count(N1, R, G, kb, rpc)
         att += BH * stream_state_bytes(d, kb, vb, G, N1, Tq1, kt) + B * Hq * d * (qbytes + 4)
         app += BH * 2 * d * 2 * 2  # read new K and V, write them to the ring
-        if Tq1 > Tq0:  # flush: read G 16-bit K/V rows, write codes and metadata
+        if Tq1 > Tq0:  # flush: read the given-up 16-bit K/V rows, write codes and metadata
             wk = (d + 10) // 11 if kb == 3 else d * kb // 32
-            app += BH * (G * 4 * d + G * 4 * (wk + d * vb // 32) + (8 * G if kt else 8 * d) + 8 * G)
+            nf = Tq1 - Tq0
+            app += BH * (nf * 4 * d + nf * 4 * (wk + d * vb // 32) + (8 * nf if kt else 8 * d * nf // G) + 8 * nf)
     return att, app
 
 
@@ -108,8 +115,8 @@ def cpu_baseline(w, seconds, layers_sample):
     cap = w.context + 4096
     layers = []
     for l in layers_sample:
-        kb, vb, R, kt = layer_row(w.layers[l])
-        o = ora.Layer(BH, g, d, kb, vb, w.G, R, cap, w.kv_dtype == "bf16", k_tok=kt)
+        kb, vb, R, kt, rpc = layer_row(w.layers[l])
+        o = ora.Layer(BH, g, d, kb, vb, w.G, R, cap, w.kv_dtype == "bf16", k_tok=kt, rpc_permille=rpc)
         k, v = synth.layer_tokens(w, l, 0, w.context, "cpu")
         o.append(synth.bits16(k.reshape(BH, w.context, d)), synth.bits16(v.reshape(BH, w.context, d)))
         layers.append((l, o))
@@ -174,8 +181,8 @@ def prefill_leg(cache, w, C, N, qbytes, rounds, stream, dev):
     flops = 4.0 * d * visible * B * Hq
     nbytes = 0
     for lc in w.layers:
-        kb, vb, R, kt = layer_row(lc)
-        nbytes += B * Hkv * stream_state_bytes(d, kb, vb, w.G, N, quantized_count(N, R, w.G, kb), kt)
+        kb, vb, R, kt, rpc = layer_row(lc)
+        nbytes += B * Hkv * stream_state_bytes(d, kb, vb, w.G, N, quantized_count(N, R, w.G, kb, rpc), kt)
     nbytes = nbytes / L + B * Hq * C * d * (qbytes + 4)
     tflops = flops / (call_us * 1e-6) / 1e12
     return {
@@ -198,6 +205,9 @@ def main():
                     help="layer table: the workload's mixed table, or uniform KV8 / KV4 baselines")
     ap.add_argument("--k-mode", default="per-channel", choices=["per-channel", "per-token"],
                     help="Key quantization: per channel over G tokens (KIVI) or per token")
+    ap.add_argument("--rpc", action="store_true",
+                    help="KVmix dynamic recent-token ratio: 20 %% on the table's higher-precision "
+                         "layers, 10 %% on the lowest-precision ones")
     ap.add_argument("--kernel-rounds", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -228,6 +238,10 @@ def main():
             print("per-token Key needs 2, 4 or 8 Key bits; this table has 3-bit layers", file=sys.stderr)
             sys.exit(2)
         w.layers = [(kb, vb, r, 1) for (kb, vb, r) in w.layers]
+    if args.rpc:
+        low = min(lc[0] + lc[1] for lc in w.layers)
+        w.layers = [(lc[0], lc[1], lc[2], lc[3] if len(lc) > 3 else 0, 200 if lc[0] + lc[1] > low else 100)
+                    for lc in w.layers]
     L, B, Hq, Hkv, d = w.n_layers, w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim
     total = args.warmup + args.steps
     qbytes = 4 if w.q_dtype == "f32" else 2
@@ -273,11 +287,11 @@ def main():
     # the state the library reports agrees with the byte model used above
     N_end = w.context + total
     for l, lc in enumerate(w.layers):
-        kb, vb, R, kt = layer_row(lc)
+        kb, vb, R, kt, rpc = layer_row(lc)
         info = cache.bytes_layer(l)
         assert info.n_tokens == N_end
         assert info.total == B * Hkv * stream_state_bytes(d, kb, vb, w.G, N_end,
-                                                         quantized_count(N_end, R, w.G, kb), kt)
+                                                         quantized_count(N_end, R, w.G, kb, rpc), kt)
 
     # dominant kernel: decode attention (one launch per call).  HIP events on
     # the stream the library launches on bracket back-to-back calls over every
@@ -320,8 +334,8 @@ def main():
     del graph
     att_per_layer = []
     for l, lc in enumerate(w.layers):
-        kb, vb, R, kt = layer_row(lc)
-        Tq = quantized_count(N_end, R, w.G, kb)
+        kb, vb, R, kt, rpc = layer_row(lc)
+        Tq = quantized_count(N_end, R, w.G, kb, rpc)
         att_per_layer.append(B * Hkv * stream_state_bytes(d, kb, vb, w.G, N_end, Tq, kt) +
                              B * Hq * d * (qbytes + 4))
     avg_att_bytes = sum(att_per_layer) / L

@@ -30,6 +30,7 @@ struct LayerState {
     kvq::LayerDev dev;
     size_t off_kw = 0, off_km = 0, off_vw = 0, off_vm = 0, off_rk = 0, off_rv = 0;
     int N = 0, Tq = 0;
+    int rpc_permille = 0;  // recent-token ratio (0: G tokens per flush)
 };
 
 struct Plan {
@@ -109,6 +110,8 @@ int plan_layout(const kvq_config *cfg, Plan *plan, std::string *err)
         if (lc.k_mode != KVQ_K_PER_CHANNEL && lc.k_mode != KVQ_K_PER_TOKEN)
             return fail(KVQ_EINVAL, "layer %d: k_mode %d is neither per-channel (0) nor per-token (1)", l,
                         lc.k_mode);
+        if (lc.rpc_permille < 0 || lc.rpc_permille >= 1000)
+            return fail(KVQ_EINVAL, "layer %d: rpc_permille %d outside [0, 1000)", l, lc.rpc_permille);
         if (lc.k_mode == KVQ_K_PER_TOKEN && lc.k_bits == 3)
             return fail(KVQ_EUNSUPPORTED, "layer %d: per-token Key needs k_bits 2, 4 or 8", l);
         LayerState &s = plan->layers[l];
@@ -118,6 +121,7 @@ int plan_layout(const kvq_config *cfg, Plan *plan, std::string *err)
         d.G = G;
         d.v_tiled = plan->v_tiled;
         d.k_tok = (lc.k_mode == KVQ_K_PER_TOKEN && lc.k_bits != 16) ? 1 : 0;
+        s.rpc_permille = lc.k_bits != 16 ? lc.rpc_permille : 0;
         if (d.kb == 16) {
             d.R = cfg->max_context;
             d.capq = G;  // unused
@@ -289,12 +293,24 @@ int kvq_append(kvq_handle *h, int layer, const void *k_new, const void *v_new, i
 
     const int N0 = s.N, N1 = s.N + n_new, Tq0 = s.Tq;
     int Tq1 = Tq0;
-    if (d.kb != 16 && N1 > d.R) {
+    if (d.kb != 16 && N1 > d.R && s.rpc_permille == 0) {
         // tokens are flushed G at a time whenever the buffer is found full
         const int over = N1 - d.R;
         Tq1 = (over + d.G - 1) / d.G * d.G;
         if (Tq1 < Tq0)
             Tq1 = Tq0;
+    } else if (d.kb != 16 && N1 > d.R) {
+        // recent-token ratio: a full buffer keeps floor(r * current) tokens and
+        // gives up the rest in whole groups (at least one); the groups given up
+        // are quantized exactly as G-token flushes, so one flush launch covers
+        // every group this append gives up
+        int n_flush = d.G;
+        const int keep = static_cast<int>(static_cast<long>(d.R) * s.rpc_permille / 1000);
+        if ((d.R - keep) / d.G * d.G > n_flush)
+            n_flush = (d.R - keep) / d.G * d.G;
+        for (int N = N0; N < N1; ++N)
+            if (N - Tq1 == d.R)
+                Tq1 += n_flush;
     }
     const int D = h->cfg.head_dim;
     const int bf16 = h->cfg.kv_dtype == KVQ_BF16;
@@ -656,6 +672,7 @@ static void layer_bytes(const kvq_handle *h, const LayerState &s, kvq_bytes_info
     info->v_bits = d.vb;
     info->residual_len = d.R;
     info->k_mode = d.k_tok ? KVQ_K_PER_TOKEN : KVQ_K_PER_CHANNEL;
+    info->rpc_permille = s.rpc_permille;
     if (d.kb == 16) {
         info->residual = BH * s.N * 4 * D;
     } else {

@@ -28,7 +28,8 @@ KVQ_K_PER_CHANNEL, KVQ_K_PER_TOKEN = 0, 1
 
 class kvq_layer_cfg(ctypes.Structure):
     _fields_ = [("k_bits", ctypes.c_int32), ("v_bits", ctypes.c_int32),
-                ("residual_len", ctypes.c_int32), ("k_mode", ctypes.c_int32)]
+                ("residual_len", ctypes.c_int32), ("k_mode", ctypes.c_int32),
+                ("rpc_permille", ctypes.c_int32)]
 
 
 class kvq_config(ctypes.Structure):
@@ -42,7 +43,8 @@ class kvq_bytes_info(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in
                 ("k_codes", "k_meta", "v_codes", "v_meta", "residual", "total")] + [
         (n, ctypes.c_int32) for n in ("n_tokens", "n_quantized", "n_residual", "k_words",
-                                      "v_words", "k_bits", "v_bits", "residual_len", "k_mode")]
+                                      "v_words", "k_bits", "v_bits", "residual_len", "k_mode",
+                                      "rpc_permille")]
 
 
 class KvqError(RuntimeError):

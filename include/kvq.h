@@ -71,6 +71,14 @@ extern "C" {
 #define KVQ_K_PER_CHANNEL 0
 #define KVQ_K_PER_TOKEN 1
 
+/* The recent-token buffer of a layer gives up, when an append finds it full,
+ * either its oldest G tokens (KIVI notes, section 6.2: rpc_permille = 0), or,
+ * with KVmix's dynamic ratio r (KVmix notes, key design 3: num_RPC =
+ * floor(r x current_RPC), 20 % for high-precision layers, 10 % for the rest),
+ * all but floor(r * current / 1000) of its current tokens, rounded down to whole
+ * groups of G and at least one group: r = rpc_permille in parts per thousand.
+ * Either way the tokens given up are quantized exactly as a G-token flush. */
+
 /* One row of the per-layer precision table.
  *   k_bits in {2, 3, 4, 8, 16}; v_bits in {2, 4, 8, 16}; 16 means the layer is
  *   not quantized and must be given as the pair (16, 16).
@@ -79,12 +87,15 @@ extern "C" {
  *   k_mode: KVQ_K_PER_CHANNEL (0) or KVQ_K_PER_TOKEN (1); per-token Key needs
  *   k_bits in {2, 4, 8} (the 3-bit layout's 2-bit slot is a per-channel
  *   format).  Ignored for (16, 16).  Both modes keep the same recent-token
- *   buffer and flush G tokens at a time. */
+ *   buffer and flush G tokens at a time.
+ *   rpc_permille: 0 (flush G tokens at a time) or a recent-token ratio in
+ *   (0, 1000) parts per thousand, see above.  Ignored for (16, 16). */
 typedef struct kvq_layer_cfg {
     int32_t k_bits;
     int32_t v_bits;
     int32_t residual_len;
     int32_t k_mode;
+    int32_t rpc_permille;
 } kvq_layer_cfg;
 
 /* Cache geometry.  All counts are >= 1.
@@ -184,6 +195,7 @@ typedef struct kvq_bytes_info {
     int32_t v_words;      /* 32-bit words per packed V row */
     int32_t k_bits, v_bits, residual_len;
     int32_t k_mode;       /* KVQ_K_PER_CHANNEL or KVQ_K_PER_TOKEN */
+    int32_t rpc_permille; /* recent-token ratio, 0 = G tokens per flush */
 } kvq_bytes_info;
 
 /* Byte breakdown and token counts of one layer (host only). */

@@ -30,9 +30,10 @@ def make_cache(w, layers=None, max_context=None):
 def make_oracle(w, layer_cfg, cap, streams=None):
     kb, vb, R = layer_cfg[:3]
     k_tok = len(layer_cfg) > 3 and layer_cfg[3] == 1
+    rpc = layer_cfg[4] if len(layer_cfg) > 4 else 0
     S = w.batch * w.n_kv_heads if streams is None else len(streams)
     return ora.Layer(S, w.g, w.head_dim, kb, vb, w.G, R if R else w.R, cap, w.kv_dtype == "bf16",
-                     k_tok=k_tok)
+                     k_tok=k_tok, rpc_permille=rpc)
 
 
 def stream_view(t, streams=None):

@@ -34,6 +34,22 @@ def _cfg(**kw):
     return kvq.make_config(**base)
 
 
+def test_recent_ratio_validation():
+    """rpc_permille must lie in [0, 1000); bytes_layer reports it."""
+    for bad in (-1, 1000, 5000):
+        assert kvq.kvq_workspace_bytes(_cfg(layers=[(4, 2, 0, 0, bad), (8, 4, 64)])) == 0
+        assert "rpc_permille" in kvq.kvq_last_error()
+    cfg = _cfg(layers=[(4, 2, 0, 0, 200), (8, 4, 64, 0, 999)])
+    n = kvq.kvq_workspace_bytes(cfg)
+    assert n > 0
+    h = kvq.kvq_create(cfg, ctypes.c_void_p(1 << 20), n)
+    try:
+        assert kvq.kvq_bytes_layer(h, 0).rpc_permille == 200
+        assert kvq.kvq_bytes_layer(h, 1).rpc_permille == 999
+    finally:
+        kvq.kvq_destroy(h)
+
+
 def test_workspace_bytes_valid_and_invalid():
     n = kvq.kvq_workspace_bytes(_cfg())
     assert n > 0 and n % kvq.KVQ_WORKSPACE_ALIGN == 0
