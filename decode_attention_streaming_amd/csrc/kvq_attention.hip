@@ -6,9 +6,9 @@
 
 namespace kvq {
 
-hipError_t launch_mfma_d64(const AttnArgs &a, hipStream_t st);
-hipError_t launch_mfma_d128(const AttnArgs &a, hipStream_t st);
-hipError_t launch_mfma_d256(const AttnArgs &a, hipStream_t st);
+hipError_t launch_mfma_d64(const AttnArgs &a, const RaggedTables *rt, hipStream_t st);
+hipError_t launch_mfma_d128(const AttnArgs &a, const RaggedTables *rt, hipStream_t st);
+hipError_t launch_mfma_d256(const AttnArgs &a, const RaggedTables *rt, hipStream_t st);
 hipError_t launch_prefill_d64(const PrefillArgs &a, hipStream_t st);
 hipError_t launch_prefill_d128(const PrefillArgs &a, hipStream_t st);
 hipError_t launch_prefill_d256(const PrefillArgs &a, hipStream_t st);
@@ -16,29 +16,52 @@ hipError_t launch_prefill_d256(const PrefillArgs &a, hipStream_t st);
 namespace {
 
 template <int D, int GM>
-__global__ __launch_bounds__(kAttnThreads) void attn_valu_kernel(AttnArgs a)
+__device__ __forceinline__ void attn_valu_body(const AttnArgs &a, const RaggedTables *rt)
 {
     const int split = blockIdx.x, bh = blockIdx.y;
     const int t_beg = a.valu_beg + split * a.valu_tps;
-    const int t_end = min(a.N, t_beg + a.valu_tps);
+    const int t_end = min(stream_dims(a, rt, bh).N, t_beg + a.valu_tps);
     extern __shared__ float smem[];
-    valu_range<D, GM>(a, bh, t_beg, t_end, split, smem);
+    valu_range<D, GM>(a, rt, bh, t_beg, t_end, split, smem);
     arrive_and_merge<D>(a, bh, gridDim.x);
 }
 
+template <int D, int GM>
+__global__ __launch_bounds__(kAttnThreads) void attn_valu_kernel(AttnArgs a)
+{
+    attn_valu_body<D, GM>(a, nullptr);
+}
+
+template <int D, int GM>
+__global__ __launch_bounds__(kAttnThreads) void attn_valu_kernel_rg(RaggedAttnArgs r)
+{
+    attn_valu_body<D, GM>(r.a, &r.t);
+}
+
+template <int D, int GM>
+void launch_valu_g(const AttnArgs &a, const RaggedTables *rt, dim3 grid, size_t lds, hipStream_t st)
+{
+    if (rt) {
+        const RaggedAttnArgs r{a, *rt};
+        hipLaunchKernelGGL((attn_valu_kernel_rg<D, GM>), grid, dim3(kAttnThreads), lds, st, r);
+    } else {
+        hipLaunchKernelGGL((attn_valu_kernel<D, GM>), grid, dim3(kAttnThreads), lds, st, a);
+    }
+}
+
 template <int D>
-void launch_valu(const AttnArgs &a, dim3 grid, size_t lds, hipStream_t st)
+void launch_valu(const AttnArgs &a, const RaggedTables *rt, dim3 grid, size_t lds, hipStream_t st)
 {
     if (a.g <= 1)
-        hipLaunchKernelGGL((attn_valu_kernel<D, 1>), grid, dim3(kAttnThreads), lds, st, a);
+        launch_valu_g<D, 1>(a, rt, grid, lds, st);
     else if (a.g <= 2)
-        hipLaunchKernelGGL((attn_valu_kernel<D, 2>), grid, dim3(kAttnThreads), lds, st, a);
+        launch_valu_g<D, 2>(a, rt, grid, lds, st);
     else if (a.g <= 4)
-        hipLaunchKernelGGL((attn_valu_kernel<D, 4>), grid, dim3(kAttnThreads), lds, st, a);
+        launch_valu_g<D, 4>(a, rt, grid, lds, st);
     else if (a.g <= 8)
-        hipLaunchKernelGGL((attn_valu_kernel<D, 8>), grid, dim3(kAttnThreads), lds, st, a);
+        launch_valu_g<D, 8>(a, rt, grid, lds, st);
     else
-        hipLaunchKernelGGL((attn_valu_kernel<D, 16>), grid, dim3(kAttnThreads), lds, st, a);
+        launch_valu_g<D, 16>(a, rt, grid, lds, st);
 }
 
 }  // namespace
@@ -82,24 +105,24 @@ static AttnArgs as_plain(const AttnArgs &a)
     return b;
 }
 
-hipError_t launch_attention(const AttnArgs &a, bool use_mfma, hipStream_t st)
+hipError_t launch_attention(const AttnArgs &a, const RaggedTables *rt, bool use_mfma, hipStream_t st)
 {
     if (use_mfma) {
         const AttnArgs b = as_plain(a);
         if (a.D == 64)
-            return launch_mfma_d64(b, st);
+            return launch_mfma_d64(b, rt, st);
         if (a.D == 128)
-            return launch_mfma_d128(b, st);
-        return launch_mfma_d256(b, st);
+            return launch_mfma_d128(b, rt, st);
+        return launch_mfma_d256(b, rt, st);
     }
     dim3 grid(a.valu_wgs, a.BH);
     const size_t lds = valu_lds_bytes(a.g, a.D);
     if (a.D == 64)
-        launch_valu<64>(a, grid, lds, st);
+        launch_valu<64>(a, rt, grid, lds, st);
     else if (a.D == 128)
-        launch_valu<128>(a, grid, lds, st);
+        launch_valu<128>(a, rt, grid, lds, st);
     else
-        launch_valu<256>(a, grid, lds, st);
+        launch_valu<256>(a, rt, grid, lds, st);
     return hipGetLastError();
 }
 

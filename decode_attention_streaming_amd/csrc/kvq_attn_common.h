@@ -66,6 +66,21 @@ struct PartBuf {
     }
 };
 
+// Lengths of stream bh: those of the launch, or, for a ragged batch, those of
+// the stream's sequence from the launch's tables.
+struct StreamDims {
+    int N, Tq, unit_groups, unit_extra, new_t;
+};
+
+__device__ __forceinline__ StreamDims stream_dims(const AttnArgs &a, const RaggedTables *rt, int bh)
+{
+    if (rt) {
+        const int b = bh / a.Hkv;
+        return StreamDims{rt->N[b], rt->Tq[b], rt->unit_groups[b], rt->unit_extra[b], rt->new_t[b]};
+    }
+    return StreamDims{a.N, a.Tq, a.unit_groups, a.unit_extra, a.new_t};
+}
+
 __device__ __forceinline__ float widen16(uint16_t x, int bf16)
 {
     if (bf16)
@@ -247,7 +262,8 @@ __device__ __forceinline__ void stage_q(const AttnArgs &a, int b, int kvh, float
 // folded into the weight, sum_t p_t (c_t s_t + z_t) = sum_t (p_t s_t) c_t +
 // sum_t p_t z_t.
 template <int D, int GM>
-__device__ void valu_range(const AttnArgs &a, int bh, int t_beg, int t_end, int slot, float *smem)
+__device__ void valu_range(const AttnArgs &a, const RaggedTables *rt, int bh, int t_beg, int t_end, int slot,
+                           float *smem)
 {
     constexpr int TT = valu_tile<D>();
     constexpr int P = kAttnThreads / TT;  // threads per token in the score phase
@@ -265,6 +281,7 @@ __device__ void valu_range(const AttnArgs &a, int bh, int t_beg, int t_end, int 
     const int b = bh / a.Hkv, kvh = bh % a.Hkv;
     const LayerDev &L = a.L;
     const int bf = a.kv_bf16;
+    const StreamDims sd = stream_dims(a, rt, bh);
 
     stage_q(a, b, kvh, q_lds);
 
@@ -280,8 +297,8 @@ __device__ void valu_range(const AttnArgs &a, int bh, int t_beg, int t_end, int 
     const int ngcap = L.capq / L.G;
     const size_t row0 = static_cast<size_t>(bh) * L.capq;
     for (int tile = t_beg; tile < t_end;) {
-        const bool quant = tile < a.Tq;
-        const int tend = min(min(tile + TT, t_end), quant ? a.Tq : t_end);
+        const bool quant = tile < sd.Tq;
+        const int tend = min(min(tile + TT, t_end), quant ? sd.Tq : t_end);
         const int nt = tend - tile;
         __syncthreads();  // previous tile's LDS reads are done (and q is staged)
         if (quant) {
@@ -289,9 +306,9 @@ __device__ void valu_range(const AttnArgs &a, int bh, int t_beg, int t_end, int 
             stage_words<4>(v_tile, L.v_words + (row0 + tile) * L.wv, nt * L.wv);
         } else {
             stage_ring<D, 4>(reinterpret_cast<uint16_t *>(k_tile), L.ring_k + static_cast<size_t>(bh) * L.R * D,
-                             L.R, tile, nt, a.new_k + static_cast<size_t>(bh) * D, a.new_t);
+                             L.R, tile, nt, a.new_k + static_cast<size_t>(bh) * D, sd.new_t);
             stage_ring<D, 4>(reinterpret_cast<uint16_t *>(v_tile), L.ring_v + static_cast<size_t>(bh) * L.R * D,
-                             L.R, tile, nt, a.new_v + static_cast<size_t>(bh) * D, a.new_t);
+                             L.R, tile, nt, a.new_v + static_cast<size_t>(bh) * D, sd.new_t);
         }
         // per-thread metadata while the tile lands
         const int ti = tid / P, part = tid % P, c0 = part * CPT;

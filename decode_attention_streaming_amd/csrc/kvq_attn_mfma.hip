@@ -83,7 +83,8 @@ struct RoundData {
 // weights enter only its own block's product (zeros elsewhere).
 // Results for head h < g go to po[h * D + c], pm[h], pl[h] (LDS).
 template <int KB, int VB, int D, bool KT>
-__device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *po, float *pm, float *pl,
+__device__ void mfma_unit(const AttnArgs &a, const RaggedTables *rt, int bh, int unit, int lane, float *po, float *pm,
+                          float *pl,
                           float *meta_lds)
 {
     constexpr int QC = D / 4;           // channels owned by one lane quad (2, 4, 8 bits)
@@ -107,9 +108,9 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *
     const bool used = (col & (S - 1)) < g;
     const int h = used ? (col & (S - 1)) : 0;
     const int jslot = used ? (col >> a.s_log2) : NG;
-    const int n_groups = a.n_groups;
-    const int g_beg = unit * a.unit_groups + min(unit, a.unit_extra);
-    const int g_end = g_beg + a.unit_groups + (unit < a.unit_extra ? 1 : 0);
+    const StreamDims sd = stream_dims(a, rt, bh);
+    const int g_beg = unit * sd.unit_groups + min(unit, sd.unit_extra);
+    const int g_end = g_beg + sd.unit_groups + (unit < sd.unit_extra ? 1 : 0);
     const int bpg = G / 32;  // blocks per group
 
     const uint32_t *kw_base = L.k_words + static_cast<size_t>(bh) * L.capq * L.wk + q * KW;
@@ -437,8 +438,8 @@ __device__ void mfma_unit(const AttnArgs &a, int bh, int unit, int lane, float *
 // ([channel][token]) so that each lane's operand (eight tokens of one channel)
 // is two 8-byte LDS reads.
 template <int D, bool BF>
-__device__ void mfma_residual_unit(const AttnArgs &a, int bh, int runit, int lane, float *po, float *pm,
-                                   float *pl)
+__device__ void mfma_residual_unit(const AttnArgs &a, const RaggedTables *rt, int bh, int runit, int lane, float *po,
+                                   float *pm, float *pl)
 {
     constexpr int NC = D / 32;
     constexpr int MT = D / 16;
@@ -448,13 +449,14 @@ __device__ void mfma_residual_unit(const AttnArgs &a, int bh, int runit, int lan
     const bool act = col < g;
     const int h = act ? col : 0;
     constexpr bool bf = BF;  // bfloat16 recent tokens (instantiated per dtype: no branches)
-    const int t_beg = a.Tq + runit * a.res_tokens;
-    const int t_end = min(a.N, t_beg + a.res_tokens);
+    const StreamDims sd = stream_dims(a, rt, bh);
+    const int t_beg = sd.Tq + runit * a.res_tokens;
+    const int t_end = min(sd.N, t_beg + a.res_tokens);
     uint16_t *vt = reinterpret_cast<uint16_t *>(po);  // [D][32] tile, then the results
     uint16_t *rk = L.ring_k + static_cast<size_t>(bh) * L.R * D;
     uint16_t *rv = L.ring_v + static_cast<size_t>(bh) * L.R * D;
     // row of token t: the ring, or the just-appended token's own row
-    const int new_t = a.new_t;
+    const int new_t = sd.new_t;
     auto k_row = [&](int t) {
         return (t == new_t) ? a.new_k + static_cast<size_t>(bh) * D : rk + static_cast<size_t>(t % L.R) * D;
     };
@@ -648,7 +650,7 @@ __host__ __device__ inline int wave_region(const AttnArgs &a)
 }
 
 template <int KB, int VB, int D, bool KT>
-__global__ __launch_bounds__(kAttnThreads, (mfma_waves_per_simd<KB, VB>())) void attn_mfma_kernel(AttnArgs a)
+__device__ __forceinline__ void attn_mfma_body(const AttnArgs &a, const RaggedTables *rt)
 {
     extern __shared__ float lds[];
     __shared__ float s_pm[kAttnThreads / 64][kMaxG], s_pl[kAttnThreads / 64][kMaxG];
@@ -659,12 +661,12 @@ __global__ __launch_bounds__(kAttnThreads, (mfma_waves_per_simd<KB, VB>())) void
     const int region = wave_region(a);
     float *po = lds + wave * region;
     if (unit < a.units_q) {
-        mfma_unit<KB, VB, D, KT>(a, bh, unit, lane, po, s_pm[wave], s_pl[wave], po);
+        mfma_unit<KB, VB, D, KT>(a, rt, bh, unit, lane, po, s_pm[wave], s_pl[wave], po);
     } else if (unit < a.units_q + a.units_r) {
         if (a.kv_bf16)
-            mfma_residual_unit<D, true>(a, bh, unit - a.units_q, lane, po, s_pm[wave], s_pl[wave]);
+            mfma_residual_unit<D, true>(a, rt, bh, unit - a.units_q, lane, po, s_pm[wave], s_pl[wave]);
         else
-            mfma_residual_unit<D, false>(a, bh, unit - a.units_q, lane, po, s_pm[wave], s_pl[wave]);
+            mfma_residual_unit<D, false>(a, rt, bh, unit - a.units_q, lane, po, s_pm[wave], s_pl[wave]);
     } else if (lane < a.g) {
         s_pm[wave][lane] = -INFINITY;
         s_pl[wave][lane] = 0.0f;
@@ -674,12 +676,31 @@ __global__ __launch_bounds__(kAttnThreads, (mfma_waves_per_simd<KB, VB>())) void
     arrive_and_merge<D>(a, bh, gridDim.x);
 }
 
+template <int KB, int VB, int D, bool KT>
+__global__ __launch_bounds__(kAttnThreads, (mfma_waves_per_simd<KB, VB>())) void attn_mfma_kernel(AttnArgs a)
+{
+    attn_mfma_body<KB, VB, D, KT>(a, nullptr);
+}
+
+// ragged batches: per-sequence lengths in the argument block
+template <int KB, int VB, int D, bool KT>
+__global__ __launch_bounds__(kAttnThreads, (mfma_waves_per_simd<KB, VB>())) void attn_mfma_kernel_rg(
+    RaggedAttnArgs r)
+{
+    attn_mfma_body<KB, VB, D, KT>(r.a, &r.t);
+}
+
 template <int KB, int VB, bool KT>
-hipError_t launch_pair(const AttnArgs &a, hipStream_t st)
+hipError_t launch_pair(const AttnArgs &a, const RaggedTables *rt, hipStream_t st)
 {
     dim3 grid(a.mfma_wgs, a.BH);
     const size_t lds = (kAttnThreads / 64) * wave_region(a) * sizeof(float);
-    hipLaunchKernelGGL((attn_mfma_kernel<KB, VB, KVQ_D, KT>), grid, dim3(kAttnThreads), lds, st, a);
+    if (rt) {
+        const RaggedAttnArgs r{a, *rt};
+        hipLaunchKernelGGL((attn_mfma_kernel_rg<KB, VB, KVQ_D, KT>), grid, dim3(kAttnThreads), lds, st, r);
+    } else {
+        hipLaunchKernelGGL((attn_mfma_kernel<KB, VB, KVQ_D, KT>), grid, dim3(kAttnThreads), lds, st, a);
+    }
     return hipGetLastError();
 }
 
@@ -688,21 +709,21 @@ hipError_t launch_pair(const AttnArgs &a, hipStream_t st)
 #define KVQ_CAT2(x, y) x##y
 #define KVQ_CAT(x, y) KVQ_CAT2(x, y)
 
-hipError_t KVQ_CAT(launch_mfma_d, KVQ_D)(const AttnArgs &a, hipStream_t st)
+hipError_t KVQ_CAT(launch_mfma_d, KVQ_D)(const AttnArgs &a, const RaggedTables *rt, hipStream_t st)
 {
     const int kb = a.L.kb, vb = a.L.vb;
 #define KVQ_PAIR(K, V)                                                        \
     if (kb == K && vb == V)                                                   \
-        return a.L.k_tok ? launch_pair<K, V, true>(a, st) : launch_pair<K, V, false>(a, st);
+        return a.L.k_tok ? launch_pair<K, V, true>(a, rt, st) : launch_pair<K, V, false>(a, rt, st);
     KVQ_PAIR(2, 2) KVQ_PAIR(2, 4) KVQ_PAIR(2, 8)
     KVQ_PAIR(4, 2) KVQ_PAIR(4, 4) KVQ_PAIR(4, 8)
     KVQ_PAIR(8, 2) KVQ_PAIR(8, 4) KVQ_PAIR(8, 8)
 #if KVQ_D == 128
     // 3-bit rows: twelve words, three per lane quad (head_dim 256 would need
     // more registers than two waves per SIMD leave)
-    if (kb == 3 && vb == 2) return launch_pair<3, 2, false>(a, st);
-    if (kb == 3 && vb == 4) return launch_pair<3, 4, false>(a, st);
-    if (kb == 3 && vb == 8) return launch_pair<3, 8, false>(a, st);
+    if (kb == 3 && vb == 2) return launch_pair<3, 2, false>(a, rt, st);
+    if (kb == 3 && vb == 4) return launch_pair<3, 4, false>(a, rt, st);
+    if (kb == 3 && vb == 8) return launch_pair<3, 8, false>(a, rt, st);
 #endif
 #undef KVQ_PAIR
     return hipErrorInvalidValue;

@@ -54,6 +54,9 @@ struct RingArgs {
     int D, n_new, N0, t_first, t_last, BH;
 };
 
+// Sequences one attention launch can take with lengths of their own.
+constexpr int kMaxRaggedSeqs = 64;
+
 struct AttnArgs {
     LayerDev L;
     const void *q;        // [B][Hq][D] in q_dtype
@@ -81,6 +84,22 @@ struct AttnArgs {
     // workgroup that attends to it; new_t = -1 when there is none
     const uint16_t *new_k, *new_v;
     int new_t;
+};
+
+// Ragged batches (sequences of different lengths): the streams of sequence b
+// (bh / Hkv == b) take N, Tq, new_t and their split of the quantized groups
+// over the launch's units_q units (unit_groups, unit_extra) from entry b; the
+// launch's own fields hold the sizes it is shaped for.  Passed by value to
+// separate kernel instantiations, so that uniform launches keep their small
+// argument block.
+struct RaggedTables {
+    int N[kMaxRaggedSeqs], Tq[kMaxRaggedSeqs], unit_groups[kMaxRaggedSeqs], unit_extra[kMaxRaggedSeqs],
+        new_t[kMaxRaggedSeqs];
+};
+
+struct RaggedAttnArgs {
+    AttnArgs a;
+    RaggedTables t;
 };
 
 // Causal attention of the queries of the last n_q appended tokens (a prefill
@@ -129,7 +148,8 @@ hipError_t launch_flush(const FlushArgs &a, hipStream_t st);
 hipError_t launch_ring_write(const RingArgs &a, hipStream_t st);
 // True when the matrix-core kernel is built for this (k_bits, v_bits, D).
 bool mfma_supported(int kb, int vb, int D);
-hipError_t launch_attention(const AttnArgs &a, bool use_mfma, hipStream_t st);
+// rt: per-sequence lengths of a ragged batch, or nullptr
+hipError_t launch_attention(const AttnArgs &a, const RaggedTables *rt, bool use_mfma, hipStream_t st);
 hipError_t launch_zero(unsigned *p, int n, hipStream_t st);
 // True when the prefill kernel is built for this layer format.
 bool prefill_supported(int kb, int vb, int D, int v_tiled);

@@ -29,9 +29,52 @@ constexpr int kMaxTileElems = 16384;  // group_size * head_dim staged by the flu
 struct LayerState {
     kvq::LayerDev dev;
     size_t off_kw = 0, off_km = 0, off_vw = 0, off_vm = 0, off_rk = 0, off_rv = 0;
-    int N = 0, Tq = 0;
+    int N = 0, Tq = 0;     // tokens appended and quantized, when every sequence has as many
     int rpc_permille = 0;  // recent-token ratio (0: G tokens per flush)
+    // per sequence: tokens appended and quantized; ragged when they differ
+    // (N and Tq above are then those of the longest sequence)
+    std::vector<int> seqN, seqTq;
+    bool ragged = false;
 };
+
+// Tokens quantized after n appends to a stream holding N0 tokens, Tq0 of them
+// quantized: before each token enters, a full recent buffer (R tokens) gives
+// up its oldest G tokens, or, with a recent-token ratio r, all but
+// floor(r * R) of them in whole groups (at least one group).
+int tq_after(const kvq::LayerDev &d, int rpc_permille, int N0, int Tq0, int n)
+{
+    int Tq1 = Tq0;
+    if (d.kb == 16 || N0 + n <= d.R)
+        return Tq1;
+    if (rpc_permille == 0) {
+        Tq1 = (N0 + n - d.R + d.G - 1) / d.G * d.G;
+        return Tq1 < Tq0 ? Tq0 : Tq1;
+    }
+    int n_flush = d.G;
+    const int keep = static_cast<int>(static_cast<long>(d.R) * rpc_permille / 1000);
+    if ((d.R - keep) / d.G * d.G > n_flush)
+        n_flush = (d.R - keep) / d.G * d.G;
+    for (int N = N0; N < N0 + n; ++N)
+        if (N - Tq1 == d.R)
+            Tq1 += n_flush;
+    return Tq1;
+}
+
+// View of streams [s0, ...) of a layer as a layer of its own.
+kvq::LayerDev sub_layer(const kvq::LayerDev &d, int s0, int D)
+{
+    kvq::LayerDev v = d;
+    const size_t S = static_cast<size_t>(s0);
+    if (d.kb != 16) {
+        v.k_words += S * d.capq * d.wk;
+        v.k_meta += d.k_tok ? S * d.capq * 2 : S * (d.capq / d.G) * 2 * D;
+        v.v_words += S * d.capq * d.wv;
+        v.v_meta += S * d.capq * 2;
+    }
+    v.ring_k += S * d.R * D;
+    v.ring_v += S * d.R * D;
+    return v;
+}
 
 struct Plan {
     std::vector<LayerState> layers;
@@ -115,6 +158,8 @@ int plan_layout(const kvq_config *cfg, Plan *plan, std::string *err)
         if (lc.k_mode == KVQ_K_PER_TOKEN && lc.k_bits == 3)
             return fail(KVQ_EUNSUPPORTED, "layer %d: per-token Key needs k_bits 2, 4 or 8", l);
         LayerState &s = plan->layers[l];
+        s.seqN.assign(cfg->batch, 0);
+        s.seqTq.assign(cfg->batch, 0);
         kvq::LayerDev &d = s.dev;
         d.kb = lc.k_bits;
         d.vb = lc.v_bits;
@@ -271,6 +316,12 @@ int kvq_create(const kvq_config *cfg, void *workspace, size_t ws_bytes, kvq_hand
     return KVQ_OK;
 }
 
+static int append_streams(kvq_handle *h, const kvq::LayerDev &dl, int s0, int nbh, const void *k_new,
+                          const void *v_new, int stride, int n, int N0, int Tq0, int rpc_permille, int *Tq_out);
+static int append_sequences(kvq_handle *h, int layer, const void *k_new, const void *v_new, const int32_t *n_new,
+                            int n_max);
+static void refresh_lengths(LayerState &s);
+
 int kvq_append(kvq_handle *h, int layer, const void *k_new, const void *v_new, int n_new)
 {
     if (!h)
@@ -286,48 +337,53 @@ int kvq_append(kvq_handle *h, int layer, const void *k_new, const void *v_new, i
     if (reinterpret_cast<uintptr_t>(k_new) % 16 || reinterpret_cast<uintptr_t>(v_new) % 16)
         return h->fail(KVQ_EINVAL, "k_new and v_new must be 16-byte aligned");
     LayerState &s = h->plan.layers[layer];
-    kvq::LayerDev &d = s.dev;
+    const kvq::LayerDev &d = s.dev;
     if (static_cast<long>(s.N) + n_new > h->cfg.max_context)
         return h->fail(KVQ_ECAPACITY, "layer %d: %d + %d tokens exceed max_context %d", layer, s.N, n_new,
                        h->cfg.max_context);
 
-    const int N0 = s.N, N1 = s.N + n_new, Tq0 = s.Tq;
-    int Tq1 = Tq0;
-    if (d.kb != 16 && N1 > d.R && s.rpc_permille == 0) {
-        // tokens are flushed G at a time whenever the buffer is found full
-        const int over = N1 - d.R;
-        Tq1 = (over + d.G - 1) / d.G * d.G;
-        if (Tq1 < Tq0)
-            Tq1 = Tq0;
-    } else if (d.kb != 16 && N1 > d.R) {
-        // recent-token ratio: a full buffer keeps floor(r * current) tokens and
-        // gives up the rest in whole groups (at least one); the groups given up
-        // are quantized exactly as G-token flushes, so one flush launch covers
-        // every group this append gives up
-        int n_flush = d.G;
-        const int keep = static_cast<int>(static_cast<long>(d.R) * s.rpc_permille / 1000);
-        if ((d.R - keep) / d.G * d.G > n_flush)
-            n_flush = (d.R - keep) / d.G * d.G;
-        for (int N = N0; N < N1; ++N)
-            if (N - Tq1 == d.R)
-                Tq1 += n_flush;
+    if (!s.ragged) {
+        int Tq1 = 0;
+        const int rc = append_streams(h, d, 0, h->BH(), k_new, v_new, n_new, n_new, s.N, s.Tq, s.rpc_permille,
+                                      &Tq1);
+        if (rc != KVQ_OK)
+            return rc;
+        s.N += n_new;
+        s.Tq = Tq1;
+        s.seqN.assign(h->cfg.batch, s.N);
+        s.seqTq.assign(h->cfg.batch, s.Tq);
+        return KVQ_OK;
     }
+    std::vector<int> n(h->cfg.batch, n_new);
+    return append_sequences(h, layer, k_new, v_new, n.data(), n_new);
+}
+
+// Append n tokens to streams [s0, s0 + nbh) of a layer, all holding N0 tokens
+// of which Tq0 are quantized: one flush launch for every group the appends
+// give up, then the ring write of the tokens that stay recent.  New tokens of
+// stream i are rows [i][0 .. n) of [nbh][stride][D].
+static int append_streams(kvq_handle *h, const kvq::LayerDev &dl, int s0, int nbh, const void *k_new,
+                          const void *v_new, int stride, int n, int N0, int Tq0, int rpc_permille, int *Tq_out)
+{
     const int D = h->cfg.head_dim;
+    const kvq::LayerDev d = s0 == 0 ? dl : sub_layer(dl, s0, D);
+    const int N1 = N0 + n;
+    const int Tq1 = tq_after(d, rpc_permille, N0, Tq0, n);
     const int bf16 = h->cfg.kv_dtype == KVQ_BF16;
     hipError_t e;
     const int t_first = Tq1 > N0 ? Tq1 : N0;
-    const bool fuse_ring = Tq1 > Tq0 && n_new == 1 && N1 > t_first;
+    const bool fuse_ring = Tq1 > Tq0 && n == 1 && N1 > t_first;
     if (Tq1 > Tq0) {
         kvq::FlushArgs fa;
         fa.L = d;
         fa.k_new = static_cast<const uint16_t *>(k_new);
         fa.v_new = static_cast<const uint16_t *>(v_new);
         fa.D = D;
-        fa.n_new = n_new;
+        fa.n_new = stride;
         fa.N0 = N0;
         fa.Tq0 = Tq0;
         fa.n_groups = (Tq1 - Tq0) / d.G;
-        fa.BH = h->BH();
+        fa.BH = nbh;
         fa.kv_bf16 = bf16;
         fa.ring_after = fuse_ring ? 1 : 0;
         e = kvq::launch_flush(fa, h->stream);
@@ -340,20 +396,110 @@ int kvq_append(kvq_handle *h, int layer, const void *k_new, const void *v_new, i
         ra.k_new = static_cast<const uint16_t *>(k_new);
         ra.v_new = static_cast<const uint16_t *>(v_new);
         ra.D = D;
-        ra.n_new = n_new;
+        ra.n_new = stride;
         ra.N0 = N0;
         ra.t_first = t_first;
         ra.t_last = N1;
-        ra.BH = h->BH();
+        ra.BH = nbh;
         e = kvq::launch_ring_write(ra, h->stream);
         if (e != hipSuccess)
             return h->dev_fail(e, "ring write launch");
     }
-    s.N = N1;
-    s.Tq = Tq1;
+    *Tq_out = Tq1;
     h->touched = true;
     return KVQ_OK;
 }
+
+// Sequence b appends n_new[b] tokens, rows [b][h][0 .. n_new[b]) of
+// [batch][n_kv_heads][n_max][D]; one flush / ring launch per sequence that
+// appends.  Arguments are already checked.
+static int append_sequences(kvq_handle *h, int layer, const void *k_new, const void *v_new, const int32_t *n_new,
+                            int n_max)
+{
+    LayerState &s = h->plan.layers[layer];
+    const int Hkv = h->cfg.n_kv_heads, D = h->cfg.head_dim;
+    const size_t seq_elems = static_cast<size_t>(Hkv) * n_max * D;
+    for (int b = 0; b < h->cfg.batch; ++b) {
+        if (n_new[b] == 0)
+            continue;
+        int Tq1 = 0;
+        const int rc = append_streams(h, s.dev, b * Hkv, Hkv, static_cast<const uint16_t *>(k_new) + b * seq_elems,
+                                      static_cast<const uint16_t *>(v_new) + b * seq_elems, n_max, n_new[b], s.seqN[b],
+                                      s.seqTq[b], s.rpc_permille, &Tq1);
+        if (rc != KVQ_OK)
+            return rc;
+        s.seqN[b] += n_new[b];
+        s.seqTq[b] = Tq1;
+    }
+    refresh_lengths(s);
+    return KVQ_OK;
+}
+
+// Uniform view of the per-sequence lengths: ragged when they differ; N and Tq
+// are those of the longest sequence.
+static void refresh_lengths(LayerState &s)
+{
+    int b_max = 0;
+    s.ragged = false;
+    for (size_t b = 0; b < s.seqN.size(); ++b) {
+        if (s.seqN[b] != s.seqN[0])
+            s.ragged = true;
+        if (s.seqN[b] > s.seqN[b_max])
+            b_max = static_cast<int>(b);
+    }
+    s.N = s.seqN[b_max];
+    s.Tq = s.seqTq[b_max];
+}
+
+int kvq_append_ragged(kvq_handle *h, int layer, const void *k_new, const void *v_new, const int32_t *n_new,
+                      int n_max)
+{
+    if (!h)
+        return KVQ_EINVAL;
+    if (layer < 0 || layer >= h->cfg.n_layers)
+        return h->fail(KVQ_EINVAL, "layer %d out of range [0, %d)", layer, h->cfg.n_layers);
+    if (!n_new)
+        return h->fail(KVQ_EINVAL, "n_new is NULL");
+    if (n_max < 0)
+        return h->fail(KVQ_EINVAL, "n_max = %d < 0", n_max);
+    LayerState &s = h->plan.layers[layer];
+    bool any = false, equal = true;
+    for (int b = 0; b < h->cfg.batch; ++b) {
+        if (n_new[b] < 0 || n_new[b] > n_max)
+            return h->fail(KVQ_EINVAL, "n_new[%d] = %d outside [0, n_max = %d]", b, n_new[b], n_max);
+        if (static_cast<long>(s.seqN[b]) + n_new[b] > h->cfg.max_context)
+            return h->fail(KVQ_ECAPACITY, "layer %d, sequence %d: %d + %d tokens exceed max_context %d", layer, b,
+                           s.seqN[b], n_new[b], h->cfg.max_context);
+        any = any || n_new[b] > 0;
+        equal = equal && n_new[b] == n_max;
+    }
+    if (!any)
+        return KVQ_OK;
+    if (!k_new || !v_new)
+        return h->fail(KVQ_EINVAL, "k_new or v_new is NULL");
+    if (reinterpret_cast<uintptr_t>(k_new) % 16 || reinterpret_cast<uintptr_t>(v_new) % 16)
+        return h->fail(KVQ_EINVAL, "k_new and v_new must be 16-byte aligned");
+    if (equal && !s.ragged)
+        return kvq_append(h, layer, k_new, v_new, n_max);
+    return append_sequences(h, layer, k_new, v_new, n_new, n_max);
+}
+
+int kvq_sequence_lengths(const kvq_handle *h, int layer, int32_t *n_tokens, int32_t *n_quantized)
+{
+    if (!h)
+        return KVQ_EINVAL;
+    if (layer < 0 || layer >= h->cfg.n_layers)
+        return const_cast<kvq_handle *>(h)->fail(KVQ_EINVAL, "layer %d out of range", layer);
+    const LayerState &s = h->plan.layers[layer];
+    for (int b = 0; b < h->cfg.batch; ++b) {
+        if (n_tokens)
+            n_tokens[b] = s.seqN[b];
+        if (n_quantized)
+            n_quantized[b] = s.seqTq[b];
+    }
+    return KVQ_OK;
+}
+
 
 // Arguments of a decode-attention call, checked before any state changes.
 static int check_attention_args(kvq_handle *h, int layer, const void *q, const float *out)
@@ -371,7 +517,7 @@ static int check_attention_args(kvq_handle *h, int layer, const void *q, const f
 // new_t was appended but is not in the ring yet (its rows are new_k / new_v);
 // the launch also stores it there.
 static int attention_launch(kvq_handle *h, int layer, const void *q, float *out, const void *new_k,
-                            const void *new_v, int new_t);
+                            const void *new_v, int new_t, const int *seq_new_t = nullptr);
 
 int kvq_decode_attention(kvq_handle *h, int layer, const void *q, float *out)
 {
@@ -380,8 +526,10 @@ int kvq_decode_attention(kvq_handle *h, int layer, const void *q, float *out)
     const int rc = check_attention_args(h, layer, q, out);
     if (rc != KVQ_OK)
         return rc;
-    if (h->plan.layers[layer].N == 0)
-        return h->fail(KVQ_EINVAL, "layer %d holds no tokens", layer);
+    const LayerState &s = h->plan.layers[layer];
+    for (int b = 0; b < h->cfg.batch; ++b)
+        if (s.seqN[b] == 0)
+            return h->fail(KVQ_EINVAL, "layer %d holds no tokens for sequence %d", layer, b);
     return attention_launch(h, layer, q, out, nullptr, nullptr, -1);
 }
 
@@ -402,6 +550,32 @@ int kvq_append_decode_attention(kvq_handle *h, int layer, const void *k_new, con
     if (static_cast<long>(s.N) + 1 > h->cfg.max_context)
         return h->fail(KVQ_ECAPACITY, "layer %d: %d + 1 tokens exceed max_context %d", layer, s.N,
                        h->cfg.max_context);
+    if (s.ragged) {
+        // per sequence: a full recent buffer is flushed first (its flush launch
+        // also stores the new token); otherwise the attention launch stores it
+        if (h->cfg.batch > kvq::kMaxRaggedSeqs)
+            return h->fail(KVQ_EUNSUPPORTED, "sequences of different lengths: batch %d exceeds %d",
+                           h->cfg.batch, kvq::kMaxRaggedSeqs);
+        const int Hkv = h->cfg.n_kv_heads, D = h->cfg.head_dim;
+        std::vector<int> nt(h->cfg.batch, -1);
+        for (int b = 0; b < h->cfg.batch; ++b) {
+            const size_t off = static_cast<size_t>(b) * Hkv * D;
+            if (d.kb != 16 && s.seqN[b] - s.seqTq[b] == d.R) {
+                int Tq1 = 0;
+                rc = append_streams(h, d, b * Hkv, Hkv, static_cast<const uint16_t *>(k_new) + off,
+                                    static_cast<const uint16_t *>(v_new) + off, 1, 1, s.seqN[b], s.seqTq[b],
+                                    s.rpc_permille, &Tq1);
+                if (rc != KVQ_OK)
+                    return rc;
+                s.seqTq[b] = Tq1;
+            } else {
+                nt[b] = s.seqN[b];
+            }
+            s.seqN[b] += 1;
+        }
+        refresh_lengths(s);
+        return attention_launch(h, layer, q, out, k_new, v_new, -1, nt.data());
+    }
     const bool flush = d.kb != 16 && s.N - s.Tq == d.R;  // the recent buffer is full
     if (flush) {
         rc = kvq_append(h, layer, k_new, v_new, 1);
@@ -414,6 +588,7 @@ int kvq_append_decode_attention(kvq_handle *h, int layer, const void *k_new, con
     rc = attention_launch(h, layer, q, out, k_new, v_new, t);
     if (rc != KVQ_OK)
         s.N = t;
+    s.seqN.assign(h->cfg.batch, s.N);
     return rc;
 }
 
@@ -426,6 +601,8 @@ int kvq_prefill_attention(kvq_handle *h, int layer, const void *q, int n_q, floa
         return rc;
     const LayerState &s = h->plan.layers[layer];
     const kvq::LayerDev &d = s.dev;
+    if (s.ragged)
+        return h->fail(KVQ_EUNSUPPORTED, "layer %d holds sequences of different lengths", layer);
     if (n_q < 1 || n_q > s.N)
         return h->fail(KVQ_EINVAL, "n_q = %d outside [1, %d] (tokens in layer %d)", n_q, s.N, layer);
     const int D = h->cfg.head_dim;
@@ -464,7 +641,7 @@ int kvq_prefill_attention(kvq_handle *h, int layer, const void *q, int n_q, floa
 }
 
 static int attention_launch(kvq_handle *h, int layer, const void *q, float *out, const void *new_k,
-                            const void *new_v, int new_t)
+                            const void *new_v, int new_t, const int *seq_new_t)
 {
     LayerState &s = h->plan.layers[layer];
     if (h->cu_count == 0) {
@@ -502,15 +679,29 @@ static int attention_launch(kvq_handle *h, int layer, const void *q, float *out,
     a.BH = BH;
     a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D)));
     a.new_t = new_t;
-    a.new_k = new_t >= 0 ? static_cast<const uint16_t *>(new_k) : d.ring_k;
-    a.new_v = new_t >= 0 ? static_cast<const uint16_t *>(new_v) : d.ring_v;
+    // launch shape: sized for the most quantized groups and the most recent
+    // tokens any sequence holds
+    int n_groups_sz = s.Tq / d.G, Tr_sz = s.N - s.Tq;
+    if (s.ragged) {
+        if (h->cfg.batch > kvq::kMaxRaggedSeqs)
+            return h->fail(KVQ_EUNSUPPORTED, "sequences of different lengths: batch %d exceeds %d", h->cfg.batch,
+                           kvq::kMaxRaggedSeqs);
+        n_groups_sz = Tr_sz = 0;
+        for (int b = 0; b < h->cfg.batch; ++b) {
+            n_groups_sz = std::max(n_groups_sz, s.seqTq[b] / d.G);
+            Tr_sz = std::max(Tr_sz, s.seqN[b] - s.seqTq[b]);
+        }
+    }
+    const bool has_new = new_t >= 0 || seq_new_t != nullptr;
+    a.new_k = has_new ? static_cast<const uint16_t *>(new_k) : d.ring_k;
+    a.new_v = has_new ? static_cast<const uint16_t *>(new_v) : d.ring_v;
     const bool use_mfma = (d.kb == 16 || (d.v_tiled && kvq::mfma_supported(d.kb, d.vb, D))) &&
                           h->env_force_valu == 0;
     int S = 0;
     if (use_mfma) {
         // matrix-core units over whole groups, then over the recent tokens
-        const int n_groups = s.Tq / d.G;
-        const int Tr = s.N - s.Tq;
+        const int n_groups = n_groups_sz;
+        const int Tr = Tr_sz;
         // recent tokens: 32-token blocks, about as many per unit as a quantized unit holds
         auto res_len = [&](long ug_) {
             int r = static_cast<int>(ug_ * d.G);
@@ -647,11 +838,23 @@ static int attention_launch(kvq_handle *h, int layer, const void *q, float *out,
         a.units_q = a.unit_groups = a.unit_extra = a.units_r = a.res_tokens = a.mfma_wgs = 0;
         a.n_groups = a.ngcap = a.s_log2 = 0;
     }
+    kvq::RaggedTables rt;
+    if (s.ragged) {
+        // each sequence's own lengths, and its groups split over the units_q units
+        for (int b = 0; b < h->cfg.batch; ++b) {
+            const int ng = s.seqTq[b] / d.G;
+            rt.N[b] = s.seqN[b];
+            rt.Tq[b] = s.seqTq[b];
+            rt.unit_groups[b] = a.units_q > 0 ? ng / a.units_q : 0;
+            rt.unit_extra[b] = a.units_q > 0 ? ng % a.units_q : 0;
+            rt.new_t[b] = seq_new_t ? seq_new_t[b] : -1;
+        }
+    }
     // one partial entry per workgroup
     a.n_part = use_mfma ? a.mfma_wgs : a.valu_wgs;
     if (a.n_part < 1 || a.n_part > kMaxPart)
         return h->fail(KVQ_EINVAL, "internal: %d partial entries per stream", a.n_part);
-    e = kvq::launch_attention(a, use_mfma, h->stream);
+    e = kvq::launch_attention(a, s.ragged ? &rt : nullptr, use_mfma, h->stream);
     if (e != hipSuccess)
         return h->dev_fail(e, "attention launch");
     h->last_splits = S;
@@ -662,27 +865,33 @@ static int attention_launch(kvq_handle *h, int layer, const void *q, float *out,
 
 static void layer_bytes(const kvq_handle *h, const LayerState &s, kvq_bytes_info *info)
 {
-    const int64_t BH = h->BH(), D = h->cfg.head_dim;
+    const int64_t Hkv = h->cfg.n_kv_heads, D = h->cfg.head_dim;
     const kvq::LayerDev &d = s.dev;
     memset(info, 0, sizeof *info);
-    info->n_tokens = s.N;
-    info->n_quantized = s.Tq;
-    info->n_residual = s.N - s.Tq;
+    // token counts: those of every sequence, or -1 when they differ
+    info->n_tokens = s.ragged ? -1 : s.N;
+    info->n_quantized = s.ragged ? -1 : s.Tq;
+    info->n_residual = s.ragged ? -1 : s.N - s.Tq;
     info->k_bits = d.kb;
     info->v_bits = d.vb;
     info->residual_len = d.R;
     info->k_mode = d.k_tok ? KVQ_K_PER_TOKEN : KVQ_K_PER_CHANNEL;
     info->rpc_permille = s.rpc_permille;
-    if (d.kb == 16) {
-        info->residual = BH * s.N * 4 * D;
-    } else {
+    if (d.kb != 16) {
         info->k_words = d.wk;
         info->v_words = d.wv;
-        info->k_codes = BH * s.Tq * 4 * d.wk;
-        info->v_codes = BH * s.Tq * 4 * d.wv;
-        info->k_meta = d.k_tok ? BH * s.Tq * 8 : BH * (s.Tq / d.G) * 8 * D;
-        info->v_meta = BH * s.Tq * 8;
-        info->residual = BH * (s.N - s.Tq) * 4 * D;
+    }
+    for (size_t b = 0; b < s.seqN.size(); ++b) {
+        const int64_t N = s.seqN[b], Tq = s.seqTq[b];
+        if (d.kb == 16) {
+            info->residual += Hkv * N * 4 * D;
+            continue;
+        }
+        info->k_codes += Hkv * Tq * 4 * d.wk;
+        info->v_codes += Hkv * Tq * 4 * d.wv;
+        info->k_meta += d.k_tok ? Hkv * Tq * 8 : Hkv * (Tq / d.G) * 8 * D;
+        info->v_meta += Hkv * Tq * 8;
+        info->residual += Hkv * (N - Tq) * 4 * D;
     }
     info->total = info->k_codes + info->v_codes + info->k_meta + info->v_meta + info->residual;
 }
@@ -710,16 +919,14 @@ int kvq_bytes_layer(const kvq_handle *h, int layer, kvq_bytes_info *info)
     return KVQ_OK;
 }
 
-int kvq_export_layer(kvq_handle *h, int layer, uint32_t *k_words, float *k_scale, float *k_zero,
-                     uint32_t *v_words, float *v_scale, float *v_zero, void *res_k, void *res_v)
+// Canonical copy of streams [s0, s0 + BH) holding N tokens, Tq quantized;
+// output arrays are indexed by the stream's position in the range.
+static int export_streams(kvq_handle *h, const kvq::LayerDev &dl, int s0, int BH, int N, int Tq, uint32_t *k_words,
+                          float *k_scale, float *k_zero, uint32_t *v_words, float *v_scale, float *v_zero,
+                          void *res_k, void *res_v)
 {
-    if (!h)
-        return KVQ_EINVAL;
-    if (layer < 0 || layer >= h->cfg.n_layers)
-        return h->fail(KVQ_EINVAL, "layer %d out of range", layer);
-    const LayerState &s = h->plan.layers[layer];
-    const kvq::LayerDev &d = s.dev;
-    const int BH = h->BH(), D = h->cfg.head_dim, Tq = s.Tq, Tr = s.N - s.Tq;
+    const int D = h->cfg.head_dim, Tr = N - Tq;
+    const kvq::LayerDev d = s0 == 0 ? dl : sub_layer(dl, s0, D);
     hipError_t e = hipStreamSynchronize(h->stream);
     if (e != hipSuccess)
         return h->dev_fail(e, "stream synchronize");
@@ -814,6 +1021,35 @@ int kvq_export_layer(kvq_handle *h, int layer, uint32_t *k_words, float *k_scale
         }
     }
     return KVQ_OK;
+}
+
+int kvq_export_layer(kvq_handle *h, int layer, uint32_t *k_words, float *k_scale, float *k_zero,
+                     uint32_t *v_words, float *v_scale, float *v_zero, void *res_k, void *res_v)
+{
+    if (!h)
+        return KVQ_EINVAL;
+    if (layer < 0 || layer >= h->cfg.n_layers)
+        return h->fail(KVQ_EINVAL, "layer %d out of range", layer);
+    const LayerState &s = h->plan.layers[layer];
+    if (s.ragged)
+        return h->fail(KVQ_EINVAL, "layer %d holds sequences of different lengths: export them one by one", layer);
+    return export_streams(h, s.dev, 0, h->BH(), s.N, s.Tq, k_words, k_scale, k_zero, v_words, v_scale, v_zero,
+                          res_k, res_v);
+}
+
+int kvq_export_sequence(kvq_handle *h, int layer, int b, uint32_t *k_words, float *k_scale, float *k_zero,
+                        uint32_t *v_words, float *v_scale, float *v_zero, void *res_k, void *res_v)
+{
+    if (!h)
+        return KVQ_EINVAL;
+    if (layer < 0 || layer >= h->cfg.n_layers)
+        return h->fail(KVQ_EINVAL, "layer %d out of range", layer);
+    if (b < 0 || b >= h->cfg.batch)
+        return h->fail(KVQ_EINVAL, "sequence %d out of range [0, %d)", b, h->cfg.batch);
+    const LayerState &s = h->plan.layers[layer];
+    const int Hkv = h->cfg.n_kv_heads;
+    return export_streams(h, s.dev, b * Hkv, Hkv, s.seqN[b], s.seqTq[b], k_words, k_scale, k_zero, v_words, v_scale,
+                          v_zero, res_k, res_v);
 }
 
 int kvq_sync(kvq_handle *h)

@@ -20,7 +20,8 @@ _DT = {"f32": KVQ_F32, "f16": KVQ_F16, "bf16": KVQ_BF16}
 
 EXPORTED = ["kvq_workspace_bytes", "kvq_create", "kvq_append", "kvq_decode_attention",
             "kvq_append_decode_attention", "kvq_bytes", "kvq_bytes_layer", "kvq_export_layer", "kvq_sync",
-            "kvq_set_stream", "kvq_last_error", "kvq_destroy", "kvq_last_launch", "kvq_prefill_attention"]
+            "kvq_set_stream", "kvq_last_error", "kvq_destroy", "kvq_last_launch", "kvq_prefill_attention",
+            "kvq_append_ragged", "kvq_sequence_lengths", "kvq_export_sequence"]
 
 
 KVQ_K_PER_CHANNEL, KVQ_K_PER_TOKEN = 0, 1
@@ -80,6 +81,9 @@ def lib():
         "kvq_destroy": (None, [P]),
         "kvq_last_launch": (I, [P, P, P]),
         "kvq_prefill_attention": (I, [P, I, P, I, P]),
+        "kvq_append_ragged": (I, [P, I, P, P, P, I]),
+        "kvq_sequence_lengths": (I, [P, I, P, P]),
+        "kvq_export_sequence": (I, [P, I, I] + [P] * 8),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -144,6 +148,25 @@ def kvq_bytes_layer(h, layer):
     info = kvq_bytes_info()
     _check(lib().kvq_bytes_layer(h, layer, ctypes.byref(info)), h)
     return info
+
+
+def kvq_append_ragged(h, layer, k_ptr, v_ptr, n_new, n_max):
+    """n_new: sequence of batch token counts (copied to a host int32 array)."""
+    arr = (ctypes.c_int32 * len(n_new))(*[int(x) for x in n_new])
+    return _check(lib().kvq_append_ragged(h, layer, k_ptr, v_ptr, arr, n_max), h)
+
+
+def kvq_sequence_lengths(h, layer, batch):
+    n = (ctypes.c_int32 * batch)()
+    tq = (ctypes.c_int32 * batch)()
+    _check(lib().kvq_sequence_lengths(h, layer, n, tq), h)
+    return list(n), list(tq)
+
+
+def kvq_export_sequence(h, layer, b, k_words=None, k_scale=None, k_zero=None, v_words=None,
+                        v_scale=None, v_zero=None, res_k=None, res_v=None):
+    return _check(lib().kvq_export_sequence(h, layer, b, k_words, k_scale, k_zero, v_words, v_scale,
+                                            v_zero, res_k, res_v), h)
 
 
 def kvq_export_layer(h, layer, k_words=None, k_scale=None, k_zero=None, v_words=None,
@@ -230,6 +253,19 @@ class Cache:
         kvq_append(self.h, layer, ctypes.c_void_p(k_new.data_ptr()),
                    ctypes.c_void_p(v_new.data_ptr()), k_new.shape[2])
 
+    def append_ragged(self, layer, k_new, v_new, n_new):
+        """Sequence b appends rows [b, :, 0:n_new[b]] of k_new / v_new [B, Hkv, n_max, d]."""
+        self._kv_check(k_new)
+        self._kv_check(v_new)
+        if k_new.shape != v_new.shape:
+            raise ValueError("K and V shapes differ")
+        kvq_append_ragged(self.h, layer, ctypes.c_void_p(k_new.data_ptr()),
+                          ctypes.c_void_p(v_new.data_ptr()), n_new, k_new.shape[2])
+
+    def sequence_lengths(self, layer):
+        """([N_b], [Tq_b]) per sequence."""
+        return kvq_sequence_lengths(self.h, layer, self.shape["batch"])
+
     def _q_check(self, q, out):
         s = self.shape
         torch = self.torch
@@ -280,15 +316,23 @@ class Cache:
     def bytes_layer(self, layer):
         return kvq_bytes_layer(self.h, layer)
 
-    def export(self, layer):
-        """Canonical host copy of one layer (numpy arrays)."""
+    def export(self, layer, seq=None):
+        """Canonical host copy of one layer (numpy arrays); with seq = b, of
+        sequence b alone (any layer, ragged or not)."""
         info = self.bytes_layer(layer)
         s = self.shape
         B, H, d, G = s["batch"], s["n_kv_heads"], s["head_dim"], s["group_size"]
-        Tq, Tr = info.n_quantized, info.n_residual
+        if seq is None:
+            if info.n_tokens < 0:  # sequences of different lengths: the library refuses
+                kvq_export_layer(self.h, layer)
+            Tq, Tr, N = info.n_quantized, info.n_residual, info.n_tokens
+        else:
+            ns, tqs = self.sequence_lengths(layer)
+            B, N, Tq = 1, ns[seq], tqs[seq]
+            Tr = N - Tq
         wk, wv = max(info.k_words, 1), max(info.v_words, 1)
         out = dict(
-            N=info.n_tokens, Tq=Tq,
+            N=N, Tq=Tq,
             k_words=np.zeros((B * H, Tq, wk), np.uint32),
             k_scale=np.zeros((B * H, Tq) if info.k_mode else (B * H, Tq // G, d), np.float32),
             k_zero=np.zeros((B * H, Tq) if info.k_mode else (B * H, Tq // G, d), np.float32),
@@ -299,8 +343,12 @@ class Cache:
             res_v=np.zeros((B * H, Tr, d), np.uint16),
         )
         p = {k: v.ctypes.data_as(ctypes.c_void_p) for k, v in out.items() if isinstance(v, np.ndarray)}
-        kvq_export_layer(self.h, layer, p["k_words"], p["k_scale"], p["k_zero"], p["v_words"],
-                         p["v_scale"], p["v_zero"], p["res_k"], p["res_v"])
+        args = (p["k_words"], p["k_scale"], p["k_zero"], p["v_words"], p["v_scale"], p["v_zero"],
+                p["res_k"], p["res_v"])
+        if seq is None:
+            kvq_export_layer(self.h, layer, *args)
+        else:
+            kvq_export_sequence(self.h, layer, seq, *args)
         if info.k_words == 0:
             out["k_words"] = out["k_words"][:, :, :0]
             out["v_words"] = out["v_words"][:, :, :0]

@@ -36,7 +36,10 @@
  *   - The caller owns every buffer, including the device workspace that holds
  *     the whole cache state; the library allocates no device memory.
  *   - Query head hq reads kv-head hq / g, g = n_q_heads / n_kv_heads.
- *   - Every sequence of the batch has the same length.
+ *   - Sequences of the batch hold the same number of tokens unless appended
+ *     with kvq_append_ragged(); then each sequence keeps its own count, applies
+ *     the streaming rule to its own recent tokens and attends to its own
+ *     tokens only.
  */
 #ifndef KVQ_H
 #define KVQ_H
@@ -141,6 +144,26 @@ int kvq_create(const kvq_config *cfg, void *workspace, size_t ws_bytes, kvq_hand
  * layer would hold more than max_context tokens), KVQ_EDEVICE. */
 int kvq_append(kvq_handle *h, int layer, const void *k_new, const void *v_new, int n_new);
 
+/* Append n_new[b] tokens to sequence b of one layer (b < batch), each sequence
+ * on its own as in kvq_append().  Serving batches hold sequences of different
+ * lengths (KIVI notes, section 8: paging and other cache managers combine with
+ * the quantized cache).
+ *   k_new, v_new: device pointers, [batch][n_kv_heads][n_max][head_dim] in
+ *   kv_dtype, 16-byte aligned; sequence b uses rows [0, n_new[b]).
+ *   n_new: host array of batch counts, 0 <= n_new[b] <= n_max.
+ * After appends of different counts the layer is ragged: decode attention
+ * (either call) then takes each sequence's own tokens, for batch <= 64
+ * (KVQ_EUNSUPPORTED above); prefill attention and kvq_export_layer() refuse
+ * it (use kvq_export_sequence()).
+ * Errors: KVQ_EINVAL, KVQ_ECAPACITY (a sequence would exceed max_context; no
+ * sequence is changed), KVQ_EDEVICE. */
+int kvq_append_ragged(kvq_handle *h, int layer, const void *k_new, const void *v_new, const int32_t *n_new,
+                      int n_max);
+
+/* Tokens held (n_tokens) and quantized (n_quantized) by each sequence of a
+ * layer: host arrays of batch entries; either pointer may be NULL. */
+int kvq_sequence_lengths(const kvq_handle *h, int layer, int32_t *n_tokens, int32_t *n_quantized);
+
 /* Decode attention of one query token per sequence over every token of `layer`
  * (quantized tokens dequantized on the fly, recent tokens in 16 bits), scale
  * 1/sqrt(head_dim).
@@ -188,9 +211,10 @@ int64_t kvq_bytes(const kvq_handle *h);
 
 typedef struct kvq_bytes_info {
     int64_t k_codes, k_meta, v_codes, v_meta, residual, total;
-    int32_t n_tokens;     /* N: tokens appended */
-    int32_t n_quantized;  /* Tq: tokens held as codes */
-    int32_t n_residual;   /* Tr = N - Tq: tokens held in 16 bits */
+    int32_t n_tokens;     /* N: tokens appended (-1: sequences differ, see
+                             kvq_sequence_lengths) */
+    int32_t n_quantized;  /* Tq: tokens held as codes (-1 likewise) */
+    int32_t n_residual;   /* Tr = N - Tq: tokens held in 16 bits (-1 likewise) */
     int32_t k_words;      /* 32-bit words per packed K row */
     int32_t v_words;      /* 32-bit words per packed V row */
     int32_t k_bits, v_bits, residual_len;
@@ -216,6 +240,11 @@ int kvq_bytes_layer(const kvq_handle *h, int layer, kvq_bytes_info *info);
  * For a (16, 16) layer Tq = 0 and res_* hold all N tokens. */
 int kvq_export_layer(kvq_handle *h, int layer, uint32_t *k_words, float *k_scale, float *k_zero,
                      uint32_t *v_words, float *v_scale, float *v_zero, void *res_k, void *res_v);
+
+/* kvq_export_layer() for sequence b alone: the same arrays with B = 1 and
+ * that sequence's Tq and Tr (kvq_sequence_lengths). */
+int kvq_export_sequence(kvq_handle *h, int layer, int b, uint32_t *k_words, float *k_scale, float *k_zero,
+                        uint32_t *v_words, float *v_scale, float *v_zero, void *res_k, void *res_v);
 
 /* Wait for all work enqueued by the handle.  KVQ_EDEVICE reports an error the
  * stream raised. */
