@@ -55,22 +55,36 @@ def quantized_count(N, R, G, kb, rpc=0):
 
 
 def step_bytes(w, N_before, qbytes):
-    """Algorithmic bytes of one decode step over all layers, and of attention only."""
+    """Algorithmic bytes of one decode step over all layers, and of attention
+    only; N_before: tokens held by each sequence before the step (a list, or
+    one count for every sequence)."""
     B, Hkv, Hq, d, G = w.batch, w.n_kv_heads, w.n_q_heads, w.head_dim, w.G
-    BH = B * Hkv
+    Ns = N_before if isinstance(N_before, (list, tuple)) else [N_before] * B
     att = app = 0
     for lc in w.layers:
         kb, vb, R, kt, rpc = layer_row(lc)
-        N1 = N_before + 1
-        Tq0 = quantized_count(N_before, R, G, kb, rpc)
-        Tq1 = quantized_count(N1, R, G, kb, rpc)
-        att += BH * stream_state_bytes(d, kb, vb, G, N1, Tq1, kt) + B * Hq * d * (qbytes + 4)
-        app += BH * 2 * d * 2 * 2  # read new K and V, write them to the ring
-        if Tq1 > Tq0:  # flush: read the given-up 16-bit K/V rows, write codes and metadata
-            wk = (d + 10) // 11 if kb == 3 else d * kb // 32
-            nf = Tq1 - Tq0
-            app += BH * (nf * 4 * d + nf * 4 * (wk + d * vb // 32) + (8 * nf if kt else 8 * d * nf // G) + 8 * nf)
+        att += B * Hq * d * (qbytes + 4)
+        for N0 in Ns:
+            N1 = N0 + 1
+            Tq0 = quantized_count(N0, R, G, kb, rpc)
+            Tq1 = quantized_count(N1, R, G, kb, rpc)
+            att += Hkv * stream_state_bytes(d, kb, vb, G, N1, Tq1, kt)
+            app += Hkv * 2 * d * 2 * 2  # read new K and V, write them to the ring
+            if Tq1 > Tq0:  # flush: read the given-up 16-bit K/V rows, write codes and metadata
+                wk = (d + 10) // 11 if kb == 3 else d * kb // 32
+                nf = Tq1 - Tq0
+                app += Hkv * (nf * 4 * d + nf * 4 * (wk + d * vb // 32) + (8 * nf if kt else 8 * d * nf // G)
+                              + 8 * nf)
     return att, app
+
+
+def ragged_contexts(context, B):
+    """Sequence b starts with context * (0.25 + 1.5 b / (B - 1)) tokens: lengths
+    spread evenly from a quarter to 1.75 times the workload's context (mean
+    about the context)."""
+    if B == 1:
+        return [context]
+    return [max(1, int(round(context * (0.25 + 1.5 * b / (B - 1))))) for b in range(B)]
 
 
 def kernel_source_digest():
@@ -208,6 +222,9 @@ def main():
     ap.add_argument("--rpc", action="store_true",
                     help="KVmix dynamic recent-token ratio: 20 %% on the table's higher-precision "
                          "layers, 10 %% on the lowest-precision ones")
+    ap.add_argument("--ragged", action="store_true",
+                    help="sequences of different lengths: sequence b starts with context x "
+                         "(0.25 + 1.5 b / (B - 1)) tokens")
     ap.add_argument("--kernel-rounds", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -245,17 +262,21 @@ def main():
     L, B, Hq, Hkv, d = w.n_layers, w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim
     total = args.warmup + args.steps
     qbytes = 4 if w.q_dtype == "f32" else 2
-    cache = kvq.Cache(L, B, Hq, Hkv, d, w.context + total, w.kv_dtype, w.q_dtype, w.G, w.R, w.layers)
+    ctx = ragged_contexts(w.context, B) if args.ragged else [w.context] * B
+    cache = kvq.Cache(L, B, Hq, Hkv, d, max(ctx) + total, w.kv_dtype, w.q_dtype, w.G, w.R, w.layers)
     stream = cache.stream
 
     # prefill every layer, then stage all decode inputs in HBM
     knew, vnew, qs = [], [], []
     for l in range(L):
         st = synth.LayerStats(w, l)
-        k, v = synth.layer_tokens(w, l, 0, w.context, dev, stats=st)
-        cache.append(l, k, v)
+        k, v = synth.layer_tokens(w, l, 0, max(ctx), dev, stats=st)
+        if args.ragged:
+            cache.append_ragged(l, k, v, ctx)
+        else:
+            cache.append(l, k, v)
         del k, v
-        k, v = synth.layer_tokens(w, l, w.context, total, dev, stats=st)
+        k, v = synth.layer_tokens(w, l, max(ctx), total, dev, stats=st)
         knew.append(k.permute(2, 0, 1, 3).contiguous().unsqueeze(3))  # [total, B, Hkv, 1, d]
         vnew.append(v.permute(2, 0, 1, 3).contiguous().unsqueeze(3))
         qs.append(synth.queries(w, l, total, dev))
@@ -273,7 +294,7 @@ def main():
 
     att_bytes = app_bytes = 0
     for s in range(args.warmup, total):
-        a, p = step_bytes(w, w.context + s, qbytes)
+        a, p = step_bytes(w, [c + s for c in ctx], qbytes)
         att_bytes += a
         app_bytes += p
 
@@ -285,13 +306,14 @@ def main():
     ms_per_step = wall / args.steps * 1e3
 
     # the state the library reports agrees with the byte model used above
-    N_end = w.context + total
+    N_end = max(ctx) + total
+    ends = [c + total for c in ctx]
     for l, lc in enumerate(w.layers):
         kb, vb, R, kt, rpc = layer_row(lc)
         info = cache.bytes_layer(l)
-        assert info.n_tokens == N_end
-        assert info.total == B * Hkv * stream_state_bytes(d, kb, vb, w.G, N_end,
-                                                         quantized_count(N_end, R, w.G, kb, rpc), kt)
+        assert cache.sequence_lengths(l)[0] == ends
+        assert info.total == sum(Hkv * stream_state_bytes(d, kb, vb, w.G, n, quantized_count(n, R, w.G, kb, rpc), kt)
+                                 for n in ends)
 
     # dominant kernel: decode attention (one launch per call).  HIP events on
     # the stream the library launches on bracket back-to-back calls over every
@@ -335,17 +357,17 @@ def main():
     att_per_layer = []
     for l, lc in enumerate(w.layers):
         kb, vb, R, kt, rpc = layer_row(lc)
-        Tq = quantized_count(N_end, R, w.G, kb, rpc)
-        att_per_layer.append(B * Hkv * stream_state_bytes(d, kb, vb, w.G, N_end, Tq, kt) +
-                             B * Hq * d * (qbytes + 4))
+        att_per_layer.append(sum(Hkv * stream_state_bytes(d, kb, vb, w.G, n, quantized_count(n, R, w.G, kb, rpc), kt)
+                                 for n in ends) + B * Hq * d * (qbytes + 4))
     avg_att_bytes = sum(att_per_layer) / L
     achieved = avg_att_bytes / (avg_call_us * 1e-6) / 1e9
     splits, variant = kvq.kvq_last_launch(cache.h)
-    traffic = stored_traffic(args.workload, args.table) if args.k_mode == "per-channel" else None
+    traffic = stored_traffic(args.workload, args.table) if args.k_mode == "per-channel" and not (
+        args.ragged or args.rpc) else None
 
     prefill = None
     C = min(args.prefill_chunk, N_end)
-    if C > 0 and (w.head_dim == 128 or all(lc[0] != 3 for lc in w.layers)) and w.G % 32 == 0:
+    if C > 0 and not args.ragged and (w.head_dim == 128 or all(lc[0] != 3 for lc in w.layers)) and w.G % 32 == 0:
         prefill = prefill_leg(cache, w, C, N_end, qbytes, rounds, stream, dev)
         if C == 256 and args.k_mode == "per-channel":
             prefill["roofline"]["traffic"] = stored_traffic(args.workload, args.table, "prefill")
@@ -378,7 +400,7 @@ def main():
         "config": {
             "workload": w.name,
             "layers": L, "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": d,
-            "context_start": w.context, "G": w.G, "R": w.R,
+            "context_start": w.context if not args.ragged else ctx, "G": w.G, "R": w.R,
             "kv_dtype": w.kv_dtype, "q_dtype": w.q_dtype,
             "table": "".join("K%dV%d " % tuple(lc[:2]) for lc in w.layers).strip(),
             "k_mode": args.k_mode,
@@ -401,7 +423,7 @@ def main():
     }
     if prefill is not None:
         res["prefill"] = prefill
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.ragged:
         sample = [0, 1] if L >= 2 else [0]
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, sample)
     cache.close()
