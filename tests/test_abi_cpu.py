@@ -50,6 +50,37 @@ def test_recent_ratio_validation():
         kvq.kvq_destroy(h)
 
 
+def test_ragged_append_validation_without_device_work():
+    """kvq_append_ragged checks every count before any device work: counts
+    outside [0, n_max], a sequence past max_context, NULL pointers; all-zero
+    counts are a no-op; per-sequence lengths start at zero."""
+    cfg = _cfg()
+    n = kvq.kvq_workspace_bytes(cfg)
+    h = kvq.kvq_create(cfg, ctypes.c_void_p(1 << 20), n)
+    p = ctypes.c_void_p(1 << 21)
+    try:
+        cases = [
+            (lambda: kvq.kvq_append_ragged(h, 0, p, p, [3, 9], 8), kvq.KVQ_EINVAL, "n_new[1] = 9 outside"),
+            (lambda: kvq.kvq_append_ragged(h, 0, p, p, [-1, 0], 8), kvq.KVQ_EINVAL, "n_new[0] = -1 outside"),
+            (lambda: kvq.kvq_append_ragged(h, 0, p, p, [0, 257], 300), kvq.KVQ_ECAPACITY, "sequence 1"),
+            (lambda: kvq.kvq_append_ragged(h, 0, None, p, [1, 0], 1), kvq.KVQ_EINVAL, "NULL"),
+            (lambda: kvq.kvq_append_ragged(h, 2, p, p, [1, 0], 1), kvq.KVQ_EINVAL, "out of range"),
+            (lambda: kvq.kvq_append_ragged(h, 0, p, p, [1, 0], -1), kvq.KVQ_EINVAL, "n_max"),
+        ]
+        for fn, code, msg in cases:
+            with pytest.raises(kvq.KvqError) as e:
+                fn()
+            assert e.value.code == code and msg in str(e.value), str(e.value)
+        kvq.kvq_append_ragged(h, 0, p, p, [0, 0], 5)  # no-op: no device work
+        assert kvq.kvq_sequence_lengths(h, 0, 2) == ([0, 0], [0, 0])
+        assert kvq.kvq_bytes_layer(h, 0).n_tokens == 0
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.kvq_export_sequence(h, 0, 2)
+        assert e.value.code == kvq.KVQ_EINVAL
+    finally:
+        kvq.kvq_destroy(h)
+
+
 def test_workspace_bytes_valid_and_invalid():
     n = kvq.kvq_workspace_bytes(_cfg())
     assert n > 0 and n % kvq.KVQ_WORKSPACE_ALIGN == 0
