@@ -59,14 +59,30 @@ __device__ __forceinline__ void split3_bf16(float x0, float x1, uint32_t &p1, ui
     p3 = (__float_as_uint(s0) >> 16) | (__float_as_uint(s1) & 0xFFFF0000u);
 }
 
+// x - (the low / high fp16 half of h2, widened): one mixed-precision FMA
+// (exact: h2's half is x rounded toward zero to fp16, so the difference is an
+// fp32 number), instead of a conversion and a subtraction
+__device__ __forceinline__ float minus_f16_lo(uint32_t h2, float x)
+{
+    float r;
+    asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h2), "v"(x));
+    return r;
+}
+__device__ __forceinline__ float minus_f16_hi(uint32_t h2, float x)
+{
+    float r;
+    asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h2), "v"(x));
+    return r;
+}
+
 // fp32 pair -> (hi, lo) fp16 pairs with x ~= hi + lo
 __device__ __forceinline__ void split_pair(float x0, float x1, uint32_t &hi, uint32_t &lo)
 {
     const auto h = __builtin_amdgcn_cvt_pkrtz(x0, x1);
-    const float r0 = x0 - static_cast<float>(h[0]);
-    const float r1 = x1 - static_cast<float>(h[1]);
-    const auto l = __builtin_amdgcn_cvt_pkrtz(r0, r1);
     hi = __builtin_bit_cast(uint32_t, h);
+    const float r0 = minus_f16_lo(hi, x0);
+    const float r1 = minus_f16_hi(hi, x1);
+    const auto l = __builtin_amdgcn_cvt_pkrtz(r0, r1);
     lo = __builtin_bit_cast(uint32_t, l);
 }
 
