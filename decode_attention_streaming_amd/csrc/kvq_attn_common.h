@@ -64,6 +64,13 @@ struct PartBuf {
     {
         return __builtin_amdgcn_raw_buffer_load_b128(r, off_f * 4, 0, kDeviceCoherent);
     }
+    // when every writer ran on this workgroup's XCD: their write-through
+    // stores passed this XCD's L2, so a load that only bypasses the L1 is
+    // coherent with them (cache-policy bit sc0)
+    __device__ f4_t load4_xcd(int off_f) const
+    {
+        return __builtin_amdgcn_raw_buffer_load_b128(r, off_f * 4, 0, 1);
+    }
 };
 
 // Lengths of stream bh: those of the launch, or, for a ragged batch, those of
@@ -515,7 +522,7 @@ __device__ __forceinline__ void wg_merge_store(const AttnArgs &a, int bh, int en
 // no masked-off entry slots are executed.
 template <int D, int KC>
 __device__ __forceinline__ void merge_stream(const AttnArgs &a, int bh, int n_sub, int tid_item, int tid_sub,
-                                             float *s_m, float *s_d, f4_t *s_acc)
+                                             float *s_m, float *s_d, f4_t *s_acc, bool xcd_local)
 {
     const int tid = threadIdx.x;
     constexpr int nc4 = D / 4;
@@ -535,8 +542,8 @@ __device__ __forceinline__ void merge_stream(const AttnArgs &a, int bh, int n_su
             for (int k = 0; k < KC; ++k) {
                 const int e = e0 + k * n_sub;
                 if (own && e < P) {
-                    ml[k] = pb.load4(pb.off(a, e, h, D));
-                    ov[k] = pb.load4(pb.off(a, e, h, 4 * c4));
+                    ml[k] = xcd_local ? pb.load4_xcd(pb.off(a, e, h, D)) : pb.load4(pb.off(a, e, h, D));
+                    ov[k] = xcd_local ? pb.load4_xcd(pb.off(a, e, h, 4 * c4)) : pb.load4(pb.off(a, e, h, 4 * c4));
                 }
             }
             float Mc = M;
@@ -588,11 +595,22 @@ __device__ __forceinline__ void merge_stream(const AttnArgs &a, int bh, int n_su
     }
 }
 
+// XCD (accelerator complex die) this wave runs on.
+__device__ __forceinline__ unsigned xcd_id()
+{
+    unsigned r;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(r));
+    return r & 7u;
+}
+
 // Called by every workgroup at its end: the last one of stream bh to arrive
 // merges the n_part partial entries (merge_stream) and re-arms the stream's
-// counter.
+// counter.  With by_xcd (at most 15 workgroups per stream), each workgroup
+// adds 1 to the 4-bit field of its XCD instead of 1: the last one then also
+// knows whether every workgroup of the stream ran on its own XCD, and if so
+// reads their partials through that XCD's L2.
 template <int D>
-__device__ __forceinline__ void arrive_and_merge(const AttnArgs &a, int bh, unsigned n_wgs)
+__device__ __forceinline__ void arrive_and_merge(const AttnArgs &a, int bh, unsigned n_wgs, bool by_xcd = false)
 {
     __shared__ int s_last;
     __shared__ float s_m[kAttnThreads], s_d[kAttnThreads];
@@ -600,13 +618,26 @@ __device__ __forceinline__ void arrive_and_merge(const AttnArgs &a, int bh, unsi
     __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are complete
     __syncthreads();
     if (threadIdx.x == 0) {
-        const unsigned prev =
-            __hip_atomic_fetch_add(a.counters + bh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (prev == n_wgs - 1);
+        if (by_xcd) {
+            const unsigned x = xcd_id();
+            const unsigned inc = 1u << (4 * x);
+            const unsigned v =
+                __hip_atomic_fetch_add(a.counters + bh, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + inc;
+            unsigned total = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                total += (v >> (4 * j)) & 15u;
+            s_last = total == n_wgs ? (((v >> (4 * x)) & 15u) == n_wgs ? 2 : 1) : 0;
+        } else {
+            const unsigned prev =
+                __hip_atomic_fetch_add(a.counters + bh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_last = (prev == n_wgs - 1);
+        }
     }
     __syncthreads();
     if (!s_last)
         return;
+    const bool xcd_local = s_last == 2;
     const int tid = threadIdx.x;
     const int n_items = a.g * (D / 4);  // <= 1024
     // n_sub = kAttnThreads / n_items threads per item (when items are fewer
@@ -622,13 +653,13 @@ __device__ __forceinline__ void arrive_and_merge(const AttnArgs &a, int bh, unsi
     }
     const int P = a.n_part;  // entries per thread: ceil(P / n_sub)
     if (P <= 2 * n_sub)
-        merge_stream<D, 2>(a, bh, n_sub, tid_item, tid_sub, s_m, s_d, s_acc);
+        merge_stream<D, 2>(a, bh, n_sub, tid_item, tid_sub, s_m, s_d, s_acc, xcd_local);
     else if (P <= 4 * n_sub)
-        merge_stream<D, 4>(a, bh, n_sub, tid_item, tid_sub, s_m, s_d, s_acc);
+        merge_stream<D, 4>(a, bh, n_sub, tid_item, tid_sub, s_m, s_d, s_acc, xcd_local);
     else if (P <= 8 * n_sub)
-        merge_stream<D, 8>(a, bh, n_sub, tid_item, tid_sub, s_m, s_d, s_acc);
+        merge_stream<D, 8>(a, bh, n_sub, tid_item, tid_sub, s_m, s_d, s_acc, xcd_local);
     else
-        merge_stream<D, 16>(a, bh, n_sub, tid_item, tid_sub, s_m, s_d, s_acc);
+        merge_stream<D, 16>(a, bh, n_sub, tid_item, tid_sub, s_m, s_d, s_acc, xcd_local);
     if (tid == 0)
         __hip_atomic_store(a.counters + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

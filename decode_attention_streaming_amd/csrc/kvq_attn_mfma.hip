@@ -656,8 +656,17 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs &a, const RaggedTa
     __shared__ float s_pm[kAttnThreads / 64][kMaxG], s_pl[kAttnThreads / 64][kMaxG];
     // the wave index is uniform across the wave: keep it (and everything derived
     // from it) in scalar registers, so that unit bounds and branches are scalar
-    const int bh = blockIdx.y, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int unit = blockIdx.x * 4 + wave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    int bh, wx;  // stream, and this workgroup's place among the stream's
+    if (a.xcd_shift > 0) {
+        const int i = blockIdx.x, k = i >> 3;
+        bh = (i & 7) + 8 * (k >> a.xcd_shift);
+        wx = k & ((1 << a.xcd_shift) - 1);
+    } else {
+        bh = blockIdx.y;
+        wx = blockIdx.x;
+    }
+    const int unit = wx * 4 + wave;
     const int region = wave_region(a);
     float *po = lds + wave * region;
     if (unit < a.units_q) {
@@ -672,8 +681,8 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs &a, const RaggedTa
         s_pl[wave][lane] = 0.0f;
     }
     __syncthreads();
-    wg_merge_store<D>(a, bh, blockIdx.x, lds, region, s_pm, s_pl);
-    arrive_and_merge<D>(a, bh, gridDim.x);
+    wg_merge_store<D>(a, bh, wx, lds, region, s_pm, s_pl);
+    arrive_and_merge<D>(a, bh, a.mfma_wgs, a.xcd_shift > 0);
 }
 
 template <int KB, int VB, int D, bool KT>
@@ -693,7 +702,7 @@ __global__ __launch_bounds__(kAttnThreads, (mfma_waves_per_simd<KB, VB>())) void
 template <int KB, int VB, bool KT>
 hipError_t launch_pair(const AttnArgs &a, const RaggedTables *rt, hipStream_t st)
 {
-    dim3 grid(a.mfma_wgs, a.BH);
+    const dim3 grid = a.xcd_shift > 0 ? dim3(a.mfma_wgs * a.BH) : dim3(a.mfma_wgs, a.BH);
     const size_t lds = (kAttnThreads / 64) * wave_region(a) * sizeof(float);
     if (rt) {
         const RaggedAttnArgs r{a, *rt};

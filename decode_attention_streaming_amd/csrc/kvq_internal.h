@@ -74,6 +74,12 @@ struct AttnArgs {
     // [Tq, N), res_tokens each (a multiple of 32); mfma_wgs = ceil((units_q +
     // units_r) / 4) workgroups
     int units_q, unit_groups, unit_extra, units_r, res_tokens, mfma_wgs;
+    // matrix-core grid numbering: 0 = 2D (x: workgroup of the stream, y:
+    // stream); s > 0 = 1D, workgroup i serving stream (i % 8) + 8 * ((i / 8) >> s)
+    // as its workgroup (i / 8) & (2^s - 1), mfma_wgs = 2^s: workgroups are dealt
+    // to the eight XCDs in turn, so each stream's workgroups share one XCD and
+    // its L2 (the hand-off then reads the partials from that L2)
+    int xcd_shift;
     // Tq / G, capq / G, and log2 of the columns per group slot of the
     // matrix-core products (S = 16 / NG, NG the largest power of two with
     // NG * g <= 16)

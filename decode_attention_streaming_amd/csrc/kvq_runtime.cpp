@@ -815,6 +815,12 @@ static int attention_launch(kvq_handle *h, int layer, const void *q, float *out,
         a.res_tokens = rt;
         a.units_r = (Tr + rt - 1) / rt;
         a.mfma_wgs = (a.units_q + a.units_r + 3) / 4;
+        // one XCD per stream when the streams fill the eight XCDs evenly and
+        // each has at most eight workgroups (a power of two)
+        a.xcd_shift = 0;
+        if (BH % 8 == 0 && a.mfma_wgs >= 2 && a.mfma_wgs <= 8 && (a.mfma_wgs & (a.mfma_wgs - 1)) == 0)
+            while ((1 << a.xcd_shift) < a.mfma_wgs)
+                ++a.xcd_shift;
         a.valu_beg = a.valu_tps = a.valu_wgs = 0;
         S = a.units_q + a.units_r;
     } else {
@@ -836,6 +842,7 @@ static int attention_launch(kvq_handle *h, int layer, const void *q, float *out,
         a.valu_tps = tps;
         a.valu_wgs = S;
         a.units_q = a.unit_groups = a.unit_extra = a.units_r = a.res_tokens = a.mfma_wgs = 0;
+        a.xcd_shift = 0;
         a.n_groups = a.ngcap = a.s_log2 = 0;
     }
     kvq::RaggedTables rt;
