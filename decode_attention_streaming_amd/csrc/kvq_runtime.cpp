@@ -778,16 +778,21 @@ static int attention_launch(kvq_handle *h, int layer, const void *q, float *out,
             // few streams: while there are more SIMDs than waves, shorter units
             // (one wave per SIMD, whole workgroups) shorten the critical path;
             // when such a unit would still walk eight or more 32-token blocks
-            // (several dependent load rounds), two waves per SIMD, each with
-            // half the groups, hide each other's load latency; the recent-token
-            // units then come on top, so that the quantized units split the
-            // groups evenly (Llama-2-70B shape: 39.9 -> 34.2 us per call)
+            // (several dependent load rounds), twice as many units, two waves
+            // per SIMD, hide each other's load latency, provided they fit one
+            // generation of resident workgroups (Llama-2-70B shape: 39.9 ->
+            // 35.2 us per call; the Qwen2.5-7B shape would need a second
+            // generation and keeps its units)
             const long u_simd = (4L * h->cu_count / BH) / 4 * 4;
-            const bool two = u_simd > ur && (n_groups + u_simd - ur - 1) / (u_simd - ur) * (d.G / 32) >= 8;
-            if (env_ug == 0 && two && 2 * u_simd > uq)
-                uq = std::min<long>(n_groups, 2 * u_simd);
-            else if (env_ug == 0 && u_simd > uq + ur)
-                uq = std::min<long>(n_groups, u_simd - ur);
+            if (env_ug == 0) {
+                const long base = std::max<long>(uq, u_simd - ur);
+                const bool walks = base > 0 && (n_groups + base - 1) / base * (d.G / 32) >= 8;
+                const long wgs2 = static_cast<long>(BH) * ((2 * base + ur + 3) / 4);
+                if (walks && wgs2 * 20 <= res_wgs * 21)
+                    uq = std::min<long>(n_groups, 2 * base);
+                else if (u_simd > uq + ur)
+                    uq = std::min<long>(n_groups, u_simd - ur);
+            }
         }
         if (rt == 0)
             rt = res_len(uq > 0 ? (n_groups + uq - 1) / uq : 1);
