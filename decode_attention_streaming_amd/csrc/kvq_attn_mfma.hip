@@ -188,16 +188,24 @@ __device__ void mfma_unit(const AttnArgs &a, const RaggedTables *rt, int bh, int
                     qv[4 * i] = v.x; qv[4 * i + 1] = v.y; qv[4 * i + 2] = v.z; qv[4 * i + 3] = v.w;
                 }
             } else {
-                const int bf = a.q_dtype == 2;
                 const uint4 *qp = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(q_lds) + h * D + q * QC);
+                if (a.q_dtype == 2) {
 #pragma unroll
-                for (int i = 0; i < QC / 8; ++i) {
-                    const uint4 v = qp[i];
-                    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+                    for (int i = 0; i < QC / 8; ++i) {
+                        const uint4 v = qp[i];
+                        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        qv[8 * i + 2 * k] = widen16(static_cast<uint16_t>(w[k] & 0xFFFFu), bf);
-                        qv[8 * i + 2 * k + 1] = widen16(static_cast<uint16_t>(w[k] >> 16), bf);
+                        for (int k = 0; k < 4; ++k)
+                            widen_pair<true>(w[k], qv[8 * i + 2 * k], qv[8 * i + 2 * k + 1]);
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < QC / 8; ++i) {
+                        const uint4 v = qp[i];
+                        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                        for (int k = 0; k < 4; ++k)
+                            widen_pair<false>(w[k], qv[8 * i + 2 * k], qv[8 * i + 2 * k + 1]);
                     }
                 }
             }

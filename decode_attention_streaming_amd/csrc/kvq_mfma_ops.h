@@ -192,6 +192,20 @@ __device__ __forceinline__ uint32_t code_reg3(const uint32_t (&w)[N], const uint
     return __builtin_bit_cast(uint32_t, k);
 }
 
+// The two 16-bit values of a word, widened to fp32: bfloat16 (a shift or a
+// mask) or IEEE fp16 (instantiated per format: no per-element select).
+template <bool BF>
+__device__ __forceinline__ void widen_pair(uint32_t w, float &lo, float &hi)
+{
+    if constexpr (BF) {
+        lo = __uint_as_float(w << 16);
+        hi = __uint_as_float(w & 0xFFFF0000u);
+    } else {
+        lo = __half2float(__ushort_as_half(static_cast<uint16_t>(w & 0xFFFFu)));
+        hi = __half2float(__ushort_as_half(static_cast<uint16_t>(w >> 16)));
+    }
+}
+
 // q values of runs i0 + stride * k, k < K, of 8 consecutive elements (fp32,
 // fp16 or bf16; 16-byte aligned): every load is issued before any is used.
 template <int K>
@@ -211,18 +225,25 @@ __device__ __forceinline__ void load_q_runs(const void *q, int dtype, size_t i0,
             r[k][4] = v[k][1].x; r[k][5] = v[k][1].y; r[k][6] = v[k][1].z; r[k][7] = v[k][1].w;
         }
     } else {
-        const int bf = dtype == 2;
         uint4 v[K];
 #pragma unroll
         for (int k = 0; k < K; ++k)
             v[k] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(q) + i0 + stride * k);
+        if (dtype == 2) {
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-            const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+            for (int k = 0; k < K; ++k) {
+                const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                r[k][2 * j] = widen16(static_cast<uint16_t>(w[j] & 0xFFFFu), bf);
-                r[k][2 * j + 1] = widen16(static_cast<uint16_t>(w[j] >> 16), bf);
+                for (int j = 0; j < 4; ++j)
+                    widen_pair<true>(w[j], r[k][2 * j], r[k][2 * j + 1]);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    widen_pair<false>(w[j], r[k][2 * j], r[k][2 * j + 1]);
             }
         }
     }
