@@ -782,14 +782,19 @@ static int attention_launch(kvq_handle *h, int layer, const void *q, float *out,
             // per SIMD, hide each other's load latency, provided they fit one
             // generation of resident workgroups (Llama-2-70B shape: 39.9 ->
             // 35.2 us per call; the Qwen2.5-7B shape would need a second
-            // generation and keeps its units)
+            // generation and keeps its units).  Only recent-token units may
+            // spill past that generation: the quantized units are capped at
+            // its unit slots (Llama-2-70B shape at 257 groups: 130 units left
+            // two quantized units per stream in a late workgroup, 39.6 us;
+            // capped at 128, 36.9 us)
             const long u_simd = (4L * h->cu_count / BH) / 4 * 4;
             if (env_ug == 0) {
                 const long base = std::max<long>(uq, u_simd - ur);
                 const bool walks = base > 0 && (n_groups + base - 1) / base * (d.G / 32) >= 8;
                 const long wgs2 = static_cast<long>(BH) * ((2 * base + ur + 3) / 4);
+                const long fit = 4 * (res_wgs / BH);
                 if (walks && wgs2 * 20 <= res_wgs * 21)
-                    uq = std::min<long>(n_groups, 2 * base);
+                    uq = std::min<long>(n_groups, std::min<long>(2 * base, std::max<long>(base, fit)));
                 else if (u_simd > uq + ur)
                     uq = std::min<long>(n_groups, u_simd - ur);
             }
