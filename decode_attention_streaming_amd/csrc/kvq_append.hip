@@ -64,26 +64,30 @@ __device__ __forceinline__ const uint16_t *src_row(const FlushArgs &a, const uin
     return fresh + (static_cast<size_t>(bh) * a.n_new + (t - a.N0)) * a.D;
 }
 
-// Copy the G x D tile of tokens [t0, t0 + G) into LDS: every thread issues all
-// of its 16-byte loads before storing any (one memory round trip).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Copy the G x D tile of tokens [t0, t0 + G) into LDS, in passes of two
+// 16-byte chunks per thread: a pass issues both loads before storing either
+// (one memory round trip per pass; one pass covers G x D = 4096).  The chunks
+// are native vectors, so they stay in registers (an array of the struct-based
+// vector type was kept in scratch memory, which made each load wait for the
+// one before).  D is a power of two: row and chunk by shifts.
 __device__ __forceinline__ void stage(const FlushArgs &a, const uint16_t *ring, const uint16_t *fresh,
                                       int bh, int t0, uint16_t *tile)
 {
-    constexpr int MAXI = kTileElems / 8 / kThreads;  // 16-byte chunks per thread at most
-    const int D = a.D, chunks = D / 8, n = a.L.G * chunks;
-    uint4 v[MAXI];
-#pragma unroll
-    for (int k = 0; k < MAXI; ++k) {
-        const int it = threadIdx.x + k * kThreads;
-        if (it < n)
-            v[k] = *reinterpret_cast<const uint4 *>(src_row(a, ring, fresh, bh, t0 + it / chunks) +
-                                                    (it % chunks) * 8);
-    }
-#pragma unroll
-    for (int k = 0; k < MAXI; ++k) {
-        const int it = threadIdx.x + k * kThreads;
-        if (it < n)
-            *reinterpret_cast<uint4 *>(tile + (it / chunks) * D + (it % chunks) * 8) = v[k];
+    const int D = a.D, cs = __builtin_ctz(static_cast<unsigned>(D / 8)), n = a.L.G << cs;
+    const int cmask = (1 << cs) - 1;
+    for (int base = 0; base < n; base += 2 * kThreads) {
+        const int i0 = base + threadIdx.x, i1 = i0 + kThreads;
+        u32x4 v0 = u32x4{0u, 0u, 0u, 0u}, v1 = v0;
+        if (i0 < n)
+            v0 = *reinterpret_cast<const u32x4 *>(src_row(a, ring, fresh, bh, t0 + (i0 >> cs)) + (i0 & cmask) * 8);
+        if (i1 < n)
+            v1 = *reinterpret_cast<const u32x4 *>(src_row(a, ring, fresh, bh, t0 + (i1 >> cs)) + (i1 & cmask) * 8);
+        if (i0 < n)
+            *reinterpret_cast<u32x4 *>(tile + (i0 >> cs) * D + (i0 & cmask) * 8) = v0;
+        if (i1 < n)
+            *reinterpret_cast<u32x4 *>(tile + (i1 >> cs) * D + (i1 & cmask) * 8) = v1;
     }
 }
 

@@ -173,25 +173,29 @@ __host__ __device__ inline int valu_lds_bytes(int g, int D)
 
 // Cooperative copies into LDS.  Every thread first issues all of its global
 // loads (up to MAXI 16-byte chunks, predicated), then stores them: one memory
-// round trip per stage instead of one per loop iteration.
+// round trip per stage instead of one per loop iteration.  The chunks are
+// native vectors, which stay in registers (an array of the struct-based uint4
+// under predicated loads was kept in scratch memory, one round trip per load).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // n 32-bit words from src (16-byte aligned when n is a multiple of 4).
 template <int MAXI>
 __device__ __forceinline__ void stage_words(uint32_t *dst, const uint32_t *src, int n)
 {
     if ((n & 3) == 0 && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
-        uint4 v[MAXI];
+        u32x4_t v[MAXI];
 #pragma unroll
         for (int k = 0; k < MAXI; ++k) {
             const int i = threadIdx.x + k * kAttnThreads;
+            v[k] = u32x4_t{0u, 0u, 0u, 0u};
             if (i < n / 4)
-                v[k] = reinterpret_cast<const uint4 *>(src)[i];
+                v[k] = reinterpret_cast<const u32x4_t *>(src)[i];
         }
 #pragma unroll
         for (int k = 0; k < MAXI; ++k) {
             const int i = threadIdx.x + k * kAttnThreads;
             if (i < n / 4)
-                reinterpret_cast<uint4 *>(dst)[i] = v[k];
+                reinterpret_cast<u32x4_t *>(dst)[i] = v[k];
         }
     } else {
         uint32_t v[4 * MAXI];
@@ -218,24 +222,25 @@ __device__ __forceinline__ void stage_ring(uint16_t *dst, uint16_t *ring, int R,
                                            const uint16_t *new_row, int new_t)
 {
     constexpr int CH = D / 8;  // 16-byte chunks per row
-    uint4 v[MAXI];
+    u32x4_t v[MAXI];
 #pragma unroll
     for (int k = 0; k < MAXI; ++k) {
         const int it = threadIdx.x + k * kAttnThreads;
+        v[k] = u32x4_t{0u, 0u, 0u, 0u};
         if (it < n * CH) {
             const int t = t0 + it / CH;
             const uint16_t *row = (t == new_t) ? new_row : ring + static_cast<size_t>(t % R) * D;
-            v[k] = reinterpret_cast<const uint4 *>(row)[it % CH];
+            v[k] = reinterpret_cast<const u32x4_t *>(row)[it % CH];
         }
     }
 #pragma unroll
     for (int k = 0; k < MAXI; ++k) {
         const int it = threadIdx.x + k * kAttnThreads;
         if (it < n * CH) {
-            reinterpret_cast<uint4 *>(dst + (it / CH) * D)[it % CH] = v[k];
+            reinterpret_cast<u32x4_t *>(dst + (it / CH) * D)[it % CH] = v[k];
             const int t = t0 + it / CH;
             if (t == new_t)
-                reinterpret_cast<uint4 *>(ring + static_cast<size_t>(t % R) * D)[it % CH] = v[k];
+                reinterpret_cast<u32x4_t *>(ring + static_cast<size_t>(t % R) * D)[it % CH] = v[k];
         }
     }
 }
