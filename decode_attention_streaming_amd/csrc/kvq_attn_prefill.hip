@@ -245,12 +245,16 @@ __device__ void prefill_tile(const PrefillArgs &a, int bh, int tile, int lane, u
     const int jq = col / g, h = col - jq * g;
     const int qi = tile * a.QT + jq;
     const bool act = jq < a.QT && qi < a.n_q;
-    const int p_col = act ? a.N - a.n_q + qi : -1;  // last token this column sees
+    // this stream's sequence length and quantized tokens (per sequence when ragged)
+    const int sb = a.ragged ? bh / a.Hkv : 0;
+    const int N = a.ragged ? a.seqN[sb] : a.N;
+    const int Tq = a.ragged ? a.seqTq[sb] : a.Tq;
+    const int p_col = act ? N - a.n_q + qi : -1;  // last token this column sees
     const size_t qrow = (static_cast<size_t>(bh * g + (act ? h : 0)) * a.n_q + (act ? qi : 0)) * D;
     // tokens [0, t_end) cover every column of the tile (uniform)
     const int qi_last = min(a.n_q - 1, tile * a.QT + a.QT - 1);
-    const int t_end = a.N - a.n_q + qi_last + 1;
-    const int tq_end = min(a.Tq, (t_end + 31) & ~31);  // quantized blocks to visit
+    const int t_end = N - a.n_q + qi_last + 1;
+    const int tq_end = min(Tq, (t_end + 31) & ~31);  // quantized blocks to visit
 
     ColState<MT> st;
 #pragma unroll
@@ -529,11 +533,11 @@ __device__ void prefill_tile(const PrefillArgs &a, int bh, int tile, int lane, u
                 st.O[m][j] = ldexpf(st.O[m][j], E) + ZB;
     }
 
-    if (a.Tq < t_end) {
+    if (Tq < t_end) {
         if (a.kv_bf16)
-            prefill_recent<D, true>(a, bh, qrow, act, p_col, a.Tq, t_end, lane, vt, st);
+            prefill_recent<D, true>(a, bh, qrow, act, p_col, Tq, t_end, lane, vt, st);
         else
-            prefill_recent<D, false>(a, bh, qrow, act, p_col, a.Tq, t_end, lane, vt, st);
+            prefill_recent<D, false>(a, bh, qrow, act, p_col, Tq, t_end, lane, vt, st);
     }
 
     const float Lc = col_sum(st.l_run);

@@ -121,6 +121,10 @@ struct PrefillArgs {
     int QT, n_tiles, n_wg;
     int ngcap;       // capq / G
     float scale_log2;  // log2(e) / sqrt(D)
+    // ragged layer: sequence b = bh / Hkv holds seqN[b] tokens, seqTq[b] of
+    // them quantized (N and Tq unused)
+    int ragged, Hkv;
+    int seqN[kMaxRaggedSeqs], seqTq[kMaxRaggedSeqs];
 };
 
 // LDS floats per wave of the matrix-core kernel, one region used three ways:

@@ -601,10 +601,16 @@ int kvq_prefill_attention(kvq_handle *h, int layer, const void *q, int n_q, floa
         return rc;
     const LayerState &s = h->plan.layers[layer];
     const kvq::LayerDev &d = s.dev;
-    if (s.ragged)
-        return h->fail(KVQ_EUNSUPPORTED, "layer %d holds sequences of different lengths", layer);
-    if (n_q < 1 || n_q > s.N)
-        return h->fail(KVQ_EINVAL, "n_q = %d outside [1, %d] (tokens in layer %d)", n_q, s.N, layer);
+    int n_min = s.N;
+    if (s.ragged) {
+        if (h->cfg.batch > kvq::kMaxRaggedSeqs)
+            return h->fail(KVQ_EUNSUPPORTED, "a ragged layer's prefill attention takes at most %d sequences",
+                           kvq::kMaxRaggedSeqs);
+        n_min = *std::min_element(s.seqN.begin(), s.seqN.end());
+    }
+    if (n_q < 1 || n_q > n_min)
+        return h->fail(KVQ_EINVAL, "n_q = %d outside [1, %d] (tokens in the shortest sequence of layer %d)", n_q,
+                       n_min, layer);
     const int D = h->cfg.head_dim;
     if (!kvq::prefill_supported(d.kb, d.vb, D, d.v_tiled))
         return h->fail(KVQ_EUNSUPPORTED,
@@ -625,6 +631,12 @@ int kvq_prefill_attention(kvq_handle *h, int layer, const void *q, int n_q, floa
     a.N = s.N;
     a.Tq = s.Tq;
     a.n_q = n_q;
+    a.ragged = s.ragged ? 1 : 0;
+    a.Hkv = h->cfg.n_kv_heads;
+    for (int b = 0; b < kvq::kMaxRaggedSeqs; ++b) {
+        a.seqN[b] = s.ragged && b < h->cfg.batch ? s.seqN[b] : 0;
+        a.seqTq[b] = s.ragged && b < h->cfg.batch ? s.seqTq[b] : 0;
+    }
     a.QT = 16 / g;
     a.n_tiles = (n_q + a.QT - 1) / a.QT;
     const long units = static_cast<long>(a.BH) * a.n_tiles;

@@ -151,10 +151,10 @@ int kvq_append(kvq_handle *h, int layer, const void *k_new, const void *v_new, i
  *   k_new, v_new: device pointers, [batch][n_kv_heads][n_max][head_dim] in
  *   kv_dtype, 16-byte aligned; sequence b uses rows [0, n_new[b]).
  *   n_new: host array of batch counts, 0 <= n_new[b] <= n_max.
- * After appends of different counts the layer is ragged: decode attention
- * (either call) then takes each sequence's own tokens, for batch <= 64
- * (KVQ_EUNSUPPORTED above); prefill attention and kvq_export_layer() refuse
- * it (use kvq_export_sequence()).
+ * After appends of different counts the layer is ragged: decode and prefill
+ * attention then take each sequence's own tokens, for batch <= 64
+ * (KVQ_EUNSUPPORTED above); kvq_export_layer() refuses it (use
+ * kvq_export_sequence()).
  * Errors: KVQ_EINVAL, KVQ_ECAPACITY (a sequence would exceed max_context; no
  * sequence is changed), KVQ_EDEVICE. */
 int kvq_append_ragged(kvq_handle *h, int layer, const void *k_new, const void *v_new, const int32_t *n_new,
@@ -185,7 +185,8 @@ int kvq_append_decode_attention(kvq_handle *h, int layer, const void *k_new, con
 
 /* Causal attention of a prefill chunk over the cache as stored: the queries of
  * the last n_q tokens appended to `layer` (append the chunk's K and V first),
- * query j (0 <= j < n_q, position p = N - n_q + j) attending to tokens 0..p,
+ * query j (0 <= j < n_q, position p = N - n_q + j) attending to tokens 0..p
+ * (on a ragged layer N is each sequence's own length),
  * quantized tokens dequantized on the fly and recent tokens in 16 bits, scale
  * 1/sqrt(head_dim).  (KVTuner summary, A3 attention equation: the query of step
  * i attends to the keys of steps up to i; A2: calibration runs prefill attention
@@ -193,11 +194,11 @@ int kvq_append_decode_attention(kvq_handle *h, int layer, const void *k_new, con
  *   q:   device pointer, [batch][n_q_heads][n_q][head_dim] in q_dtype,
  *        16-byte aligned.
  *   out: device pointer, [batch][n_q_heads][n_q][head_dim] fp32, 16-byte aligned.
- *   1 <= n_q <= tokens in the layer.
+ *   1 <= n_q <= tokens in the layer (in its shortest sequence when ragged).
  * Supported layers: k_bits in {2, 4, 8} (either Key mode) or 3 (head_dim 128),
  * v_bits in {2, 4, 8}, with group_size a multiple of 32; or (16, 16) layers.
  * Errors: KVQ_EINVAL (bad layer, pointer or n_q), KVQ_EUNSUPPORTED (layer
- * format), KVQ_EDEVICE. */
+ * format; a ragged layer of more than 64 sequences), KVQ_EDEVICE. */
 int kvq_prefill_attention(kvq_handle *h, int layer, const void *q, int n_q, float *out);
 
 /* Live bytes of the cache state over all layers, host arithmetic only: per

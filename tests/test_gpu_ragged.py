@@ -10,7 +10,8 @@ import pytest
 import torch
 
 from decode_attention_streaming_amd import kvq, synth
-from gpu_common import ad_hoc_workload, check_attention, compare_export, make_cache, make_oracle, stream_view
+from gpu_common import (MAX_ABS, REL_L2, ad_hoc_workload, check_attention, compare_export, make_cache,
+                        make_oracle, stream_view)
 
 pytestmark = pytest.mark.gpu
 
@@ -101,9 +102,10 @@ def test_ragged_refusals_and_uniform_again():
     k, v = synth.layer_tokens(w, 0, 0, 60, DEV)
     cache.append_ragged(0, k, v, [60, 20])
     q = synth.queries(w, 0, 4, DEV).permute(1, 2, 0, 3).contiguous()
+    q21 = synth.queries(w, 0, 21, DEV).permute(1, 2, 0, 3).contiguous()
     with pytest.raises(kvq.KvqError) as e:
-        cache.prefill_attention(0, q)
-    assert e.value.code == kvq.KVQ_EUNSUPPORTED
+        cache.prefill_attention(0, q21)  # more queries than the shorter sequence holds
+    assert e.value.code == kvq.KVQ_EINVAL
     with pytest.raises(kvq.KvqError) as e:
         cache.export(0)
     assert e.value.code == kvq.KVQ_EINVAL
@@ -117,4 +119,54 @@ def test_ragged_refusals_and_uniform_again():
     cache.prefill_attention(0, q)
     cache.export(0)
     torch.cuda.synchronize()
+    cache.close()
+
+
+PREFILL_CASES = {
+    # name: (B, Hq, Hkv, d, kb, vb, G, R, k_mode, rpc, kv, q, lengths before the chunk, n_q)
+    "k4v2_g4": (4, 8, 2, 128, 4, 2, 32, 32, 0, 0, "bf16", "bf16", [300, 37, 129, 1], 24),
+    "k3v4_d128_recent_ratio": (3, 8, 2, 128, 3, 4, 32, 64, 0, 250, "f16", "f16", [400, 61, 200], 40),
+    "k8v8_per_token_key_g8": (2, 16, 2, 128, 8, 8, 64, 64, 1, 0, "bf16", "f32", [257, 64], 33),
+    "plain16_d64": (3, 4, 2, 64, 16, 16, 32, 32, 0, 0, "f16", "f32", [70, 3, 33], 5),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PREFILL_CASES))
+def test_ragged_prefill_parity(name):
+    """Prefill attention on a ragged layer: after a ragged fill, one uniform
+    append of an n_q-token chunk, whose queries then attend causally over each
+    sequence's own tokens (query j of sequence b at position N_b - n_q + j)."""
+    B, Hq, Hkv, d, kb, vb, G, R, km, rpc, kv, qd, lens, n_q = PREFILL_CASES[name]
+    lc = (kb, vb, R, km, rpc)
+    n_max = max(lens)
+    w = ad_hoc_workload(sorted(PREFILL_CASES).index(name) + 8100, B, Hq, Hkv, d, kb, vb, G, R,
+                        n_max + n_q + 8, kv, qd)
+    w.layers = [lc]
+    print("ragged prefill case", name, flush=True)
+    cache = make_cache(w, layers=[lc])
+    orcs = _oracles(w, lc, B)
+    st = synth.LayerStats(w, 0, 0)
+    k, v = synth.layer_tokens(w, 0, 0, n_max, DEV, stats=st)
+    cache.append_ragged(0, k, v, lens)
+    for b in range(B):
+        orcs[b].append(stream_view(k[b:b + 1, :, :lens[b]].contiguous()),
+                       stream_view(v[b:b + 1, :, :lens[b]].contiguous()))
+    k, v = synth.layer_tokens(w, 0, n_max, n_q, DEV, stats=st)
+    cache.append(0, k, v)
+    for b in range(B):
+        orcs[b].append(stream_view(k[b:b + 1]), stream_view(v[b:b + 1]))
+    q = synth.queries(w, 0, n_q, DEV, seed=3).permute(1, 2, 0, 3).contiguous()
+    out = cache.prefill_attention(0, q)
+    torch.cuda.synchronize()
+    _check_state(cache, orcs)
+    g = Hq // Hkv
+    for b in range(B):
+        qb = synth.as_f64(q[b].reshape(Hkv, g, n_q, d))
+        ref = orcs[b].prefill_attention(qb)
+        ob = synth.as_f64(out[b].reshape(Hkv, g, n_q, d))
+        diff = ob - ref
+        rel = np.linalg.norm(diff) / np.linalg.norm(ref)
+        mx = np.abs(diff).max()
+        print("  seq %d N=%d Tq=%d rel-L2 %.2e max-abs %.2e" % (b, orcs[b].N, orcs[b].Tq, rel, mx), flush=True)
+        assert np.isfinite(rel) and rel <= REL_L2 and mx <= MAX_ABS, (name, b, rel, mx)
     cache.close()
