@@ -167,12 +167,12 @@ def cpu_baseline(w, seconds, layers_sample):
 MFMA_F16_PEAK_TFLOPS = 2500.0
 
 
-def prefill_leg(cache, w, C, N, qbytes, rounds, stream, dev):
+def prefill_leg(cache, w, C, ends, qbytes, rounds, stream, dev):
     """Causal attention of the last C tokens' queries over every layer's cache
-    (the chunk is already appended), timed with HIP events on the library's
-    stream over back-to-back calls.  Algorithmic flops: 2 d per visible (query
-    head, token) pair for q.K and 2 d for P.V; algorithmic bytes: the layer's
-    cache state once, q and out."""
+    (the chunk is already appended; sequence b holds ends[b] tokens), timed
+    with HIP events on the library's stream over back-to-back calls.
+    Algorithmic flops: 2 d per visible (query head, token) pair for q.K and
+    2 d for P.V; algorithmic bytes: the layer's cache state once, q and out."""
     import torch
 
     from decode_attention_streaming_amd import synth
@@ -191,16 +191,17 @@ def prefill_leg(cache, w, C, N, qbytes, rounds, stream, dev):
     ev1.record(stream)
     torch.cuda.synchronize()
     call_us = ev0.elapsed_time(ev1) * 1e3 / (rounds * L)
-    visible = C * (N - C) + C * (C + 1) // 2  # (query, token) pairs per head
-    flops = 4.0 * d * visible * B * Hq
+    visible = sum(C * (n - C) + C * (C + 1) // 2 for n in ends)  # (query, token) pairs per head
+    flops = 4.0 * d * visible * Hq
     nbytes = 0
     for lc in w.layers:
         kb, vb, R, kt, rpc = layer_row(lc)
-        nbytes += B * Hkv * stream_state_bytes(d, kb, vb, w.G, N, quantized_count(N, R, w.G, kb, rpc), kt)
+        nbytes += Hkv * sum(stream_state_bytes(d, kb, vb, w.G, n, quantized_count(n, R, w.G, kb, rpc), kt)
+                            for n in ends)
     nbytes = nbytes / L + B * Hq * C * d * (qbytes + 4)
     tflops = flops / (call_us * 1e-6) / 1e12
     return {
-        "chunk": C, "context": N, "avg_call_us": round(call_us, 3),
+        "chunk": C, "context": ends[0] if len(set(ends)) == 1 else ends, "avg_call_us": round(call_us, 3),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4)},
         "gbs": round(nbytes / (call_us * 1e-6) / 1e9, 1),
@@ -306,7 +307,6 @@ def main():
     ms_per_step = wall / args.steps * 1e3
 
     # the state the library reports agrees with the byte model used above
-    N_end = max(ctx) + total
     ends = [c + total for c in ctx]
     for l, lc in enumerate(w.layers):
         kb, vb, R, kt, rpc = layer_row(lc)
@@ -366,10 +366,10 @@ def main():
         args.ragged or args.rpc) else None
 
     prefill = None
-    C = min(args.prefill_chunk, N_end)
-    if C > 0 and not args.ragged and (w.head_dim == 128 or all(lc[0] != 3 for lc in w.layers)) and w.G % 32 == 0:
-        prefill = prefill_leg(cache, w, C, N_end, qbytes, rounds, stream, dev)
-        if C == 256 and args.k_mode == "per-channel":
+    C = min(args.prefill_chunk, min(ends))
+    if C > 0 and (w.head_dim == 128 or all(lc[0] != 3 for lc in w.layers)) and w.G % 32 == 0:
+        prefill = prefill_leg(cache, w, C, ends, qbytes, rounds, stream, dev)
+        if C == 256 and args.k_mode == "per-channel" and not (args.ragged or args.rpc):
             prefill["roofline"]["traffic"] = stored_traffic(args.workload, args.table, "prefill")
 
     if args.copy_mb > 0:  # a plain copy of known size, for scaling memory counters
