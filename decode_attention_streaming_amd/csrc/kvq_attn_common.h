@@ -627,7 +627,7 @@ __device__ __forceinline__ void arrive_and_merge(const AttnArgs &a, int bh, unsi
             const unsigned x = xcd_id();
             const unsigned inc = 1u << (4 * x);
             const unsigned v =
-                __hip_atomic_fetch_add(a.counters + bh, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + inc;
+                __hip_atomic_fetch_add(a.counters + bh * kCounterStride, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + inc;
             unsigned total = 0;
 #pragma unroll
             for (int j = 0; j < 8; ++j)
@@ -635,7 +635,7 @@ __device__ __forceinline__ void arrive_and_merge(const AttnArgs &a, int bh, unsi
             s_last = total == n_wgs ? (((v >> (4 * x)) & 15u) == n_wgs ? 2 : 1) : 0;
         } else {
             const unsigned prev =
-                __hip_atomic_fetch_add(a.counters + bh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_add(a.counters + bh * kCounterStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             s_last = (prev == n_wgs - 1);
         }
     }
@@ -666,7 +666,7 @@ __device__ __forceinline__ void arrive_and_merge(const AttnArgs &a, int bh, unsi
     else
         merge_stream<D, 16>(a, bh, n_sub, tid_item, tid_sub, s_m, s_d, s_acc, xcd_local);
     if (tid == 0)
-        __hip_atomic_store(a.counters + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.counters + bh * kCounterStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace kvq

@@ -54,6 +54,11 @@ struct RingArgs {
     int D, n_new, N0, t_first, t_last, BH;
 };
 
+// Arrival counters of the attention launches: one per stream, each on a
+// 128-byte line of its own, so that the device-scope atomics of different
+// streams do not queue on one line.
+constexpr int kCounterStride = 32;  // u32 words between consecutive streams' counters
+
 // Sequences one attention launch can take with lengths of their own.
 constexpr int kMaxRaggedSeqs = 64;
 
@@ -62,7 +67,7 @@ struct AttnArgs {
     const void *q;        // [B][Hq][D] in q_dtype
     float *out;           // [B][Hq][D]
     float *part;          // [BH][n_part][g][D + 4]: o[D], m (log2 domain), l, 2 unused
-    unsigned *counters;   // [BH] arrival counters, zero between calls
+    unsigned *counters;   // arrival counter of stream bh at bh * kCounterStride, zero between calls
     int q_dtype, kv_bf16;
     int D, g, Hkv, N, Tq, BH;
     int n_part;           // partial entries per stream (one per workgroup)

@@ -199,7 +199,7 @@ int plan_layout(const kvq_config *cfg, Plan *plan, std::string *err)
     plan->off_part = off;
     off = align_up(off + static_cast<size_t>(cfg->batch) * cfg->n_q_heads * kMaxPart * (D + 4) * 4, A);
     plan->off_cnt = off;
-    off = align_up(off + BH * 4, A);
+    off = align_up(off + BH * 4 * kvq::kCounterStride, A);
     plan->total = off;
     return KVQ_OK;
 }
@@ -670,7 +670,7 @@ static int attention_launch(kvq_handle *h, int layer, const void *q, float *out,
     hipError_t e;
     unsigned *counters = reinterpret_cast<unsigned *>(h->ws + h->plan.off_cnt);
     if (!h->counters_ready) {
-        e = kvq::launch_zero(counters, BH, h->stream);
+        e = kvq::launch_zero(counters, BH * kvq::kCounterStride, h->stream);
         if (e != hipSuccess)
             return h->dev_fail(e, "counter init");
         h->counters_ready = true;
