@@ -47,14 +47,14 @@ struct PartBuf {
 
     __device__ PartBuf(const AttnArgs &a, int bh)
     {
-        const size_t n = static_cast<size_t>(a.n_part) * a.g * part_stride(a.D);
+        const size_t n = static_cast<size_t>(a.n_part) * part_entry_floats(a.g, a.D);
         r = __builtin_amdgcn_make_buffer_rsrc(a.part + static_cast<size_t>(bh) * n, 0,
                                               static_cast<int>(n * 4), 0x00020000);
     }
     // float offset of (entry, head, channel)
     __device__ int off(const AttnArgs &a, int entry, int h, int c) const
     {
-        return (entry * a.g + h) * part_stride(a.D) + c;
+        return entry * part_entry_floats(a.g, a.D) + h * part_stride(a.D) + c;
     }
     __device__ void store4(int off_f, f4_t v) const
     {
@@ -465,7 +465,7 @@ __device__ void valu_range(const AttnArgs &a, const RaggedTables *rt, int bh, in
     }
 
     const int ps = part_stride(D);
-    float *part = a.part + (static_cast<size_t>(bh) * a.n_part + slot) * g * ps;
+    float *part = a.part + (static_cast<size_t>(bh) * a.n_part + slot) * part_entry_floats(g, D);
 #pragma unroll
     for (int k = 0; k < GM; ++k) {
         const int h = oh0 + k * hstep;

@@ -59,6 +59,14 @@ struct RingArgs {
 // streams do not queue on one line.
 constexpr int kCounterStride = 32;  // u32 words between consecutive streams' counters
 
+// Floats of one workgroup's partial entry (g heads of o[D], m, l and two
+// unused floats), rounded up to whole 128-byte lines so that the entries of
+// different workgroups share no line.
+__host__ __device__ inline int part_entry_floats(int g, int D)
+{
+    return (g * (D + 4) + 31) & ~31;
+}
+
 // Sequences one attention launch can take with lengths of their own.
 constexpr int kMaxRaggedSeqs = 64;
 
@@ -66,7 +74,7 @@ struct AttnArgs {
     LayerDev L;
     const void *q;        // [B][Hq][D] in q_dtype
     float *out;           // [B][Hq][D]
-    float *part;          // [BH][n_part][g][D + 4]: o[D], m (log2 domain), l, 2 unused
+    float *part;          // [BH][n_part] entries of part_entry_floats(g, D): [g][D + 4] o[D], m (log2 domain), l, 2 unused
     unsigned *counters;   // arrival counter of stream bh at bh * kCounterStride, zero between calls
     int q_dtype, kv_bf16;
     int D, g, Hkv, N, Tq, BH;

@@ -197,7 +197,8 @@ int plan_layout(const kvq_config *cfg, Plan *plan, std::string *err)
         off = align_up(off + BH * static_cast<size_t>(d.R) * D * 2, A);
     }
     plan->off_part = off;
-    off = align_up(off + static_cast<size_t>(cfg->batch) * cfg->n_q_heads * kMaxPart * (D + 4) * 4, A);
+    off = align_up(off + BH * kMaxPart * static_cast<size_t>(kvq::part_entry_floats(cfg->n_q_heads / cfg->n_kv_heads, D)) * 4,
+                   A);
     plan->off_cnt = off;
     off = align_up(off + BH * 4 * kvq::kCounterStride, A);
     plan->total = off;
