@@ -32,7 +32,25 @@ MUTANTS = {
                            "const int keep = (int)(((long long)current * (1000 - L->rpc_permille)) / 1000);"),
     "pack_msb_first": ("*shift = bits * (c % per_word);",
                        "*shift = 32 - bits * (1 + c % per_word);"),
+    # per-token Key
+    "k_tok_qmax_of_value_bits": ("kvqo_quantize(x, d, 1, (1 << L->k_bits) - 1, codes, 1,",
+                                 "kvqo_quantize(x, d, 1, (1 << L->v_bits) - 1, codes, 1,"),
+    "k_tok_dequant_zero_as_scale": (
+        "return (double)row_codes[c] * (double)L->k_scale[tt] + (double)L->k_zero[tt];",
+        "return (double)row_codes[c] * (double)L->k_scale[tt] + (double)L->k_scale[tt];"),
+    "k_tok_dequant_other_token": (
+        "return (double)row_codes[c] * (double)L->k_scale[tt] + (double)L->k_zero[tt];",
+        "return (double)row_codes[c] * (double)L->k_scale[tt ^ 1] + (double)L->k_zero[tt ^ 1];"),
+    # live byte count
+    "bytes_k_tok_meta_per_channel": ("long long kmeta = k_tok ? Tq * 8LL : (Tq / G) * 8LL * d;",
+                                     "long long kmeta = (Tq / G) * 8LL * d;"),
+    "bytes_v_meta_dropped": ("long long vmeta = Tq * 8LL;", "long long vmeta = 0;"),
+    "bytes_recent_one_tensor": ("return code_bytes + kmeta + vmeta + Tr * 4LL * d;",
+                                "return code_bytes + kmeta + vmeta + Tr * 2LL * d;"),
 }
+
+# pin suites run against each mutant
+PIN_FILES = ["test_oracle_pins.py", "test_oracle_key_per_token.py"]
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
@@ -47,6 +65,6 @@ def test_pins_catch_mutant(name, tmp_path):
                            "-fPIC", "-shared", str(tmp_path / "kvq_oracle.c"), "-o", str(so), "-lm"])
     env = dict(os.environ, KVQ_ORACLE_SO=str(so))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        ] + [os.path.join(ROOT, "tests", f) for f in PIN_FILES],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, "pins did not catch mutant %s\n%s" % (name, r.stdout[-2000:])

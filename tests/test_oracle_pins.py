@@ -562,3 +562,40 @@ def test_rpc_prefill_token_by_token_and_attention_on_grid(kb, vb, G, R, r, N, g,
         assert np.asarray(ea[key]).tobytes() == np.asarray(eb[key]).tobytes(), key
     q = rng.standard_normal((S, g, d))
     np.testing.assert_allclose(a.attention(q), _sdpa64(q, K, V), rtol=1e-11, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Byte accounting against the stored state (KIVI notes, section 2.1: the KV
+# size is what the cache holds; KVTuner summary, A3: codes plus one scale and
+# zero per quantization group)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kb,vb,k_tok,rpc,G,R,N", [
+    (2, 2, False, 0, 32, 32, 150), (3, 4, False, 0, 32, 40, 170), (4, 2, False, 0, 16, 16, 75),
+    (4, 4, False, 0, 32, 32, 33), (8, 4, False, 0, 8, 24, 61), (8, 8, False, 0, 32, 32, 96),
+    (2, 8, True, 0, 16, 16, 90), (4, 2, True, 0, 32, 48, 130), (8, 8, True, 0, 8, 8, 41),
+    (4, 4, False, 200, 8, 50, 140), (3, 2, False, 100, 16, 80, 230), (4, 2, True, 150, 8, 40, 111),
+    (16, 16, False, 0, 32, 32, 70), (4, 2, False, 0, 32, 32, 20)])
+def test_live_bytes_equal_exported_state(kb, vb, k_tok, rpc, G, R, N):
+    """The live byte count is the size of the state the layer actually holds:
+    Layer.bytes() equals the summed sizes of the arrays its canonical export
+    returns (packed K and V words, K and V scales and zeros, 16-bit recent K and
+    V), for every bit pair, both Key modes, a recent-token ratio and a layer kept
+    in 16 bits, before and after flushes.  The export's array shapes come from
+    the stored state (tokens held, words per row, one scale and zero per group
+    and channel or per token), not from the byte formula."""
+    rng = np.random.default_rng(1000 + kb * 100 + vb * 10 + N)
+    S, d, g = 3, 64, 2
+    lay = ora.Layer(S, g, d, kb, vb, G, R, N + 8, kb == 4, k_tok=k_tok, rpc_permille=rpc)
+    seen = set()
+    for n in (N // 3, 1, N - N // 3 - 1):
+        if n <= 0:
+            continue
+        lay.append(_rand_tokens(rng, S, n, d, kb == 4), _rand_tokens(rng, S, n, d, kb == 4))
+        ex = lay.export()
+        held = sum(ex[k].nbytes for k in ("k_words", "k_scale", "k_zero", "v_words", "v_scale",
+                                           "v_zero", "res_k", "res_v"))
+        assert lay.bytes() == held, (lay.N, lay.Tq)
+        seen.add(lay.Tq > 0)
+    if kb != 16 and N > R:
+        assert True in seen  # the case crossed at least one flush
