@@ -54,17 +54,21 @@ struct RingArgs {
     int D, n_new, N0, t_first, t_last, BH;
 };
 
-// Arrival counters of the attention launches: one per stream, each on a
-// 128-byte line of its own, so that the device-scope atomics of different
-// streams do not queue on one line.
-constexpr int kCounterStride = 32;  // u32 words between consecutive streams' counters
+// Hand-off words of the attention launches: one 64-bit word per stream, each
+// on a 128-byte line of its own (so that the device-scope atomics of different
+// streams do not queue on one line): bits 63..32 hold the stream's call epoch,
+// bits 31..0 the workgroups of the current call that have finished.  The
+// workgroup that finishes last stores (epoch + 1) << 32 and merges the call's
+// partial entries.  Initialised to 1 << 32 with every partial entry zeroed.
+constexpr int kCounterStride = 32;  // u32 words between consecutive streams' hand-off words
 
-// Floats of one workgroup's partial entry (g heads of o[D], m, l and two
-// unused floats), rounded up to whole 128-byte lines so that the entries of
-// different workgroups share no line.
-__host__ __device__ inline int part_entry_floats(int g, int D)
+// 64-bit slots of one workgroup's partial entry: for each of the g heads, o[D],
+// m (log2 domain) and l, each slot holding a float and the call epoch (low and
+// high 32 bits, written and read as one 8-byte access), rounded up to whole
+// 128-byte lines so that the entries of different workgroups share no line.
+__host__ __device__ inline int part_entry_slots(int g, int D)
 {
-    return (g * (D + 4) + 31) & ~31;
+    return (g * (D + 2) + 15) & ~15;
 }
 
 // Sequences one attention launch can take with lengths of their own.
@@ -74,8 +78,8 @@ struct AttnArgs {
     LayerDev L;
     const void *q;        // [B][Hq][D] in q_dtype
     float *out;           // [B][Hq][D]
-    float *part;          // [BH][n_part] entries of part_entry_floats(g, D): [g][D + 4] o[D], m (log2 domain), l, 2 unused
-    unsigned *counters;   // arrival counter of stream bh at bh * kCounterStride, zero between calls
+    unsigned long long *part;  // [BH][n_part] entries of part_entry_slots(g, D): [g][D + 2] (value, epoch)
+    unsigned *counters;   // hand-off word of stream bh at bh * kCounterStride (64-bit, see above)
     int q_dtype, kv_bf16;
     int D, g, Hkv, N, Tq, BH;
     int n_part;           // partial entries per stream (one per workgroup)
@@ -174,6 +178,10 @@ bool mfma_supported(int kb, int vb, int D);
 // rt: per-sequence lengths of a ragged batch, or nullptr
 hipError_t launch_attention(const AttnArgs &a, const RaggedTables *rt, bool use_mfma, hipStream_t st);
 hipError_t launch_zero(unsigned *p, int n, hipStream_t st);
+// Hand-off state of n_streams streams: words (stride kCounterStride u32) set to
+// 1 << 32, and n_part_slots partial slots zeroed.
+hipError_t launch_handoff_init(unsigned *counters, int n_streams, unsigned long long *part, size_t n_part_slots,
+                               hipStream_t st);
 // True when the prefill kernel is built for this layer format.
 bool prefill_supported(int kb, int vb, int D, int v_tiled);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st);

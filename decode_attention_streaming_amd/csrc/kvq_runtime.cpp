@@ -197,7 +197,7 @@ int plan_layout(const kvq_config *cfg, Plan *plan, std::string *err)
         off = align_up(off + BH * static_cast<size_t>(d.R) * D * 2, A);
     }
     plan->off_part = off;
-    off = align_up(off + BH * kMaxPart * static_cast<size_t>(kvq::part_entry_floats(cfg->n_q_heads / cfg->n_kv_heads, D)) * 4,
+    off = align_up(off + BH * kMaxPart * static_cast<size_t>(kvq::part_entry_slots(cfg->n_q_heads / cfg->n_kv_heads, D)) * 8,
                    A);
     plan->off_cnt = off;
     off = align_up(off + BH * 4 * kvq::kCounterStride, A);
@@ -670,17 +670,21 @@ static int attention_launch(kvq_handle *h, int layer, const void *q, float *out,
     const kvq::LayerDev &d = s.dev;
     hipError_t e;
     unsigned *counters = reinterpret_cast<unsigned *>(h->ws + h->plan.off_cnt);
+    unsigned long long *part = reinterpret_cast<unsigned long long *>(h->ws + h->plan.off_part);
+    const size_t part_slots = static_cast<size_t>(BH) * kMaxPart *
+                              kvq::part_entry_slots(h->cfg.n_q_heads / h->cfg.n_kv_heads, D);
     if (!h->counters_ready) {
-        e = kvq::launch_zero(counters, BH * kvq::kCounterStride, h->stream);
+        // hand-off words at epoch 1, every partial slot at epoch 0
+        e = kvq::launch_handoff_init(counters, BH, part, part_slots, h->stream);
         if (e != hipSuccess)
-            return h->dev_fail(e, "counter init");
+            return h->dev_fail(e, "hand-off init");
         h->counters_ready = true;
     }
     kvq::AttnArgs a;
     a.L = d;
     a.q = q;
     a.out = out;
-    a.part = reinterpret_cast<float *>(h->ws + h->plan.off_part);
+    a.part = part;
     a.counters = counters;
     a.q_dtype = h->cfg.q_dtype;
     a.kv_bf16 = h->cfg.kv_dtype == KVQ_BF16;

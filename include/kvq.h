@@ -251,7 +251,12 @@ int kvq_export_sequence(kvq_handle *h, int layer, int b, uint32_t *k_words, floa
  * stream raised. */
 int kvq_sync(kvq_handle *h);
 
-/* Replace the handle's stream (for calls made after this one). */
+/* Replace the handle's stream (for calls made after this one).  All calls on
+ * one handle share its cache state and its attention hand-off words and
+ * partial results, so its device work must stay ordered: before switching,
+ * the caller makes the new stream wait for the old one (an event, or a
+ * synchronize); attention calls of one handle in flight on two streams at once
+ * would mix each other's partial results. */
 int kvq_set_stream(kvq_handle *h, void *stream);
 
 /* Message of the last failed call on h; with h == NULL, of the last failed

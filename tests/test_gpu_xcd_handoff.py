@@ -47,3 +47,40 @@ def test_xcd_local_handoff(name):
     assert wgs in seen, seen  # the shape ran with the intended number of workgroups per stream
     compare_export(cache.export(0), orc.export())
     cache.close()
+
+
+def test_handoff_interleaved_launch_shapes():
+    """One handle, layers whose calls use very different numbers of workgroups
+    per stream (a long layer, a short one, a medium one), called in turn for
+    several decode steps: each stream's partial entries are rewritten by calls
+    of every size, so an entry left by an earlier, wider call must never be
+    taken for the current call's.  Every output is checked against the
+    oracle."""
+    layers = [(4, 2, 32), (2, 2, 32), (8, 4, 32)]
+    lens = [1900, 40, 330]
+    steps = 5
+    w = synth.Workload(9200, "interleaved", len(layers), 2, 8, 2, 128, max(lens) + 2 * steps, "bf16", "bf16",
+                       32, 32, layers=layers)
+    cache = make_cache(w)
+    orcs, stats = [], []
+    for l, lc in enumerate(layers):
+        orc = make_oracle(w, lc, lens[l] + 2 * steps)
+        st = synth.LayerStats(w, l)
+        k, v = synth.layer_tokens(w, l, 0, lens[l], DEV, stats=st)
+        cache.append(l, k, v)
+        orc.append(stream_view(k), stream_view(v))
+        orcs.append(orc)
+        stats.append(st)
+    wgs = set()
+    for s in range(steps):
+        for l in (0, 1, 2, 1, 0):
+            k, v = synth.layer_tokens(w, l, orcs[l].N, 1, DEV, stats=stats[l])
+            q = synth.query(w, l, 10 * s + l, DEV)
+            out = cache.append_decode_attention(l, k, v, q)
+            orcs[l].append(stream_view(k), stream_view(v))
+            torch.cuda.synchronize()
+            units, variant = kvq.kvq_last_launch(cache.h)
+            wgs.add((units + 3) // 4)
+            check_attention(out, orcs[l].attention(q_streams(q, w.g)), w.g, what="layer %d step %d" % (l, s))
+    assert len(wgs) >= 3 and max(wgs) >= 8, wgs
+    cache.close()
