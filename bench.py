@@ -100,9 +100,9 @@ def kernel_source_digest():
 
 
 def stored_traffic(workload, table, kind="attention"):
-    """HBM bytes per launch (kind: "attention" for decode, "prefill") from the
-    stored FETCH_SIZE / WRITE_SIZE measurement of this workload, or None when
-    the kernels have changed since."""
+    """The stored FETCH_SIZE / WRITE_SIZE measurement of this workload (decode:
+    the record, with the state it was taken at; prefill: HBM bytes per
+    launch), or None when the kernels have changed since."""
     path = os.path.join(ROOT, "profiles", "%s_traffic_workload%d_%s.json" % (kind, workload, table))
     if not os.path.exists(path):
         return None
@@ -110,15 +110,33 @@ def stored_traffic(workload, table, kind="attention"):
         rec = json.load(f)
     if rec.get("kernel_source_digest") != kernel_source_digest():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec if kind == "attention" else rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, seconds, layers_sample):
-    """Time the CPU oracle (single thread) on a sample of the same workload:
-    prefill the sampled layers (untimed), then repeat decode steps (append one
-    token + attention) until `seconds` have passed; scale to all layers."""
-    import numpy as np
-    import torch
+def host_cores():
+    """CPUs this process may run on (read at run time), and the host's model name."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return n, model
+
+
+def _oracle_decode_run(w, layers_sample, threads, seconds):
+    """The oracle as it stands on a sample of the workload: the sampled layers'
+    streams are split into `threads` independent oracle layers (disjoint
+    (sequence, kv-head) streams, so the results do not change), prefilled
+    untimed; then decode steps (append one token + fp64 attention on every
+    stream) run until `seconds` of wall time have passed, each step's oracle
+    calls spread over a pool of `threads` threads (the oracle's C calls release
+    the interpreter lock).  Returns (steps, bytes, elapsed seconds)."""
+    from concurrent.futures import ThreadPoolExecutor
 
     from decode_attention_streaming_amd import synth
     from oracle import oracle as ora
@@ -126,41 +144,76 @@ def cpu_baseline(w, seconds, layers_sample):
     B, Hkv, g, d = w.batch, w.n_kv_heads, w.g, w.head_dim
     BH = B * Hkv
     qb = 2 if w.q_dtype != "f32" else 4
-    cap = w.context + 4096
-    layers = []
+    cap = w.context + 2048
+    bounds = [(BH * i // threads, BH * (i + 1) // threads) for i in range(threads)]
+    parts = []  # (layer index, [(s0, s1, oracle layer)])
     for l in layers_sample:
         kb, vb, R, kt, rpc = layer_row(w.layers[l])
-        o = ora.Layer(BH, g, d, kb, vb, w.G, R, cap, w.kv_dtype == "bf16", k_tok=kt, rpc_permille=rpc)
         k, v = synth.layer_tokens(w, l, 0, w.context, "cpu")
-        o.append(synth.bits16(k.reshape(BH, w.context, d)), synth.bits16(v.reshape(BH, w.context, d)))
-        layers.append((l, o))
-    steps = 0
-    nbytes = 0
+        k16 = synth.bits16(k.reshape(BH, w.context, d))
+        v16 = synth.bits16(v.reshape(BH, w.context, d))
+        subs = []
+        for s0, s1 in bounds:
+            o = ora.Layer(s1 - s0, g, d, kb, vb, w.G, R, cap, w.kv_dtype == "bf16", k_tok=kt, rpc_permille=rpc)
+            o.append(k16[s0:s1], v16[s0:s1])
+            subs.append((s0, s1, o))
+        parts.append((l, subs))
+    steps = nbytes = 0
     el = 0.0  # oracle time only; input generation is excluded
-    while el < seconds:
-        for l, o in layers:
-            k, v = synth.layer_tokens(w, l, o.N, 1, "cpu")
-            q = synth.as_f64(synth.query(w, l, steps, "cpu").reshape(BH, g, d))
-            kb16 = synth.bits16(k.reshape(BH, 1, d))
-            vb16 = synth.bits16(v.reshape(BH, 1, d))
+    with ThreadPoolExecutor(max_workers=threads) as pool:
+        while el < seconds:
+            work = []
+            for l, subs in parts:
+                k, v = synth.layer_tokens(w, l, subs[0][2].N, 1, "cpu")
+                q = synth.as_f64(synth.query(w, l, steps, "cpu").reshape(BH, g, d))
+                kb16 = synth.bits16(k.reshape(BH, 1, d))
+                vb16 = synth.bits16(v.reshape(BH, 1, d))
+                for s0, s1, o in subs:
+                    work.append((o, kb16[s0:s1], vb16[s0:s1], q[s0:s1]))
+
+            def run(item):
+                o, kk, vv, qq = item
+                o.append(kk, vv)
+                o.attention(qq)
+
             t0 = time.perf_counter()
-            o.append(kb16, vb16)
-            o.attention(q)
+            list(pool.map(run, work))
             el += time.perf_counter() - t0
-            nbytes += BH * stream_state_bytes(d, o.k_bits, o.v_bits, o.G, o.N, o.Tq, o.k_tok) + \
-                B * w.n_q_heads * d * (qb + 4) + BH * 2 * d * 2 * 2
-        steps += 1
-    layer_steps = steps * len(layers)
-    step_time = el / layer_steps * len(w.layers)  # one full step over all layers
+            for l, subs in parts:
+                o0 = subs[0][2]
+                nbytes += BH * stream_state_bytes(d, o0.k_bits, o0.v_bits, o0.G, o0.N, o0.Tq, o0.k_tok) + \
+                    B * w.n_q_heads * d * (qb + 4) + BH * 2 * d * 2 * 2
+            steps += 1
+    return steps, nbytes, el
+
+
+def cpu_baseline(w, seconds, layers_sample):
+    """Time the CPU oracle on a sample of the same workload, on one core and
+    on every host core this process may use (core count read at run time), and
+    scale tok/s to all layers."""
+    n_cores, model = host_cores()
+    B, BH = w.batch, w.batch * w.n_kv_heads
+    threads = max(1, min(n_cores, BH))
+    res = {}
+    for key, t, sec in (("one", 1, seconds / 2), ("all", threads, seconds / 2)):
+        steps, nbytes, el = _oracle_decode_run(w, layers_sample, t, sec)
+        step_time = el / steps * len(w.layers) / len(layers_sample)  # one full step over all layers
+        res[key] = dict(value=round(nbytes / el / 1e9, 4), tok_per_s=round(B / step_time, 3), steps=steps,
+                        seconds=round(el, 2), threads=t)
+    one, allc = res["one"], res["all"]
     return {
-        "value": round(nbytes / el / 1e9, 4),
+        "value": allc["value"],
         "unit": "GB/s",
-        "cores": 1,
+        "cores": threads,
         "kind": "oracle",
-        "tok_per_s": round(B / step_time, 3),
-        "sample": "%d decode steps (append 1 token + fp64 attention) on layers %s of %d, all %d "
-                  "streams, %.1f s of oracle time; tok/s scaled to all layers"
-                  % (steps, list(layers_sample), len(w.layers), BH, el),
+        "tok_per_s": allc["tok_per_s"],
+        "one_core": {"value": one["value"], "unit": "GB/s", "tok_per_s": one["tok_per_s"]},
+        "host": {"cpus_available": n_cores, "model": model},
+        "sample": "decode steps (append 1 token + fp64 attention, all %d streams) on layers %s of %d: "
+                  "%d steps in %.1f s on 1 thread, %d steps in %.1f s of wall time on %d threads "
+                  "(streams split into %d independent oracle layers); tok/s scaled to all layers"
+                  % (BH, list(layers_sample), len(w.layers), one["steps"], one["seconds"], allc["steps"],
+                     allc["seconds"], threads, threads),
     }
 
 
@@ -210,6 +263,79 @@ def prefill_leg(cache, w, C, ends, qbytes, rounds, stream, dev):
     }
 
 
+def build_cache(kvq, synth, w, ctx, cap_tokens, dev, ragged):
+    """A cache of workload w holding ctx[b] prefilled tokens per sequence."""
+    L, B, Hq, Hkv, d = w.n_layers, w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim
+    cache = kvq.Cache(L, B, Hq, Hkv, d, cap_tokens, w.kv_dtype, w.q_dtype, w.G, w.R, w.layers)
+    for l in range(L):
+        k, v = synth.layer_tokens(w, l, 0, max(ctx), dev, stats=synth.LayerStats(w, l))
+        if ragged:
+            cache.append_ragged(l, k, v, ctx)
+        else:
+            cache.append(l, k, v)
+        del k, v
+    return cache
+
+
+def decode_inputs(synth, w, t0, n_steps, dev):
+    """Per layer: K and V of the next n_steps tokens ([n_steps, B, Hkv, 1, d])
+    and n_steps queries ([n_steps, B, Hq, d])."""
+    knew, vnew, qs = [], [], []
+    for l in range(w.n_layers):
+        k, v = synth.layer_tokens(w, l, t0, n_steps, dev, stats=synth.LayerStats(w, l))
+        knew.append(k.permute(2, 0, 1, 3).contiguous().unsqueeze(3))
+        vnew.append(v.permute(2, 0, 1, 3).contiguous().unsqueeze(3))
+        qs.append(synth.queries(w, l, n_steps, dev))
+    return knew, vnew, qs
+
+
+def timed_calls(torch, stream, fn, rounds):
+    """Average time of fn() (one round of back-to-back calls) from HIP events
+    on `stream` around `rounds` rounds."""
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()
+    ev0.record(stream)
+    for _ in range(rounds):
+        fn()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) * 1e-3 / rounds
+
+
+def copy_ceiling(torch, stream, nbytes, L, rounds, dev):
+    """Plain device copies timed like the attention calls: L buffers of nbytes
+    (read + write = nbytes per call), cycled back to back; a sum over L buffers
+    of nbytes (a read-only pass); and one 256 MiB copy (the box's streaming
+    rate).  GB/s of bytes moved."""
+    nbytes = int(nbytes)
+    half = max(16, nbytes // 2 // 16 * 16)
+    src = [torch.ones(half // 4, dtype=torch.float32, device=dev) for _ in range(L)]
+    dst = [torch.empty_like(x) for x in src]
+    t_copy = timed_calls(torch, stream, lambda: [b.copy_(a) for a, b in zip(src, dst)], rounds) / L
+    del src, dst
+    full = max(16, nbytes // 16 * 16)
+    bufs = [torch.ones(full // 4, dtype=torch.float32, device=dev) for _ in range(L)]
+    sink = torch.empty(L, dtype=torch.float32, device=dev)
+    t_sum = timed_calls(torch, stream, lambda: [torch.sum(b, dim=0, out=sink[i]) for i, b in enumerate(bufs)],
+                        rounds) / L
+    del bufs
+    big = 256 << 20
+    a = torch.ones(big // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    t_big = timed_calls(torch, stream, lambda: b.copy_(a), 5)
+    del a, b
+    res = {
+        "bytes_per_call": int(nbytes),
+        "copy_gbs": round(2 * half / t_copy / 1e9, 1),
+        "copy_us": round(t_copy * 1e6, 3),
+        "read_sum_gbs": round(full / t_sum / 1e9, 1),
+        "read_sum_us": round(t_sum * 1e6, 3),
+        "stream_copy_256mib_gbs": round(2 * big / t_big / 1e9, 1),
+    }
+    res["ceiling_gbs"] = max(res["copy_gbs"], res["read_sum_gbs"])
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -227,13 +353,16 @@ def main():
                     help="sequences of different lengths: sequence b starts with context x "
                          "(0.25 + 1.5 b / (B - 1)) tokens")
     ap.add_argument("--kernel-rounds", type=int, default=20)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-chunk", type=int, default=256,
                     help="also time causal prefill attention of the last C tokens of every layer "
                          "(0 = skip)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="also run a plain device copy of this size (counter scaling)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the second cache instance, the flush probe, the copy ceiling and the "
+                         "KV8 comparison (shorter runs under a profiler)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -262,35 +391,23 @@ def main():
                     for lc in w.layers]
     L, B, Hq, Hkv, d = w.n_layers, w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim
     total = args.warmup + args.steps
+    probe = 0 if args.no_extras else 2 * w.G  # flush probe: steps after the timed ones
     qbytes = 4 if w.q_dtype == "f32" else 2
     ctx = ragged_contexts(w.context, B) if args.ragged else [w.context] * B
-    cache = kvq.Cache(L, B, Hq, Hkv, d, max(ctx) + total, w.kv_dtype, w.q_dtype, w.G, w.R, w.layers)
+    cap_tokens = max(ctx) + total + probe + 1
+    cache = build_cache(kvq, synth, w, ctx, cap_tokens, dev, args.ragged)
     stream = cache.stream
-
-    # prefill every layer, then stage all decode inputs in HBM
-    knew, vnew, qs = [], [], []
-    for l in range(L):
-        st = synth.LayerStats(w, l)
-        k, v = synth.layer_tokens(w, l, 0, max(ctx), dev, stats=st)
-        if args.ragged:
-            cache.append_ragged(l, k, v, ctx)
-        else:
-            cache.append(l, k, v)
-        del k, v
-        k, v = synth.layer_tokens(w, l, max(ctx), total, dev, stats=st)
-        knew.append(k.permute(2, 0, 1, 3).contiguous().unsqueeze(3))  # [total, B, Hkv, 1, d]
-        vnew.append(v.permute(2, 0, 1, 3).contiguous().unsqueeze(3))
-        qs.append(synth.queries(w, l, total, dev))
+    knew, vnew, qs = decode_inputs(synth, w, max(ctx), total + probe, dev)
     outs = [torch.empty((B, Hq, d), dtype=torch.float32, device=dev) for _ in range(L)]
     torch.cuda.synchronize()
 
-    def step(s):
+    def step(c, s):
         # one call per layer: append one token per sequence, then attend
         for l in range(L):
-            cache.append_decode_attention(l, knew[l][s], vnew[l][s], qs[l][s], outs[l])
+            c.append_decode_attention(l, knew[l][s], vnew[l][s], qs[l][s], outs[l])
 
     for s in range(args.warmup):
-        step(s)
+        step(cache, s)
     torch.cuda.synchronize()
 
     att_bytes = app_bytes = 0
@@ -301,10 +418,17 @@ def main():
 
     t0 = time.perf_counter()
     for s in range(args.warmup, total):
-        step(s)
+        step(cache, s)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall / args.steps * 1e3
+    # flush launches inside the timed steps (a layer whose recent buffer is full)
+    timed_flushes = 0
+    for s in range(args.warmup, total):
+        for lc in w.layers:
+            kb, vb, R, kt, rpc = layer_row(lc)
+            timed_flushes += sum(quantized_count(c + s + 1, R, w.G, kb, rpc) > quantized_count(c + s, R, w.G, kb, rpc)
+                                 for c in ctx)
 
     # the state the library reports agrees with the byte model used above
     ends = [c + total for c in ctx]
@@ -314,21 +438,24 @@ def main():
         assert cache.sequence_lengths(l)[0] == ends
         assert info.total == sum(Hkv * stream_state_bytes(d, kb, vb, w.G, n, quantized_count(n, R, w.G, kb, rpc), kt)
                                  for n in ends)
+    att_per_layer = []
+    for l, lc in enumerate(w.layers):
+        kb, vb, R, kt, rpc = layer_row(lc)
+        att_per_layer.append(sum(Hkv * stream_state_bytes(d, kb, vb, w.G, n, quantized_count(n, R, w.G, kb, rpc), kt)
+                                 for n in ends) + B * Hq * d * (qbytes + 4))
+    avg_att_bytes = sum(att_per_layer) / L
 
     # dominant kernel: decode attention (one launch per call).  HIP events on
     # the stream the library launches on bracket back-to-back calls over every
     # layer (state fixed), several rounds; average = elapsed / calls.
     rounds = args.kernel_rounds
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for l in range(L):  # warm
-        cache.decode_attention(l, qs[l][total - 1], outs[l])
-    ev0.record(stream)
-    for r in range(rounds):
+    qlast = [qs[l][total - 1] for l in range(L)]
+
+    def one_round(c):
         for l in range(L):
-            cache.decode_attention(l, qs[l][total - 1], outs[l])
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    avg_call_us = ev0.elapsed_time(ev1) * 1e3 / (rounds * L)
+            c.decode_attention(l, qlast[l], outs[l])
+
+    avg_call_us = timed_calls(torch, stream, lambda: one_round(cache), rounds) * 1e6 / L
 
     # the same calls captured once in a HIP graph and replayed: no host work
     # between the launches (the library allocates nothing and sets no memory
@@ -339,31 +466,78 @@ def main():
     cache.set_stream(side)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=side):
-        for l in range(L):
-            cache.decode_attention(l, qs[l][total - 1], outs[l])
+        one_round(cache)
     cache.set_stream(stream)
     torch.cuda.synchronize()
     graph.replay()
     torch.cuda.synchronize()
     assert all(torch.equal(o, r) for o, r in zip(outs, ref)), "graph replay differs from eager calls"
-    gev0, gev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    gev0.record()
-    for r in range(rounds):
-        graph.replay()
-    gev1.record()
-    torch.cuda.synchronize()
-    graph_call_us = gev0.elapsed_time(gev1) * 1e3 / (rounds * L)
+    graph_call_us = timed_calls(torch, torch.cuda.current_stream(), graph.replay, rounds) * 1e6 / L
     del graph
-    att_per_layer = []
-    for l, lc in enumerate(w.layers):
-        kb, vb, R, kt, rpc = layer_row(lc)
-        att_per_layer.append(sum(Hkv * stream_state_bytes(d, kb, vb, w.G, n, quantized_count(n, R, w.G, kb, rpc), kt)
-                                 for n in ends) + B * Hq * d * (qbytes + 4))
-    avg_att_bytes = sum(att_per_layer) / L
-    achieved = avg_att_bytes / (avg_call_us * 1e-6) / 1e9
+
+    # a second cache instance with the same state: calls alternate between the
+    # two, so that the working set (2 x all layers) is well beyond the 256 MB
+    # last-level cache and every call reads its state from HBM
+    two_call_us = None
+    if not args.no_extras:
+        cache2 = build_cache(kvq, synth, w, ctx, cap_tokens, dev, args.ragged)
+        for s in range(total):
+            step(cache2, s)
+        outs2 = [torch.empty_like(o) for o in outs]
+
+        def two_rounds():
+            for l in range(L):
+                cache.decode_attention(l, qlast[l], outs[l])
+                cache2.decode_attention(l, qlast[l], outs2[l])
+
+        two_call_us = timed_calls(torch, stream, two_rounds, rounds) * 1e6 / (2 * L)
+        assert all(torch.equal(a, b) for a, b in zip(outs, outs2)), "second instance differs"
+        cache2.close()
+        del cache2, outs2
+        torch.cuda.empty_cache()
+
     splits, variant = kvq.kvq_last_launch(cache.h)
-    traffic = stored_traffic(args.workload, args.table) if args.k_mode == "per-channel" and not (
-        args.ragged or args.rpc) else None
+    call_us = two_call_us if two_call_us is not None else avg_call_us
+    achieved = avg_att_bytes / (call_us * 1e-6) / 1e9
+    traffic = None
+    if args.k_mode == "per-channel" and not (args.ragged or args.rpc):
+        traffic = stored_traffic(args.workload, args.table)
+
+    # flush probe: 2G more steps timed one by one with events; the steps in
+    # which some layer's recent buffer is full carry a flush launch
+    flush = None
+    if probe > 0:
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(probe + 1)]
+        evs[0].record(stream)
+        for i in range(probe):
+            step(cache, total + i)
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        times = [evs[i].elapsed_time(evs[i + 1]) for i in range(probe)]
+        nfl = []
+        for i in range(probe):
+            n = 0
+            for lc in w.layers:
+                kb, vb, R, kt, rpc = layer_row(lc)
+                n += sum(quantized_count(c + total + i + 1, R, w.G, kb, rpc) >
+                         quantized_count(c + total + i, R, w.G, kb, rpc) for c in ctx)
+            nfl.append(n)
+        fl = [t for t, n in zip(times, nfl) if n > 0]
+        plain = [t for t, n in zip(times, nfl) if n == 0]
+        flush = {"probe_steps": probe, "flush_steps": len(fl), "flush_launches": sum(nfl),
+                 "plain_step_ms": round(sum(plain) / len(plain), 4) if plain else None,
+                 "flush_step_ms": round(sum(fl) / len(fl), 4) if fl else None,
+                 "timed_window_flush_launches": timed_flushes}
+        if fl and plain:
+            extra = sum(fl) / len(fl) - sum(plain) / len(plain)
+            flush["extra_ms_per_flush_step"] = round(extra, 4)
+            flush["amortized_ms_per_step"] = round(extra * len(fl) / probe, 4)
+            flush["per_flush_launch_us"] = round(1e3 * extra * len(fl) / sum(nfl), 3)
+        ends = [c + total + probe for c in ctx]
+
+    ceiling = None
+    if not args.no_extras:
+        ceiling = copy_ceiling(torch, stream, avg_att_bytes, L, rounds, dev)
 
     prefill = None
     C = min(args.prefill_chunk, min(ends))
@@ -371,6 +545,36 @@ def main():
         prefill = prefill_leg(cache, w, C, ends, qbytes, rounds, stream, dev)
         if C == 256 and args.k_mode == "per-channel" and not (args.ragged or args.rpc):
             prefill["roofline"]["traffic"] = stored_traffic(args.workload, args.table, "prefill")
+    cache.close()
+    del cache
+    torch.cuda.empty_cache()
+
+    # KIVI-KV8 analogue: the same shape with every layer K8V8, same steps
+    kv8 = None
+    if not args.no_extras and args.table == "default" and args.k_mode == "per-channel" and not (
+            args.ragged or args.rpc) and all(lc[0] != 3 for lc in w.layers):
+        w8 = synth.workload(args.workload)
+        w8.layers = [(8, 8, r) for (_, _, r) in w8.layers]
+        c8 = build_cache(kvq, synth, w8, ctx, cap_tokens, dev, False)
+        for s in range(args.warmup):
+            step(c8, s)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(args.warmup, total):
+            step(c8, s)
+        torch.cuda.synchronize()
+        wall8 = time.perf_counter() - t0
+        a8 = p8 = 0
+        for s in range(args.warmup, total):
+            a, p = step_bytes(w8, [c + s for c in ctx], qbytes)
+            a8 += a
+            p8 += p
+        c8.close()
+        del c8
+        kv8 = {"table": "K8V8 on every layer", "ms_per_step": round(wall8 / args.steps * 1e3, 4),
+               "tok_per_s": round(B * args.steps / wall8, 1), "gbs": round((a8 + p8) / wall8 / 1e9, 2),
+               "bytes_ratio_vs_table": round((a8 + p8) / (att_bytes + app_bytes), 3),
+               "table_speedup_vs_kv8": round(wall8 / wall, 3)}
 
     if args.copy_mb > 0:  # a plain copy of known size, for scaling memory counters
         n = args.copy_mb * (1 << 20)
@@ -392,7 +596,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16/bf16 matrix-core products (fp32 factors as hi+lo fp16 pairs), fp32 accumulation",
         "data": "synthetic",
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tok_per_s": round(B * args.steps / wall, 1),
@@ -413,20 +617,34 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
+            "traffic": traffic["hbm_bytes_per_launch"] if traffic else None,
             "kernel": "decode attention (one launch per call: split units + in-kernel merge), "
                       "variant %d (1 = matrix core), %d work units per stream" % (variant, splits),
-            "avg_call_us": round(avg_call_us, 3),
+            "avg_call_us": round(call_us, 3),
+            "timing": ("two cache instances with the same state, calls alternating (working set %.0f MB)"
+                       % (2 * sum(att_per_layer) / 1e6)) if two_call_us is not None else
+                      "one cache instance, calls over every layer",
+            "single_instance_avg_call_us": round(avg_call_us, 3),
             "graph_avg_call_us": round(graph_call_us, 3),
             "bytes_per_call": int(avg_att_bytes),
+            "state_tokens": max(c + total for c in ctx),
         },
     }
+    if traffic:
+        res["roofline"]["traffic_measured"] = {
+            k: traffic.get(k) for k in ("state_tokens", "algorithmic_bytes_per_launch", "ratio")}
+    if ceiling is not None:
+        ceiling["frac_of_ceiling"] = round(achieved / ceiling["ceiling_gbs"], 4)
+        res["roofline"]["copy_ceiling"] = ceiling
+    if flush is not None:
+        res["flush"] = flush
     if prefill is not None:
         res["prefill"] = prefill
+    if kv8 is not None:
+        res["kv8_comparison"] = kv8
     if not args.no_cpu_baseline and not args.ragged:
         sample = [0, 1] if L >= 2 else [0]
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, sample)
-    cache.close()
     print(json.dumps(res))
 
 
