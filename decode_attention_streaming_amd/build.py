@@ -16,7 +16,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # (source, object name, extra flags); the matrix-core kernels are built once per head_dim
 SOURCES = [("kvq_runtime.cpp", "kvq_runtime", []), ("kvq_append.hip", "kvq_append", []),
-           ("kvq_attention.hip", "kvq_attention", [])] + [
+           ("kvq_attention.hip", "kvq_attention", []), ("kvq_scratch.hip", "kvq_scratch", [])] + [
     ("kvq_attn_mfma.hip", "kvq_attn_mfma_d%d" % d, ["-DKVQ_D=%d" % d]) for d in (64, 128, 256)] + [
     ("kvq_attn_prefill.hip", "kvq_attn_prefill_d%d" % d, ["-DKVQ_D=%d" % d]) for d in (64, 128, 256)]
 FLAGS = [

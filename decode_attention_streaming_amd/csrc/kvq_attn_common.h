@@ -706,7 +706,8 @@ __device__ __forceinline__ void finish_stream(const AttnArgs &a, int bh, int ent
             __hip_atomic_fetch_add(handoff_word(a, bh), 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = static_cast<unsigned>(prev) == n_wgs - 1;
         if (s_last)  // every workgroup of this call has arrived: the word is free for the next call
-            __hip_atomic_store(handoff_word(a, bh), static_cast<unsigned long long>(epoch + 1) << 32,
+            __hip_atomic_store(handoff_word(a, bh),
+                               static_cast<unsigned long long>(a.reset_after ? 1u : epoch + 1) << 32,
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
@@ -732,6 +733,15 @@ __device__ __forceinline__ void finish_stream(const AttnArgs &a, int bh, int ent
         merge_stream<D, 4>(a, bh, epoch, own_entry, n_sub, tid_item, tid_sub, lds, own_m, own_l, s_m, s_d, s_acc);
     else
         merge_stream<D, 8>(a, bh, epoch, own_entry, n_sub, tid_item, tid_sub, lds, own_m, own_l, s_m, s_d, s_acc);
+    if (a.reset_after) {
+        // every slot of the call has been read (each thread loaded its own
+        // before the barrier); back to the initial state: all slots zero
+        __syncthreads();
+        unsigned long long *p = part_entry(a, bh, 0);
+        const int n = P * part_entry_slots(a.g, D);
+        for (int i = tid; i < n; i += kAttnThreads)
+            __hip_atomic_store(p + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 }  // namespace kvq

@@ -71,6 +71,20 @@ __host__ __device__ inline int part_entry_slots(int g, int D)
     return (g * (D + 2) + 15) & ~15;
 }
 
+// The statically allocated scratch of kvq_decode_attention_noalloc(): hand-off
+// words of up to kStaticScratchStreams streams (one 128-byte line each), then
+// the partial entries of one call (a stream's entries contiguous, as in a
+// workspace).  Between two calls every word holds epoch 1 with no arrivals and
+// every partial slot is zero: the merging workgroup of each stream restores
+// that state after it has read the call's slots (AttnArgs::reset_after).
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+constexpr int kStaticScratchStreams = 4096;
+constexpr size_t kStaticScratchWordsBytes = size_t(kStaticScratchStreams) * kCounterStride * 4;
+
+// Device address of this GPU's static scratch (set up on first use: its
+// hand-off state is initialised on stream st).
+hipError_t static_scratch(int device, hipStream_t st, void **out);
+
 // Sequences one attention launch can take with lengths of their own.
 constexpr int kMaxRaggedSeqs = 64;
 
@@ -80,6 +94,10 @@ struct AttnArgs {
     float *out;           // [B][Hq][D]
     unsigned long long *part;  // [BH][n_part] entries of part_entry_slots(g, D): [g][D + 2] (value, epoch)
     unsigned *counters;   // hand-off word of stream bh at bh * kCounterStride (64-bit, see above)
+    // 0: the merging workgroup leaves the next epoch in the word; 1 (static
+    // scratch): it leaves epoch 1 and zeroes the call's partial slots, so that
+    // the next call, of any handle and shape, starts from the initial state
+    int reset_after;
     int q_dtype, kv_bf16;
     int D, g, Hkv, N, Tq, BH;
     int n_part;           // partial entries per stream (one per workgroup)

@@ -518,7 +518,8 @@ static int check_attention_args(kvq_handle *h, int layer, const void *q, const f
 // new_t was appended but is not in the ring yet (its rows are new_k / new_v);
 // the launch also stores it there.
 static int attention_launch(kvq_handle *h, int layer, const void *q, float *out, const void *new_k,
-                            const void *new_v, int new_t, const int *seq_new_t = nullptr);
+                            const void *new_v, int new_t, const int *seq_new_t = nullptr,
+                            bool static_scratch = false);
 
 int kvq_decode_attention(kvq_handle *h, int layer, const void *q, float *out)
 {
@@ -532,6 +533,20 @@ int kvq_decode_attention(kvq_handle *h, int layer, const void *q, float *out)
         if (s.seqN[b] == 0)
             return h->fail(KVQ_EINVAL, "layer %d holds no tokens for sequence %d", layer, b);
     return attention_launch(h, layer, q, out, nullptr, nullptr, -1);
+}
+
+int kvq_decode_attention_noalloc(kvq_handle *h, int layer, const void *q, float *out)
+{
+    if (!h)
+        return KVQ_EINVAL;
+    const int rc = check_attention_args(h, layer, q, out);
+    if (rc != KVQ_OK)
+        return rc;
+    const LayerState &s = h->plan.layers[layer];
+    for (int b = 0; b < h->cfg.batch; ++b)
+        if (s.seqN[b] == 0)
+            return h->fail(KVQ_EINVAL, "layer %d holds no tokens for sequence %d", layer, b);
+    return attention_launch(h, layer, q, out, nullptr, nullptr, -1, nullptr, true);
 }
 
 int kvq_append_decode_attention(kvq_handle *h, int layer, const void *k_new, const void *v_new, const void *q,
@@ -654,38 +669,26 @@ int kvq_prefill_attention(kvq_handle *h, int layer, const void *q, int n_q, floa
 }
 
 static int attention_launch(kvq_handle *h, int layer, const void *q, float *out, const void *new_k,
-                            const void *new_v, int new_t, const int *seq_new_t)
+                            const void *new_v, int new_t, const int *seq_new_t, bool static_scratch)
 {
     LayerState &s = h->plan.layers[layer];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return h->dev_fail(e, "device query");
     if (h->cu_count == 0) {
-        int dev = 0, n = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e == hipSuccess)
-            e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        int n = 0;
+        e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess)
             return h->dev_fail(e, "device query");
         h->cu_count = n > 0 ? n : 256;
     }
     const int D = h->cfg.head_dim, BH = h->BH();
     const kvq::LayerDev &d = s.dev;
-    hipError_t e;
-    unsigned *counters = reinterpret_cast<unsigned *>(h->ws + h->plan.off_cnt);
-    unsigned long long *part = reinterpret_cast<unsigned long long *>(h->ws + h->plan.off_part);
-    const size_t part_slots = static_cast<size_t>(BH) * kMaxPart *
-                              kvq::part_entry_slots(h->cfg.n_q_heads / h->cfg.n_kv_heads, D);
-    if (!h->counters_ready) {
-        // hand-off words at epoch 1, every partial slot at epoch 0
-        e = kvq::launch_handoff_init(counters, BH, part, part_slots, h->stream);
-        if (e != hipSuccess)
-            return h->dev_fail(e, "hand-off init");
-        h->counters_ready = true;
-    }
     kvq::AttnArgs a;
     a.L = d;
     a.q = q;
     a.out = out;
-    a.part = part;
-    a.counters = counters;
     a.q_dtype = h->cfg.q_dtype;
     a.kv_bf16 = h->cfg.kv_dtype == KVQ_BF16;
     a.D = D;
@@ -888,6 +891,37 @@ static int attention_launch(kvq_handle *h, int layer, const void *q, float *out,
     a.n_part = use_mfma ? a.mfma_wgs : a.valu_wgs;
     if (a.n_part < 1 || a.n_part > kMaxPart)
         return h->fail(KVQ_EINVAL, "internal: %d partial entries per stream", a.n_part);
+    const int g = h->cfg.n_q_heads / h->cfg.n_kv_heads;
+    if (static_scratch) {
+        // hand-off words and this call's partial entries in the library's
+        // static scratch, left in their initial state by the call itself
+        const size_t need = static_cast<size_t>(BH) * a.n_part * kvq::part_entry_slots(g, D) * 8;
+        if (BH > kvq::kStaticScratchStreams || need > kvq::kStaticScratchBytes - kvq::kStaticScratchWordsBytes)
+            return h->fail(KVQ_ENOMEM,
+                           "layer %d: %d streams x %d partial entries need %zu bytes of static scratch; at most %d "
+                           "streams and %zu bytes are available",
+                           layer, BH, a.n_part, need, kvq::kStaticScratchStreams,
+                           kvq::kStaticScratchBytes - kvq::kStaticScratchWordsBytes);
+        void *p = nullptr;
+        e = kvq::static_scratch(dev, h->stream, &p);
+        if (e != hipSuccess)
+            return h->dev_fail(e, "static scratch set-up");
+        a.counters = static_cast<unsigned *>(p);
+        a.part = reinterpret_cast<unsigned long long *>(static_cast<char *>(p) + kvq::kStaticScratchWordsBytes);
+        a.reset_after = 1;
+    } else {
+        a.counters = reinterpret_cast<unsigned *>(h->ws + h->plan.off_cnt);
+        a.part = reinterpret_cast<unsigned long long *>(h->ws + h->plan.off_part);
+        a.reset_after = 0;
+        if (!h->counters_ready) {
+            // hand-off words at epoch 1, every partial slot at epoch 0
+            const size_t part_slots = static_cast<size_t>(BH) * kMaxPart * kvq::part_entry_slots(g, D);
+            e = kvq::launch_handoff_init(a.counters, BH, a.part, part_slots, h->stream);
+            if (e != hipSuccess)
+                return h->dev_fail(e, "hand-off init");
+            h->counters_ready = true;
+        }
+    }
     e = kvq::launch_attention(a, s.ragged ? &rt : nullptr, use_mfma, h->stream);
     if (e != hipSuccess)
         return h->dev_fail(e, "attention launch");

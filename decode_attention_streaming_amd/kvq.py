@@ -21,7 +21,8 @@ _DT = {"f32": KVQ_F32, "f16": KVQ_F16, "bf16": KVQ_BF16}
 EXPORTED = ["kvq_workspace_bytes", "kvq_create", "kvq_append", "kvq_decode_attention",
             "kvq_append_decode_attention", "kvq_bytes", "kvq_bytes_layer", "kvq_export_layer", "kvq_sync",
             "kvq_set_stream", "kvq_last_error", "kvq_destroy", "kvq_last_launch", "kvq_prefill_attention",
-            "kvq_append_ragged", "kvq_sequence_lengths", "kvq_export_sequence"]
+            "kvq_append_ragged", "kvq_sequence_lengths", "kvq_export_sequence",
+            "kvq_decode_attention_noalloc"]
 
 
 KVQ_K_PER_CHANNEL, KVQ_K_PER_TOKEN = 0, 1
@@ -84,6 +85,7 @@ def lib():
         "kvq_append_ragged": (I, [P, I, P, P, P, I]),
         "kvq_sequence_lengths": (I, [P, I, P, P]),
         "kvq_export_sequence": (I, [P, I, I] + [P] * 8),
+        "kvq_decode_attention_noalloc": (I, [P, I, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -130,6 +132,10 @@ def kvq_append(h, layer, k_ptr, v_ptr, n_new):
 
 def kvq_decode_attention(h, layer, q_ptr, out_ptr):
     return _check(lib().kvq_decode_attention(h, layer, q_ptr, out_ptr), h)
+
+
+def kvq_decode_attention_noalloc(h, layer, q_ptr, out_ptr):
+    return _check(lib().kvq_decode_attention_noalloc(h, layer, q_ptr, out_ptr), h)
 
 
 def kvq_append_decode_attention(h, layer, k_ptr, v_ptr, q_ptr, out_ptr):
@@ -281,6 +287,14 @@ class Cache:
         out = self._q_check(q, out)
         kvq_decode_attention(self.h, layer, ctypes.c_void_p(q.data_ptr()),
                              ctypes.c_void_p(out.data_ptr()))
+        return out
+
+    def decode_attention_noalloc(self, layer, q, out=None):
+        """decode_attention() with its hand-off in the library's static scratch
+        (no device memory of the handle's workspace is used for it)."""
+        out = self._q_check(q, out)
+        kvq_decode_attention_noalloc(self.h, layer, ctypes.c_void_p(q.data_ptr()),
+                                     ctypes.c_void_p(out.data_ptr()))
         return out
 
     def append_decode_attention(self, layer, k_new, v_new, q, out=None):

@@ -173,6 +173,28 @@ int kvq_sequence_lengths(const kvq_handle *h, int layer, int32_t *n_tokens, int3
  * KVQ_EDEVICE. */
 int kvq_decode_attention(kvq_handle *h, int layer, const void *q, float *out);
 
+/* kvq_decode_attention() for callers that cannot allocate device memory or
+ * must not (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same kernels and the same result, bit for bit, but
+ * the hand-off between the workgroups of each (sequence, kv-head) stream --
+ * per-stream hand-off words and the partial results of the call's workgroups
+ * -- lives in the library's static device buffer instead of the handle's
+ * workspace.  That buffer is 16 MiB per GPU, allocated when the library's code
+ * is loaded and held until the process ends; on each GPU it is set up (its
+ * address looked up and its hand-off state initialised by one small kernel on
+ * the handle's stream) by the first call made there.  This call allocates
+ * nothing: no hipMalloc, no hipFree.
+ * Every call on one GPU, from any handle, shares that GPU's buffer, and each
+ * call leaves it in its initial state when it completes: calls that overlap in
+ * time on one GPU (different streams, different threads) race and give wrong
+ * results; order them on one stream or with events.
+ * Errors: those of kvq_decode_attention(), and KVQ_ENOMEM when the call would
+ * need more than 4096 streams (batch x n_kv_heads) or more than 16 MiB - 512
+ * KiB of partial results (batch x n_kv_heads x workgroups per stream x
+ * (n_q_heads / n_kv_heads) x (head_dim + 2) x 8 bytes, each stream's entries
+ * rounded up to 128 bytes); nothing is enqueued then. */
+int kvq_decode_attention_noalloc(kvq_handle *h, int layer, const void *q, float *out);
+
 /* One decode step of one layer: kvq_append of one token per sequence
  * (k_new, v_new: [batch][n_kv_heads][1][head_dim]) followed by
  * kvq_decode_attention, with results identical to those two calls (state,

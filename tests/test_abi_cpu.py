@@ -134,6 +134,9 @@ def test_handle_validation_leaves_state_unchanged():
             (lambda: kvq.kvq_decode_attention(h, 0, p, p), kvq.KVQ_EINVAL, "no tokens"),
             (lambda: kvq.kvq_decode_attention(h, 1, None, p), kvq.KVQ_EINVAL, "NULL"),
             (lambda: kvq.kvq_decode_attention(h, 5, p, p), kvq.KVQ_EINVAL, "out of range"),
+            (lambda: kvq.kvq_decode_attention_noalloc(h, 0, p, p), kvq.KVQ_EINVAL, "no tokens"),
+            (lambda: kvq.kvq_decode_attention_noalloc(h, 1, None, p), kvq.KVQ_EINVAL, "NULL"),
+            (lambda: kvq.kvq_decode_attention_noalloc(h, 5, p, p), kvq.KVQ_EINVAL, "out of range"),
             (lambda: kvq.kvq_bytes_layer(h, 9), kvq.KVQ_EINVAL, "out of range"),
             (lambda: kvq.kvq_prefill_attention(h, 0, p, 1, p), kvq.KVQ_EINVAL, "n_q = 1 outside"),
             (lambda: kvq.kvq_prefill_attention(h, 0, p, 0, p), kvq.KVQ_EINVAL, "n_q = 0 outside"),
