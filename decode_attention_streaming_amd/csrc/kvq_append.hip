@@ -139,6 +139,8 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a)
     const int t0 = a.Tq0 + j * G;
     const int gi = t0 / G;
     const int bf = a.kv_bf16;
+    const QAddr qa(a.L, bh);  // rows of the group's tokens (one page when paged)
+    const size_t row0 = qa.row(t0);
 
     __shared__ uint16_t tile[kTileElems];
     __shared__ float red_mn[kThreads], red_mx[kThreads];
@@ -149,7 +151,7 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a)
         stage(a, a.L.ring_k, a.k_new, bh, t0, tile);
         __syncthreads();
         const int kb = a.L.kb, kq = (1 << kb) - 1, wk = a.L.wk;
-        token_scales(tile, G, D, bf, kq, a.L.k_meta + (static_cast<size_t>(bh) * a.L.capq + t0) * 2, s_c, mn_c,
+        token_scales(tile, G, D, bf, kq, a.L.k_meta + row0 * 2, s_c, mn_c,
                      red_mn, red_mx);
         const int epw = 32 / kb;
         for (int it = tid; it < G * wk; it += kThreads) {
@@ -159,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a)
                 const int cc = w * epw + sl;
                 word |= code_of(widen16(tile[i * D + cc], bf), mn_c[i], s_c[i], kq) << (kb * sl);
             }
-            a.L.k_words[(static_cast<size_t>(bh) * a.L.capq + t0 + i) * wk + w] = word;
+            a.L.k_words[(row0 + i) * wk + w] = word;
         }
     } else if (!is_v) {
         // ---- Key: min / max per channel over the G tokens ----
@@ -184,7 +186,7 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a)
             const float s = (mx - mn) / static_cast<float>(qmax_of(a.L.kb, c));
             s_c[c] = s;
             mn_c[c] = mn;
-            float *meta = a.L.k_meta + (static_cast<size_t>(bh) * (a.L.capq / G) + gi) * 2 * D;
+            float *meta = a.L.k_meta + qa.grp(gi) * 2 * D;
             meta[c] = (s == 0.0f) ? 0.0f : s;
             meta[D + c] = (mn == 0.0f) ? 0.0f : mn;
         }
@@ -209,18 +211,18 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a)
                     word |= code_of(widen16(row[cc], bf), mn_c[cc], s_c[cc], qm) << (kb * sl);
                 }
             }
-            a.L.k_words[(static_cast<size_t>(bh) * a.L.capq + t0 + i) * wk + w] = word;
+            a.L.k_words[(row0 + i) * wk + w] = word;
         }
     } else {
         // ---- Value: min / max per token over the D channels, tpt threads per token ----
         stage(a, a.L.ring_v, a.v_new, bh, t0, tile);
         __syncthreads();
         const int vb = a.L.vb, vq = (1 << vb) - 1;
-        token_scales(tile, G, D, bf, vq, a.L.v_meta + (static_cast<size_t>(bh) * a.L.capq + t0) * 2, s_c, mn_c,
+        token_scales(tile, G, D, bf, vq, a.L.v_meta + row0 * 2, s_c, mn_c,
                      red_mn, red_mx);
 
         const int wv = a.L.wv;
-        uint32_t *vrow0 = a.L.v_words + (static_cast<size_t>(bh) * a.L.capq + t0) * wv;
+        uint32_t *vrow0 = a.L.v_words + row0 * wv;
         if (a.L.v_tiled) {
             // 32-token blocks of operand fragments (layout in kvq_layout.h)
             const int fw = D * vb / 64, P = 16 / vb, blk_words = D * vb;

@@ -156,18 +156,6 @@ __device__ __forceinline__ uint32_t row_code(const uint32_t *row, int bits, int 
     return (row[bitpos >> 5] >> (bitpos & 31)) & ((1u << bits) - 1u);
 }
 
-// V code of token t (quantized), channel c, in either V layout.
-__device__ __forceinline__ uint32_t v_code(const LayerDev &L, int bh, int t, int c, int D)
-{
-    const uint32_t *base = L.v_words + static_cast<size_t>(bh) * L.capq * L.wv;
-    if (L.v_tiled) {
-        int word, bit;
-        v_tile_pos(t & 31, c, L.vb, D, &word, &bit);
-        return (base[static_cast<size_t>(t & ~31) * L.wv + word] >> bit) & ((1u << L.vb) - 1u);
-    }
-    return row_code(base + static_cast<size_t>(t) * L.wv, L.vb, c);
-}
-
 // Tokens per tile of the vector-ALU pass: 16 KB of 16-bit K (or V) per tile.
 template <int D>
 constexpr int valu_tile() { return 8192 / D; }
@@ -315,16 +303,18 @@ __device__ void valu_range(const AttnArgs &a, const RaggedTables *rt, int bh, in
         l[k] = 0.0f;
     }
 
-    const int ngcap = L.capq / L.G;
-    const size_t row0 = static_cast<size_t>(bh) * L.capq;
+    const QAddr qa(L, bh);  // rows of the stream's tokens (through the page table when paged)
     for (int tile = t_beg; tile < t_end;) {
         const bool quant = tile < sd.Tq;
         const int tend = min(min(tile + TT, t_end), quant ? sd.Tq : t_end);
         const int nt = tend - tile;
         __syncthreads();  // previous tile's LDS reads are done (and q is staged)
         if (quant) {
-            stage_words<4>(k_tile, L.k_words + (row0 + tile) * L.wk, nt * L.wk);
-            stage_words<4>(v_tile, L.v_words + (row0 + tile) * L.wv, nt * L.wv);
+            // a tile never crosses a page: tiles start at multiples of its
+            // length, which divides the page length
+            const size_t r0 = qa.row(tile);
+            stage_words<4>(k_tile, L.k_words + r0 * L.wk, nt * L.wk);
+            stage_words<4>(v_tile, L.v_words + r0 * L.wv, nt * L.wv);
         } else {
             stage_ring<D, 4>(reinterpret_cast<uint16_t *>(k_tile), L.ring_k + static_cast<size_t>(bh) * L.R * D,
                              L.R, tile, nt, a.new_k + static_cast<size_t>(bh) * D, sd.new_t);
@@ -339,14 +329,14 @@ __device__ void valu_range(const AttnArgs &a, const RaggedTables *rt, int bh, in
         float vs = 1.0f, vz = 0.0f;
         if (quant && valid && L.k_tok) {
             // per-token Key: one scale and zero for the whole row
-            const float2 k2 = *reinterpret_cast<const float2 *>(L.k_meta + (row0 + t) * 2);
+            const float2 k2 = *reinterpret_cast<const float2 *>(L.k_meta + qa.row(t) * 2);
 #pragma unroll
             for (int i = 0; i < CPT; ++i) {
                 ks[i] = k2.x;
                 kz[i] = k2.y;
             }
         } else if (quant && valid) {
-            const float *km = L.k_meta + (static_cast<size_t>(bh) * ngcap + t / L.G) * 2 * D + c0;
+            const float *km = L.k_meta + qa.grp(t / L.G) * 2 * D + c0;
 #pragma unroll
             for (int i = 0; i < CPT; i += 4) {
                 const float4 s4 = *reinterpret_cast<const float4 *>(km + i);
@@ -356,7 +346,7 @@ __device__ void valu_range(const AttnArgs &a, const RaggedTables *rt, int bh, in
             }
         }
         if (quant && valid) {
-            const float2 vm = *reinterpret_cast<const float2 *>(L.v_meta + (row0 + t) * 2);
+            const float2 vm = *reinterpret_cast<const float2 *>(L.v_meta + qa.row(t) * 2);
             vs = vm.x;
             vz = vm.y;
         }

@@ -113,11 +113,8 @@ __device__ void mfma_unit(const AttnArgs &a, const RaggedTables *rt, int bh, int
     const int g_end = g_beg + sd.unit_groups + (unit < sd.unit_extra ? 1 : 0);
     const int bpg = G / 32;  // blocks per group
 
-    const uint32_t *kw_base = L.k_words + static_cast<size_t>(bh) * L.capq * L.wk + q * KW;
-    const uint32_t *vw_base = L.v_words + static_cast<size_t>(bh) * L.capq * L.wv + lane * FW;
-    const float *vm_base = L.v_meta + static_cast<size_t>(bh) * L.capq * 2;
-    constexpr bool ktok = KT;  // per-token Key
-    const float *km_tok = L.k_meta + static_cast<size_t>(bh) * L.capq * 2;  // its [capq][2] meta
+    const QAddr qa(L, bh);  // rows of the stream's tokens (through the page table when paged)
+    constexpr bool ktok = KT;  // per-token Key (its meta: 2 floats per row)
 
     float m_run = -INFINITY, l_run = 0.0f, zb_run = 0.0f;
     int E = -1000;  // running V-scale exponent of this column: its weights carry 2^-E
@@ -136,11 +133,13 @@ __device__ void mfma_unit(const AttnArgs &a, const RaggedTables *rt, int bh, int
     const int qbytes = a.q_dtype == 0 ? 4 : 2;
     float *q_lds = meta_lds + NG * 2 * D;
     auto setup_issue = [&](int w0, int nwin) {
-        const float *src = L.k_meta + (static_cast<size_t>(bh) * a.ngcap + w0) * 2 * D;
+        constexpr int gp_log2 = __builtin_ctz(D / 2);  // 16-byte pieces per group: D / 2
         const int n16 = ktok ? 0 : nwin * D / 2;  // 16-byte pieces of nwin groups' [2][D] floats
         for (int i0 = 0; i0 < n16; i0 += 64) {
-            if (i0 + lane < n16)
-                __builtin_amdgcn_global_load_lds(src + 4 * (i0 + lane), meta_lds + 4 * i0, 16, 0, 0);
+            const int i = i0 + lane, j = i >> gp_log2;  // piece i of group w0 + j
+            if (i < n16)
+                __builtin_amdgcn_global_load_lds(L.k_meta + qa.grp(w0 + j) * 2 * D + 4 * (i & (D / 2 - 1)),
+                                                 meta_lds + 4 * i0, 16, 0, 0);
         }
         const char *qsrc = static_cast<const char *>(a.q) + static_cast<size_t>(bh) * g * D * qbytes;
         const int nq16 = g * D * qbytes / 16;
@@ -265,24 +264,23 @@ __device__ void mfma_unit(const AttnArgs &a, const RaggedTables *rt, int bh, int
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             if (i < nb) {
-                const int t0 = t_first + i * G;
-                load_words(kw_base + static_cast<size_t>(t0 + col) * L.wk, d.k0[i]);
-                load_words(kw_base + static_cast<size_t>(t0 + 16 + col) * L.wk, d.k1[i]);
-                load_words(vw_base + static_cast<size_t>(t0) * L.wv, d.v[i]);
+                const size_t r0 = qa.row(t_first + i * G);  // the block's 32 rows are consecutive
+                load_words(L.k_words + (r0 + col) * L.wk + q * KW, d.k0[i]);
+                load_words(L.k_words + (r0 + 16 + col) * L.wk + q * KW, d.k1[i]);
+                load_words(L.v_words + r0 * L.wv + lane * FW, d.v[i]);
             }
         }
-        const int tm = t_first + my_b * G;
-        const float4 *m0 = reinterpret_cast<const float4 *>(vm_base + static_cast<size_t>(tm + 4 * q) * 2);
-        const float4 *m1 = reinterpret_cast<const float4 *>(vm_base + static_cast<size_t>(tm + 16 + 4 * q) * 2);
+        const size_t rm = qa.row(t_first + my_b * G);
+        const float4 *m0 = reinterpret_cast<const float4 *>(L.v_meta + (rm + 4 * q) * 2);
+        const float4 *m1 = reinterpret_cast<const float4 *>(L.v_meta + (rm + 16 + 4 * q) * 2);
         d.vm[0] = m0[0];
         d.vm[1] = m0[1];
         d.vm[2] = m1[0];
         d.vm[3] = m1[1];
         if constexpr (KT) {
             {
-                const float4 *k0 = reinterpret_cast<const float4 *>(km_tok + static_cast<size_t>(tm + 4 * q) * 2);
-                const float4 *k1 =
-                    reinterpret_cast<const float4 *>(km_tok + static_cast<size_t>(tm + 16 + 4 * q) * 2);
+                const float4 *k0 = reinterpret_cast<const float4 *>(L.k_meta + (rm + 4 * q) * 2);
+                const float4 *k1 = reinterpret_cast<const float4 *>(L.k_meta + (rm + 16 + 4 * q) * 2);
                 d.km[0] = k0[0];
                 d.km[1] = k0[1];
                 d.km[2] = k1[0];

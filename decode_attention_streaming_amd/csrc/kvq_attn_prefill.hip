@@ -262,10 +262,7 @@ __device__ void prefill_tile(const PrefillArgs &a, int bh, int tile, int lane, u
         st.O[m] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
     if (tq_end > 0) {
-        const uint32_t *kw_base = L.k_words + static_cast<size_t>(bh) * L.capq * L.wk + q * KW;
-        const uint32_t *vw_base = L.v_words + static_cast<size_t>(bh) * L.capq * L.wv + lane * FW;
-        const float *vm_base = L.v_meta + static_cast<size_t>(bh) * L.capq * 2;
-        const float *km_tok = L.k_meta + static_cast<size_t>(bh) * L.capq * 2;
+        const QAddr qa(L, bh);  // rows of the stream's tokens (through the page table when paged)
         float zb_run = 0.0f;
         int E = -1000;  // running V-scale exponent: the weights carry 2^(kWShift - E)
         Frag bhi[NC], blo[NC];
@@ -293,7 +290,7 @@ __device__ void prefill_tile(const PrefillArgs &a, int bh, int tile, int lane, u
         // K scales and zeros of group gi ([2][D] floats) into LDS slot gi & 1
         // with direct-to-LDS loads: no registers held while they fly
         auto meta_issue = [&](int gi) {
-            const float *src = L.k_meta + (static_cast<size_t>(bh) * a.ngcap + gi) * 2 * D;
+            const float *src = L.k_meta + qa.grp(gi) * 2 * D;
             float *dst = meta_lds + (gi & 1) * 2 * D;
             constexpr int n16 = D / 2;  // 16-byte pieces
 #pragma unroll
@@ -382,18 +379,19 @@ __device__ void prefill_tile(const PrefillArgs &a, int bh, int tile, int lane, u
             float4 vm[4], km[4];
         };
         auto load_blk = [&](Blk &b, int t0) {
-            load_words(kw_base + static_cast<size_t>(t0 + col) * L.wk, b.k0);
-            load_words(kw_base + static_cast<size_t>(t0 + 16 + col) * L.wk, b.k1);
-            load_words(vw_base + static_cast<size_t>(t0) * L.wv, b.vw);
-            const float4 *m0 = reinterpret_cast<const float4 *>(vm_base + static_cast<size_t>(t0 + 4 * q) * 2);
-            const float4 *m1 = reinterpret_cast<const float4 *>(vm_base + static_cast<size_t>(t0 + 16 + 4 * q) * 2);
+            const size_t r0 = qa.row(t0);  // the block's 32 rows are consecutive
+            load_words(L.k_words + (r0 + col) * L.wk + q * KW, b.k0);
+            load_words(L.k_words + (r0 + 16 + col) * L.wk + q * KW, b.k1);
+            load_words(L.v_words + r0 * L.wv + lane * FW, b.vw);
+            const float4 *m0 = reinterpret_cast<const float4 *>(L.v_meta + (r0 + 4 * q) * 2);
+            const float4 *m1 = reinterpret_cast<const float4 *>(L.v_meta + (r0 + 16 + 4 * q) * 2);
             b.vm[0] = m0[0];
             b.vm[1] = m0[1];
             b.vm[2] = m1[0];
             b.vm[3] = m1[1];
             if constexpr (KT) {
-                const float4 *c0 = reinterpret_cast<const float4 *>(km_tok + static_cast<size_t>(t0 + 4 * q) * 2);
-                const float4 *c1 = reinterpret_cast<const float4 *>(km_tok + static_cast<size_t>(t0 + 16 + 4 * q) * 2);
+                const float4 *c0 = reinterpret_cast<const float4 *>(L.k_meta + (r0 + 4 * q) * 2);
+                const float4 *c1 = reinterpret_cast<const float4 *>(L.k_meta + (r0 + 16 + 4 * q) * 2);
                 b.km[0] = c0[0];
                 b.km[1] = c0[1];
                 b.km[2] = c1[0];

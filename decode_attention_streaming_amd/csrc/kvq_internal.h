@@ -34,6 +34,57 @@ struct LayerDev {
     int capq;           // quantized-token capacity per stream (multiple of G and 32)
     int v_tiled;        // V code layout, see above
     int k_tok;          // 1: Key quantized per token (k_meta per token), 0: per channel
+    // Paging (table != nullptr): the quantized state lives in a pool of
+    // n_pages pages (plus one spare page that out-of-range page ids fall on),
+    // each holding 2^P_log2 consecutive tokens of one sequence for all Hkv
+    // heads; token t of sequence b is in page table[b * tstride + (t >>
+    // P_log2)].  The arrays above are then [n_pages + 1][Hkv][P][...] instead
+    // of [BH][capq][...].  bh0 is added to a stream index before the table is
+    // read (a view of streams bh0.. of the layer).  Unpaged: table == nullptr.
+    const int32_t *table;
+    int P_log2, Hkv, tstride, n_pages, bh0;
+};
+
+// Addressing of one stream's quantized state: row(t) indexes the rows of
+// k_words (wk words), v_words (wv words), v_meta (2 floats) and the per-token
+// k_meta (2 floats) of token t; grp(gi) the [2][D] per-channel k_meta block of
+// group gi.  A 32-token block (t a multiple of 32) and a whole group stay in
+// one page, so their rows are consecutive.
+struct QAddr {
+    const int32_t *trow;  // the sequence's page ids (paged), or nullptr
+    size_t base;          // unpaged: the stream's first row
+    int h, P_log2, n_pages, Hkv, G;
+
+    __host__ __device__ QAddr(const LayerDev &L, int bh)
+        : trow(nullptr), base(static_cast<size_t>(bh) * L.capq), h(0), P_log2(L.P_log2), n_pages(L.n_pages),
+          Hkv(L.Hkv), G(L.G)
+    {
+        if (L.table) {
+            const int gbh = bh + L.bh0, b = gbh / L.Hkv;
+            trow = L.table + static_cast<size_t>(b) * L.tstride;
+            h = gbh - b * L.Hkv;
+        }
+    }
+    __host__ __device__ size_t page_base(int t) const
+    {
+        int page = trow[t >> P_log2];
+        if (static_cast<unsigned>(page) >= static_cast<unsigned>(n_pages))
+            page = n_pages;  // the spare page: memory-safe, contents undefined
+        return (static_cast<size_t>(page) * Hkv + h) << P_log2;
+    }
+    __host__ __device__ size_t row(int t) const
+    {
+        if (!trow)
+            return base + t;
+        return page_base(t) + (t & ((1 << P_log2) - 1));
+    }
+    __host__ __device__ size_t grp(int gi) const
+    {
+        if (!trow)
+            return base / G + gi;
+        const int t = gi * G;
+        return (page_base(t) + (t & ((1 << P_log2) - 1))) / G;
+    }
 };
 
 // Quantize and pack groups [Tq0 + j*G, Tq0 + (j+1)*G), j < n_groups, for every

@@ -65,7 +65,9 @@ kvq::LayerDev sub_layer(const kvq::LayerDev &d, int s0, int D)
 {
     kvq::LayerDev v = d;
     const size_t S = static_cast<size_t>(s0);
-    if (d.kb != 16) {
+    if (d.table) {
+        v.bh0 = d.bh0 + s0;  // pooled pages: the streams' rows come from the table
+    } else if (d.kb != 16) {
         v.k_words += S * d.capq * d.wk;
         v.k_meta += d.k_tok ? S * d.capq * 2 : S * (d.capq / d.G) * 2 * D;
         v.v_words += S * d.capq * d.wv;
@@ -140,6 +142,22 @@ int plan_layout(const kvq_config *cfg, Plan *plan, std::string *err)
     const size_t BH = static_cast<size_t>(cfg->batch) * cfg->n_kv_heads;
     const int D = cfg->head_dim, G = cfg->group_size;
     const size_t A = KVQ_WORKSPACE_ALIGN;
+    const int P = cfg->page_tokens;
+    int P_log2 = 0;
+    if (P != 0) {
+        if (P < 128 || (P & (P - 1)) != 0 || P % G != 0)
+            return fail(KVQ_EINVAL, "page_tokens %d must be 0, or a power of two >= 128 and a multiple of group_size %d",
+                        P, G);
+        while ((1 << P_log2) < P)
+            ++P_log2;
+        if (cfg->n_pages < 1)
+            return fail(KVQ_EINVAL, "n_pages must be >= 1 with page_tokens %d", P);
+        if (!cfg->block_table)
+            return fail(KVQ_EINVAL, "block_table is NULL with page_tokens %d", P);
+        if (static_cast<long>(cfg->table_stride) * P < cfg->max_context)
+            return fail(KVQ_EINVAL, "table_stride %d x page_tokens %d < max_context %d", cfg->table_stride, P,
+                        cfg->max_context);
+    }
     size_t off = 0;
     plan->layers.assign(cfg->n_layers, LayerState());
     // V codes use the matrix-core tile layout when groups are whole 32-token blocks
@@ -167,6 +185,12 @@ int plan_layout(const kvq_config *cfg, Plan *plan, std::string *err)
         d.v_tiled = plan->v_tiled;
         d.k_tok = (lc.k_mode == KVQ_K_PER_TOKEN && lc.k_bits != 16) ? 1 : 0;
         s.rpc_permille = lc.k_bits != 16 ? lc.rpc_permille : 0;
+        d.table = nullptr;  // set at create for paged quantized layers
+        d.P_log2 = P_log2;
+        d.Hkv = cfg->n_kv_heads;
+        d.tstride = cfg->table_stride;
+        d.n_pages = cfg->n_pages;
+        d.bh0 = 0;
         if (d.kb == 16) {
             d.R = cfg->max_context;
             d.capq = G;  // unused
@@ -181,7 +205,18 @@ int plan_layout(const kvq_config *cfg, Plan *plan, std::string *err)
             d.wk = words_per_row(D, d.kb);
             d.wv = words_per_row(D, d.vb);
         }
-        if (d.kb != 16) {
+        if (d.kb != 16 && P != 0) {
+            // a pool of n_pages pages (+ the spare page) of P tokens for all kv heads
+            const size_t rows = (static_cast<size_t>(cfg->n_pages) + 1) * cfg->n_kv_heads * P;
+            s.off_kw = off;
+            off = align_up(off + rows * d.wk * 4, A);
+            s.off_km = off;
+            off = align_up(off + (d.k_tok ? rows * 2 * 4 : rows / G * 2 * D * 4), A);
+            s.off_vw = off;
+            off = align_up(off + rows * d.wv * 4, A);
+            s.off_vm = off;
+            off = align_up(off + rows * 2 * 4, A);
+        } else if (d.kb != 16) {
             s.off_kw = off;
             off = align_up(off + BH * d.capq * d.wk * 4, A);
             s.off_km = off;
@@ -311,6 +346,8 @@ int kvq_create(const kvq_config *cfg, void *workspace, size_t ws_bytes, kvq_hand
         }
         d.ring_k = reinterpret_cast<uint16_t *>(h->ws + s.off_rk);
         d.ring_v = reinterpret_cast<uint16_t *>(h->ws + s.off_rv);
+        if (cfg->page_tokens != 0 && d.kb != 16)
+            d.table = cfg->block_table;
         (void)BH;
     }
     *out = h;
@@ -322,6 +359,23 @@ static int append_streams(kvq_handle *h, const kvq::LayerDev &dl, int s0, int nb
 static int append_sequences(kvq_handle *h, int layer, const void *k_new, const void *v_new, const int32_t *n_new,
                             int n_max);
 static void refresh_lengths(LayerState &s);
+
+// Paged layers: pages the layer's sequences occupy when sequence b holds tq[b]
+// quantized tokens must fit its pool.
+static int check_pages(kvq_handle *h, int layer, const std::vector<int> &tq)
+{
+    const int P = h->cfg.page_tokens;
+    const LayerState &s = h->plan.layers[layer];
+    if (P == 0 || s.dev.kb == 16)
+        return KVQ_OK;
+    long pages = 0;
+    for (int t : tq)
+        pages += (t + P - 1) / P;
+    if (pages > h->cfg.n_pages)
+        return h->fail(KVQ_ECAPACITY, "layer %d: its sequences would occupy %ld pages of %d tokens; the pool has %d",
+                       layer, pages, P, h->cfg.n_pages);
+    return KVQ_OK;
+}
 
 int kvq_append(kvq_handle *h, int layer, const void *k_new, const void *v_new, int n_new)
 {
@@ -345,8 +399,10 @@ int kvq_append(kvq_handle *h, int layer, const void *k_new, const void *v_new, i
 
     if (!s.ragged) {
         int Tq1 = 0;
-        const int rc = append_streams(h, d, 0, h->BH(), k_new, v_new, n_new, n_new, s.N, s.Tq, s.rpc_permille,
-                                      &Tq1);
+        int rc = check_pages(h, layer, std::vector<int>(h->cfg.batch, tq_after(d, s.rpc_permille, s.N, s.Tq, n_new)));
+        if (rc != KVQ_OK)
+            return rc;
+        rc = append_streams(h, d, 0, h->BH(), k_new, v_new, n_new, n_new, s.N, s.Tq, s.rpc_permille, &Tq1);
         if (rc != KVQ_OK)
             return rc;
         s.N += n_new;
@@ -420,6 +476,12 @@ static int append_sequences(kvq_handle *h, int layer, const void *k_new, const v
     LayerState &s = h->plan.layers[layer];
     const int Hkv = h->cfg.n_kv_heads, D = h->cfg.head_dim;
     const size_t seq_elems = static_cast<size_t>(Hkv) * n_max * D;
+    std::vector<int> tq1(h->cfg.batch);
+    for (int b = 0; b < h->cfg.batch; ++b)
+        tq1[b] = tq_after(s.dev, s.rpc_permille, s.seqN[b], s.seqTq[b], n_new[b]);
+    const int rc0 = check_pages(h, layer, tq1);
+    if (rc0 != KVQ_OK)
+        return rc0;
     for (int b = 0; b < h->cfg.batch; ++b) {
         if (n_new[b] == 0)
             continue;
@@ -483,6 +545,20 @@ int kvq_append_ragged(kvq_handle *h, int layer, const void *k_new, const void *v
     if (equal && !s.ragged)
         return kvq_append(h, layer, k_new, v_new, n_max);
     return append_sequences(h, layer, k_new, v_new, n_new, n_max);
+}
+
+int kvq_reset_sequence(kvq_handle *h, int b)
+{
+    if (!h)
+        return KVQ_EINVAL;
+    if (b < 0 || b >= h->cfg.batch)
+        return h->fail(KVQ_EINVAL, "sequence %d out of range [0, %d)", b, h->cfg.batch);
+    for (LayerState &s : h->plan.layers) {
+        s.seqN[b] = 0;
+        s.seqTq[b] = 0;
+        refresh_lengths(s);
+    }
+    return KVQ_OK;
 }
 
 int kvq_sequence_lengths(const kvq_handle *h, int layer, int32_t *n_tokens, int32_t *n_quantized)
@@ -573,6 +649,12 @@ int kvq_append_decode_attention(kvq_handle *h, int layer, const void *k_new, con
             return h->fail(KVQ_EUNSUPPORTED, "sequences of different lengths: batch %d exceeds %d",
                            h->cfg.batch, kvq::kMaxRaggedSeqs);
         const int Hkv = h->cfg.n_kv_heads, D = h->cfg.head_dim;
+        std::vector<int> tq1(h->cfg.batch);
+        for (int b = 0; b < h->cfg.batch; ++b)
+            tq1[b] = tq_after(d, s.rpc_permille, s.seqN[b], s.seqTq[b], 1);
+        rc = check_pages(h, layer, tq1);
+        if (rc != KVQ_OK)
+            return rc;
         std::vector<int> nt(h->cfg.batch, -1);
         for (int b = 0; b < h->cfg.batch; ++b) {
             const size_t off = static_cast<size_t>(b) * Hkv * D;
@@ -999,20 +1081,49 @@ static int export_streams(kvq_handle *h, const kvq::LayerDev &dl, int s0, int BH
     if (e != hipSuccess)
         return h->dev_fail(e, "stream synchronize");
     if (d.kb != 16 && Tq > 0) {
-        const int ng = Tq / d.G, ngcap = d.capq / d.G;
+        const int ng = Tq / d.G;
+        // rows are addressed as the kernels address them; with paging through
+        // a host copy of the page table (its rows of this view's sequences)
+        kvq::LayerDev dh = d;
+        std::vector<int32_t> tab;
+        if (d.table) {
+            tab.assign(static_cast<size_t>(h->cfg.batch) * d.tstride, 0);
+            if ((e = hipMemcpy(tab.data(), d.table, tab.size() * 4, hipMemcpyDeviceToHost)) != hipSuccess)
+                return h->dev_fail(e, "export block table");
+            dh.table = tab.data();
+        }
+        // copy rows [first, first + count) of stream bh (unit 1: token rows of
+        // row_bytes; unit G: group rows) to dst, one piece per page
+        auto gather = [&](const void *dev, size_t row_bytes, int bh, int first, int count, bool groups,
+                          void *dst) -> hipError_t {
+            const kvq::QAddr qa(dh, bh);
+            const int per_page = groups ? (1 << d.P_log2) / d.G : (1 << d.P_log2);
+            for (int i = 0; i < count;) {
+                const int r = first + i;
+                const size_t row = groups ? qa.grp(r) : qa.row(r);
+                int n = count - i;
+                if (d.table)
+                    n = std::min(n, per_page - r % per_page);
+                const hipError_t er =
+                    hipMemcpy(static_cast<char *>(dst) + static_cast<size_t>(i) * row_bytes,
+                              static_cast<const char *>(dev) + row * row_bytes, static_cast<size_t>(n) * row_bytes,
+                              hipMemcpyDeviceToHost);
+                if (er != hipSuccess)
+                    return er;
+                i += n;
+            }
+            return hipSuccess;
+        };
         for (int bh = 0; bh < BH; ++bh) {
-            const size_t row0 = static_cast<size_t>(bh) * d.capq;
-            if (k_words &&
-                (e = hipMemcpy(k_words + static_cast<size_t>(bh) * Tq * d.wk, d.k_words + row0 * d.wk,
-                               static_cast<size_t>(Tq) * d.wk * 4, hipMemcpyDeviceToHost)) != hipSuccess)
+            if (k_words && (e = gather(d.k_words, d.wk * 4, bh, 0, Tq, false,
+                                       k_words + static_cast<size_t>(bh) * Tq * d.wk)) != hipSuccess)
                 return h->dev_fail(e, "export k_words");
             if (v_words) {
                 uint32_t *dst = v_words + static_cast<size_t>(bh) * Tq * d.wv;
                 if (d.v_tiled) {
                     // 32-token operand tiles -> token-major rows
                     std::vector<uint32_t> tiles(static_cast<size_t>(Tq) * d.wv);
-                    if ((e = hipMemcpy(tiles.data(), d.v_words + row0 * d.wv, tiles.size() * 4,
-                                       hipMemcpyDeviceToHost)) != hipSuccess)
+                    if ((e = gather(d.v_words, d.wv * 4, bh, 0, Tq, false, tiles.data())) != hipSuccess)
                         return h->dev_fail(e, "export v_words");
                     memset(dst, 0, tiles.size() * 4);
                     const int epw = 32 / d.vb;
@@ -1025,15 +1136,13 @@ static int export_streams(kvq_handle *h, const kvq::LayerDev &dl, int s0, int BH
                                 (tiles[static_cast<size_t>(t & ~31) * d.wv + word] >> bit) & mask;
                             dst[static_cast<size_t>(t) * d.wv + c / epw] |= code << (d.vb * (c % epw));
                         }
-                } else if ((e = hipMemcpy(dst, d.v_words + row0 * d.wv, static_cast<size_t>(Tq) * d.wv * 4,
-                                          hipMemcpyDeviceToHost)) != hipSuccess) {
+                } else if ((e = gather(d.v_words, d.wv * 4, bh, 0, Tq, false, dst)) != hipSuccess) {
                     return h->dev_fail(e, "export v_words");
                 }
             }
             if ((k_scale || k_zero) && d.k_tok) {
                 std::vector<float> m(static_cast<size_t>(Tq) * 2);
-                if ((e = hipMemcpy(m.data(), d.k_meta + row0 * 2, m.size() * 4, hipMemcpyDeviceToHost)) !=
-                    hipSuccess)
+                if ((e = gather(d.k_meta, 8, bh, 0, Tq, false, m.data())) != hipSuccess)
                     return h->dev_fail(e, "export k_meta");
                 for (int t = 0; t < Tq; ++t) {
                     if (k_scale)
@@ -1043,8 +1152,7 @@ static int export_streams(kvq_handle *h, const kvq::LayerDev &dl, int s0, int BH
                 }
             } else if (k_scale || k_zero) {
                 std::vector<float> m(static_cast<size_t>(ng) * 2 * D);
-                if ((e = hipMemcpy(m.data(), d.k_meta + static_cast<size_t>(bh) * ngcap * 2 * D,
-                                   m.size() * 4, hipMemcpyDeviceToHost)) != hipSuccess)
+                if ((e = gather(d.k_meta, static_cast<size_t>(2) * D * 4, bh, 0, ng, true, m.data())) != hipSuccess)
                     return h->dev_fail(e, "export k_meta");
                 for (int gi = 0; gi < ng; ++gi)
                     for (int c = 0; c < D; ++c) {
@@ -1057,8 +1165,7 @@ static int export_streams(kvq_handle *h, const kvq::LayerDev &dl, int s0, int BH
             }
             if (v_scale || v_zero) {
                 std::vector<float> m(static_cast<size_t>(Tq) * 2);
-                if ((e = hipMemcpy(m.data(), d.v_meta + row0 * 2, m.size() * 4, hipMemcpyDeviceToHost)) !=
-                    hipSuccess)
+                if ((e = gather(d.v_meta, 8, bh, 0, Tq, false, m.data())) != hipSuccess)
                     return h->dev_fail(e, "export v_meta");
                 for (int t = 0; t < Tq; ++t) {
                     if (v_scale)

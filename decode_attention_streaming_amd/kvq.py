@@ -22,7 +22,7 @@ EXPORTED = ["kvq_workspace_bytes", "kvq_create", "kvq_append", "kvq_decode_atten
             "kvq_append_decode_attention", "kvq_bytes", "kvq_bytes_layer", "kvq_export_layer", "kvq_sync",
             "kvq_set_stream", "kvq_last_error", "kvq_destroy", "kvq_last_launch", "kvq_prefill_attention",
             "kvq_append_ragged", "kvq_sequence_lengths", "kvq_export_sequence",
-            "kvq_decode_attention_noalloc"]
+            "kvq_decode_attention_noalloc", "kvq_reset_sequence"]
 
 
 KVQ_K_PER_CHANNEL, KVQ_K_PER_TOKEN = 0, 1
@@ -38,7 +38,9 @@ class kvq_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("n_layers", "batch", "n_q_heads", "n_kv_heads", "head_dim", "max_context",
                  "kv_dtype", "q_dtype", "group_size", "residual_len")] + [
-        ("layers", ctypes.POINTER(kvq_layer_cfg)), ("stream", ctypes.c_void_p)]
+        ("layers", ctypes.POINTER(kvq_layer_cfg)), ("stream", ctypes.c_void_p),
+        ("page_tokens", ctypes.c_int32), ("n_pages", ctypes.c_int32),
+        ("block_table", ctypes.c_void_p), ("table_stride", ctypes.c_int32)]
 
 
 class kvq_bytes_info(ctypes.Structure):
@@ -86,6 +88,7 @@ def lib():
         "kvq_sequence_lengths": (I, [P, I, P, P]),
         "kvq_export_sequence": (I, [P, I, I] + [P] * 8),
         "kvq_decode_attention_noalloc": (I, [P, I, P, P]),
+        "kvq_reset_sequence": (I, [P, I]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -96,12 +99,16 @@ def lib():
 
 
 def make_config(n_layers, batch, n_q_heads, n_kv_heads, head_dim, max_context, kv_dtype, q_dtype,
-                group_size, residual_len, layers, stream=None):
-    """Build a kvq_config; `layers` is a list of (k_bits, v_bits, residual_len)."""
+                group_size, residual_len, layers, stream=None, page_tokens=0, n_pages=0, block_table=None,
+                table_stride=0):
+    """Build a kvq_config; `layers` is a list of (k_bits, v_bits, residual_len[, k_mode[,
+    rpc_permille]]); paging: page_tokens, n_pages, block_table (a device address) and
+    table_stride."""
     arr = (kvq_layer_cfg * len(layers))(*[kvq_layer_cfg(*l) for l in layers])
     cfg = kvq_config(n_layers, batch, n_q_heads, n_kv_heads, head_dim, max_context,
                      _DT.get(kv_dtype, kv_dtype), _DT.get(q_dtype, q_dtype), group_size,
-                     residual_len, ctypes.cast(arr, ctypes.POINTER(kvq_layer_cfg)), stream)
+                     residual_len, ctypes.cast(arr, ctypes.POINTER(kvq_layer_cfg)), stream,
+                     page_tokens, n_pages, block_table, table_stride)
     cfg._keep = arr  # keep the table alive as long as the config
     return cfg
 
@@ -162,6 +169,10 @@ def kvq_append_ragged(h, layer, k_ptr, v_ptr, n_new, n_max):
     return _check(lib().kvq_append_ragged(h, layer, k_ptr, v_ptr, arr, n_max), h)
 
 
+def kvq_reset_sequence(h, b):
+    return _check(lib().kvq_reset_sequence(h, b), h)
+
+
 def kvq_sequence_lengths(h, layer, batch):
     n = (ctypes.c_int32 * batch)()
     tq = (ctypes.c_int32 * batch)()
@@ -203,7 +214,11 @@ class Cache:
     """A kvq handle whose workspace, inputs and outputs are torch tensors."""
 
     def __init__(self, n_layers, batch, n_q_heads, n_kv_heads, head_dim, max_context, kv_dtype,
-                 q_dtype, group_size, residual_len, layers, device="cuda", stream=None):
+                 q_dtype, group_size, residual_len, layers, device="cuda", stream=None,
+                 page_tokens=0, n_pages=0, block_table=None):
+        """Paging: page_tokens > 0, n_pages pages per quantized layer, and block_table a
+        contiguous int32 device tensor [batch, table_stride] of page ids (kept alive here; the
+        caller may rewrite its entries between calls, in stream order)."""
         import torch
         self.torch = torch
         self.layers = list(layers)
@@ -213,9 +228,16 @@ class Cache:
         self.kv_dtype, self.q_dtype = kv_dtype, q_dtype
         st = stream if stream is not None else torch.cuda.current_stream(device)
         self.stream = st
+        self.block_table = block_table
+        table_ptr, stride = None, 0
+        if page_tokens:
+            if block_table is None or block_table.dtype != torch.int32 or not block_table.is_contiguous() \
+                    or block_table.dim() != 2 or block_table.shape[0] != batch:
+                raise ValueError("block_table must be a contiguous int32 [batch, table_stride] tensor")
+            table_ptr, stride = ctypes.c_void_p(block_table.data_ptr()), block_table.shape[1]
         self.cfg = make_config(n_layers, batch, n_q_heads, n_kv_heads, head_dim, max_context,
                                kv_dtype, q_dtype, group_size, residual_len, self.layers,
-                               ctypes.c_void_p(st.cuda_stream))
+                               ctypes.c_void_p(st.cuda_stream), page_tokens, n_pages, table_ptr, stride)
         nbytes = kvq_workspace_bytes(self.cfg)
         if nbytes == 0:
             raise KvqError(KVQ_EINVAL, kvq_last_error())
@@ -267,6 +289,10 @@ class Cache:
             raise ValueError("K and V shapes differ")
         kvq_append_ragged(self.h, layer, ctypes.c_void_p(k_new.data_ptr()),
                           ctypes.c_void_p(v_new.data_ptr()), n_new, k_new.shape[2])
+
+    def reset_sequence(self, b):
+        """Empty sequence b in every layer (its pages may then be named for others)."""
+        kvq_reset_sequence(self.h, b)
 
     def sequence_lengths(self, layer):
         """([N_b], [Tq_b]) per sequence."""

@@ -106,7 +106,32 @@ typedef struct kvq_layer_cfg {
  *   <= 16; head_dim in {64, 128, 256}; kv_dtype in {KVQ_F16, KVQ_BF16};
  *   q_dtype in {KVQ_F32, KVQ_F16, KVQ_BF16}; group_size G >= 1;
  *   residual_len R >= G; layers points to n_layers rows (copied at create);
- *   stream is a hipStream_t (NULL selects the null stream). */
+ *   stream is a hipStream_t (NULL selects the null stream).
+ *
+ * Paging (KIVI notes, section 8: a block-table cache manager combines with the
+ * quantized cache; KVTuner summary: compatible with serving engines' paged
+ * attention).  page_tokens = 0: every (sequence, kv-head) stream keeps its
+ * quantized tokens in a region of its own sized for max_context.  Otherwise the
+ * quantized state (codes, scales and zeros) of each quantized layer lives in a
+ * pool of n_pages pages, one page holding page_tokens consecutive tokens of one
+ * sequence for all its kv heads, and block_table gives the pages:
+ *   page_tokens  P: a power of two, >= 128 and a multiple of group_size;
+ *   n_pages      pages in each quantized layer's pool (every layer has a pool
+ *                of its own, indexed by the same page ids);
+ *   block_table  device memory owned by the caller, int32 [batch][table_stride],
+ *                shared by all layers: entry j of row b is the page holding
+ *                tokens [j P, (j + 1) P) of sequence b;
+ *   table_stride entries per row, table_stride * P >= max_context.
+ * The kernels read the table when they run, in stream order: before any call
+ * that makes sequence b hold Tq quantized tokens in some layer (an append that
+ * flushes), entries [0, ceil(Tq / P)) of row b must name pages in
+ * [0, n_pages), and the pages named for different (sequence, entry) pairs must
+ * differ; between calls the caller may rewrite entries of pages no longer held
+ * (after kvq_reset_sequence).  An entry outside [0, n_pages) sends the kernels
+ * to a spare page: memory stays safe, that sequence's results are undefined.
+ * Appends check on the host that every layer's sequences fit the pool (sum over
+ * b of ceil(Tq_b / P) <= n_pages; KVQ_ECAPACITY otherwise).  The recent-token
+ * buffers and (16, 16) layers are not paged. */
 typedef struct kvq_config {
     int32_t n_layers;
     int32_t batch;
@@ -120,6 +145,10 @@ typedef struct kvq_config {
     int32_t residual_len;
     const kvq_layer_cfg *layers;
     void *stream;
+    int32_t page_tokens;
+    int32_t n_pages;
+    const int32_t *block_table;
+    int32_t table_stride;
 } kvq_config;
 
 typedef struct kvq_handle kvq_handle;
@@ -163,6 +192,12 @@ int kvq_append_ragged(kvq_handle *h, int layer, const void *k_new, const void *v
 /* Tokens held (n_tokens) and quantized (n_quantized) by each sequence of a
  * layer: host arrays of batch entries; either pointer may be NULL. */
 int kvq_sequence_lengths(const kvq_handle *h, int layer, int32_t *n_tokens, int32_t *n_quantized);
+
+/* Empty sequence b in every layer (host bookkeeping only; no device work): its
+ * next append starts a new sequence in that batch slot, and with paging the
+ * pages it held may be named for other sequences.  Calls enqueued before still
+ * see the old contents.  Errors: KVQ_EINVAL (b out of range). */
+int kvq_reset_sequence(kvq_handle *h, int b);
 
 /* Decode attention of one query token per sequence over every token of `layer`
  * (quantized tokens dequantized on the fly, recent tokens in 16 bits), scale

@@ -175,3 +175,38 @@ def test_key_mode_validation():
     assert "per-token" in kvq.kvq_last_error()
     assert kvq.kvq_workspace_bytes(_cfg(layers=[(4, 2, 0, 1), (8, 8, 0, 1)])) > 0
     assert kvq.kvq_workspace_bytes(_cfg(layers=[(16, 16, 0, 1), (2, 2, 0, 1)])) > 0
+
+
+def test_paging_config_validation():
+    """Paging parameters are checked at create: page length a power of two >=
+    128 and a multiple of the group size, a pool of at least one page, a
+    table, and rows long enough for max_context; the pooled workspace is
+    sized by the pool, not by batch x max_context."""
+    T = ctypes.c_void_p(1 << 22)  # create does no device work: any address stands in for the table
+    base = dict(n_layers=1, batch=4, n_q_heads=8, n_kv_heads=2, head_dim=128, max_context=4096,
+                kv_dtype="bf16", q_dtype="bf16", group_size=32, residual_len=32, layers=[(4, 2, 0)])
+    bad = [dict(page_tokens=96, n_pages=8, block_table=T, table_stride=64),
+           dict(page_tokens=64, n_pages=8, block_table=T, table_stride=64),
+           dict(page_tokens=256, n_pages=0, block_table=T, table_stride=16),
+           dict(page_tokens=256, n_pages=8, block_table=None, table_stride=16),
+           dict(page_tokens=256, n_pages=8, block_table=T, table_stride=15)]
+    for kw in bad:
+        cfg = kvq.make_config(**base, **kw)
+        assert kvq.kvq_workspace_bytes(cfg) == 0, kw
+    g48 = dict(base, group_size=48, residual_len=48)
+    assert kvq.kvq_workspace_bytes(kvq.make_config(**g48, page_tokens=256, n_pages=8, block_table=T,
+                                                    table_stride=16)) == 0  # 48 does not divide 256
+    flat = kvq.kvq_workspace_bytes(kvq.make_config(**base))
+    paged = kvq.kvq_workspace_bytes(kvq.make_config(**base, page_tokens=256, n_pages=8, block_table=T,
+                                                    table_stride=16))
+    assert 0 < paged < flat
+    cfg = kvq.make_config(**base, page_tokens=256, n_pages=8, block_table=T, table_stride=16)
+    h = kvq.kvq_create(cfg, ctypes.c_void_p(1 << 20), kvq.kvq_workspace_bytes(cfg))
+    try:
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.kvq_reset_sequence(h, 4)
+        assert e.value.code == kvq.KVQ_EINVAL
+        kvq.kvq_reset_sequence(h, 3)  # host bookkeeping only
+        assert kvq.kvq_sequence_lengths(h, 0, 4) == ([0] * 4, [0] * 4)
+    finally:
+        kvq.kvq_destroy(h)
