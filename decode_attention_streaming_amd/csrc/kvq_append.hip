@@ -294,18 +294,6 @@ __global__ void zero_kernel(unsigned *p, int n)
         p[i] = 0u;
 }
 
-// Hand-off state: stream words to epoch 1 with no arrivals, partial slots to 0
-// (epoch 0, which no call uses).  Grid-stride over the partial slots.
-__global__ void handoff_init_kernel(unsigned long long *cnt, int n_streams, unsigned long long *part, size_t n_slots)
-{
-    const size_t i0 = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    const size_t step = static_cast<size_t>(gridDim.x) * blockDim.x;
-    if (i0 < static_cast<size_t>(n_streams))
-        cnt[i0 * (kCounterStride / 2)] = 1ull << 32;
-    for (size_t i = i0; i < n_slots; i += step)
-        part[i] = 0ull;
-}
-
 }  // namespace
 
 hipError_t launch_flush(const FlushArgs &a, hipStream_t st)
@@ -329,18 +317,6 @@ hipError_t launch_ring_write(const RingArgs &a, hipStream_t st)
 hipError_t launch_zero(unsigned *p, int n, hipStream_t st)
 {
     hipLaunchKernelGGL(zero_kernel, dim3((n + 255) / 256), dim3(256), 0, st, p, n);
-    return hipGetLastError();
-}
-
-hipError_t launch_handoff_init(unsigned *counters, int n_streams, unsigned long long *part, size_t n_part_slots,
-                               hipStream_t st)
-{
-    size_t blocks = (n_part_slots + 255) / 256;
-    const size_t sblocks = (static_cast<size_t>(n_streams) + 255) / 256;
-    blocks = blocks < sblocks ? sblocks : blocks;
-    blocks = blocks > 4096 ? 4096 : (blocks < 1 ? 1 : blocks);
-    hipLaunchKernelGGL(handoff_init_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
-                       reinterpret_cast<unsigned long long *>(counters), n_streams, part, n_part_slots);
     return hipGetLastError();
 }
 

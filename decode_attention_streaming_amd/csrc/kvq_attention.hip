@@ -22,13 +22,8 @@ __device__ __forceinline__ void attn_valu_body(const AttnArgs &a, const RaggedTa
     const int t_beg = a.valu_beg + split * a.valu_tps;
     const int t_end = min(stream_dims(a, rt, bh).N, t_beg + a.valu_tps);
     extern __shared__ float smem[];
-    __shared__ unsigned s_epoch;
-    if (threadIdx.x == 0)
-        s_epoch = handoff_epoch(a, bh);
-    __syncthreads();
-    const unsigned epoch = s_epoch;
-    valu_range<D, GM>(a, rt, bh, t_beg, t_end, split, epoch, smem);
-    finish_stream<D>(a, bh, split, epoch, gridDim.x, nullptr, 0, nullptr, nullptr);
+    valu_range<D, GM>(a, rt, bh, t_beg, t_end, split, smem);
+    arrive_and_merge<D>(a, bh, gridDim.x);
 }
 
 template <int D, int GM>

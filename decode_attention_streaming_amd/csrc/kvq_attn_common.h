@@ -21,66 +21,57 @@ namespace kvq {
 constexpr int kAttnThreads = 256;
 constexpr int kMaxG = 16;
 
-// Hand-off of per-workgroup partial results between the workgroups of one
-// stream, which may run on different XCDs (whose L2 caches are not coherent
-// with each other).  Only relaxed agent-scope atomics are used, so the memory
-// model's coherence of each single location is all the hand-off relies on: no
-// fence, no ordering between locations, no cache-policy bits chosen by hand.
-//
-// The stream's 64-bit hand-off word holds the call's epoch (high half) and the
-// number of its workgroups that have finished (low half).  Each workgroup
-// reads the epoch when it starts (the word only changes to the next epoch
-// after every workgroup of the call has finished, so all of them read the same
-// value), stores its partial results (o, m, l per head) as (value, epoch)
-// slots, each one 8-byte atomic store, and then adds 1 to the word.  The one
-// that makes the count complete merges: it stores the next epoch with a zero
-// count, then loads the other workgroups' slots with 8-byte atomic loads until
-// each carries the call's epoch (a slot is one location, so its value is seen
-// together with the epoch it was stored with; a slot left by an earlier call
-// carries an older epoch).  It waits only for stores already issued by
-// workgroups that have finished, so the wait ends whatever the dispatch order,
-// residency or XCD placement.
-__device__ __forceinline__ void slot_store(unsigned long long *p, float v, unsigned epoch)
+// Partial entry of one (stream, workgroup, head): o[D], then m (log2 domain),
+// l and two unused floats.  16-byte aligned (D is a multiple of 4).
+__device__ __forceinline__ int part_stride(int D) { return D + 4; }
+
+// Partials pass between workgroups of one launch, which may run on different
+// XCDs with separate L2 caches.  They are written and read with device-coherent
+// accesses (write-through stores, loads that bypass a possibly stale L2), so
+// the hand-off needs no whole-cache write-back or invalidation.
+__device__ __forceinline__ void part_store(float *p, float v)
 {
-    const unsigned long long x = (static_cast<unsigned long long>(epoch) << 32) | __float_as_uint(v);
-    __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ unsigned long long slot_load(const unsigned long long *p)
-{
-    return __hip_atomic_load(const_cast<unsigned long long *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ float slot_value(unsigned long long x) { return __uint_as_float(static_cast<unsigned>(x)); }
-__device__ __forceinline__ unsigned slot_epoch(unsigned long long x) { return static_cast<unsigned>(x >> 32); }
-
-// Slots of one head's partial result: o[D], then m (log2 domain) and l.
-__device__ __forceinline__ int part_head_slots(int D) { return D + 2; }
-
-// Partial entry e (the stream's workgroup e) of stream bh.
-__device__ __forceinline__ unsigned long long *part_entry(const AttnArgs &a, int bh, int e)
-{
-    return a.part + (static_cast<size_t>(bh) * a.n_part + e) * part_entry_slots(a.g, a.D);
-}
-
-// The stream's hand-off word.
-__device__ __forceinline__ unsigned long long *handoff_word(const AttnArgs &a, int bh)
-{
-    return reinterpret_cast<unsigned long long *>(a.counters + static_cast<size_t>(bh) * kCounterStride);
-}
-
-// The current call's epoch (read by one thread when its workgroup starts).
-__device__ __forceinline__ unsigned handoff_epoch(const AttnArgs &a, int bh)
-{
-    return static_cast<unsigned>(slot_load(handoff_word(a, bh)) >> 32);
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 typedef float f4_t __attribute__((ext_vector_type(4)));
 
-// Polls of a slot before the merger gives up (a safety bound: the writers
-// have already issued their stores, which arrive within microseconds); a slot
-// still missing then yields NaN in the output instead of a hang.
-constexpr int kMaxPolls = 1 << 20;
+// Cache-policy bit of a buffer access that makes it coherent across the
+// device (the agent-scope bit; the accesses skip or write through L2).
+constexpr int kDeviceCoherent = 16;
+
+// Buffer view of the partial entries of one stream, with 16-byte coherent
+// accesses (hardware range-checked against the stream's entries).
+struct PartBuf {
+    __amdgpu_buffer_rsrc_t r;
+
+    __device__ PartBuf(const AttnArgs &a, int bh)
+    {
+        const size_t n = static_cast<size_t>(a.n_part) * part_entry_floats(a.g, a.D);
+        r = __builtin_amdgcn_make_buffer_rsrc(a.part + static_cast<size_t>(bh) * n, 0,
+                                              static_cast<int>(n * 4), 0x00020000);
+    }
+    // float offset of (entry, head, channel)
+    __device__ int off(const AttnArgs &a, int entry, int h, int c) const
+    {
+        return entry * part_entry_floats(a.g, a.D) + h * part_stride(a.D) + c;
+    }
+    __device__ void store4(int off_f, f4_t v) const
+    {
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, off_f * 4, 0, kDeviceCoherent);
+    }
+    __device__ f4_t load4(int off_f) const
+    {
+        return __builtin_amdgcn_raw_buffer_load_b128(r, off_f * 4, 0, kDeviceCoherent);
+    }
+    // when every writer ran on this workgroup's XCD: their write-through
+    // stores passed this XCD's L2, so a load that only bypasses the L1 is
+    // coherent with them (cache-policy bit sc0)
+    __device__ f4_t load4_xcd(int off_f) const
+    {
+        return __builtin_amdgcn_raw_buffer_load_b128(r, off_f * 4, 0, 1);
+    }
+};
 
 // Lengths of stream bh: those of the launch, or, for a ragged batch, those of
 // the stream's sequence from the launch's tables.
@@ -272,7 +263,7 @@ __device__ __forceinline__ void stage_q(const AttnArgs &a, int b, int kvh, float
 // sum_t p_t z_t.
 template <int D, int GM>
 __device__ void valu_range(const AttnArgs &a, const RaggedTables *rt, int bh, int t_beg, int t_end, int slot,
-                           unsigned epoch, float *smem)
+                           float *smem)
 {
     constexpr int TT = valu_tile<D>();
     constexpr int P = kAttnThreads / TT;  // threads per token in the score phase
@@ -463,16 +454,16 @@ __device__ void valu_range(const AttnArgs &a, const RaggedTables *rt, int bh, in
         tile = tend;
     }
 
-    const int ps = part_head_slots(D);
-    unsigned long long *part = part_entry(a, bh, slot);
+    const int ps = part_stride(D);
+    float *part = a.part + (static_cast<size_t>(bh) * a.n_part + slot) * part_entry_floats(g, D);
 #pragma unroll
     for (int k = 0; k < GM; ++k) {
         const int h = oh0 + k * hstep;
         if (h < g) {
-            slot_store(part + h * ps + oc, o[k], epoch);
+            part_store(part + h * ps + oc, o[k]);
             if (oc == 0) {
-                slot_store(part + h * ps + D, m[h], epoch);
-                slot_store(part + h * ps + D + 1, l[h], epoch);
+                part_store(part + h * ps + D, m[h]);
+                part_store(part + h * ps + D + 1, l[h]);
             }
         }
     }
@@ -483,18 +474,14 @@ __device__ void valu_range(const AttnArgs &a, const RaggedTables *rt, int bh, in
 
 // Workgroup-level merge: the waves of one workgroup have left their per-head
 // results in LDS (o[g][D] at wave * region floats, m and l in pm / pl; m =
-// -inf marks an empty one); per head, o = sum_w 2^(m_w - M) o_w, l = sum_w
-// 2^(m_w - M) l_w, M = max_w m_w.  The workgroup stores them as its partial
-// entry (entry = its index among the stream's workgroups) and also keeps them
-// in LDS (own_o[g][D], own_m, own_l), for merge_stream if it merges.
+// -inf marks an empty one); the workgroup writes one partial entry per head,
+// o = sum_w 2^(m_w - M) o_w, l = sum_w 2^(m_w - M) l_w, M = max_w m_w.
 template <int D>
-__device__ __forceinline__ void wg_merge(const AttnArgs &a, int bh, int entry, unsigned epoch, float *lds, int region,
-                                         const float (*pm)[kMaxG], const float (*pl)[kMaxG], float *own_o,
-                                         float *own_m, float *own_l)
+__device__ __forceinline__ void wg_merge_store(const AttnArgs &a, int bh, int entry, const float *lds,
+                                               int region, const float (*pm)[kMaxG], const float (*pl)[kMaxG])
 {
     constexpr int nc4 = D / 4;
-    unsigned long long *part = part_entry(a, bh, entry);
-    const int ps = part_head_slots(D);
+    const PartBuf pb(a, bh);
     for (int it = threadIdx.x; it < a.g * nc4; it += kAttnThreads) {
         const int h = it / nc4, c4 = it % nc4;
         float M = -INFINITY;
@@ -514,43 +501,29 @@ __device__ __forceinline__ void wg_merge(const AttnArgs &a, int bh, int entry, u
                 l = __builtin_fmaf(f, pl[w][h], l);
             }
         }
-        unsigned long long *p = part + h * ps + 4 * c4;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            slot_store(p + j, o[j], epoch);
-        if (c4 == 0) {
-            slot_store(part + h * ps + D, M, epoch);
-            slot_store(part + h * ps + D + 1, l, epoch);
-        }
-        // the same thread read wave 0's value at this place above: no other
-        // thread reads it, so it can be overwritten
-        *reinterpret_cast<f4_t *>(own_o + h * D + 4 * c4) = o;
-        if (c4 == 0) {
-            own_m[h] = M;
-            own_l[h] = l;
-        }
+        pb.store4(pb.off(a, entry, h, 4 * c4), o);
+        if (c4 == 0)
+            pb.store4(pb.off(a, entry, h, D), f4_t{M, l, 0.0f, 0.0f});
     }
 }
 
-// Merge by the stream's last workgroup of its own result (own_*, in LDS; none
-// when own_entry < 0) and the partial entries of the other workgroups:
+// Merge of the n_part partial entries of stream bh by its last workgroup:
 // out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, M = max_s m_s.
 // Thread t owns four channels of one head (item tid_item) and the entries
-// tid_sub, tid_sub + n_sub, ...  It loads the slots of up to KC of its entries
-// together (one memory round trip), polls again those that do not yet carry
-// the call's epoch, merges them online, and the n_sub partial states of an
-// item are merged through LDS (s_m, s_d, s_acc).  KC is instantiated to the
-// entries a thread actually has, so that no masked-off entry slots run.
+// tid_sub, tid_sub + n_sub, ...  It issues the (m, l) and o loads of up to KC
+// of its entries together (one memory round trip), merges them online, and
+// the n_sub partial states of an item are merged through LDS (s_m, s_d,
+// s_acc).  KC is instantiated to the entries a thread actually has, so that
+// no masked-off entry slots are executed.
 template <int D, int KC>
-__device__ __forceinline__ void merge_stream(const AttnArgs &a, int bh, unsigned epoch, int own_entry, int n_sub,
-                                             int tid_item, int tid_sub, const float *own_o, const float *own_m,
-                                             const float *own_l, float *s_m, float *s_d, f4_t *s_acc)
+__device__ __forceinline__ void merge_stream(const AttnArgs &a, int bh, int n_sub, int tid_item, int tid_sub,
+                                             float *s_m, float *s_d, f4_t *s_acc, bool xcd_local)
 {
     const int tid = threadIdx.x;
     constexpr int nc4 = D / 4;
     const int g = a.g, P = a.n_part;
     const int n_items = g * nc4;  // <= 1024
-    const int ps = part_head_slots(D);
+    const PartBuf pb(a, bh);
     for (int it0 = 0; it0 < n_items; it0 += kAttnThreads) {
         const int item = it0 + tid_item;
         const int sub = tid_sub;
@@ -558,66 +531,21 @@ __device__ __forceinline__ void merge_stream(const AttnArgs &a, int bh, unsigned
         const int h = own ? item / nc4 : 0, c4 = own ? item % nc4 : 0;
         float M = -INFINITY, den = 0.0f;
         f4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        bool lost = false;
-        // entries in increasing order whichever workgroup merges (the merger's
-        // own entry taken from LDS at its place): the result does not depend
-        // on which workgroup arrived last
         for (int e0 = sub; e0 < P; e0 += KC * n_sub) {
-            unsigned long long sl[KC][6];
-            bool need[KC], mine[KC];
+            f4_t ml[KC], ov[KC];
 #pragma unroll
             for (int k = 0; k < KC; ++k) {
                 const int e = e0 + k * n_sub;
-                need[k] = own && e < P;
-                mine[k] = e == own_entry;
-            }
-            for (int poll = 0;; ++poll) {
-                bool missing = false;
-#pragma unroll
-                for (int k = 0; k < KC; ++k) {
-                    if (need[k] && !mine[k]) {
-                        const unsigned long long *p = part_entry(a, bh, e0 + k * n_sub) + h * ps;
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            sl[k][j] = slot_load(p + 4 * c4 + j);
-                        sl[k][4] = slot_load(p + D);
-                        sl[k][5] = slot_load(p + D + 1);
-                    }
-                }
-#pragma unroll
-                for (int k = 0; k < KC; ++k) {
-                    if (need[k] && !mine[k]) {
-                        bool ok = true;
-#pragma unroll
-                        for (int j = 0; j < 6; ++j)
-                            ok = ok && slot_epoch(sl[k][j]) == epoch;
-                        missing = missing || !ok;
-                    }
-                }
-                if (!missing)
-                    break;
-                if (poll >= kMaxPolls) {
-                    lost = true;
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
-            }
-#pragma unroll
-            for (int k = 0; k < KC; ++k) {
-                if (need[k] && mine[k]) {
-                    const f4_t v = *reinterpret_cast<const f4_t *>(own_o + h * D + 4 * c4);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        sl[k][j] = __float_as_uint(v[j]);
-                    sl[k][4] = __float_as_uint(own_m[h]);
-                    sl[k][5] = __float_as_uint(own_l[h]);
+                if (own && e < P) {
+                    ml[k] = xcd_local ? pb.load4_xcd(pb.off(a, e, h, D)) : pb.load4(pb.off(a, e, h, D));
+                    ov[k] = xcd_local ? pb.load4_xcd(pb.off(a, e, h, 4 * c4)) : pb.load4(pb.off(a, e, h, 4 * c4));
                 }
             }
             float Mc = M;
 #pragma unroll
             for (int k = 0; k < KC; ++k)
-                if (need[k])
-                    Mc = fmaxf(Mc, slot_value(sl[k][4]));
+                if (own && e0 + k * n_sub < P)
+                    Mc = fmaxf(Mc, ml[k][0]);
             if (Mc == -INFINITY)
                 continue;
             const float r = (M == -INFINITY) ? 0.0f : exp2f(M - Mc);
@@ -626,17 +554,13 @@ __device__ __forceinline__ void merge_stream(const AttnArgs &a, int bh, unsigned
             M = Mc;
 #pragma unroll
             for (int k = 0; k < KC; ++k) {
-                const float mk = slot_value(sl[k][4]);
-                if (need[k] && mk != -INFINITY) {
-                    const float w = exp2f(mk - M);
-                    acc += w * f4_t{slot_value(sl[k][0]), slot_value(sl[k][1]), slot_value(sl[k][2]),
-                                    slot_value(sl[k][3])};
-                    den = __builtin_fmaf(w, slot_value(sl[k][5]), den);
+                if (own && e0 + k * n_sub < P && ml[k][0] != -INFINITY) {
+                    const float w = exp2f(ml[k][0] - M);
+                    acc += w * ov[k];
+                    den = __builtin_fmaf(w, ml[k][1], den);
                 }
             }
         }
-        if (lost)
-            den = __builtin_nanf("");
         if (n_sub > 1) {
             // merge the n_sub states of each item (entry sets of its threads)
             s_m[tid] = M;
@@ -652,15 +576,11 @@ __device__ __forceinline__ void merge_stream(const AttnArgs &a, int bh, unsigned
                 den *= r0;
                 for (int j = 1; j < n_sub; ++j) {
                     const float mj = s_m[tid + j * n_items];
-                    const float dj = s_d[tid + j * n_items];
-                    if (mj == -INFINITY) {
-                        if (dj != dj)  // a slot that never arrived: NaN out
-                            den = dj;
+                    if (mj == -INFINITY)
                         continue;
-                    }
                     const float rj = exp2f(mj - Mt);
                     acc += rj * s_acc[tid + j * n_items];
-                    den = __builtin_fmaf(rj, dj, den);
+                    den = __builtin_fmaf(rj, s_d[tid + j * n_items], den);
                 }
             }
         }
@@ -670,39 +590,49 @@ __device__ __forceinline__ void merge_stream(const AttnArgs &a, int bh, unsigned
     }
 }
 
-// End of every workgroup of stream bh (epoch: read when the workgroup
-// started; n_wgs workgroups per stream, entry = this one's index among them).
-// With lds (the matrix-core kernel) the waves' results are merged and stored
-// first (wg_merge); without (the vector-ALU kernel) the workgroup has stored
-// its entry already.  Then the workgroup arrives; the last to arrive opens the
-// next epoch and merges everything into out.
-template <int D>
-__device__ __forceinline__ void finish_stream(const AttnArgs &a, int bh, int entry, unsigned epoch, unsigned n_wgs,
-                                              float *lds, int region, const float (*pm)[kMaxG],
-                                              const float (*pl)[kMaxG])
+// XCD (accelerator complex die) this wave runs on.
+__device__ __forceinline__ unsigned xcd_id()
 {
+    unsigned r;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(r));
+    return r & 7u;
+}
+
+// Called by every workgroup at its end: the last one of stream bh to arrive
+// merges the n_part partial entries (merge_stream) and re-arms the stream's
+// counter.  With by_xcd (at most 15 workgroups per stream), each workgroup
+// adds 1 to the 4-bit field of its XCD instead of 1: the last one then also
+// knows whether every workgroup of the stream ran on its own XCD, and if so
+// reads their partials through that XCD's L2.
+template <int D>
+__device__ __forceinline__ void arrive_and_merge(const AttnArgs &a, int bh, unsigned n_wgs, bool by_xcd = false)
+{
+    __shared__ int s_last;
     __shared__ float s_m[kAttnThreads], s_d[kAttnThreads];
     __shared__ f4_t s_acc[kAttnThreads];
-    __shared__ float own_m[kMaxG], own_l[kMaxG];
-    __shared__ int s_last;
-    int own_entry = -1;
-    if (lds) {
-        wg_merge<D>(a, bh, entry, epoch, lds, region, pm, pl, lds, own_m, own_l);
-        own_entry = entry;
-    }
-    __syncthreads();  // every slot store of the workgroup is issued
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are complete
+    __syncthreads();
     if (threadIdx.x == 0) {
-        const unsigned long long prev =
-            __hip_atomic_fetch_add(handoff_word(a, bh), 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = static_cast<unsigned>(prev) == n_wgs - 1;
-        if (s_last)  // every workgroup of this call has arrived: the word is free for the next call
-            __hip_atomic_store(handoff_word(a, bh),
-                               static_cast<unsigned long long>(a.reset_after ? 1u : epoch + 1) << 32,
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (by_xcd) {
+            const unsigned x = xcd_id();
+            const unsigned inc = 1u << (4 * x);
+            const unsigned v =
+                __hip_atomic_fetch_add(a.counters + bh * kCounterStride, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + inc;
+            unsigned total = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                total += (v >> (4 * j)) & 15u;
+            s_last = total == n_wgs ? (((v >> (4 * x)) & 15u) == n_wgs ? 2 : 1) : 0;
+        } else {
+            const unsigned prev =
+                __hip_atomic_fetch_add(a.counters + bh * kCounterStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_last = (prev == n_wgs - 1);
+        }
     }
     __syncthreads();
     if (!s_last)
         return;
+    const bool xcd_local = s_last == 2;
     const int tid = threadIdx.x;
     const int n_items = a.g * (D / 4);  // <= 1024
     // n_sub = kAttnThreads / n_items threads per item (when items are fewer
@@ -716,22 +646,17 @@ __device__ __forceinline__ void finish_stream(const AttnArgs &a, int bh, int ent
             ++tid_sub;
         }
     }
-    const int P = a.n_part;  // entries per thread: ceil(P / n_sub), taken KC at a time
+    const int P = a.n_part;  // entries per thread: ceil(P / n_sub)
     if (P <= 2 * n_sub)
-        merge_stream<D, 2>(a, bh, epoch, own_entry, n_sub, tid_item, tid_sub, lds, own_m, own_l, s_m, s_d, s_acc);
+        merge_stream<D, 2>(a, bh, n_sub, tid_item, tid_sub, s_m, s_d, s_acc, xcd_local);
     else if (P <= 4 * n_sub)
-        merge_stream<D, 4>(a, bh, epoch, own_entry, n_sub, tid_item, tid_sub, lds, own_m, own_l, s_m, s_d, s_acc);
+        merge_stream<D, 4>(a, bh, n_sub, tid_item, tid_sub, s_m, s_d, s_acc, xcd_local);
+    else if (P <= 8 * n_sub)
+        merge_stream<D, 8>(a, bh, n_sub, tid_item, tid_sub, s_m, s_d, s_acc, xcd_local);
     else
-        merge_stream<D, 8>(a, bh, epoch, own_entry, n_sub, tid_item, tid_sub, lds, own_m, own_l, s_m, s_d, s_acc);
-    if (a.reset_after) {
-        // every slot of the call has been read (each thread loaded its own
-        // before the barrier); back to the initial state: all slots zero
-        __syncthreads();
-        unsigned long long *p = part_entry(a, bh, 0);
-        const int n = P * part_entry_slots(a.g, D);
-        for (int i = tid; i < n; i += kAttnThreads)
-            __hip_atomic_store(p + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+        merge_stream<D, 16>(a, bh, n_sub, tid_item, tid_sub, s_m, s_d, s_acc, xcd_local);
+    if (tid == 0)
+        __hip_atomic_store(a.counters + bh * kCounterStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace kvq

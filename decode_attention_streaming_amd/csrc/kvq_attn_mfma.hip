@@ -675,12 +675,6 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs &a, const RaggedTa
     const int unit = wx * 4 + wave;
     const int region = wave_region(a);
     float *po = lds + wave * region;
-    // the call's epoch: needed only at the end, so the load's round trip
-    // overlaps the units' first loads
-    __shared__ unsigned s_epoch;
-    unsigned epoch = 0;
-    if (threadIdx.x == 0)
-        epoch = handoff_epoch(a, bh);
     if (unit < a.units_q) {
         mfma_unit<KB, VB, D, KT>(a, rt, bh, unit, lane, po, s_pm[wave], s_pl[wave], po);
     } else if (unit < a.units_q + a.units_r) {
@@ -692,10 +686,9 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs &a, const RaggedTa
         s_pm[wave][lane] = -INFINITY;
         s_pl[wave][lane] = 0.0f;
     }
-    if (threadIdx.x == 0)
-        s_epoch = epoch;
     __syncthreads();
-    finish_stream<D>(a, bh, wx, s_epoch, a.mfma_wgs, lds, region, s_pm, s_pl);
+    wg_merge_store<D>(a, bh, wx, lds, region, s_pm, s_pl);
+    arrive_and_merge<D>(a, bh, a.mfma_wgs, a.xcd_shift > 0);
 }
 
 template <int KB, int VB, int D, bool KT>

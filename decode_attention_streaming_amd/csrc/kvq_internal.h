@@ -32,6 +32,7 @@ struct LayerDev {
     int R;              // recent-token capacity (max_context for a 16-bit layer)
     int G;              // tokens per K group
     int capq;           // quantized-token capacity per stream (multiple of G and 32)
+    int ngq;            // capq / G: K groups per stream
     int v_tiled;        // V code layout, see above
     int k_tok;          // 1: Key quantized per token (k_meta per token), 0: per channel
     // Paging (table != nullptr): the quantized state lives in a pool of
@@ -43,6 +44,7 @@ struct LayerDev {
     // read (a view of streams bh0.. of the layer).  Unpaged: table == nullptr.
     const int32_t *table;
     int P_log2, Hkv, tstride, n_pages, bh0;
+    int gpp;            // 2^P_log2 / G: K groups per page
 };
 
 // Addressing of one stream's quantized state: row(t) indexes the rows of
@@ -52,12 +54,12 @@ struct LayerDev {
 // one page, so their rows are consecutive.
 struct QAddr {
     const int32_t *trow;  // the sequence's page ids (paged), or nullptr
-    size_t base;          // unpaged: the stream's first row
-    int h, P_log2, n_pages, Hkv, G;
+    size_t base, gbase;   // unpaged: the stream's first row and first group
+    int h, P_log2, n_pages, Hkv, gpp, G;
 
     __host__ __device__ QAddr(const LayerDev &L, int bh)
-        : trow(nullptr), base(static_cast<size_t>(bh) * L.capq), h(0), P_log2(L.P_log2), n_pages(L.n_pages),
-          Hkv(L.Hkv), G(L.G)
+        : trow(nullptr), base(static_cast<size_t>(bh) * L.capq), gbase(static_cast<size_t>(bh) * L.ngq), h(0),
+          P_log2(L.P_log2), n_pages(L.n_pages), Hkv(L.Hkv), gpp(L.gpp), G(L.G)
     {
         if (L.table) {
             const int gbh = bh + L.bh0, b = gbh / L.Hkv;
@@ -65,25 +67,26 @@ struct QAddr {
             h = gbh - b * L.Hkv;
         }
     }
-    __host__ __device__ size_t page_base(int t) const
+    // first row of token t's page, in pages of one kv head (page * Hkv + h)
+    __host__ __device__ size_t page_slot(int t) const
     {
         int page = trow[t >> P_log2];
         if (static_cast<unsigned>(page) >= static_cast<unsigned>(n_pages))
             page = n_pages;  // the spare page: memory-safe, contents undefined
-        return (static_cast<size_t>(page) * Hkv + h) << P_log2;
+        return static_cast<size_t>(page) * Hkv + h;
     }
     __host__ __device__ size_t row(int t) const
     {
         if (!trow)
             return base + t;
-        return page_base(t) + (t & ((1 << P_log2) - 1));
+        return (page_slot(t) << P_log2) + (t & ((1 << P_log2) - 1));
     }
     __host__ __device__ size_t grp(int gi) const
     {
         if (!trow)
-            return base / G + gi;
-        const int t = gi * G;
-        return (page_base(t) + (t & ((1 << P_log2) - 1))) / G;
+            return gbase + gi;
+        const int t = gi * G, pi = t >> P_log2;
+        return page_slot(t) * gpp + (gi - pi * gpp);
     }
 };
 
@@ -105,35 +108,31 @@ struct RingArgs {
     int D, n_new, N0, t_first, t_last, BH;
 };
 
-// Hand-off words of the attention launches: one 64-bit word per stream, each
-// on a 128-byte line of its own (so that the device-scope atomics of different
-// streams do not queue on one line): bits 63..32 hold the stream's call epoch,
-// bits 31..0 the workgroups of the current call that have finished.  The
-// workgroup that finishes last stores (epoch + 1) << 32 and merges the call's
-// partial entries.  Initialised to 1 << 32 with every partial entry zeroed.
-constexpr int kCounterStride = 32;  // u32 words between consecutive streams' hand-off words
+// Arrival counters of the attention launches: one per stream, each on a
+// 128-byte line of its own, so that the device-scope atomics of different
+// streams do not queue on one line.
+constexpr int kCounterStride = 32;  // u32 words between consecutive streams' counters
 
-// 64-bit slots of one workgroup's partial entry: for each of the g heads, o[D],
-// m (log2 domain) and l, each slot holding a float and the call epoch (low and
-// high 32 bits, written and read as one 8-byte access), rounded up to whole
-// 128-byte lines so that the entries of different workgroups share no line.
-__host__ __device__ inline int part_entry_slots(int g, int D)
+// Floats of one workgroup's partial entry (g heads of o[D], m, l and two
+// unused floats), rounded up to whole 128-byte lines so that the entries of
+// different workgroups share no line.
+__host__ __device__ inline int part_entry_floats(int g, int D)
 {
-    return (g * (D + 2) + 15) & ~15;
+    return (g * (D + 4) + 31) & ~31;
 }
 
-// The statically allocated scratch of kvq_decode_attention_noalloc(): hand-off
-// words of up to kStaticScratchStreams streams (one 128-byte line each), then
-// the partial entries of one call (a stream's entries contiguous, as in a
-// workspace).  Between two calls every word holds epoch 1 with no arrivals and
-// every partial slot is zero: the merging workgroup of each stream restores
-// that state after it has read the call's slots (AttnArgs::reset_after).
+// The statically allocated scratch of kvq_decode_attention_noalloc(): the
+// arrival counters of up to kStaticScratchStreams streams (one 128-byte line
+// each), then the partial entries of one call (a stream's entries contiguous,
+// as in a workspace).  Between two calls every counter is zero: the merging
+// workgroup of each stream re-arms its counter, and the partial entries need
+// no initial value (each call writes the entries it reads).
 constexpr size_t kStaticScratchBytes = size_t(16) << 20;
 constexpr int kStaticScratchStreams = 4096;
 constexpr size_t kStaticScratchWordsBytes = size_t(kStaticScratchStreams) * kCounterStride * 4;
 
 // Device address of this GPU's static scratch (set up on first use: its
-// hand-off state is initialised on stream st).
+// counters are zeroed on stream st).
 hipError_t static_scratch(int device, hipStream_t st, void **out);
 
 // Sequences one attention launch can take with lengths of their own.
@@ -143,12 +142,8 @@ struct AttnArgs {
     LayerDev L;
     const void *q;        // [B][Hq][D] in q_dtype
     float *out;           // [B][Hq][D]
-    unsigned long long *part;  // [BH][n_part] entries of part_entry_slots(g, D): [g][D + 2] (value, epoch)
-    unsigned *counters;   // hand-off word of stream bh at bh * kCounterStride (64-bit, see above)
-    // 0: the merging workgroup leaves the next epoch in the word; 1 (static
-    // scratch): it leaves epoch 1 and zeroes the call's partial slots, so that
-    // the next call, of any handle and shape, starts from the initial state
-    int reset_after;
+    float *part;          // [BH][n_part] entries of part_entry_floats(g, D): [g][D + 4] o[D], m (log2 domain), l, 2 unused
+    unsigned *counters;   // arrival counter of stream bh at bh * kCounterStride, zero between calls
     int q_dtype, kv_bf16;
     int D, g, Hkv, N, Tq, BH;
     int n_part;           // partial entries per stream (one per workgroup)
@@ -247,10 +242,6 @@ bool mfma_supported(int kb, int vb, int D);
 // rt: per-sequence lengths of a ragged batch, or nullptr
 hipError_t launch_attention(const AttnArgs &a, const RaggedTables *rt, bool use_mfma, hipStream_t st);
 hipError_t launch_zero(unsigned *p, int n, hipStream_t st);
-// Hand-off state of n_streams streams: words (stride kCounterStride u32) set to
-// 1 << 32, and n_part_slots partial slots zeroed.
-hipError_t launch_handoff_init(unsigned *counters, int n_streams, unsigned long long *part, size_t n_part_slots,
-                               hipStream_t st);
 // True when the prefill kernel is built for this layer format.
 bool prefill_supported(int kb, int vb, int D, int v_tiled);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st);

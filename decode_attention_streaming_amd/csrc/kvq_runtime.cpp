@@ -191,9 +191,11 @@ int plan_layout(const kvq_config *cfg, Plan *plan, std::string *err)
         d.tstride = cfg->table_stride;
         d.n_pages = cfg->n_pages;
         d.bh0 = 0;
+        d.gpp = P != 0 ? P / G : 0;
         if (d.kb == 16) {
             d.R = cfg->max_context;
             d.capq = G;  // unused
+            d.ngq = 1;
             d.wk = d.wv = 0;
         } else {
             d.R = lc.residual_len == 0 ? cfg->residual_len : lc.residual_len;
@@ -202,6 +204,7 @@ int plan_layout(const kvq_config *cfg, Plan *plan, std::string *err)
             if (d.R < 0 || d.R > cfg->max_context + G)
                 return fail(KVQ_EINVAL, "layer %d: residual_len %d out of range", l, d.R);
             d.capq = (cfg->max_context + cap_unit - 1) / cap_unit * cap_unit;
+            d.ngq = d.capq / G;
             d.wk = words_per_row(D, d.kb);
             d.wv = words_per_row(D, d.vb);
         }
@@ -232,7 +235,7 @@ int plan_layout(const kvq_config *cfg, Plan *plan, std::string *err)
         off = align_up(off + BH * static_cast<size_t>(d.R) * D * 2, A);
     }
     plan->off_part = off;
-    off = align_up(off + BH * kMaxPart * static_cast<size_t>(kvq::part_entry_slots(cfg->n_q_heads / cfg->n_kv_heads, D)) * 8,
+    off = align_up(off + BH * kMaxPart * static_cast<size_t>(kvq::part_entry_floats(cfg->n_q_heads / cfg->n_kv_heads, D)) * 4,
                    A);
     plan->off_cnt = off;
     off = align_up(off + BH * 4 * kvq::kCounterStride, A);
@@ -977,7 +980,7 @@ static int attention_launch(kvq_handle *h, int layer, const void *q, float *out,
     if (static_scratch) {
         // hand-off words and this call's partial entries in the library's
         // static scratch, left in their initial state by the call itself
-        const size_t need = static_cast<size_t>(BH) * a.n_part * kvq::part_entry_slots(g, D) * 8;
+        const size_t need = static_cast<size_t>(BH) * a.n_part * kvq::part_entry_floats(g, D) * 4;
         if (BH > kvq::kStaticScratchStreams || need > kvq::kStaticScratchBytes - kvq::kStaticScratchWordsBytes)
             return h->fail(KVQ_ENOMEM,
                            "layer %d: %d streams x %d partial entries need %zu bytes of static scratch; at most %d "
@@ -989,18 +992,14 @@ static int attention_launch(kvq_handle *h, int layer, const void *q, float *out,
         if (e != hipSuccess)
             return h->dev_fail(e, "static scratch set-up");
         a.counters = static_cast<unsigned *>(p);
-        a.part = reinterpret_cast<unsigned long long *>(static_cast<char *>(p) + kvq::kStaticScratchWordsBytes);
-        a.reset_after = 1;
+        a.part = reinterpret_cast<float *>(static_cast<char *>(p) + kvq::kStaticScratchWordsBytes);
     } else {
         a.counters = reinterpret_cast<unsigned *>(h->ws + h->plan.off_cnt);
-        a.part = reinterpret_cast<unsigned long long *>(h->ws + h->plan.off_part);
-        a.reset_after = 0;
+        a.part = reinterpret_cast<float *>(h->ws + h->plan.off_part);
         if (!h->counters_ready) {
-            // hand-off words at epoch 1, every partial slot at epoch 0
-            const size_t part_slots = static_cast<size_t>(BH) * kMaxPart * kvq::part_entry_slots(g, D);
-            e = kvq::launch_handoff_init(a.counters, BH, a.part, part_slots, h->stream);
+            e = kvq::launch_zero(a.counters, BH * kvq::kCounterStride, h->stream);
             if (e != hipSuccess)
-                return h->dev_fail(e, "hand-off init");
+                return h->dev_fail(e, "counter init");
             h->counters_ready = true;
         }
     }

@@ -32,11 +32,8 @@ hipError_t static_scratch(int device, hipStream_t st, void **out)
         hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
         if (e != hipSuccess)
             return e;
-        // hand-off words at epoch 1 with no arrivals, every partial slot zero
-        unsigned long long *words = static_cast<unsigned long long *>(p);
-        e = launch_handoff_init(reinterpret_cast<unsigned *>(words), kStaticScratchStreams,
-                                words + kStaticScratchStreams * (kCounterStride / 2),
-                                (kStaticScratchBytes - kStaticScratchWordsBytes) / 8, st);
+        // arrival counters start at zero (each call re-arms the ones it uses)
+        e = launch_zero(static_cast<unsigned *>(p), kStaticScratchStreams * kCounterStride, st);
         if (e != hipSuccess)
             return e;
         g_ptr[device] = p;
