@@ -263,10 +263,27 @@ def prefill_leg(cache, w, C, ends, qbytes, rounds, stream, dev):
     }
 
 
-def build_cache(kvq, synth, w, ctx, cap_tokens, dev, ragged):
-    """A cache of workload w holding ctx[b] prefilled tokens per sequence."""
+def page_table(B, cap_tokens, P, seed, dev):
+    """A block table for B sequences of up to cap_tokens tokens in pages of P:
+    every (sequence, page) entry a distinct page of a pool with a few unused
+    pages, in a seeded random order (non-contiguous).  Returns (table, n_pages)."""
+    import numpy as np
+    import torch
+    stride = -(-cap_tokens // P)
+    n_pages = B * stride + 8
+    perm = np.random.default_rng(seed).permutation(n_pages)[:B * stride].astype(np.int32)
+    return torch.from_numpy(perm.reshape(B, stride)).to(dev), n_pages
+
+
+def build_cache(kvq, synth, w, ctx, cap_tokens, dev, ragged, paged=0, seed=0):
+    """A cache of workload w holding ctx[b] prefilled tokens per sequence
+    (paged > 0: its quantized state in pages of that many tokens)."""
     L, B, Hq, Hkv, d = w.n_layers, w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim
-    cache = kvq.Cache(L, B, Hq, Hkv, d, cap_tokens, w.kv_dtype, w.q_dtype, w.G, w.R, w.layers)
+    kw = {}
+    if paged:
+        table, n_pages = page_table(B, cap_tokens, paged, seed, dev)
+        kw = dict(page_tokens=paged, n_pages=n_pages, block_table=table)
+    cache = kvq.Cache(L, B, Hq, Hkv, d, cap_tokens, w.kv_dtype, w.q_dtype, w.G, w.R, w.layers, **kw)
     for l in range(L):
         k, v = synth.layer_tokens(w, l, 0, max(ctx), dev, stats=synth.LayerStats(w, l))
         if ragged:
@@ -352,6 +369,9 @@ def main():
     ap.add_argument("--ragged", action="store_true",
                     help="sequences of different lengths: sequence b starts with context x "
                          "(0.25 + 1.5 b / (B - 1)) tokens")
+    ap.add_argument("--paged", type=int, default=0, metavar="P",
+                    help="keep each quantized layer's state in pages of P tokens named by a shuffled "
+                         "block table (0: a region per stream)")
     ap.add_argument("--kernel-rounds", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -395,7 +415,7 @@ def main():
     qbytes = 4 if w.q_dtype == "f32" else 2
     ctx = ragged_contexts(w.context, B) if args.ragged else [w.context] * B
     cap_tokens = max(ctx) + total + probe + 1
-    cache = build_cache(kvq, synth, w, ctx, cap_tokens, dev, args.ragged)
+    cache = build_cache(kvq, synth, w, ctx, cap_tokens, dev, args.ragged, args.paged, seed=1)
     stream = cache.stream
     knew, vnew, qs = decode_inputs(synth, w, max(ctx), total + probe, dev)
     outs = [torch.empty((B, Hq, d), dtype=torch.float32, device=dev) for _ in range(L)]
@@ -427,8 +447,9 @@ def main():
     for s in range(args.warmup, total):
         for lc in w.layers:
             kb, vb, R, kt, rpc = layer_row(lc)
-            timed_flushes += sum(quantized_count(c + s + 1, R, w.G, kb, rpc) > quantized_count(c + s, R, w.G, kb, rpc)
-                                 for c in ctx)
+            due = [quantized_count(c + s + 1, R, w.G, kb, rpc) > quantized_count(c + s, R, w.G, kb, rpc)
+                   for c in ctx]
+            timed_flushes += sum(due) if args.ragged else int(any(due))
 
     # the state the library reports agrees with the byte model used above
     ends = [c + total for c in ctx]
@@ -480,7 +501,7 @@ def main():
     # last-level cache and every call reads its state from HBM
     two_call_us = None
     if not args.no_extras:
-        cache2 = build_cache(kvq, synth, w, ctx, cap_tokens, dev, args.ragged)
+        cache2 = build_cache(kvq, synth, w, ctx, cap_tokens, dev, args.ragged, args.paged, seed=2)
         for s in range(total):
             step(cache2, s)
         outs2 = [torch.empty_like(o) for o in outs]
@@ -500,7 +521,7 @@ def main():
     call_us = two_call_us if two_call_us is not None else avg_call_us
     achieved = avg_att_bytes / (call_us * 1e-6) / 1e9
     traffic = None
-    if args.k_mode == "per-channel" and not (args.ragged or args.rpc):
+    if args.k_mode == "per-channel" and not (args.ragged or args.rpc or args.paged):
         traffic = stored_traffic(args.workload, args.table)
 
     # flush probe: 2G more steps timed one by one with events; the steps in
@@ -514,13 +535,14 @@ def main():
             evs[i + 1].record(stream)
         torch.cuda.synchronize()
         times = [evs[i].elapsed_time(evs[i + 1]) for i in range(probe)]
-        nfl = []
+        nfl = []  # flush launches per step: one per layer, or one per sequence of a ragged batch
         for i in range(probe):
             n = 0
             for lc in w.layers:
                 kb, vb, R, kt, rpc = layer_row(lc)
-                n += sum(quantized_count(c + total + i + 1, R, w.G, kb, rpc) >
-                         quantized_count(c + total + i, R, w.G, kb, rpc) for c in ctx)
+                due = [quantized_count(c + total + i + 1, R, w.G, kb, rpc) >
+                       quantized_count(c + total + i, R, w.G, kb, rpc) for c in ctx]
+                n += sum(due) if args.ragged else int(any(due))
             nfl.append(n)
         fl = [t for t, n in zip(times, nfl) if n > 0]
         plain = [t for t, n in zip(times, nfl) if n == 0]
@@ -543,7 +565,7 @@ def main():
     C = min(args.prefill_chunk, min(ends))
     if C > 0 and (w.head_dim == 128 or all(lc[0] != 3 for lc in w.layers)) and w.G % 32 == 0:
         prefill = prefill_leg(cache, w, C, ends, qbytes, rounds, stream, dev)
-        if C == 256 and args.k_mode == "per-channel" and not (args.ragged or args.rpc):
+        if C == 256 and args.k_mode == "per-channel" and not (args.ragged or args.rpc or args.paged):
             prefill["roofline"]["traffic"] = stored_traffic(args.workload, args.table, "prefill")
     cache.close()
     del cache
@@ -552,7 +574,7 @@ def main():
     # KIVI-KV8 analogue: the same shape with every layer K8V8, same steps
     kv8 = None
     if not args.no_extras and args.table == "default" and args.k_mode == "per-channel" and not (
-            args.ragged or args.rpc) and all(lc[0] != 3 for lc in w.layers):
+            args.ragged or args.rpc or args.paged) and all(lc[0] != 3 for lc in w.layers):
         w8 = synth.workload(args.workload)
         w8.layers = [(8, 8, r) for (_, _, r) in w8.layers]
         c8 = build_cache(kvq, synth, w8, ctx, cap_tokens, dev, False)
@@ -609,6 +631,8 @@ def main():
             "table": "".join("K%dV%d " % tuple(lc[:2]) for lc in w.layers).strip(),
             "k_mode": args.k_mode,
             "equiv_bits": w.equiv_bits()["kv"],
+            "paged": ({"page_tokens": args.paged, "table": "shuffled, non-contiguous"} if args.paged
+                      else None),
             "parallelism": "single GPU",
         },
         "roofline": {

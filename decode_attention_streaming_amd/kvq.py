@@ -11,7 +11,8 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkvq.so")
+# KVQ_LIB: another build of this same library (the CPU sanitizer tests use one)
+LIB_PATH = os.environ.get("KVQ_LIB") or os.path.join(_HERE, "libkvq.so")
 
 KVQ_OK, KVQ_EINVAL, KVQ_ENOMEM, KVQ_ECAPACITY, KVQ_EUNSUPPORTED, KVQ_EDEVICE = 0, -1, -2, -3, -4, -5
 KVQ_F32, KVQ_F16, KVQ_BF16 = 0, 1, 2

@@ -11,7 +11,8 @@ import pytest
 import torch
 
 from decode_attention_streaming_amd import kvq, synth
-from gpu_common import (ad_hoc_workload, check_attention, compare_export, make_oracle, q_streams, stream_view)
+from gpu_common import (GUARD_REL_L2, MAX_ABS, REL_L2, ad_hoc_workload, check_attention, compare_export, make_oracle,
+                        q_streams, stream_view)
 
 pytestmark = pytest.mark.gpu
 
@@ -162,7 +163,7 @@ def test_paged_prefill_attention():
     ref = orc.prefill_attention(synth.as_f64(q.reshape(B * Hkv, w.g, C, d)))
     o = synth.as_f64(op.reshape(B * Hkv, w.g, C, d))
     rel = np.linalg.norm(o - ref) / np.linalg.norm(ref)
-    assert rel <= 1e-3 and np.abs(o - ref).max() <= 5e-3, rel
+    assert rel <= REL_L2 and np.abs(o - ref).max() <= MAX_ABS and rel <= GUARD_REL_L2, rel
     flat.close()
     paged.close()
 

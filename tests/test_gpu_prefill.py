@@ -8,7 +8,8 @@ import pytest
 import torch
 
 from decode_attention_streaming_amd import kvq, synth
-from gpu_common import MAX_ABS, REL_L2, ad_hoc_workload, compare_export, make_cache, make_oracle, stream_view
+from gpu_common import (GUARD_REL_L2, MAX_ABS, REL_L2, ad_hoc_workload, compare_export, make_cache, make_oracle,
+                        stream_view)
 
 pytestmark = pytest.mark.gpu
 
@@ -38,6 +39,7 @@ def _check(out, ref, g, streams=None, what=""):
     rel = np.linalg.norm(diff) / np.linalg.norm(ref)
     mx = np.abs(diff).max()
     assert np.isfinite(rel) and rel <= REL_L2 and mx <= MAX_ABS, "%s rel-L2 %.3e max-abs %.3e" % (what, rel, mx)
+    assert rel <= GUARD_REL_L2, "%s: rel-L2 %.3e above the precision guard" % (what, rel)
     return rel, mx
 
 

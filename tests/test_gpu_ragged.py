@@ -10,7 +10,7 @@ import pytest
 import torch
 
 from decode_attention_streaming_amd import kvq, synth
-from gpu_common import (MAX_ABS, REL_L2, ad_hoc_workload, check_attention, compare_export, make_cache,
+from gpu_common import (GUARD_REL_L2, MAX_ABS, REL_L2, ad_hoc_workload, check_attention, compare_export, make_cache,
                         make_oracle, stream_view)
 
 pytestmark = pytest.mark.gpu
@@ -169,4 +169,5 @@ def test_ragged_prefill_parity(name):
         mx = np.abs(diff).max()
         print("  seq %d N=%d Tq=%d rel-L2 %.2e max-abs %.2e" % (b, orcs[b].N, orcs[b].Tq, rel, mx), flush=True)
         assert np.isfinite(rel) and rel <= REL_L2 and mx <= MAX_ABS, (name, b, rel, mx)
+        assert rel <= GUARD_REL_L2, (name, b, rel)
     cache.close()
