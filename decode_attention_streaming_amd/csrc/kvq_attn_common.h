@@ -21,6 +21,45 @@ namespace kvq {
 constexpr int kAttnThreads = 256;
 constexpr int kMaxG = 16;
 
+// Page ids of up to 64 consecutive pages of one sequence, one per lane of a
+// wave (paged layers).  A kernel loads them once for a run of tokens and then
+// takes each block's page from a register (readlane for a wave-uniform token,
+// bpermute for a per-lane one), so that no data load waits on a table read in
+// the middle of a round.
+struct WavePages {
+    int first = 0;  // page index within the sequence held by lane 0
+    int n = 0;      // pages held
+    int id = 0;     // this lane's page id (first + lane), clamped into the pool
+
+    // pages of tokens [t0, t1) all held?
+    __device__ bool covers(const QAddr &qa, int t0, int t1) const
+    {
+        const int p0 = t0 >> qa.P_log2, p1 = (t1 - 1) >> qa.P_log2;
+        return p0 >= first && p1 < first + n;
+    }
+    // hold the pages from token t0's on (up to 64, none past token t_end - 1)
+    __device__ void load(const QAddr &qa, int lane, int t0, int t_end)
+    {
+        first = t0 >> qa.P_log2;
+        const int last = (t_end - 1) >> qa.P_log2;
+        n = min(64, last - first + 1);
+        id = qa.clamp_page(qa.trow[first + min(lane, n - 1)]);
+    }
+    // row of token t: t the same in every lane / per lane (every lane active)
+    __device__ size_t row_u(const QAddr &qa, int t) const
+    {
+        return qa.page_row(__builtin_amdgcn_readlane(id, (t >> qa.P_log2) - first), t);
+    }
+    __device__ size_t row_v(const QAddr &qa, int t) const
+    {
+        return qa.page_row(__builtin_amdgcn_ds_bpermute(((t >> qa.P_log2) - first) << 2, id), t);
+    }
+    __device__ size_t grp_v(const QAddr &qa, int gi) const
+    {
+        return qa.page_grp(__builtin_amdgcn_ds_bpermute((((gi * qa.G) >> qa.P_log2) - first) << 2, id), gi);
+    }
+};
+
 // Partial entry of one (stream, workgroup, head): o[D], then m (log2 domain),
 // l and two unused floats.  16-byte aligned (D is a multiple of 4).
 __device__ __forceinline__ int part_stride(int D) { return D + 4; }

@@ -82,7 +82,7 @@ struct RoundData {
 // softmax work of one round serves nb blocks.  In the P.V products a lane's
 // weights enter only its own block's product (zeros elsewhere).
 // Results for head h < g go to po[h * D + c], pm[h], pl[h] (LDS).
-template <int KB, int VB, int D, bool KT>
+template <int KB, int VB, int D, bool KT, bool PG>
 __device__ void mfma_unit(const AttnArgs &a, const RaggedTables *rt, int bh, int unit, int lane, float *po, float *pm,
                           float *pl,
                           float *meta_lds)
@@ -114,7 +114,13 @@ __device__ void mfma_unit(const AttnArgs &a, const RaggedTables *rt, int bh, int
     const int bpg = G / 32;  // blocks per group
 
     const QAddr qa(L, bh);  // rows of the stream's tokens (through the page table when paged)
+    constexpr bool paged = PG;  // (the launch picks the instantiation by the layer's layout)
+    WavePages wp;           // paged: page ids of the current window's tokens, one per lane
     constexpr bool ktok = KT;  // per-token Key (its meta: 2 floats per row)
+    // this lane's word offsets in a block's K rows (tiles of tokens col and
+    // 16 + col) and V fragments, from the block's first row
+    const size_t koff0 = static_cast<size_t>(col) * L.wk + q * KW, koff1 = koff0 + 16 * static_cast<size_t>(L.wk);
+    const int voff = lane * FW;
 
     float m_run = -INFINITY, l_run = 0.0f, zb_run = 0.0f;
     int E = -1000;  // running V-scale exponent of this column: its weights carry 2^-E
@@ -136,9 +142,10 @@ __device__ void mfma_unit(const AttnArgs &a, const RaggedTables *rt, int bh, int
         constexpr int gp_log2 = __builtin_ctz(D / 2);  // 16-byte pieces per group: D / 2
         const int n16 = ktok ? 0 : nwin * D / 2;  // 16-byte pieces of nwin groups' [2][D] floats
         for (int i0 = 0; i0 < n16; i0 += 64) {
-            const int i = i0 + lane, j = i >> gp_log2;  // piece i of group w0 + j
+            const int i = i0 + lane, j = min(i >> gp_log2, nwin - 1);  // piece i of group w0 + j
+            const size_t gr = paged ? wp.grp_v(qa, w0 + j) : qa.gbase + w0 + j;
             if (i < n16)
-                __builtin_amdgcn_global_load_lds(L.k_meta + qa.grp(w0 + j) * 2 * D + 4 * (i & (D / 2 - 1)),
+                __builtin_amdgcn_global_load_lds(L.k_meta + gr * 2 * D + 4 * (i & (D / 2 - 1)),
                                                  meta_lds + 4 * i0, 16, 0, 0);
         }
         const char *qsrc = static_cast<const char *>(a.q) + static_cast<size_t>(bh) * g * D * qbytes;
@@ -261,16 +268,31 @@ __device__ void mfma_unit(const AttnArgs &a, const RaggedTables *rt, int bh, int
 
     // ---- one round: nb blocks starting at tokens t_first + i * G ----
     auto load_round = [&](RoundData<NB, KW, FW> &d, int t_first, int nb, int my_b) {
+        // each block's 32 rows are consecutive; its first row is the same in
+        // every lane (one branch on the layout per round)
+        size_t r0[NB];
+        const int tm = t_first + my_b * G;
+        size_t rm;
+        if (paged) {
+#pragma unroll
+            for (int i = 0; i < NB; ++i)
+                r0[i] = wp.row_u(qa, t_first + min(i, nb - 1) * G);
+            rm = wp.row_v(qa, tm);
+        } else {
+#pragma unroll
+            for (int i = 0; i < NB; ++i)
+                r0[i] = qa.base + t_first + i * G;
+            rm = qa.base + tm;
+        }
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             if (i < nb) {
-                const size_t r0 = qa.row(t_first + i * G);  // the block's 32 rows are consecutive
-                load_words(L.k_words + (r0 + col) * L.wk + q * KW, d.k0[i]);
-                load_words(L.k_words + (r0 + 16 + col) * L.wk + q * KW, d.k1[i]);
-                load_words(L.v_words + r0 * L.wv + lane * FW, d.v[i]);
+                const uint32_t *kr = L.k_words + r0[i] * L.wk;
+                load_words(kr + koff0, d.k0[i]);
+                load_words(kr + koff1, d.k1[i]);
+                load_words(L.v_words + r0[i] * L.wv + voff, d.v[i]);
             }
         }
-        const size_t rm = qa.row(t_first + my_b * G);
         const float4 *m0 = reinterpret_cast<const float4 *>(L.v_meta + (rm + 4 * q) * 2);
         const float4 *m1 = reinterpret_cast<const float4 *>(L.v_meta + (rm + 16 + 4 * q) * 2);
         d.vm[0] = m0[0];
@@ -413,6 +435,8 @@ __device__ void mfma_unit(const AttnArgs &a, const RaggedTables *rt, int bh, int
     for (int w0 = g_beg; w0 < g_end; w0 += NG) {
         const int nwin = __builtin_amdgcn_readfirstlane(min(NG, g_end - w0));  // uniform
         const bool in_win = jslot < nwin;
+        if (paged && !wp.covers(qa, w0 * G, (w0 + nwin) * G))
+            wp.load(qa, lane, w0 * G, g_end * G);  // once per 64 pages of the unit
         setup_issue(w0, nwin);
         for (int r = 0; r < bpg; ++r) {
             for (int u = 0; u < nwin; u += NB) {
@@ -655,7 +679,7 @@ __host__ __device__ inline int wave_region(const AttnArgs &a)
     return mfma_wave_region(a.D, a.g, a.units_q > 0, a.units_r > 0);
 }
 
-template <int KB, int VB, int D, bool KT>
+template <int KB, int VB, int D, bool KT, bool PG>
 __device__ __forceinline__ void attn_mfma_body(const AttnArgs &a, const RaggedTables *rt)
 {
     extern __shared__ float lds[];
@@ -676,7 +700,7 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs &a, const RaggedTa
     const int region = wave_region(a);
     float *po = lds + wave * region;
     if (unit < a.units_q) {
-        mfma_unit<KB, VB, D, KT>(a, rt, bh, unit, lane, po, s_pm[wave], s_pl[wave], po);
+        mfma_unit<KB, VB, D, KT, PG>(a, rt, bh, unit, lane, po, s_pm[wave], s_pl[wave], po);
     } else if (unit < a.units_q + a.units_r) {
         if (a.kv_bf16)
             mfma_residual_unit<D, true>(a, rt, bh, unit - a.units_q, lane, po, s_pm[wave], s_pl[wave]);
@@ -691,30 +715,30 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs &a, const RaggedTa
     arrive_and_merge<D>(a, bh, a.mfma_wgs, a.xcd_shift > 0);
 }
 
-template <int KB, int VB, int D, bool KT>
+template <int KB, int VB, int D, bool KT, bool PG>
 __global__ __launch_bounds__(kAttnThreads, (mfma_waves_per_simd<KB, VB>())) void attn_mfma_kernel(AttnArgs a)
 {
-    attn_mfma_body<KB, VB, D, KT>(a, nullptr);
+    attn_mfma_body<KB, VB, D, KT, PG>(a, nullptr);
 }
 
 // ragged batches: per-sequence lengths in the argument block
-template <int KB, int VB, int D, bool KT>
+template <int KB, int VB, int D, bool KT, bool PG>
 __global__ __launch_bounds__(kAttnThreads, (mfma_waves_per_simd<KB, VB>())) void attn_mfma_kernel_rg(
     RaggedAttnArgs r)
 {
-    attn_mfma_body<KB, VB, D, KT>(r.a, &r.t);
+    attn_mfma_body<KB, VB, D, KT, PG>(r.a, &r.t);
 }
 
-template <int KB, int VB, bool KT>
+template <int KB, int VB, bool KT, bool PG>
 hipError_t launch_pair(const AttnArgs &a, const RaggedTables *rt, hipStream_t st)
 {
     const dim3 grid = a.xcd_shift > 0 ? dim3(a.mfma_wgs * a.BH) : dim3(a.mfma_wgs, a.BH);
     const size_t lds = (kAttnThreads / 64) * wave_region(a) * sizeof(float);
     if (rt) {
         const RaggedAttnArgs r{a, *rt};
-        hipLaunchKernelGGL((attn_mfma_kernel_rg<KB, VB, KVQ_D, KT>), grid, dim3(kAttnThreads), lds, st, r);
+        hipLaunchKernelGGL((attn_mfma_kernel_rg<KB, VB, KVQ_D, KT, PG>), grid, dim3(kAttnThreads), lds, st, r);
     } else {
-        hipLaunchKernelGGL((attn_mfma_kernel<KB, VB, KVQ_D, KT>), grid, dim3(kAttnThreads), lds, st, a);
+        hipLaunchKernelGGL((attn_mfma_kernel<KB, VB, KVQ_D, KT, PG>), grid, dim3(kAttnThreads), lds, st, a);
     }
     return hipGetLastError();
 }
@@ -727,18 +751,20 @@ hipError_t launch_pair(const AttnArgs &a, const RaggedTables *rt, hipStream_t st
 hipError_t KVQ_CAT(launch_mfma_d, KVQ_D)(const AttnArgs &a, const RaggedTables *rt, hipStream_t st)
 {
     const int kb = a.L.kb, vb = a.L.vb;
+    const bool pg = a.L.table != nullptr;  // paged layer: its own instantiation
 #define KVQ_PAIR(K, V)                                                        \
     if (kb == K && vb == V)                                                   \
-        return a.L.k_tok ? launch_pair<K, V, true>(a, rt, st) : launch_pair<K, V, false>(a, rt, st);
+        return pg ? (a.L.k_tok ? launch_pair<K, V, true, true>(a, rt, st) : launch_pair<K, V, false, true>(a, rt, st)) \
+                  : (a.L.k_tok ? launch_pair<K, V, true, false>(a, rt, st) : launch_pair<K, V, false, false>(a, rt, st));
     KVQ_PAIR(2, 2) KVQ_PAIR(2, 4) KVQ_PAIR(2, 8)
     KVQ_PAIR(4, 2) KVQ_PAIR(4, 4) KVQ_PAIR(4, 8)
     KVQ_PAIR(8, 2) KVQ_PAIR(8, 4) KVQ_PAIR(8, 8)
 #if KVQ_D == 128
     // 3-bit rows: twelve words, three per lane quad (head_dim 256 would need
     // more registers than two waves per SIMD leave)
-    if (kb == 3 && vb == 2) return launch_pair<3, 2, false>(a, rt, st);
-    if (kb == 3 && vb == 4) return launch_pair<3, 4, false>(a, rt, st);
-    if (kb == 3 && vb == 8) return launch_pair<3, 8, false>(a, rt, st);
+    if (kb == 3 && vb == 2) return pg ? launch_pair<3, 2, false, true>(a, rt, st) : launch_pair<3, 2, false, false>(a, rt, st);
+    if (kb == 3 && vb == 4) return pg ? launch_pair<3, 4, false, true>(a, rt, st) : launch_pair<3, 4, false, false>(a, rt, st);
+    if (kb == 3 && vb == 8) return pg ? launch_pair<3, 8, false, true>(a, rt, st) : launch_pair<3, 8, false, false>(a, rt, st);
 #endif
 #undef KVQ_PAIR
     return hipErrorInvalidValue;

@@ -88,6 +88,21 @@ struct QAddr {
         const int t = gi * G, pi = t >> P_log2;
         return page_slot(t) * gpp + (gi - pi * gpp);
     }
+    // the same with token t's (or group gi's) page id already read
+    // (clamped into the pool)
+    __host__ __device__ size_t page_row(int page, int t) const
+    {
+        return ((static_cast<size_t>(page) * Hkv + h) << P_log2) + (t & ((1 << P_log2) - 1));
+    }
+    __host__ __device__ size_t page_grp(int page, int gi) const
+    {
+        const int pi = (gi * G) >> P_log2;
+        return (static_cast<size_t>(page) * Hkv + h) * gpp + (gi - pi * gpp);
+    }
+    __host__ __device__ int clamp_page(int page) const
+    {
+        return static_cast<unsigned>(page) >= static_cast<unsigned>(n_pages) ? n_pages : page;
+    }
 };
 
 // Quantize and pack groups [Tq0 + j*G, Tq0 + (j+1)*G), j < n_groups, for every
