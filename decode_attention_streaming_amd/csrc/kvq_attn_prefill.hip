@@ -31,41 +31,6 @@
 namespace kvq {
 namespace {
 
-// q of this lane's column, channels c0 .. c0 + QC - 1 (16-byte aligned runs),
-// widened to fp32
-template <int QC>
-__device__ __forceinline__ void load_q_slice(const void *q, int dtype, size_t i0, float (&r)[QC])
-{
-    if (dtype == 0) {
-        float4 v[QC / 4];
-#pragma unroll
-        for (int i = 0; i < QC / 4; ++i)
-            v[i] = reinterpret_cast<const float4 *>(static_cast<const float *>(q) + i0)[i];
-#pragma unroll
-        for (int i = 0; i < QC / 4; ++i) {
-            r[4 * i] = v[i].x;
-            r[4 * i + 1] = v[i].y;
-            r[4 * i + 2] = v[i].z;
-            r[4 * i + 3] = v[i].w;
-        }
-    } else {
-        const int bf = dtype == 2;
-        uint4 v[QC / 8];
-#pragma unroll
-        for (int i = 0; i < QC / 8; ++i)
-            v[i] = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(q) + i0)[i];
-#pragma unroll
-        for (int i = 0; i < QC / 8; ++i) {
-            const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                r[8 * i + 2 * k] = widen16(static_cast<uint16_t>(w[k] & 0xFFFFu), bf);
-                r[8 * i + 2 * k + 1] = widen16(static_cast<uint16_t>(w[k] >> 16), bf);
-            }
-        }
-    }
-}
-
 // Per-wave state of one tile: the column's online softmax (log2 domain) and
 // its output accumulators.
 template <int MT>
@@ -225,36 +190,80 @@ __device__ __forceinline__ void prefill_recent(const PrefillArgs &a, int bh, siz
     }
 }
 
-// One tile: queries tile * QT .. tile * QT + QT - 1 of stream bh.
+// Workgroups of kPrefillWaves waves, all on one stream: wave w takes query
+// tile wg * kPrefillWaves + w.  The quantized tokens are walked once per
+// workgroup, 32 at a time: the workgroup dequantizes the block's K into LDS
+// (k^ = s code + z in fp32, as fp16 hi and lo halves, token-major) and unpacks
+// its V codes into each lane's P.V operand registers (exact fp16 integers, the
+// V scale going into the weights), and every wave then reads them as matrix
+// operands for its own tile.  The block's dequantization is paid once per
+// workgroup instead of once per tile, and q.K needs no per-group rebuild of its
+// q operand (the scales are on the K side).
+constexpr int kPrefillWaves = 8;
+constexpr int kPrefillThreads = 64 * kPrefillWaves;
+
+// A block's bytes as stored (K codes, V codes, V scales and zeros, K scales
+// and zeros: the group's [2][D] floats, or per-token Key [32][2]), in the order
+// they are staged in LDS.  Every segment is a whole number of 16-byte pieces.
 template <int KB, int VB, int D, bool KT>
-__device__ void prefill_tile(const PrefillArgs &a, int bh, int tile, int lane, uint16_t *vt, float *meta_lds)
+struct PfRaw {
+    static constexpr int WK = KB == 3 ? 4 * ((D + 43) / 44) : D * KB / 32;  // K words per row
+    static constexpr int K_BYTES = 32 * WK * 4;
+    static constexpr int V_BYTES = 32 * (D * VB / 32) * 4;
+    static constexpr int VM_OFF = K_BYTES + V_BYTES;
+    static constexpr int KM_OFF = VM_OFF + 32 * 8;
+    static constexpr int KM_BYTES = KT ? 32 * 8 : 2 * D * 4;
+    static constexpr int BYTES = KM_OFF + KM_BYTES;
+    static constexpr int PIECES = BYTES / 16;
+    static constexpr int NP = (PIECES + kPrefillThreads - 1) / kPrefillThreads;  // pieces per thread
+    static constexpr int SLOT = NP * kPrefillThreads * 16;                        // bytes of a ring slot
+};
+
+template <int KB, int VB, int D, bool KT>
+struct PfLds {
+    static constexpr int KROW = D + 8;                 // halves per K row (padding: no bank conflicts)
+    static constexpr int KPLANE = 32 * KROW;           // halves per plane (hi, then lo)
+    static constexpr int MT = D / 16;
+    static constexpr int VROW = 4 * MT + 4;            // u32 per lane of V operand registers (padded)
+    static constexpr int K_BYTES = 2 * KPLANE * 2;
+    static constexpr int BUF_BYTES = K_BYTES + 64 * VROW * 4;
+    static constexpr int RAW_OFF = 2 * BUF_BYTES;      // three ring slots of stored block bytes follow
+    static constexpr int QUANT_BYTES = RAW_OFF + 3 * PfRaw<KB, VB, D, KT>::SLOT;
+    static constexpr int RECENT_BYTES = kPrefillWaves * D * 32 * 2;  // per-wave V tiles of the recent phase
+    static constexpr int BYTES = QUANT_BYTES > RECENT_BYTES ? QUANT_BYTES : RECENT_BYTES;
+};
+
+template <int KB, int VB, int D, bool KT, bool PG>
+__device__ __forceinline__ void prefill_wg(const PrefillArgs &a, int bh, int wg_in, int wave, int lane, char *lds)
 {
-    constexpr int KW = D * KB / 128;  // K words per lane per token (3 bits: D / 11 rounded up, / 4)
-    constexpr int PK = KB == 3 ? 1 : 16 / KB;   // K code pairs per word
-    constexpr int CW = KB == 3 ? 11 : 32 / KB;  // K channels per word
-    // channels of a quad's K words (3 bits: 11 per word, some past D), and
-    // 32-position chunks of q.K (3 bits: six registers per word, padded)
-    constexpr int QC = KB == 3 ? 11 * KW : D / 4;
-    constexpr int NC = KB == 3 ? (6 * KW + 3) / 4 : D / 32;
-    constexpr int FW = D * VB / 64;   // V words per lane per 32-token block
+    constexpr int KW = D * KB / 128;  // (unused for the K side here: rows are read per item)
+    (void)KW;
+    constexpr int NC = D / 32;        // 32-channel chunks of q.K
     constexpr int MT = D / 16;        // 16-channel tiles of P.V
+    constexpr int FW = D * VB / 64;   // V words per fragment (lane) of a block
+    constexpr int P = 16 / VB;        // V operand registers per word
+    using Lay = PfLds<KB, VB, D, KT>;
+    using Raw = PfRaw<KB, VB, D, KT>;
 
     const LayerDev &L = a.L;
     const int g = a.g, G = L.G;
+    const int tid = threadIdx.x;
     const int col = lane & 15, q = lane >> 4;
+    const int tile = wg_in * kPrefillWaves + wave;
     const int jq = col / g, h = col - jq * g;
     const int qi = tile * a.QT + jq;
-    const bool act = jq < a.QT && qi < a.n_q;
-    // this stream's sequence length and quantized tokens (per sequence when ragged)
+    const bool act = tile < a.n_tiles && jq < a.QT && qi < a.n_q;
     const int sb = a.ragged ? bh / a.Hkv : 0;
     const int N = a.ragged ? a.seqN[sb] : a.N;
     const int Tq = a.ragged ? a.seqTq[sb] : a.Tq;
     const int p_col = act ? N - a.n_q + qi : -1;  // last token this column sees
     const size_t qrow = (static_cast<size_t>(bh * g + (act ? h : 0)) * a.n_q + (act ? qi : 0)) * D;
-    // tokens [0, t_end) cover every column of the tile (uniform)
-    const int qi_last = min(a.n_q - 1, tile * a.QT + a.QT - 1);
+    // the workgroup's tokens [0, t_end): those of its last query (uniform)
+    const int qi_last = min(a.n_q - 1, (wg_in + 1) * kPrefillWaves * a.QT - 1);
     const int t_end = N - a.n_q + qi_last + 1;
-    const int tq_end = min(Tq, (t_end + 31) & ~31);  // quantized blocks to visit
+    const int tq_end = min(Tq, (t_end + 31) & ~31);  // quantized blocks to visit (Tq: whole blocks)
+    // first token any column of this wave's tile sees: blocks past it need the mask
+    const int p_first = N - a.n_q + min(a.n_q - 1, tile * a.QT);
 
     ColState<MT> st;
 #pragma unroll
@@ -262,213 +271,246 @@ __device__ void prefill_tile(const PrefillArgs &a, int bh, int tile, int lane, u
         st.O[m] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
     if (tq_end > 0) {
-        const QAddr qa(L, bh);  // rows of the stream's tokens (through the page table when paged)
-        float zb_run = 0.0f;
-        int E = -1000;  // running V-scale exponent: the weights carry 2^(kWShift - E)
+        const QAddr qa(L, bh);
+        WavePages wp;
+        const int nb = tq_end / 32;
+
+        // B operand of q.K: this column's q (times log2(e) / sqrt(D) and 2^sh),
+        // chunk k, quad q -> channels 32k + 8q + i, as hi/lo fp16
         Frag bhi[NC], blo[NC];
-        float bias = 0.0f, kscale = 0.0f;
-
-        // this column's q over the quad's channels, times log2(e) / sqrt(D)
-        float qq[QC];
-        if constexpr (KB == 3) {
-            // channels 11 * KW * q + i; those past D weigh 0
-#pragma unroll
-            for (int i = 0; i < QC; ++i) {
-                const int c = QC * q + i;
-                qq[i] = c < D ? load_q(a.q, a.q_dtype, qrow + (c < D ? c : 0)) : 0.0f;
-            }
-        } else {
-            load_q_slice<QC>(a.q, a.q_dtype, qrow + q * QC, qq);
-        }
+        float kscale;
         {
-            const float qscale = act ? a.scale_log2 : 0.0f;
-#pragma unroll
-            for (int i = 0; i < QC; ++i)
-                qq[i] *= qscale;
-        }
-
-        // K scales and zeros of group gi ([2][D] floats) into LDS slot gi & 1
-        // with direct-to-LDS loads: no registers held while they fly
-        auto meta_issue = [&](int gi) {
-            const float *src = L.k_meta + qa.grp(gi) * 2 * D;
-            float *dst = meta_lds + (gi & 1) * 2 * D;
-            constexpr int n16 = D / 2;  // 16-byte pieces
-#pragma unroll
-            for (int i0 = 0; i0 < n16; i0 += 64) {
-                if (i0 + lane < n16)
-                    __builtin_amdgcn_global_load_lds(src + 4 * (i0 + lane), dst + 4 * i0, 16, 0, 0);
-            }
-        };
-        // B operand of q.K for group gi (per-token Key: q alone, built once):
-        // q * s as hi/lo fp16 in the code-register order of the quad's words
-        auto build_b = [&](int gi) {
-            // the group's direct-to-LDS loads (issued one block earlier) must have
-            // landed: wait for them explicitly, the compiler does not always
-            // order LDS reads after them
-            if constexpr (!KT)
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            float qs[QC];
+            float qv[NC][8];
             float amax = 0.0f;
-            bias = 0.0f;
-            if constexpr (KB == 3) {
-                const float *sp = meta_lds + (gi & 1) * 2 * D;
-#pragma unroll
-                for (int i = 0; i < QC; ++i) {
-                    const int c = QC * q + i;
-                    const int cc = c < D ? c : 0;  // qq is 0 past D
-                    qs[i] = qq[i] * sp[cc];
-                    bias = __builtin_fmaf(qq[i], sp[D + cc], bias);
-                    amax = fmaxf(amax, fabsf(qs[i]));
-                }
-            }
-            const float *sp = meta_lds + (gi & 1) * 2 * D + q * QC;
-            const float *zp = sp + D;
-#pragma unroll
-            for (int i = 0; i < (KB == 3 ? 0 : QC); i += 4) {
-                const float4 one = {1.0f, 1.0f, 1.0f, 1.0f};
-                const float4 s4 = KT ? one : *reinterpret_cast<const float4 *>(sp + i);
-                const float4 z4 = KT ? one : *reinterpret_cast<const float4 *>(zp + i);
-                const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
-                const float zv[4] = {z4.x, z4.y, z4.z, z4.w};
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    qs[i + k] = qq[i + k] * sv[k];
-                    bias = __builtin_fmaf(qq[i + k], zv[k], bias);
-                    amax = fmaxf(amax, fabsf(qs[i + k]));
-                }
-            }
-            // the slot may be loaded again only after these reads
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            bias = col_sum(bias);
-            amax = col_max(amax);
-            const int sexp = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) : 0;
-            const int sh = 14 - sexp;  // |q s| * 2^sh < 2^14
+            load_q_runs<NC>(a.q, a.q_dtype, qrow + 8 * q, 32, qv);
 #pragma unroll
             for (int k = 0; k < NC; ++k)
 #pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const int R = 4 * k + p;
+                for (int i = 0; i < 8; ++i) {
+                    qv[k][i] = act ? qv[k][i] * a.scale_log2 : 0.0f;
+                    amax = fmaxf(amax, fabsf(qv[k][i]));
+                }
+            amax = col_max(amax);
+            const int sh = amax > 0.0f ? 14 - __builtin_amdgcn_frexp_expf(amax) : 0;
+#pragma unroll
+            for (int k = 0; k < NC; ++k)
+#pragma unroll
+                for (int p = 0; p < 4; ++p)
+                    split_pair(ldexpf(qv[k][2 * p], sh), ldexpf(qv[k][2 * p + 1], sh), bhi[k].u[p], blo[k].u[p]);
+            kscale = ldexpf(1.0f, -sh);
+        }
+
+        // first row of the block of token t0 (same in every lane)
+        auto block_row = [&](int t0) -> size_t {
+            if constexpr (PG) {
+                if (!wp.covers(qa, t0, t0 + 32))
+                    wp.load(qa, lane, t0, tq_end);
+                return wp.row_u(qa, t0);
+            } else {
+                return qa.base + t0;
+            }
+        };
+        // this thread's 16-byte pieces of a block's stored bytes: segment
+        // (0 K codes, 1 V codes, 2 V meta, 3 K meta) and offset in it, fixed for
+        // the walk.  Pieces past the block's bytes re-read its last piece, so
+        // that every thread issues the same loads in every step.
+        int pseg[Raw::NP], poff[Raw::NP];
+#pragma unroll
+        for (int ip = 0; ip < Raw::NP; ++ip) {
+            const int o = min(16 * (tid + kPrefillThreads * ip), Raw::BYTES - 16);
+            pseg[ip] = o < Raw::K_BYTES ? 0 : o < Raw::VM_OFF ? 1 : o < Raw::KM_OFF ? 2 : 3;
+            poff[ip] = o - (o < Raw::K_BYTES ? 0 : o < Raw::VM_OFF ? Raw::K_BYTES : o < Raw::KM_OFF ? Raw::VM_OFF
+                                                                                                   : Raw::KM_OFF);
+        }
+        // block t0's pieces, into registers
+        auto issue = [&](uint4 (&r)[Raw::NP], int t0) {
+            const size_t r0 = block_row(t0);
+            const char *ksrc = reinterpret_cast<const char *>(L.k_words + r0 * L.wk);
+            const char *vsrc = reinterpret_cast<const char *>(L.v_words + r0 * L.wv);
+            const char *vmsrc = reinterpret_cast<const char *>(L.v_meta + r0 * 2);
+            const char *kmsrc;
+            if constexpr (KT) {
+                kmsrc = reinterpret_cast<const char *>(L.k_meta + r0 * 2);
+            } else {
+                const int gi = t0 / G;
+                size_t gr;
+                if constexpr (PG)
+                    gr = qa.page_grp(__builtin_amdgcn_readlane(wp.id, (t0 >> qa.P_log2) - wp.first), gi);
+                else
+                    gr = qa.gbase + gi;
+                kmsrc = reinterpret_cast<const char *>(L.k_meta + gr * 2 * D);
+            }
+#pragma unroll
+            for (int ip = 0; ip < Raw::NP; ++ip) {
+                const char *base = pseg[ip] == 0 ? ksrc : pseg[ip] == 1 ? vsrc : pseg[ip] == 2 ? vmsrc : kmsrc;
+                r[ip] = *reinterpret_cast<const uint4 *>(base + poff[ip]);
+            }
+        };
+        // ring slot of block b's stored bytes
+        auto raw_slot = [&](int b) { return lds + Lay::RAW_OFF + (b % 3) * Raw::SLOT; };
+        auto stage = [&](const uint4 (&r)[Raw::NP], int b) {
+            char *dst = raw_slot(b);
+#pragma unroll
+            for (int ip = 0; ip < Raw::NP; ++ip) {
+                const int o = 16 * (tid + kPrefillThreads * ip);
+                if (o < Raw::BYTES)
+                    *reinterpret_cast<uint4 *>(dst + o) = r[ip];
+            }
+        };
+        // the dequantized block in LDS buffer buf
+        auto kplane = [&](int buf) { return reinterpret_cast<_Float16 *>(lds + buf * Lay::BUF_BYTES); };
+        auto vregs = [&](int buf) {
+            return reinterpret_cast<uint32_t *>(lds + buf * Lay::BUF_BYTES + Lay::K_BYTES);
+        };
+        // this thread's share of block b's dequantization, from its ring slot
+        // into buffer b & 1
+        auto dequant = [&](int b) {
+            const char *raw = raw_slot(b);
+            const int buf = b & 1;
+            _Float16 *khi = kplane(buf), *klo = khi + Lay::KPLANE;
+            const float *km = reinterpret_cast<const float *>(raw + Raw::KM_OFF);
+            constexpr int ITEMS = KB == 3 ? 32 * 12 : 32 * D / 8;
+            constexpr int NI = (ITEMS + kPrefillThreads - 1) / kPrefillThreads;
+#pragma unroll
+            for (int ii = 0; ii < NI; ++ii) {
+                const int i = tid + kPrefillThreads * ii;
+                if (i < ITEMS) {
                     if constexpr (KB == 3) {
-                        // register r of word w: the lo slot (and the hi slot) of the
-                        // 3-bit map, each divided by its bit offset
-                        if (R < 6 * KW) {
-                            const int w = R / 6, r = R % 6;
-                            const float xlo = ldexpf(qs[11 * w + r], sh - k3_lo_e(r));
-                            const float xhi =
-                                k3_hi_slot(r) < 0 ? 0.0f : ldexpf(qs[11 * w + k3_hi_slot(r)], sh - k3_hi_e(r));
-                            split_pair(xlo, xhi, bhi[k].u[p], blo[k].u[p]);
-                        } else {
-                            bhi[k].u[p] = 0u;
-                            blo[k].u[p] = 0u;
+                        // one word: channels 11 wi + j (j < 10: 3 bits at 3j; j = 10: 2 bits at 30)
+                        const int tok = i / 12, wi = i - tok * 12, c0 = 11 * wi;
+                        const uint32_t w = reinterpret_cast<const uint32_t *>(raw)[tok * Raw::WK + wi];
+#pragma unroll
+                        for (int j = 0; j < 11; ++j) {
+                            const int c = c0 + j;
+                            if (c < D) {
+                                const uint32_t code = j < 10 ? (w >> (3 * j)) & 7u : w >> 30;
+                                const float x = __builtin_fmaf(km[c], static_cast<float>(code), km[D + c]);
+                                const _Float16 hv = static_cast<_Float16>(x);
+                                khi[tok * Lay::KROW + c] = hv;
+                                klo[tok * Lay::KROW + c] = static_cast<_Float16>(x - static_cast<float>(hv));
+                            }
                         }
                     } else {
-                        const int clo = (R / PK) * CW + (R % PK), chi = clo + PK;
-                        const int e = sh - class_exp<KB>(R);
-                        split_pair(ldexpf(qs[clo], e), ldexpf(qs[chi], e), bhi[k].u[p], blo[k].u[p]);
+                        // eight channels c0 .. c0 + 7 of one token (8 KB bits)
+                        const int tok = i / (D / 8), c0 = 8 * (i - tok * (D / 8));
+                        const char *row = raw + tok * Raw::WK * 4;
+                        uint32_t w0, w1 = 0;
+                        if constexpr (KB == 2) {
+                            w0 = *reinterpret_cast<const uint16_t *>(row + c0 / 4);
+                        } else if constexpr (KB == 4) {
+                            w0 = *reinterpret_cast<const uint32_t *>(row + c0 / 2);
+                        } else {
+                            const uint2 v = *reinterpret_cast<const uint2 *>(row + c0);
+                            w0 = v.x;
+                            w1 = v.y;
+                        }
+                        float sc[8], zc[8];
+                        if constexpr (KT) {
+                            const float2 m = reinterpret_cast<const float2 *>(km)[tok];
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) {
+                                sc[j] = m.x;
+                                zc[j] = m.y;
+                            }
+                        } else {
+                            const float4 s0 = *reinterpret_cast<const float4 *>(km + c0);
+                            const float4 s1 = *reinterpret_cast<const float4 *>(km + c0 + 4);
+                            const float4 z0 = *reinterpret_cast<const float4 *>(km + D + c0);
+                            const float4 z1 = *reinterpret_cast<const float4 *>(km + D + c0 + 4);
+                            sc[0] = s0.x; sc[1] = s0.y; sc[2] = s0.z; sc[3] = s0.w;
+                            sc[4] = s1.x; sc[5] = s1.y; sc[6] = s1.z; sc[7] = s1.w;
+                            zc[0] = z0.x; zc[1] = z0.y; zc[2] = z0.z; zc[3] = z0.w;
+                            zc[4] = z1.x; zc[5] = z1.y; zc[6] = z1.z; zc[7] = z1.w;
+                        }
+                        float x[8];
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            uint32_t code;
+                            if constexpr (KB == 8)
+                                code = ((j < 4 ? w0 : w1) >> (8 * (j & 3))) & 0xFFu;
+                            else
+                                code = (w0 >> (KB * j)) & ((1u << KB) - 1u);
+                            x[j] = __builtin_fmaf(sc[j], static_cast<float>(code), zc[j]);
+                        }
+                        uint4 hi, lo;
+                        split_pair(x[0], x[1], hi.x, lo.x);
+                        split_pair(x[2], x[3], hi.y, lo.y);
+                        split_pair(x[4], x[5], hi.z, lo.z);
+                        split_pair(x[6], x[7], hi.w, lo.w);
+                        *reinterpret_cast<uint4 *>(khi + tok * Lay::KROW + c0) = hi;
+                        *reinterpret_cast<uint4 *>(klo + tok * Lay::KROW + c0) = lo;
                     }
                 }
-            kscale = ldexpf(1.0f, -sh);
-        };
-        if constexpr (KT)
-            build_b(0);
-
-        // one 32-token block: K rows of both 16-token tiles, the V fragment, the
-        // V meta of this lane's eight tokens (and their K meta, per-token Key)
-        struct Blk {
-            uint32_t k0[KW], k1[KW], vw[FW];
-            float4 vm[4], km[4];
-        };
-        auto load_blk = [&](Blk &b, int t0) {
-            const size_t r0 = qa.row(t0);  // the block's 32 rows are consecutive
-            load_words(L.k_words + (r0 + col) * L.wk + q * KW, b.k0);
-            load_words(L.k_words + (r0 + 16 + col) * L.wk + q * KW, b.k1);
-            load_words(L.v_words + r0 * L.wv + lane * FW, b.vw);
-            const float4 *m0 = reinterpret_cast<const float4 *>(L.v_meta + (r0 + 4 * q) * 2);
-            const float4 *m1 = reinterpret_cast<const float4 *>(L.v_meta + (r0 + 16 + 4 * q) * 2);
-            b.vm[0] = m0[0];
-            b.vm[1] = m0[1];
-            b.vm[2] = m1[0];
-            b.vm[3] = m1[1];
-            if constexpr (KT) {
-                const float4 *c0 = reinterpret_cast<const float4 *>(L.k_meta + (r0 + 4 * q) * 2);
-                const float4 *c1 = reinterpret_cast<const float4 *>(L.k_meta + (r0 + 16 + 4 * q) * 2);
-                b.km[0] = c0[0];
-                b.km[1] = c0[1];
-                b.km[2] = c1[0];
-                b.km[3] = c1[1];
+            }
+            // V: word w of the block's tiled codes -> lane w / FW's operand
+            // registers (w % FW) * P .. + P - 1
+            uint32_t *vr = vregs(buf);
+            constexpr int VWORDS = D * VB;
+            constexpr int NV = (VWORDS + kPrefillThreads - 1) / kPrefillThreads;
+#pragma unroll
+            for (int vi = 0; vi < NV; ++vi) {
+                const int w = tid + kPrefillThreads * vi;
+                if (w < VWORDS) {
+                    const int f = w / FW, wi = w - f * FW;
+                    const uint32_t word = reinterpret_cast<const uint32_t *>(raw + Raw::K_BYTES)[w];
+                    const uint32_t ww[1] = {word}, w8[1] = {word >> 8};
+                    uint32_t o[P];
+#pragma unroll
+                    for (int j = 0; j < P; ++j)
+                        o[j] = code_reg<VB>(ww, w8, j);
+                    uint32_t *dst = vr + f * Lay::VROW + wi * P;
+                    if constexpr (P == 8) {
+                        reinterpret_cast<uint4 *>(dst)[0] = uint4{o[0], o[1], o[2], o[3]};
+                        reinterpret_cast<uint4 *>(dst)[1] = uint4{o[P > 4 ? 4 : 0], o[P > 5 ? 5 : 0], o[P > 6 ? 6 : 0],
+                                                                  o[P > 7 ? 7 : 0]};
+                    } else if constexpr (P == 4) {
+                        *reinterpret_cast<uint4 *>(dst) = uint4{o[0], o[1], o[2], o[3]};
+                    } else {
+                        *reinterpret_cast<uint2 *>(dst) = uint2{o[0], o[1]};
+                    }
+                }
             }
         };
 
-        // Software pipeline, one block ahead: while block t0 is computed, the
-        // loads of block t0 + 32 (and of its group's meta when it starts a
-        // group) are in flight.  The last iteration reloads its own block
-        // (in bounds, unused) so that every iteration issues the same loads.
-        Blk cur, nxt;
-        if constexpr (!KT)
-            meta_issue(0);
-        load_blk(cur, 0);
-        for (int t0 = 0; t0 < tq_end; t0 += 32) {
-            if constexpr (!KT) {
-                if (t0 % G == 0)  // G is a multiple of 32: a group starts on a block
-                    build_b(t0 / G);
-            }
-            const int t1 = min(t0 + 32, tq_end - 32);
-            if constexpr (!KT) {
-                if (t1 > t0 && t1 % G == 0)
-                    meta_issue(t1 / G);
-            }
-            load_blk(nxt, t1);
-
-            // q.K for tokens 4q + j (acc0) and 16 + 4q + j (acc1)
-            uint32_t k08[KW], k18[KW];
-            shift8(cur.k0, k08);
-            shift8(cur.k1, k18);
+        float zb_run = 0.0f;
+        int E = -1000;  // running V-scale exponent: the weights carry 2^(kWShift - E)
+        // one block of the wave's tile from buffer buf
+        auto compute = [&](int b) {
+            const int t0 = 32 * b, buf = b & 1;
+            const _Float16 *khi = kplane(buf), *klo = khi + Lay::KPLANE;
             f4_t acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int k = 0; k < NC; ++k) {
-                Frag a0, a1;
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const int R = 4 * k + p;
-                    if constexpr (KB == 3) {
-                        a0.u[p] = R < 6 * KW ? code_reg3(cur.k0, k08, R) : 0u;
-                        a1.u[p] = R < 6 * KW ? code_reg3(cur.k1, k18, R) : 0u;
-                    } else {
-                        a0.u[p] = code_reg<KB>(cur.k0, k08, R);
-                        a1.u[p] = code_reg<KB>(cur.k1, k18, R);
-                    }
-                }
-                acc0 = mfma(a0, bhi[k], acc0);
-                acc0 = mfma(a0, blo[k], acc0);
-                acc1 = mfma(a1, bhi[k], acc1);
-                acc1 = mfma(a1, blo[k], acc1);
+                Frag ah0, al0, ah1, al1;
+                const int off0 = col * Lay::KROW + 32 * k + 8 * q, off1 = off0 + 16 * Lay::KROW;
+                ah0.h = *reinterpret_cast<const half8_t *>(khi + off0);
+                al0.h = *reinterpret_cast<const half8_t *>(klo + off0);
+                ah1.h = *reinterpret_cast<const half8_t *>(khi + off1);
+                al1.h = *reinterpret_cast<const half8_t *>(klo + off1);
+                acc0 = mfma(ah0, bhi[k], acc0);
+                acc1 = mfma(ah1, bhi[k], acc1);
+                acc0 = mfma(ah0, blo[k], acc0);
+                acc1 = mfma(ah1, blo[k], acc1);
+                acc0 = mfma(al0, bhi[k], acc0);
+                acc1 = mfma(al1, bhi[k], acc1);
             }
             float sc[8];
-            if constexpr (KT) {
-                // score_t = s_t sum_c q_c code_tc + z_t sum_c q_c
-                const float4 *km = cur.km;
-                const float ks[8] = {km[0].x, km[0].z, km[1].x, km[1].z, km[2].x, km[2].z, km[3].x, km[3].z};
-                const float kz[8] = {km[0].y, km[0].w, km[1].y, km[1].w, km[2].y, km[2].w, km[3].y, km[3].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                sc[j] = acc0[j] * kscale;
+                sc[4 + j] = acc1[j] * kscale;
+            }
+            if (t0 + 31 > p_first) {  // causal mask (uniform: only blocks that reach the tile's queries)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    sc[j] = __builtin_fmaf(acc0[j] * kscale, ks[j], kz[j] * bias);
-                    sc[4 + j] = __builtin_fmaf(acc1[j] * kscale, ks[4 + j], kz[4 + j] * bias);
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    sc[j] = __builtin_fmaf(acc0[j], kscale, bias);
-                    sc[4 + j] = __builtin_fmaf(acc1[j], kscale, bias);
+                    sc[j] = (t0 + 4 * q + j <= p_col) ? sc[j] : -INFINITY;
+                    sc[4 + j] = (t0 + 16 + 4 * q + j <= p_col) ? sc[4 + j] : -INFINITY;
                 }
             }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {  // causal mask
-                sc[j] = (t0 + 4 * q + j <= p_col) ? sc[j] : -INFINITY;
-                sc[4 + j] = (t0 + 16 + 4 * q + j <= p_col) ? sc[4 + j] : -INFINITY;
-            }
-            const float4 *vm = cur.vm;
-            const float vs[8] = {vm[0].x, vm[0].z, vm[1].x, vm[1].z, vm[2].x, vm[2].z, vm[3].x, vm[3].z};
-            const float vz[8] = {vm[0].y, vm[0].w, vm[1].y, vm[1].w, vm[2].y, vm[2].w, vm[3].y, vm[3].w};
+            const float4 *vmp = reinterpret_cast<const float4 *>(raw_slot(b) + Raw::VM_OFF);
+            const float4 vm0 = vmp[2 * q], vm1 = vmp[2 * q + 1], vm2 = vmp[8 + 2 * q], vm3 = vmp[8 + 2 * q + 1];
+            const float vs[8] = {vm0.x, vm0.z, vm1.x, vm1.z, vm2.x, vm2.z, vm3.x, vm3.z};
+            const float vz[8] = {vm0.y, vm0.w, vm1.y, vm1.w, vm2.y, vm2.w, vm3.y, vm3.w};
             float tmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
                                fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
             tmax = col_max(tmax);
@@ -509,18 +551,55 @@ __device__ void prefill_tile(const PrefillArgs &a, int bh, int tile, int lane, u
                 split_pair(ldexpf(p[2 * r] * vs[2 * r], e), ldexpf(p[2 * r + 1] * vs[2 * r + 1], e), whi.u[r],
                            wlo.u[r]);
             }
-            uint32_t v8[FW];
-            shift8(cur.vw, v8);
+            const uint32_t *vr = vregs(buf) + lane * Lay::VROW;
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
                 Frag av;
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    av.u[r] = code_reg<VB>(cur.vw, v8, 4 * m + r);
+                const uint4 v = *reinterpret_cast<const uint4 *>(vr + 4 * m);
+                av.u[0] = v.x; av.u[1] = v.y; av.u[2] = v.z; av.u[3] = v.w;
                 st.O[m] = mfma(av, whi, st.O[m]);
                 st.O[m] = mfma(av, wlo, st.O[m]);
             }
-            cur = nxt;
+        };
+
+        // Pipeline, one workgroup barrier per block.  In step b: block b is
+        // computed (dequantized LDS buffer b & 1), block b + 1 is dequantized
+        // from its ring slot into the other buffer, block b + 2's stored bytes
+        // (loaded into registers kRegSets steps earlier) are staged into the
+        // ring, and the loads of block b + 2 + kRegSets are issued into the
+        // registers that frees.  Loads past the last block re-read it (in
+        // bounds).
+        constexpr int kRegSets = 4;  // (four named sets below)
+        uint4 rs0[Raw::NP], rs1[Raw::NP], rs2[Raw::NP], rs3[Raw::NP];
+        issue(rs0, 0);
+        issue(rs1, 32 * min(1, nb - 1));
+        issue(rs2, 32 * min(2, nb - 1));
+        issue(rs3, 32 * min(3, nb - 1));
+        stage(rs0, 0);
+        issue(rs0, 32 * min(kRegSets, nb - 1));
+        stage(rs1, 1);  // block 1 (a re-read of block 0 when nb == 1: unused)
+        issue(rs1, 32 * min(kRegSets + 1, nb - 1));
+        __syncthreads();
+        dequant(0);
+        __syncthreads();
+        // one step; block b + 2 sits in set rs ((b + 2) % kRegSets).  The
+        // steps past the last block only stage re-reads into free slots: the
+        // sets are loaded and consumed unconditionally, so that their loads
+        // stay in flight across steps.
+        auto step = [&](int b, uint4 (&rs)[Raw::NP]) {
+            if (b < nb)  // uniform
+                compute(b);
+            if (b + 1 < nb)
+                dequant(b + 1);
+            stage(rs, b + 2);
+            issue(rs, 32 * min(b + 2 + kRegSets, nb - 1));
+            __syncthreads();
+        };
+        for (int b0 = 0; b0 < nb; b0 += kRegSets) {
+            step(b0, rs2);
+            step(b0 + 1, rs3);
+            step(b0 + 2, rs0);
+            step(b0 + 3, rs1);
         }
         // into the recent-token units (2^kWShift): o = O 2^(E - kWShift) + sum_t p_t z_t
         const float ZB = ldexpf(col_sum(zb_run), kWShift);
@@ -531,6 +610,9 @@ __device__ void prefill_tile(const PrefillArgs &a, int bh, int tile, int lane, u
                 st.O[m][j] = ldexpf(st.O[m][j], E) + ZB;
     }
 
+    if (tile >= a.n_tiles)
+        return;  // no barrier follows
+    uint16_t *vt = reinterpret_cast<uint16_t *>(lds) + wave * D * 32;
     if (Tq < t_end) {
         if (a.kv_bf16)
             prefill_recent<D, true>(a, bh, qrow, act, p_col, Tq, t_end, lane, vt, st);
@@ -548,34 +630,25 @@ __device__ void prefill_tile(const PrefillArgs &a, int bh, int tile, int lane, u
     }
 }
 
-// LDS floats per wave: V tile (D * 32 halves = D * 16 floats) + 2 * 2 * D
-constexpr int kPrefillWaveFloats = KVQ_D * 16 + 4 * KVQ_D;
-
-template <int KB, int VB, int D, bool KT>
-__global__ __launch_bounds__(256, 2) void attn_prefill_kernel(PrefillArgs a)
+template <int KB, int VB, int D, bool KT, bool PG>
+__global__ __launch_bounds__(kPrefillThreads, 1) void attn_prefill_kernel(PrefillArgs a)
 {
-    // per wave: a [D][32] 16-bit V tile (recent tokens), then two [2][D]
-    // float slots of K scales and zeros (quantized tokens)
-    extern __shared__ float lds_all[];
+    extern __shared__ __align__(16) char lds_pf[];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     // Workgroups are dealt to the eight XCDs in turn; number them so that
-    // consecutive slots (tiles of one stream, which read the same cache rows)
-    // land on the same XCD and share its L2.
+    // consecutive slots (workgroups of one stream, which read the same cache
+    // rows) land on the same XCD and share its L2.
     const int id = blockIdx.x;
     const int slot = (a.n_wg % 8 == 0) ? (id % 8) * (a.n_wg / 8) + id / 8 : id;
-    const int unit = slot * 4 + wave;
-    if (unit >= a.BH * a.n_tiles)
-        return;  // no workgroup barrier follows: a wave may leave alone
-    const int bh = unit / a.n_tiles, tile = unit - bh * a.n_tiles;
-    float *region = lds_all + wave * kPrefillWaveFloats;
-    prefill_tile<KB, VB, D, KT>(a, bh, tile, lane, reinterpret_cast<uint16_t *>(region), region + D * 16);
+    const int bh = slot / a.wg_per_stream, wg_in = slot - bh * a.wg_per_stream;
+    prefill_wg<KB, VB, D, KT, PG>(a, bh, wg_in, wave, lane, lds_pf);
 }
 
-template <int KB, int VB, bool KT>
+template <int KB, int VB, bool KT, bool PG>
 hipError_t launch_prefill_pair(const PrefillArgs &a, hipStream_t st)
 {
-    const size_t lds = 4 * kPrefillWaveFloats * sizeof(float);
-    hipLaunchKernelGGL((attn_prefill_kernel<KB, VB, KVQ_D, KT>), dim3(a.n_wg), dim3(256), lds, st, a);
+    constexpr size_t lds = PfLds<KB, VB, KVQ_D, KT>::BYTES;
+    hipLaunchKernelGGL((attn_prefill_kernel<KB, VB, KVQ_D, KT, PG>), dim3(a.n_wg), dim3(kPrefillThreads), lds, st, a);
     return hipGetLastError();
 }
 
@@ -584,20 +657,24 @@ hipError_t launch_prefill_pair(const PrefillArgs &a, hipStream_t st)
 hipError_t KVQ_CAT(launch_prefill_d, KVQ_D)(const PrefillArgs &a, hipStream_t st)
 {
     const int kb = a.L.kb, vb = a.L.vb;
+    const bool pg = a.L.table != nullptr;  // paged layer: its own instantiation
     if (kb == 16)  // recent tokens only: any instantiation serves
-        return launch_prefill_pair<2, 2, false>(a, st);
-#define KVQ_PAIR(K, V)                                                        \
-    if (kb == K && vb == V)                                                   \
-        return a.L.k_tok ? launch_prefill_pair<K, V, true>(a, st) : launch_prefill_pair<K, V, false>(a, st);
+        return launch_prefill_pair<2, 2, false, false>(a, st);
+#define KVQ_PAIR(K, V)                                                                                   \
+    if (kb == K && vb == V)                                                                              \
+        return pg ? (a.L.k_tok ? launch_prefill_pair<K, V, true, true>(a, st)                              \
+                               : launch_prefill_pair<K, V, false, true>(a, st))                            \
+                  : (a.L.k_tok ? launch_prefill_pair<K, V, true, false>(a, st)                             \
+                               : launch_prefill_pair<K, V, false, false>(a, st));
     KVQ_PAIR(2, 2) KVQ_PAIR(2, 4) KVQ_PAIR(2, 8)
     KVQ_PAIR(4, 2) KVQ_PAIR(4, 4) KVQ_PAIR(4, 8)
     KVQ_PAIR(8, 2) KVQ_PAIR(8, 4) KVQ_PAIR(8, 8)
 #undef KVQ_PAIR
 #if KVQ_D == 128
     // 3-bit rows (per-channel Key only): twelve words, three per lane quad
-    if (kb == 3 && vb == 2) return launch_prefill_pair<3, 2, false>(a, st);
-    if (kb == 3 && vb == 4) return launch_prefill_pair<3, 4, false>(a, st);
-    if (kb == 3 && vb == 8) return launch_prefill_pair<3, 8, false>(a, st);
+    if (kb == 3 && vb == 2) return pg ? launch_prefill_pair<3, 2, false, true>(a, st) : launch_prefill_pair<3, 2, false, false>(a, st);
+    if (kb == 3 && vb == 4) return pg ? launch_prefill_pair<3, 4, false, true>(a, st) : launch_prefill_pair<3, 4, false, false>(a, st);
+    if (kb == 3 && vb == 8) return pg ? launch_prefill_pair<3, 8, false, true>(a, st) : launch_prefill_pair<3, 8, false, false>(a, st);
 #endif
     return hipErrorInvalidValue;
 }

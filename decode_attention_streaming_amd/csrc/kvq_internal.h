@@ -206,15 +206,15 @@ struct RaggedAttnArgs {
 
 // Causal attention of the queries of the last n_q appended tokens (a prefill
 // chunk): query j (position N - n_q + j) attends to tokens 0 .. N - n_q + j.
-// One wave per tile of QT = 16 / g queries of one stream; n_wg workgroups of
-// four waves cover BH * n_tiles tiles.
+// One wave per tile of QT = 16 / g queries of one stream; workgroups of eight
+// waves (tiles) of one stream, wg_per_stream of them per stream, n_wg in all.
 struct PrefillArgs {
     LayerDev L;
     const void *q;   // [B][Hq][n_q][D] in q_dtype
     float *out;      // [B][Hq][n_q][D]
     int q_dtype, kv_bf16;
     int D, g, BH, N, Tq, n_q;
-    int QT, n_tiles, n_wg;
+    int QT, n_tiles, n_wg, wg_per_stream;
     int ngcap;       // capq / G
     float scale_log2;  // log2(e) / sqrt(D)
     // ragged layer: sequence b = bh / Hkv holds seqN[b] tokens, seqTq[b] of

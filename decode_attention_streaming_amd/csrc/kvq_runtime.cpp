@@ -740,10 +740,12 @@ int kvq_prefill_attention(kvq_handle *h, int layer, const void *q, int n_q, floa
     }
     a.QT = 16 / g;
     a.n_tiles = (n_q + a.QT - 1) / a.QT;
-    const long units = static_cast<long>(a.BH) * a.n_tiles;
-    if (units > 4L * INT32_MAX / 8)
-        return h->fail(KVQ_EUNSUPPORTED, "%ld query tiles exceed one launch", units);
-    a.n_wg = static_cast<int>((units + 3) / 4);
+    // workgroups of eight query tiles (waves), each on one stream
+    a.wg_per_stream = (a.n_tiles + 7) / 8;
+    const long wgs = static_cast<long>(a.BH) * a.wg_per_stream;
+    if (wgs > INT32_MAX / 2)
+        return h->fail(KVQ_EUNSUPPORTED, "%ld prefill workgroups exceed one launch", wgs);
+    a.n_wg = static_cast<int>(wgs);
     a.ngcap = d.capq / d.G;
     a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D)));
     const hipError_t e = kvq::launch_prefill(a, h->stream);
