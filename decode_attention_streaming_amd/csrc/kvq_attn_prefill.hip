@@ -201,6 +201,9 @@ __device__ __forceinline__ void prefill_recent(const PrefillArgs &a, int bh, siz
 // q operand (the scales are on the K side).
 constexpr int kPrefillWaves = 8;
 constexpr int kPrefillThreads = 64 * kPrefillWaves;
+// query tiles per wave (each LDS operand read feeds all of them): two up to
+// head_dim 128, one beyond (registers)
+__host__ __device__ constexpr int prefill_tw(int D) { return D <= 128 ? 2 : 1; }
 
 // A block's bytes as stored (K codes, V codes, V scales and zeros, K scales
 // and zeros: the group's [2][D] floats, or per-token Key [32][2]), in the order
@@ -244,31 +247,42 @@ __device__ __forceinline__ void prefill_wg(const PrefillArgs &a, int bh, int wg_
     constexpr int P = 16 / VB;        // V operand registers per word
     using Lay = PfLds<KB, VB, D, KT>;
     using Raw = PfRaw<KB, VB, D, KT>;
+    constexpr int TW = prefill_tw(D);
+    constexpr int TILES = kPrefillWaves * TW;  // tiles per workgroup
 
     const LayerDev &L = a.L;
     const int g = a.g, G = L.G;
     const int tid = threadIdx.x;
     const int col = lane & 15, q = lane >> 4;
-    const int tile = wg_in * kPrefillWaves + wave;
     const int jq = col / g, h = col - jq * g;
-    const int qi = tile * a.QT + jq;
-    const bool act = tile < a.n_tiles && jq < a.QT && qi < a.n_q;
     const int sb = a.ragged ? bh / a.Hkv : 0;
     const int N = a.ragged ? a.seqN[sb] : a.N;
     const int Tq = a.ragged ? a.seqTq[sb] : a.Tq;
-    const int p_col = act ? N - a.n_q + qi : -1;  // last token this column sees
-    const size_t qrow = (static_cast<size_t>(bh * g + (act ? h : 0)) * a.n_q + (act ? qi : 0)) * D;
+    // the wave's tiles: wg_in * TILES + wave * TW + i
+    int tile[TW], p_col[TW], p_first[TW];
+    bool act[TW];
+    size_t qrow[TW];
+#pragma unroll
+    for (int i = 0; i < TW; ++i) {
+        tile[i] = wg_in * TILES + wave * TW + i;
+        const int qi = tile[i] * a.QT + jq;
+        act[i] = tile[i] < a.n_tiles && jq < a.QT && qi < a.n_q;
+        p_col[i] = act[i] ? N - a.n_q + qi : -1;  // last token this column sees
+        qrow[i] = (static_cast<size_t>(bh * g + (act[i] ? h : 0)) * a.n_q + (act[i] ? qi : 0)) * D;
+        // first token any column of the tile sees: blocks past it need the mask
+        p_first[i] = N - a.n_q + min(a.n_q - 1, tile[i] * a.QT);
+    }
     // the workgroup's tokens [0, t_end): those of its last query (uniform)
-    const int qi_last = min(a.n_q - 1, (wg_in + 1) * kPrefillWaves * a.QT - 1);
+    const int qi_last = min(a.n_q - 1, (wg_in + 1) * TILES * a.QT - 1);
     const int t_end = N - a.n_q + qi_last + 1;
     const int tq_end = min(Tq, (t_end + 31) & ~31);  // quantized blocks to visit (Tq: whole blocks)
-    // first token any column of this wave's tile sees: blocks past it need the mask
-    const int p_first = N - a.n_q + min(a.n_q - 1, tile * a.QT);
 
-    ColState<MT> st;
+    ColState<MT> st[TW];
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
-        st.O[m] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int i = 0; i < TW; ++i)
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+            st[i].O[m] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
     if (tq_end > 0) {
         const QAddr qa(L, bh);
@@ -277,17 +291,18 @@ __device__ __forceinline__ void prefill_wg(const PrefillArgs &a, int bh, int wg_
 
         // B operand of q.K: this column's q (times log2(e) / sqrt(D) and 2^sh),
         // chunk k, quad q -> channels 32k + 8q + i, as hi/lo fp16
-        Frag bhi[NC], blo[NC];
-        float kscale;
-        {
+        Frag bhi[TW][NC], blo[TW][NC];
+        float kscale[TW];
+#pragma unroll
+        for (int t = 0; t < TW; ++t) {
             float qv[NC][8];
             float amax = 0.0f;
-            load_q_runs<NC>(a.q, a.q_dtype, qrow + 8 * q, 32, qv);
+            load_q_runs<NC>(a.q, a.q_dtype, qrow[t] + 8 * q, 32, qv);
 #pragma unroll
             for (int k = 0; k < NC; ++k)
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    qv[k][i] = act ? qv[k][i] * a.scale_log2 : 0.0f;
+                    qv[k][i] = act[t] ? qv[k][i] * a.scale_log2 : 0.0f;
                     amax = fmaxf(amax, fabsf(qv[k][i]));
                 }
             amax = col_max(amax);
@@ -296,8 +311,9 @@ __device__ __forceinline__ void prefill_wg(const PrefillArgs &a, int bh, int wg_
             for (int k = 0; k < NC; ++k)
 #pragma unroll
                 for (int p = 0; p < 4; ++p)
-                    split_pair(ldexpf(qv[k][2 * p], sh), ldexpf(qv[k][2 * p + 1], sh), bhi[k].u[p], blo[k].u[p]);
-            kscale = ldexpf(1.0f, -sh);
+                    split_pair(ldexpf(qv[k][2 * p], sh), ldexpf(qv[k][2 * p + 1], sh), bhi[t][k].u[p],
+                               blo[t][k].u[p]);
+            kscale[t] = ldexpf(1.0f, -sh);
         }
 
         // first row of the block of token t0 (same in every lane)
@@ -472,13 +488,23 @@ __device__ __forceinline__ void prefill_wg(const PrefillArgs &a, int bh, int wg_
             }
         };
 
-        float zb_run = 0.0f;
-        int E = -1000;  // running V-scale exponent: the weights carry 2^(kWShift - E)
-        // one block of the wave's tile from buffer buf
+        float zb_run[TW];
+        int E[TW];  // running V-scale exponent: the weights carry 2^(kWShift - E)
+#pragma unroll
+        for (int t = 0; t < TW; ++t) {
+            zb_run[t] = 0.0f;
+            E[t] = -1000;
+        }
+        // one block of the wave's tiles from buffer buf
         auto compute = [&](int b) {
             const int t0 = 32 * b, buf = b & 1;
             const _Float16 *khi = kplane(buf), *klo = khi + Lay::KPLANE;
-            f4_t acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+            f4_t acc0[TW], acc1[TW];
+#pragma unroll
+            for (int t = 0; t < TW; ++t) {
+                acc0[t] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                acc1[t] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            }
 #pragma unroll
             for (int k = 0; k < NC; ++k) {
                 Frag ah0, al0, ah1, al1;
@@ -487,69 +513,76 @@ __device__ __forceinline__ void prefill_wg(const PrefillArgs &a, int bh, int wg_
                 al0.h = *reinterpret_cast<const half8_t *>(klo + off0);
                 ah1.h = *reinterpret_cast<const half8_t *>(khi + off1);
                 al1.h = *reinterpret_cast<const half8_t *>(klo + off1);
-                acc0 = mfma(ah0, bhi[k], acc0);
-                acc1 = mfma(ah1, bhi[k], acc1);
-                acc0 = mfma(ah0, blo[k], acc0);
-                acc1 = mfma(ah1, blo[k], acc1);
-                acc0 = mfma(al0, bhi[k], acc0);
-                acc1 = mfma(al1, bhi[k], acc1);
-            }
-            float sc[8];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                sc[j] = acc0[j] * kscale;
-                sc[4 + j] = acc1[j] * kscale;
-            }
-            if (t0 + 31 > p_first) {  // causal mask (uniform: only blocks that reach the tile's queries)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    sc[j] = (t0 + 4 * q + j <= p_col) ? sc[j] : -INFINITY;
-                    sc[4 + j] = (t0 + 16 + 4 * q + j <= p_col) ? sc[4 + j] : -INFINITY;
+                for (int t = 0; t < TW; ++t) {
+                    acc0[t] = mfma(ah0, bhi[t][k], acc0[t]);
+                    acc1[t] = mfma(ah1, bhi[t][k], acc1[t]);
+                    acc0[t] = mfma(ah0, blo[t][k], acc0[t]);
+                    acc1[t] = mfma(ah1, blo[t][k], acc1[t]);
+                    acc0[t] = mfma(al0, bhi[t][k], acc0[t]);
+                    acc1[t] = mfma(al1, bhi[t][k], acc1[t]);
                 }
             }
             const float4 *vmp = reinterpret_cast<const float4 *>(raw_slot(b) + Raw::VM_OFF);
             const float4 vm0 = vmp[2 * q], vm1 = vmp[2 * q + 1], vm2 = vmp[8 + 2 * q], vm3 = vmp[8 + 2 * q + 1];
             const float vs[8] = {vm0.x, vm0.z, vm1.x, vm1.z, vm2.x, vm2.z, vm3.x, vm3.z};
             const float vz[8] = {vm0.y, vm0.w, vm1.y, vm1.w, vm2.y, vm2.w, vm3.y, vm3.w};
-            float tmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                               fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-            tmax = col_max(tmax);
             float vmax = fmaxf(fmaxf(fmaxf(vs[0], vs[1]), fmaxf(vs[2], vs[3])),
                                fmaxf(fmaxf(vs[4], vs[5]), fmaxf(vs[6], vs[7])));
             vmax = col_max(vmax);
             const int eb = vmax > 0.0f ? __builtin_amdgcn_frexp_expf(vmax) : -1000;
-            const bool need_m = act && (tmax > st.m_run + kTau);
-            const bool need_e = act && (eb > E);
-            if (__builtin_amdgcn_ballot_w64(need_m || need_e) != 0) {
-                const float m_new = need_m ? tmax : st.m_run;
-                const int E_new = need_e ? eb : E;
-                const float alpha = (m_new == st.m_run) ? 1.0f : exp2f(st.m_run - m_new);
-                const float f = ldexpf(alpha, E - E_new);
-#pragma unroll
-                for (int m = 0; m < MT; ++m)
-                    st.O[m] *= f;
-                st.l_run *= alpha;
-                zb_run *= alpha;
-                st.m_run = m_new;
-                E = E_new;
-            }
-            const float mo = act ? st.m_run : INFINITY;
-            float p[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                p[j] = weight_exp2(sc[j] - mo);
-                st.l_run += p[j];
-                zb_run = __builtin_fmaf(p[j], vz[j], zb_run);
-            }
-            // B operand of P.V: weights p s 2^(kWShift - E), k-slot pairs, each
+            // B operands of P.V: weights p s 2^(kWShift - E), k-slot pairs, each
             // divided by its code class factor
-            Frag whi, wlo;
-            const int wsh = kWShift - E;
+            Frag whi[TW], wlo[TW];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int e = wsh - class_exp<VB>(r);
-                split_pair(ldexpf(p[2 * r] * vs[2 * r], e), ldexpf(p[2 * r + 1] * vs[2 * r + 1], e), whi.u[r],
-                           wlo.u[r]);
+            for (int t = 0; t < TW; ++t) {
+                float sc[8];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    sc[j] = acc0[t][j] * kscale[t];
+                    sc[4 + j] = acc1[t][j] * kscale[t];
+                }
+                if (t0 + 31 > p_first[t]) {  // causal mask (uniform: only blocks that reach the tile's queries)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        sc[j] = (t0 + 4 * q + j <= p_col[t]) ? sc[j] : -INFINITY;
+                        sc[4 + j] = (t0 + 16 + 4 * q + j <= p_col[t]) ? sc[4 + j] : -INFINITY;
+                    }
+                }
+                float tmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                                   fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+                tmax = col_max(tmax);
+                ColState<MT> &c = st[t];
+                const bool need_m = act[t] && (tmax > c.m_run + kTau);
+                const bool need_e = act[t] && (eb > E[t]);
+                if (__builtin_amdgcn_ballot_w64(need_m || need_e) != 0) {
+                    const float m_new = need_m ? tmax : c.m_run;
+                    const int E_new = need_e ? eb : E[t];
+                    const float alpha = (m_new == c.m_run) ? 1.0f : exp2f(c.m_run - m_new);
+                    const float f = ldexpf(alpha, E[t] - E_new);
+#pragma unroll
+                    for (int m = 0; m < MT; ++m)
+                        c.O[m] *= f;
+                    c.l_run *= alpha;
+                    zb_run[t] *= alpha;
+                    c.m_run = m_new;
+                    E[t] = E_new;
+                }
+                const float mo = act[t] ? c.m_run : INFINITY;
+                float p[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    p[j] = weight_exp2(sc[j] - mo);
+                    c.l_run += p[j];
+                    zb_run[t] = __builtin_fmaf(p[j], vz[j], zb_run[t]);
+                }
+                const int wsh = kWShift - E[t];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int e = wsh - class_exp<VB>(r);
+                    split_pair(ldexpf(p[2 * r] * vs[2 * r], e), ldexpf(p[2 * r + 1] * vs[2 * r + 1], e),
+                               whi[t].u[r], wlo[t].u[r]);
+                }
             }
             const uint32_t *vr = vregs(buf) + lane * Lay::VROW;
 #pragma unroll
@@ -557,8 +590,11 @@ __device__ __forceinline__ void prefill_wg(const PrefillArgs &a, int bh, int wg_
                 Frag av;
                 const uint4 v = *reinterpret_cast<const uint4 *>(vr + 4 * m);
                 av.u[0] = v.x; av.u[1] = v.y; av.u[2] = v.z; av.u[3] = v.w;
-                st.O[m] = mfma(av, whi, st.O[m]);
-                st.O[m] = mfma(av, wlo, st.O[m]);
+#pragma unroll
+                for (int t = 0; t < TW; ++t) {
+                    st[t].O[m] = mfma(av, whi[t], st[t].O[m]);
+                    st[t].O[m] = mfma(av, wlo[t], st[t].O[m]);
+                }
             }
         };
 
@@ -569,12 +605,16 @@ __device__ __forceinline__ void prefill_wg(const PrefillArgs &a, int bh, int wg_
         // ring, and the loads of block b + 2 + kRegSets are issued into the
         // registers that frees.  Loads past the last block re-read it (in
         // bounds).
-        constexpr int kRegSets = 4;  // (four named sets below)
+        // register sets: four blocks in flight, two when a block takes two or
+        // more pieces per thread (registers)
+        constexpr int kRegSets = Raw::NP == 1 ? 4 : 2;
         uint4 rs0[Raw::NP], rs1[Raw::NP], rs2[Raw::NP], rs3[Raw::NP];
         issue(rs0, 0);
         issue(rs1, 32 * min(1, nb - 1));
-        issue(rs2, 32 * min(2, nb - 1));
-        issue(rs3, 32 * min(3, nb - 1));
+        if constexpr (kRegSets == 4) {
+            issue(rs2, 32 * min(2, nb - 1));
+            issue(rs3, 32 * min(3, nb - 1));
+        }
         stage(rs0, 0);
         issue(rs0, 32 * min(kRegSets, nb - 1));
         stage(rs1, 1);  // block 1 (a re-read of block 0 when nb == 1: unused)
@@ -596,37 +636,48 @@ __device__ __forceinline__ void prefill_wg(const PrefillArgs &a, int bh, int wg_
             __syncthreads();
         };
         for (int b0 = 0; b0 < nb; b0 += kRegSets) {
-            step(b0, rs2);
-            step(b0 + 1, rs3);
-            step(b0 + 2, rs0);
-            step(b0 + 3, rs1);
+            if constexpr (kRegSets == 4) {
+                step(b0, rs2);
+                step(b0 + 1, rs3);
+                step(b0 + 2, rs0);
+                step(b0 + 3, rs1);
+            } else {
+                step(b0, rs0);
+                step(b0 + 1, rs1);
+            }
         }
         // into the recent-token units (2^kWShift): o = O 2^(E - kWShift) + sum_t p_t z_t
-        const float ZB = ldexpf(col_sum(zb_run), kWShift);
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
+        for (int t = 0; t < TW; ++t) {
+            const float ZB = ldexpf(col_sum(zb_run[t]), kWShift);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                st.O[m][j] = ldexpf(st.O[m][j], E) + ZB;
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    st[t].O[m][j] = ldexpf(st[t].O[m][j], E[t]) + ZB;
+        }
     }
 
-    if (tile >= a.n_tiles)
-        return;  // no barrier follows
+    // recent tokens and the output, one tile at a time (no barrier follows)
     uint16_t *vt = reinterpret_cast<uint16_t *>(lds) + wave * D * 32;
-    if (Tq < t_end) {
-        if (a.kv_bf16)
-            prefill_recent<D, true>(a, bh, qrow, act, p_col, Tq, t_end, lane, vt, st);
-        else
-            prefill_recent<D, false>(a, bh, qrow, act, p_col, Tq, t_end, lane, vt, st);
-    }
-
-    const float Lc = col_sum(st.l_run);
-    if (act) {
-        const float inv = ldexpf(1.0f / Lc, -kWShift);
-        float *o = a.out + qrow + 4 * q;
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
-            *reinterpret_cast<f4_t *>(o + 16 * m) = st.O[m] * inv;
+    for (int t = 0; t < TW; ++t) {
+        if (tile[t] >= a.n_tiles)
+            break;
+        if (Tq < t_end) {
+            if (a.kv_bf16)
+                prefill_recent<D, true>(a, bh, qrow[t], act[t], p_col[t], Tq, t_end, lane, vt, st[t]);
+            else
+                prefill_recent<D, false>(a, bh, qrow[t], act[t], p_col[t], Tq, t_end, lane, vt, st[t]);
+        }
+        const float Lc = col_sum(st[t].l_run);
+        if (act[t]) {
+            const float inv = ldexpf(1.0f / Lc, -kWShift);
+            float *o = a.out + qrow[t] + 4 * q;
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                *reinterpret_cast<f4_t *>(o + 16 * m) = st[t].O[m] * inv;
+        }
     }
 }
 

@@ -206,8 +206,9 @@ struct RaggedAttnArgs {
 
 // Causal attention of the queries of the last n_q appended tokens (a prefill
 // chunk): query j (position N - n_q + j) attends to tokens 0 .. N - n_q + j.
-// One wave per tile of QT = 16 / g queries of one stream; workgroups of eight
-// waves (tiles) of one stream, wg_per_stream of them per stream, n_wg in all.
+// Tiles of QT = 16 / g queries of one stream, two per wave (one for head_dim
+// 256); workgroups of eight waves of one stream, wg_per_stream of them per
+// stream, n_wg in all.
 struct PrefillArgs {
     LayerDev L;
     const void *q;   // [B][Hq][n_q][D] in q_dtype

@@ -740,8 +740,10 @@ int kvq_prefill_attention(kvq_handle *h, int layer, const void *q, int n_q, floa
     }
     a.QT = 16 / g;
     a.n_tiles = (n_q + a.QT - 1) / a.QT;
-    // workgroups of eight query tiles (waves), each on one stream
-    a.wg_per_stream = (a.n_tiles + 7) / 8;
+    // workgroups of eight waves, each on one stream, two query tiles per wave
+    // up to head_dim 128 and one beyond
+    const int tiles_wg = D <= 128 ? 16 : 8;
+    a.wg_per_stream = (a.n_tiles + tiles_wg - 1) / tiles_wg;
     const long wgs = static_cast<long>(a.BH) * a.wg_per_stream;
     if (wgs > INT32_MAX / 2)
         return h->fail(KVQ_EUNSUPPORTED, "%ld prefill workgroups exceed one launch", wgs);
