@@ -626,10 +626,16 @@ __device__ __forceinline__ void prefill_wg(const PrefillArgs &a, int bh, int wg_
         // steps past the last block only stage re-reads into free slots: the
         // sets are loaded and consumed unconditionally, so that their loads
         // stay in flight across steps.
+        // The two waves that share a SIMD (w and w + 4) take the step's two
+        // halves in opposite orders, so that one's matrix products overlap the
+        // other's dequantization (the halves touch different buffers).
+        const bool deq_first = wave >= kPrefillWaves / 2;
         auto step = [&](int b, uint4 (&rs)[Raw::NP]) {
+            if (deq_first && b + 1 < nb)
+                dequant(b + 1);
             if (b < nb)  // uniform
                 compute(b);
-            if (b + 1 < nb)
+            if (!deq_first && b + 1 < nb)
                 dequant(b + 1);
             stage(rs, b + 2);
             issue(rs, 32 * min(b + 2 + kRegSets, nb - 1));
