@@ -248,7 +248,10 @@ __device__ __forceinline__ void prefill_wg(const PrefillArgs &a, int bh, int wg_
     using Lay = PfLds<KB, VB, D, KT>;
     using Raw = PfRaw<KB, VB, D, KT>;
     constexpr int TW = prefill_tw(D);
-    constexpr int TILES = kPrefillWaves * TW;  // tiles per workgroup
+    // tiles per wave in this launch: TW, or one when the launch has too few
+    // workgroups to fill the device with TW (few streams)
+    const int tw = a.tw;
+    const int TILES = kPrefillWaves * tw;  // tiles per workgroup
 
     const LayerDev &L = a.L;
     const int g = a.g, G = L.G;
@@ -264,7 +267,7 @@ __device__ __forceinline__ void prefill_wg(const PrefillArgs &a, int bh, int wg_
     size_t qrow[TW];
 #pragma unroll
     for (int i = 0; i < TW; ++i) {
-        tile[i] = wg_in * TILES + wave * TW + i;
+        tile[i] = i < tw ? wg_in * TILES + wave * tw + i : a.n_tiles;  // (past the last tile: inactive)
         const int qi = tile[i] * a.QT + jq;
         act[i] = tile[i] < a.n_tiles && jq < a.QT && qi < a.n_q;
         p_col[i] = act[i] ? N - a.n_q + qi : -1;  // last token this column sees
@@ -515,6 +518,8 @@ __device__ __forceinline__ void prefill_wg(const PrefillArgs &a, int bh, int wg_
                 al1.h = *reinterpret_cast<const half8_t *>(klo + off1);
 #pragma unroll
                 for (int t = 0; t < TW; ++t) {
+                    if (t > 0 && tw == 1)
+                        break;  // uniform
                     acc0[t] = mfma(ah0, bhi[t][k], acc0[t]);
                     acc1[t] = mfma(ah1, bhi[t][k], acc1[t]);
                     acc0[t] = mfma(ah0, blo[t][k], acc0[t]);
@@ -536,6 +541,8 @@ __device__ __forceinline__ void prefill_wg(const PrefillArgs &a, int bh, int wg_
             Frag whi[TW], wlo[TW];
 #pragma unroll
             for (int t = 0; t < TW; ++t) {
+                if (t > 0 && tw == 1)
+                    break;  // uniform
                 float sc[8];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -592,6 +599,8 @@ __device__ __forceinline__ void prefill_wg(const PrefillArgs &a, int bh, int wg_
                 av.u[0] = v.x; av.u[1] = v.y; av.u[2] = v.z; av.u[3] = v.w;
 #pragma unroll
                 for (int t = 0; t < TW; ++t) {
+                    if (t > 0 && tw == 1)
+                        break;  // uniform
                     st[t].O[m] = mfma(av, whi[t], st[t].O[m]);
                     st[t].O[m] = mfma(av, wlo[t], st[t].O[m]);
                 }

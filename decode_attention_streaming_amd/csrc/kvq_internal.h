@@ -206,9 +206,10 @@ struct RaggedAttnArgs {
 
 // Causal attention of the queries of the last n_q appended tokens (a prefill
 // chunk): query j (position N - n_q + j) attends to tokens 0 .. N - n_q + j.
-// Tiles of QT = 16 / g queries of one stream, two per wave (one for head_dim
-// 256); workgroups of eight waves of one stream, wg_per_stream of them per
-// stream, n_wg in all.
+// Tiles of QT = 16 / g queries of one stream, tw per wave (two up to head_dim
+// 128 when that still gives a workgroup per compute unit, else one);
+// workgroups of eight waves of one stream, wg_per_stream of them per stream,
+// n_wg in all.
 struct PrefillArgs {
     LayerDev L;
     const void *q;   // [B][Hq][n_q][D] in q_dtype
@@ -216,6 +217,7 @@ struct PrefillArgs {
     int q_dtype, kv_bf16;
     int D, g, BH, N, Tq, n_q;
     int QT, n_tiles, n_wg, wg_per_stream;
+    int tw;          // query tiles per wave: 2 (head_dim <= 128, enough workgroups) or 1
     int ngcap;       // capq / G
     float scale_log2;  // log2(e) / sqrt(D)
     // ragged layer: sequence b = bh / Hkv holds seqN[b] tokens, seqTq[b] of

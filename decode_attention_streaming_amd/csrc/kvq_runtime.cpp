@@ -693,6 +693,19 @@ int kvq_append_decode_attention(kvq_handle *h, int layer, const void *k_new, con
     return rc;
 }
 
+// Compute units of device dev, read once per handle (launch shapes depend on it).
+static hipError_t ensure_cu_count(kvq_handle *h, int dev)
+{
+    if (h->cu_count == 0) {
+        int n = 0;
+        const hipError_t e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess)
+            return e;
+        h->cu_count = n > 0 ? n : 256;
+    }
+    return hipSuccess;
+}
+
 int kvq_prefill_attention(kvq_handle *h, int layer, const void *q, int n_q, float *out)
 {
     if (!h)
@@ -740,9 +753,19 @@ int kvq_prefill_attention(kvq_handle *h, int layer, const void *q, int n_q, floa
     }
     a.QT = 16 / g;
     a.n_tiles = (n_q + a.QT - 1) / a.QT;
-    // workgroups of eight waves, each on one stream, two query tiles per wave
-    // up to head_dim 128 and one beyond
-    const int tiles_wg = D <= 128 ? 16 : 8;
+    // workgroups of eight waves, each on one stream: two query tiles per wave
+    // (up to head_dim 128) when that still leaves a workgroup for every
+    // compute unit, else one
+    int dev = 0;
+    hipError_t e0 = hipGetDevice(&dev);
+    if (e0 == hipSuccess)
+        e0 = ensure_cu_count(h, dev);
+    if (e0 != hipSuccess)
+        return h->dev_fail(e0, "device query");
+    a.tw = 1;
+    if (D <= 128 && static_cast<long>(a.BH) * ((a.n_tiles + 15) / 16) >= h->cu_count)
+        a.tw = 2;
+    const int tiles_wg = 8 * a.tw;
     a.wg_per_stream = (a.n_tiles + tiles_wg - 1) / tiles_wg;
     const long wgs = static_cast<long>(a.BH) * a.wg_per_stream;
     if (wgs > INT32_MAX / 2)
@@ -765,13 +788,9 @@ static int attention_launch(kvq_handle *h, int layer, const void *q, float *out,
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
         return h->dev_fail(e, "device query");
-    if (h->cu_count == 0) {
-        int n = 0;
-        e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess)
-            return h->dev_fail(e, "device query");
-        h->cu_count = n > 0 ? n : 256;
-    }
+    e = ensure_cu_count(h, dev);
+    if (e != hipSuccess)
+        return h->dev_fail(e, "device query");
     const int D = h->cfg.head_dim, BH = h->BH();
     const kvq::LayerDev &d = s.dev;
     kvq::AttnArgs a;
