@@ -30,10 +30,17 @@ def _oracle_asan(tmp_path, src_text):
     return so
 
 
+def _preload(*libs):
+    """The sanitizer runtimes first (they must come first), then whatever the
+    environment already preloads, unchanged."""
+    rest = os.environ.get("LD_PRELOAD", "")
+    return " ".join([x for x in libs if x] + ([rest] if rest else []))
+
+
 def _run_pins(so, files, log=None):
     opts = "detect_leaks=0" + (":log_path=%s" % log if log else "")
     env = dict(os.environ, KVQ_ORACLE_SO=str(so), ASAN_OPTIONS=opts,
-               LD_PRELOAD=" ".join([_gcc_rt("libasan.so"), _gcc_rt("libubsan.so")]))
+               LD_PRELOAD=_preload(_gcc_rt("libasan.so"), _gcc_rt("libubsan.so")))
     return subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider"] +
                           [os.path.join(ROOT, "tests", f) for f in files],
                           cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
@@ -94,7 +101,7 @@ def test_host_runtime_checks_under_sanitizers(tmp_path):
     subprocess.check_call([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-Xarch_host", "-fsanitize=address",
                            "-Xarch_host", "-fsanitize=undefined", "-o", so] + objs,
                           stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
-    env = dict(os.environ, KVQ_LIB=so, ASAN_OPTIONS="detect_leaks=0", LD_PRELOAD=_clang_asan_rt())
+    env = dict(os.environ, KVQ_LIB=so, ASAN_OPTIONS="detect_leaks=0", LD_PRELOAD=_preload(_clang_asan_rt()))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         os.path.join(ROOT, "tests", "test_abi_cpu.py")], cwd=ROOT, env=env, capture_output=True,
                        text=True, timeout=600)
