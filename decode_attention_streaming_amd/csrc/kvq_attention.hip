@@ -22,7 +22,11 @@ __device__ __forceinline__ void attn_valu_body(const AttnArgs &a, const RaggedTa
     const int t_beg = a.valu_beg + split * a.valu_tps;
     const int t_end = min(stream_dims(a, rt, bh).N, t_beg + a.valu_tps);
     extern __shared__ float smem[];
-    valu_range<D, GM>(a, rt, bh, t_beg, t_end, split, smem);
+    // heads h0 .. h0 + GM - 1 at a time (two passes over the range for more
+    // than eight heads per kv head: their per-head state would not fit the
+    // registers at once)
+    for (int h0 = 0; h0 < a.g; h0 += GM)
+        valu_range<D, GM>(a, rt, bh, t_beg, t_end, split, smem, h0);
     arrive_and_merge<D>(a, bh, gridDim.x);
 }
 
@@ -58,10 +62,8 @@ void launch_valu(const AttnArgs &a, const RaggedTables *rt, dim3 grid, size_t ld
         launch_valu_g<D, 2>(a, rt, grid, lds, st);
     else if (a.g <= 4)
         launch_valu_g<D, 4>(a, rt, grid, lds, st);
-    else if (a.g <= 8)
-        launch_valu_g<D, 8>(a, rt, grid, lds, st);
     else
-        launch_valu_g<D, 16>(a, rt, grid, lds, st);
+        launch_valu_g<D, 8>(a, rt, grid, lds, st);  // g > 8: two passes of eight heads
 }
 
 }  // namespace

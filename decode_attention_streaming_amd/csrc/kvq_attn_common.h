@@ -302,7 +302,7 @@ __device__ __forceinline__ void stage_q(const AttnArgs &a, int b, int kvh, float
 // sum_t p_t z_t.
 template <int D, int GM>
 __device__ void valu_range(const AttnArgs &a, const RaggedTables *rt, int bh, int t_beg, int t_end, int slot,
-                           float *smem)
+                           float *smem, int h0)
 {
     constexpr int TT = valu_tile<D>();
     constexpr int P = kAttnThreads / TT;  // threads per token in the score phase
@@ -396,8 +396,8 @@ __device__ void valu_range(const AttnArgs &a, const RaggedTables *rt, int bh, in
                     const float x = __builtin_fmaf(static_cast<float>(row_code(row, L.kb, c)), ks[i], kz[i]);
 #pragma unroll
                     for (int h = 0; h < GM; ++h)
-                        if (h < g)
-                            sc[h] = __builtin_fmaf(q_l(h, c), x, sc[h]);
+                        if (h0 + h < g)
+                            sc[h] = __builtin_fmaf(q_l(h0 + h, c), x, sc[h]);
                 }
             } else {
                 const uint16_t *row = reinterpret_cast<const uint16_t *>(k_tile) + ti * D + c0;
@@ -406,8 +406,8 @@ __device__ void valu_range(const AttnArgs &a, const RaggedTables *rt, int bh, in
                     const float x = widen16(row[i], bf);
 #pragma unroll
                     for (int h = 0; h < GM; ++h)
-                        if (h < g)
-                            sc[h] = __builtin_fmaf(q_l(h, c0 + i), x, sc[h]);
+                        if (h0 + h < g)
+                            sc[h] = __builtin_fmaf(q_l(h0 + h, c0 + i), x, sc[h]);
                 }
             }
         }
@@ -419,7 +419,7 @@ __device__ void valu_range(const AttnArgs &a, const RaggedTables *rt, int bh, in
         // ---- tile maximum, weights, normalizer and z-term per head ----
 #pragma unroll
         for (int h = 0; h < GM; ++h) {
-            if (h < g) {
+            if (h0 + h < g) {
                 const float w = wave_max(valid ? sc[h] : -INFINITY);
                 if (lane == 0)
                     red(0, wave, h) = w;
@@ -429,7 +429,7 @@ __device__ void valu_range(const AttnArgs &a, const RaggedTables *rt, int bh, in
         float alpha[GM];
 #pragma unroll
         for (int h = 0; h < GM; ++h) {
-            if (h < g) {
+            if (h0 + h < g) {
                 const float tm = fmaxf(fmaxf(red(0, 0, h), red(0, 1, h)), fmaxf(red(0, 2, h), red(0, 3, h)));
                 const float mnew = fmaxf(m[h], tm);
                 alpha[h] = exp2f(m[h] - mnew);
@@ -450,12 +450,12 @@ __device__ void valu_range(const AttnArgs &a, const RaggedTables *rt, int bh, in
         __syncthreads();
 #pragma unroll
         for (int h = 0; h < GM; ++h)
-            if (h < g)
+            if (h0 + h < g)
                 l[h] = l[h] * alpha[h] + (red(1, 0, h) + red(1, 1, h) + red(1, 2, h) + red(1, 3, h));
 #pragma unroll
         for (int k = 0; k < GM; ++k) {
             const int h = oh0 + k * hstep;
-            if (h < g)
+            if (h < GM && h0 + h < g)
                 o[k] = o[k] * red(3, 0, h) + (red(2, 0, h) + red(2, 1, h) + red(2, 2, h) + red(2, 3, h));
         }
 
@@ -474,7 +474,7 @@ __device__ void valu_range(const AttnArgs &a, const RaggedTables *rt, int bh, in
 #pragma unroll
                 for (int k = 0; k < GM; ++k) {
                     const int h = oh0 + k * hstep;
-                    if (h < g)
+                    if (h < GM && h0 + h < g)
                         o[k] = __builtin_fmaf(p_l(h, i), x, o[k]);
                 }
             }
@@ -485,7 +485,7 @@ __device__ void valu_range(const AttnArgs &a, const RaggedTables *rt, int bh, in
 #pragma unroll
                 for (int k = 0; k < GM; ++k) {
                     const int h = oh0 + k * hstep;
-                    if (h < g)
+                    if (h < GM && h0 + h < g)
                         o[k] = __builtin_fmaf(p_l(h, i), x, o[k]);
                 }
             }
@@ -498,11 +498,11 @@ __device__ void valu_range(const AttnArgs &a, const RaggedTables *rt, int bh, in
 #pragma unroll
     for (int k = 0; k < GM; ++k) {
         const int h = oh0 + k * hstep;
-        if (h < g) {
-            part_store(part + h * ps + oc, o[k]);
+        if (h < GM && h0 + h < g) {
+            part_store(part + (h0 + h) * ps + oc, o[k]);
             if (oc == 0) {
-                part_store(part + h * ps + D, m[h]);
-                part_store(part + h * ps + D + 1, l[h]);
+                part_store(part + (h0 + h) * ps + D, m[h]);
+                part_store(part + (h0 + h) * ps + D + 1, l[h]);
             }
         }
     }

@@ -64,6 +64,10 @@ CASES = {
     "mfma_k4v4_g8_G128": (1, 8, 1, 128, 4, 4, 128, 128, 700, "bf16", "bf16", [600, 3]),
     "mfma_k2v4_g5_d64": (2, 10, 2, 64, 2, 4, 64, 70, 500, "f16", "f32", [400, 30]),
     "mfma_k8v8_g4_long": (1, 4, 1, 128, 8, 8, 32, 32, 2100, "bf16", "bf16", [2050, 1]),
+    # head_dim 256 with windows of 16 (g = 1) and 4 (g = 4) groups: the largest
+    # per-wave LDS regions (one workgroup per compute unit at g = 1)
+    "mfma_k8v8_g1_d256": (2, 2, 2, 256, 8, 8, 32, 32, 400, "bf16", "f32", [330, 2]),
+    "mfma_k2v4_g4_d256": (1, 4, 1, 256, 2, 4, 32, 40, 500, "f16", "f16", [420, 3]),
     # more streams than resident workgroups: units sized per stream, the recent
     # tokens split over several units
     "mfma_k2v2_many_streams": (8, 40, 40, 128, 2, 2, 32, 256, 640, "f16", "f16", [600, 1]),
