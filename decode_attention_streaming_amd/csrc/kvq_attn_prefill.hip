@@ -201,9 +201,10 @@ __device__ __forceinline__ void prefill_recent(const PrefillArgs &a, int bh, siz
 // q operand (the scales are on the K side).
 constexpr int kPrefillWaves = 8;
 constexpr int kPrefillThreads = 64 * kPrefillWaves;
-// query tiles per wave (each LDS operand read feeds all of them): two up to
-// head_dim 128, one beyond (registers)
-__host__ __device__ constexpr int prefill_tw(int D) { return D <= 128 ? 2 : 1; }
+// Query tiles per wave (each LDS operand read feeds all of them): two up to
+// head_dim 128 (one beyond: registers), or one when two would leave compute
+// units without a workgroup; each count is its own instantiation, so that the
+// tiles' independent products interleave in straight-line code.
 
 // A block's bytes as stored (K codes, V codes, V scales and zeros, K scales
 // and zeros: the group's [2][D] floats, or per-token Key [32][2]), in the order
@@ -236,7 +237,7 @@ struct PfLds {
     static constexpr int BYTES = QUANT_BYTES > RECENT_BYTES ? QUANT_BYTES : RECENT_BYTES;
 };
 
-template <int KB, int VB, int D, bool KT, bool PG>
+template <int KB, int VB, int D, bool KT, bool PG, int TW>
 __device__ __forceinline__ void prefill_wg(const PrefillArgs &a, int bh, int wg_in, int wave, int lane, char *lds)
 {
     constexpr int KW = D * KB / 128;  // (unused for the K side here: rows are read per item)
@@ -247,11 +248,7 @@ __device__ __forceinline__ void prefill_wg(const PrefillArgs &a, int bh, int wg_
     constexpr int P = 16 / VB;        // V operand registers per word
     using Lay = PfLds<KB, VB, D, KT>;
     using Raw = PfRaw<KB, VB, D, KT>;
-    constexpr int TW = prefill_tw(D);
-    // tiles per wave in this launch: TW, or one when the launch has too few
-    // workgroups to fill the device with TW (few streams)
-    const int tw = a.tw;
-    const int TILES = kPrefillWaves * tw;  // tiles per workgroup
+    constexpr int TILES = kPrefillWaves * TW;  // tiles per workgroup
 
     const LayerDev &L = a.L;
     const int g = a.g, G = L.G;
@@ -267,7 +264,7 @@ __device__ __forceinline__ void prefill_wg(const PrefillArgs &a, int bh, int wg_
     size_t qrow[TW];
 #pragma unroll
     for (int i = 0; i < TW; ++i) {
-        tile[i] = i < tw ? wg_in * TILES + wave * tw + i : a.n_tiles;  // (past the last tile: inactive)
+        tile[i] = wg_in * TILES + wave * TW + i;
         const int qi = tile[i] * a.QT + jq;
         act[i] = tile[i] < a.n_tiles && jq < a.QT && qi < a.n_q;
         p_col[i] = act[i] ? N - a.n_q + qi : -1;  // last token this column sees
@@ -518,8 +515,6 @@ __device__ __forceinline__ void prefill_wg(const PrefillArgs &a, int bh, int wg_
                 al1.h = *reinterpret_cast<const half8_t *>(klo + off1);
 #pragma unroll
                 for (int t = 0; t < TW; ++t) {
-                    if (t > 0 && tw == 1)
-                        break;  // uniform
                     acc0[t] = mfma(ah0, bhi[t][k], acc0[t]);
                     acc1[t] = mfma(ah1, bhi[t][k], acc1[t]);
                     acc0[t] = mfma(ah0, blo[t][k], acc0[t]);
@@ -541,8 +536,6 @@ __device__ __forceinline__ void prefill_wg(const PrefillArgs &a, int bh, int wg_
             Frag whi[TW], wlo[TW];
 #pragma unroll
             for (int t = 0; t < TW; ++t) {
-                if (t > 0 && tw == 1)
-                    break;  // uniform
                 float sc[8];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -599,8 +592,6 @@ __device__ __forceinline__ void prefill_wg(const PrefillArgs &a, int bh, int wg_
                 av.u[0] = v.x; av.u[1] = v.y; av.u[2] = v.z; av.u[3] = v.w;
 #pragma unroll
                 for (int t = 0; t < TW; ++t) {
-                    if (t > 0 && tw == 1)
-                        break;  // uniform
                     st[t].O[m] = mfma(av, whi[t], st[t].O[m]);
                     st[t].O[m] = mfma(av, wlo[t], st[t].O[m]);
                 }
@@ -696,7 +687,7 @@ __device__ __forceinline__ void prefill_wg(const PrefillArgs &a, int bh, int wg_
     }
 }
 
-template <int KB, int VB, int D, bool KT, bool PG>
+template <int KB, int VB, int D, bool KT, bool PG, int TW>
 __global__ __launch_bounds__(kPrefillThreads, 1) void attn_prefill_kernel(PrefillArgs a)
 {
     extern __shared__ __align__(16) char lds_pf[];
@@ -707,14 +698,21 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void attn_prefill_kernel(Prefil
     const int id = blockIdx.x;
     const int slot = (a.n_wg % 8 == 0) ? (id % 8) * (a.n_wg / 8) + id / 8 : id;
     const int bh = slot / a.wg_per_stream, wg_in = slot - bh * a.wg_per_stream;
-    prefill_wg<KB, VB, D, KT, PG>(a, bh, wg_in, wave, lane, lds_pf);
+    prefill_wg<KB, VB, D, KT, PG, TW>(a, bh, wg_in, wave, lane, lds_pf);
 }
 
 template <int KB, int VB, bool KT, bool PG>
 hipError_t launch_prefill_pair(const PrefillArgs &a, hipStream_t st)
 {
     constexpr size_t lds = PfLds<KB, VB, KVQ_D, KT>::BYTES;
-    hipLaunchKernelGGL((attn_prefill_kernel<KB, VB, KVQ_D, KT, PG>), dim3(a.n_wg), dim3(kPrefillThreads), lds, st, a);
+#if KVQ_D <= 128
+    if (a.tw == 2) {
+        hipLaunchKernelGGL((attn_prefill_kernel<KB, VB, KVQ_D, KT, PG, 2>), dim3(a.n_wg), dim3(kPrefillThreads), lds,
+                           st, a);
+        return hipGetLastError();
+    }
+#endif
+    hipLaunchKernelGGL((attn_prefill_kernel<KB, VB, KVQ_D, KT, PG, 1>), dim3(a.n_wg), dim3(kPrefillThreads), lds, st, a);
     return hipGetLastError();
 }
 
