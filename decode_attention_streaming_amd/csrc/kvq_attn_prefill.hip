@@ -339,7 +339,7 @@ __device__ __forceinline__ void prefill_wg(const PrefillArgs &a, int bh, int wg_
                                                                                                    : Raw::KM_OFF);
         }
         // block t0's pieces, into registers
-        auto issue = [&](uint4 (&r)[Raw::NP], int t0) {
+        auto issue = [&](u32x4_t (&r)[Raw::NP], int t0) {
             const size_t r0 = block_row(t0);
             const char *ksrc = reinterpret_cast<const char *>(L.k_words + r0 * L.wk);
             const char *vsrc = reinterpret_cast<const char *>(L.v_words + r0 * L.wv);
@@ -359,19 +359,18 @@ __device__ __forceinline__ void prefill_wg(const PrefillArgs &a, int bh, int wg_
 #pragma unroll
             for (int ip = 0; ip < Raw::NP; ++ip) {
                 const char *base = pseg[ip] == 0 ? ksrc : pseg[ip] == 1 ? vsrc : pseg[ip] == 2 ? vmsrc : kmsrc;
-                r[ip] = *reinterpret_cast<const uint4 *>(base + poff[ip]);
+                r[ip] = *reinterpret_cast<const u32x4_t *>(base + poff[ip]);
             }
         };
         // ring slot of block b's stored bytes
         auto raw_slot = [&](int b) { return lds + Lay::RAW_OFF + (b % 3) * Raw::SLOT; };
-        auto stage = [&](const uint4 (&r)[Raw::NP], int b) {
+        // (every thread stores all its pieces: the slot has room for them, and
+        // the pieces past the block's bytes land in its unused tail)
+        auto stage = [&](const u32x4_t (&r)[Raw::NP], int b) {
             char *dst = raw_slot(b);
 #pragma unroll
-            for (int ip = 0; ip < Raw::NP; ++ip) {
-                const int o = 16 * (tid + kPrefillThreads * ip);
-                if (o < Raw::BYTES)
-                    *reinterpret_cast<uint4 *>(dst + o) = r[ip];
-            }
+            for (int ip = 0; ip < Raw::NP; ++ip)
+                *reinterpret_cast<u32x4_t *>(dst + 16 * (tid + kPrefillThreads * ip)) = r[ip];
         };
         // the dequantized block in LDS buffer buf
         auto kplane = [&](int buf) { return reinterpret_cast<_Float16 *>(lds + buf * Lay::BUF_BYTES); };
@@ -608,7 +607,9 @@ __device__ __forceinline__ void prefill_wg(const PrefillArgs &a, int bh, int wg_
         // register sets: four blocks in flight, two when a block takes two or
         // more pieces per thread (registers)
         constexpr int kRegSets = Raw::NP == 1 ? 4 : 2;
-        uint4 rs0[Raw::NP], rs1[Raw::NP], rs2[Raw::NP], rs3[Raw::NP];
+        // (a native vector type: the struct type's copies are memcpys, which keep
+        // an array of two pieces in scratch)
+        u32x4_t rs0[Raw::NP], rs1[Raw::NP], rs2[Raw::NP], rs3[Raw::NP];
         issue(rs0, 0);
         issue(rs1, 32 * min(1, nb - 1));
         if constexpr (kRegSets == 4) {
@@ -630,7 +631,7 @@ __device__ __forceinline__ void prefill_wg(const PrefillArgs &a, int bh, int wg_
         // halves in opposite orders, so that one's matrix products overlap the
         // other's dequantization (the halves touch different buffers).
         const bool deq_first = wave >= kPrefillWaves / 2;
-        auto step = [&](int b, uint4 (&rs)[Raw::NP]) {
+        auto step = [&](int b, u32x4_t (&rs)[Raw::NP]) {
             if (deq_first && b + 1 < nb)
                 dequant(b + 1);
             if (b < nb)  // uniform
