@@ -25,6 +25,8 @@
 // The four waves of a workgroup then merge their results through LDS into one
 // partial entry per head.  Query heads of a GQA group share every K/V read
 // (KIVI notes, section 7.2).
+#include <type_traits>
+
 #include "kvq_mfma_ops.h"
 
 #ifndef KVQ_D
@@ -33,6 +35,18 @@
 
 namespace kvq {
 namespace {
+
+// Blocks per round of the double-buffered walk (windows of at most this many
+// groups).
+constexpr int kPipeBlocks = 2;
+
+// Types with a double-buffered instantiation: those whose two rounds of
+// kPipeBlocks blocks take no more registers than one round (four-block
+// rounds), 3-bit Key excluded, per-token Key with narrow codes only.
+__host__ __device__ constexpr bool mfma_pipe_ok(int kb, int vb, int D, bool kt)
+{
+    return D <= 128 && mfma_round_blocks(kb, vb, D) >= 2 * kPipeBlocks && kb != 3 && (!kt || kb + vb <= 8);
+}
 
 // End of a quantized unit: this lane's column state (l, z-term, o; weights
 // carry 2^(kWShift - E)); the S-strided columns of one head are rescaled to
@@ -70,6 +84,7 @@ __device__ __forceinline__ void finish_unit(float m_run, float l_run, float zb_r
 // its own block.
 template <int NB, int KW, int FW>
 struct RoundData {
+    static constexpr int N = NB;
     uint32_t k0[NB][KW], k1[NB][KW], v[NB][FW];
     float4 vm[4];
     float4 km[4];  // per-token Key: (scale, zero) of the same eight tokens
@@ -82,7 +97,7 @@ struct RoundData {
 // softmax work of one round serves nb blocks.  In the P.V products a lane's
 // weights enter only its own block's product (zeros elsewhere).
 // Results for head h < g go to po[h * D + c], pm[h], pl[h] (LDS).
-template <int KB, int VB, int D, bool KT, bool PG>
+template <int KB, int VB, int D, bool KT, bool PG, bool PP>
 __device__ void mfma_unit(const AttnArgs &a, const RaggedTables *rt, int bh, int unit, int lane, float *po, float *pm,
                           float *pl,
                           float *meta_lds)
@@ -157,8 +172,11 @@ __device__ void mfma_unit(const AttnArgs &a, const RaggedTables *rt, int bh, int
     };
     // ---- B operand of q.K for this lane's column, q * s as hi/lo fp16; waits
     // for every load issued so far ----
-    auto setup_compute = [&](int nwin) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // (dma: the window's meta came by direct-to-LDS loads, which the
+    // compiler does not wait for by itself)
+    auto setup_compute = [&](int nwin, auto dma) {
+        if (dma)
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         const bool act_win = jslot < nwin;
         const float qscale = act_win ? a.scale_log2 : 0.0f;
         float qs[QK];
@@ -267,7 +285,12 @@ __device__ void mfma_unit(const AttnArgs &a, const RaggedTables *rt, int bh, int
     };
 
     // ---- one round: nb blocks starting at tokens t_first + i * G ----
-    auto load_round = [&](RoundData<NB, KW, FW> &d, int t_first, int nb, int my_b) {
+    // every_slot: all NB slots are loaded, those past nb with a re-read of
+    // block nb - 1, so that the loads issued do not depend on nb (the
+    // compiler then waits for exactly this round's loads, not for every load
+    // in flight)
+    auto load_round = [&](auto &d, int t_first, int nb, int my_b, auto every_slot) {
+        constexpr int NB = std::decay_t<decltype(d)>::N;
         // each block's 32 rows are consecutive; its first row is the same in
         // every lane (one branch on the layout per round)
         size_t r0[NB];
@@ -281,12 +304,12 @@ __device__ void mfma_unit(const AttnArgs &a, const RaggedTables *rt, int bh, int
         } else {
 #pragma unroll
             for (int i = 0; i < NB; ++i)
-                r0[i] = qa.base + t_first + i * G;
+                r0[i] = qa.base + t_first + (every_slot ? min(i, nb - 1) : i) * G;
             rm = qa.base + tm;
         }
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
-            if (i < nb) {
+            if (every_slot || i < nb) {
                 const uint32_t *kr = L.k_words + r0[i] * L.wk;
                 load_words(kr + koff0, d.k0[i]);
                 load_words(kr + koff1, d.k1[i]);
@@ -311,7 +334,8 @@ __device__ void mfma_unit(const AttnArgs &a, const RaggedTables *rt, int bh, int
         }
     };
 
-    auto process_round = [&](const RoundData<NB, KW, FW> &d, int nb, bool mine, int my_b) {
+    auto process_round = [&](const auto &d, int nb, bool mine, int my_b) {
+        constexpr int NB = std::decay_t<decltype(d)>::N;
         // q.K for tokens 4q + j (acc0) and 16 + 4q + j (acc1) of each block;
         // this lane keeps its own block's scores
         float sc[8];
@@ -432,22 +456,103 @@ __device__ void mfma_unit(const AttnArgs &a, const RaggedTables *rt, int bh, int
         }
     };
 
-    for (int w0 = g_beg; w0 < g_end; w0 += NG) {
-        const int nwin = __builtin_amdgcn_readfirstlane(min(NG, g_end - w0));  // uniform
-        const bool in_win = jslot < nwin;
+    static_assert(!PP || mfma_pipe_ok(KB, VB, D, KT), "no double-buffered walk for this type");
+    if constexpr (PP) {
+        // A window fits one round of kPipeBlocks blocks (g > 16 / kPipeBlocks):
+        // two round buffers of that size (no more registers than one round of
+        // NB), and the loads of the next round -- with the K scales and zeros
+        // of the window it belongs to -- are issued before this round is
+        // processed, so that the memory round trip overlaps the processing.
+        // Those scales come into registers (a pending direct-to-LDS load would
+        // make the compiler wait for every load before this round's products)
+        // and go to LDS after them, when the next round starts a window; q
+        // stays in LDS from the unit's first set-up.
+        RoundData<kPipeBlocks, KW, FW> dA, dB;
+        int w0 = g_beg, r = 0;
+        int nwin = __builtin_amdgcn_readfirstlane(min(NG, g_end - w0));
+        bool in_win = jslot < nwin;
         if (paged && !wp.covers(qa, w0 * G, (w0 + nwin) * G))
-            wp.load(qa, lane, w0 * G, g_end * G);  // once per 64 pages of the unit
+            wp.load(qa, lane, w0 * G, g_end * G);
         setup_issue(w0, nwin);
-        for (int r = 0; r < bpg; ++r) {
-            for (int u = 0; u < nwin; u += NB) {
-                const int nb = __builtin_amdgcn_readfirstlane(min(NB, nwin - u));
-                const bool mine = in_win && jslot >= u && jslot < u + nb;
-                const int my_b = mine ? jslot - u : 0;
-                RoundData<NB, KW, FW> d;
-                load_round(d, (w0 + u) * G + r * 32, nb, my_b);
-                if (r == 0 && u == 0)  // one memory round trip for the set-up and the first round
-                    setup_compute(nwin);
-                process_round(d, nb, mine, my_b);
+        load_round(dA, w0 * G, nwin, in_win ? jslot : 0, std::true_type{});
+        setup_compute(nwin, std::true_type{});
+        // a window's [nwin][2][D] floats as 16-byte pieces, lane + 64 i (those
+        // past the window re-read its last pieces)
+        constexpr int MP = KT ? 1 : (kPipeBlocks * D / 2 + 63) / 64;
+        u32x4_t mreg[MP];
+        auto meta_load = [&](int w1, int nwin1) {
+            if constexpr (!KT) {
+                constexpr int gp_log2 = __builtin_ctz(D / 2);
+#pragma unroll
+                for (int ip = 0; ip < MP; ++ip) {
+                    const int i = min(64 * ip + lane, nwin1 * D / 2 - 1), j = i >> gp_log2;
+                    const size_t gr = paged ? wp.grp_v(qa, w1 + j) : qa.gbase + w1 + j;
+                    mreg[ip] = *reinterpret_cast<const u32x4_t *>(L.k_meta + gr * 2 * D + 4 * (i & (D / 2 - 1)));
+                }
+            }
+        };
+        auto meta_store = [&](int nwin1) {
+            if constexpr (!KT) {
+#pragma unroll
+                for (int ip = 0; ip < MP; ++ip)
+                    if (64 * ip + lane < nwin1 * D / 2)
+                        *reinterpret_cast<u32x4_t *>(meta_lds + 4 * (64 * ip + lane)) = mreg[ip];
+            }
+        };
+        // one round from cur (window w0, block r) with the loads of the next
+        // into nxt; false after the unit's last round.  The loads are issued
+        // unconditionally (after the last round: a re-read of this one, from
+        // L2), so that the wait before the products is for cur's loads only.
+        auto pipe_step = [&](auto &cur, auto &nxt) -> bool {
+            int w1 = w0, r1 = r + 1, nwin1 = nwin;
+            const bool new_win = r1 == bpg;
+            if (new_win) {
+                w1 = w0 + NG;
+                r1 = 0;
+                nwin1 = __builtin_amdgcn_readfirstlane(min(NG, g_end - w1));
+            }
+            const bool more = w1 < g_end;  // uniform
+            if (!more) {
+                w1 = w0;
+                r1 = r;
+                nwin1 = nwin;
+            }
+            const bool in_win1 = jslot < nwin1;
+            if (paged && more && new_win && !wp.covers(qa, w1 * G, (w1 + nwin1) * G))
+                wp.load(qa, lane, w1 * G, g_end * G);  // (its own wait: once per 64 pages)
+            meta_load(w1, nwin1);
+            load_round(nxt, w1 * G + r1 * 32, nwin1, in_win1 ? jslot : 0, std::true_type{});
+            process_round(cur, nwin, in_win, in_win ? jslot : 0);
+            if (more && new_win) {
+                meta_store(nwin1);
+                setup_compute(nwin1, std::false_type{});
+            }
+            w0 = w1;
+            r = r1;
+            nwin = nwin1;
+            in_win = in_win1;
+            return more;
+        };
+        while (pipe_step(dA, dB) && pipe_step(dB, dA)) {
+        }
+    } else {
+        for (int w0 = g_beg; w0 < g_end; w0 += NG) {
+            const int nwin = __builtin_amdgcn_readfirstlane(min(NG, g_end - w0));  // uniform
+            const bool in_win = jslot < nwin;
+            if (paged && !wp.covers(qa, w0 * G, (w0 + nwin) * G))
+                wp.load(qa, lane, w0 * G, g_end * G);  // once per 64 pages of the unit
+            setup_issue(w0, nwin);
+            for (int r = 0; r < bpg; ++r) {
+                for (int u = 0; u < nwin; u += NB) {
+                    const int nb = __builtin_amdgcn_readfirstlane(min(NB, nwin - u));
+                    const bool mine = in_win && jslot >= u && jslot < u + nb;
+                    const int my_b = mine ? jslot - u : 0;
+                    RoundData<NB, KW, FW> d;
+                    load_round(d, (w0 + u) * G + r * 32, nb, my_b, std::false_type{});
+                    if (r == 0 && u == 0)  // one memory round trip for the set-up and the first round
+                        setup_compute(nwin, std::true_type{});
+                    process_round(d, nb, mine, my_b);
+                }
             }
         }
     }
@@ -679,7 +784,7 @@ __host__ __device__ inline int wave_region(const AttnArgs &a)
     return mfma_wave_region(a.D, a.g, a.units_q > 0, a.units_r > 0);
 }
 
-template <int KB, int VB, int D, bool KT, bool PG>
+template <int KB, int VB, int D, bool KT, bool PG, bool PP>
 __device__ __forceinline__ void attn_mfma_body(const AttnArgs &a, const RaggedTables *rt)
 {
     extern __shared__ float lds[];
@@ -700,7 +805,7 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs &a, const RaggedTa
     const int region = wave_region(a);
     float *po = lds + wave * region;
     if (unit < a.units_q) {
-        mfma_unit<KB, VB, D, KT, PG>(a, rt, bh, unit, lane, po, s_pm[wave], s_pl[wave], po);
+        mfma_unit<KB, VB, D, KT, PG, PP>(a, rt, bh, unit, lane, po, s_pm[wave], s_pl[wave], po);
     } else if (unit < a.units_q + a.units_r) {
         if (a.kv_bf16)
             mfma_residual_unit<D, true>(a, rt, bh, unit - a.units_q, lane, po, s_pm[wave], s_pl[wave]);
@@ -715,32 +820,45 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs &a, const RaggedTa
     arrive_and_merge<D>(a, bh, a.mfma_wgs, a.xcd_shift > 0);
 }
 
-template <int KB, int VB, int D, bool KT, bool PG>
+template <int KB, int VB, int D, bool KT, bool PG, bool PP>
 __global__ __launch_bounds__(kAttnThreads, (mfma_waves_per_simd<KB, VB>())) void attn_mfma_kernel(AttnArgs a)
 {
-    attn_mfma_body<KB, VB, D, KT, PG>(a, nullptr);
+    attn_mfma_body<KB, VB, D, KT, PG, PP>(a, nullptr);
 }
 
 // ragged batches: per-sequence lengths in the argument block
-template <int KB, int VB, int D, bool KT, bool PG>
+template <int KB, int VB, int D, bool KT, bool PG, bool PP>
 __global__ __launch_bounds__(kAttnThreads, (mfma_waves_per_simd<KB, VB>())) void attn_mfma_kernel_rg(
     RaggedAttnArgs r)
 {
-    attn_mfma_body<KB, VB, D, KT, PG>(r.a, &r.t);
+    attn_mfma_body<KB, VB, D, KT, PG, PP>(r.a, &r.t);
 }
 
-template <int KB, int VB, bool KT, bool PG>
-hipError_t launch_pair(const AttnArgs &a, const RaggedTables *rt, hipStream_t st)
+template <int KB, int VB, bool KT, bool PG, bool PP>
+hipError_t launch_kernel(const AttnArgs &a, const RaggedTables *rt, hipStream_t st)
 {
     const dim3 grid = a.xcd_shift > 0 ? dim3(a.mfma_wgs * a.BH) : dim3(a.mfma_wgs, a.BH);
     const size_t lds = (kAttnThreads / 64) * wave_region(a) * sizeof(float);
     if (rt) {
         const RaggedAttnArgs r{a, *rt};
-        hipLaunchKernelGGL((attn_mfma_kernel_rg<KB, VB, KVQ_D, KT, PG>), grid, dim3(kAttnThreads), lds, st, r);
+        hipLaunchKernelGGL((attn_mfma_kernel_rg<KB, VB, KVQ_D, KT, PG, PP>), grid, dim3(kAttnThreads), lds, st, r);
     } else {
-        hipLaunchKernelGGL((attn_mfma_kernel<KB, VB, KVQ_D, KT, PG>), grid, dim3(kAttnThreads), lds, st, a);
+        hipLaunchKernelGGL((attn_mfma_kernel<KB, VB, KVQ_D, KT, PG, PP>), grid, dim3(kAttnThreads), lds, st, a);
     }
     return hipGetLastError();
+}
+
+// The double-buffered instantiation where the type has one and a window holds
+// at most kPipeBlocks groups (g > 16 / kPipeBlocks); otherwise the plain one
+// (separate kernels: the plain walk's code is not affected by the other's).
+template <int KB, int VB, bool KT, bool PG>
+hipError_t launch_pair(const AttnArgs &a, const RaggedTables *rt, hipStream_t st)
+{
+    if constexpr (mfma_pipe_ok(KB, VB, KVQ_D, KT)) {
+        if (a.pipe && (16 >> a.s_log2) <= kPipeBlocks)
+            return launch_kernel<KB, VB, KT, PG, true>(a, rt, st);
+    }
+    return launch_kernel<KB, VB, KT, PG, false>(a, rt, st);
 }
 
 }  // namespace

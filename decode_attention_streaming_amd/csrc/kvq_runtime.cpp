@@ -255,9 +255,10 @@ struct kvq_handle {
     int cu_count = 0;
     int last_splits = 0, last_variant = -1;
     // launch-shape overrides for tests and tuning, read once at create from
-    // KVQ_FORCE_VALU, KVQ_UNIT_GROUPS, KVQ_UNITS_Q, KVQ_RES_TOKENS, KVQ_SPLITS
-    // (0 = not set)
-    int env_force_valu = 0, env_unit_groups = 0, env_units_q = 0, env_res_tokens = 0, env_splits = 0;
+    // KVQ_FORCE_VALU, KVQ_UNIT_GROUPS, KVQ_UNITS_Q, KVQ_RES_TOKENS, KVQ_SPLITS,
+    // KVQ_NO_PIPE (0 = not set)
+    int env_force_valu = 0, env_unit_groups = 0, env_units_q = 0, env_res_tokens = 0, env_splits = 0,
+        env_no_pipe = 0;
     bool touched = false;  // device work was enqueued
     bool counters_ready = false;
     std::string err = "no error";
@@ -338,6 +339,7 @@ int kvq_create(const kvq_config *cfg, void *workspace, size_t ws_bytes, kvq_hand
     h->env_units_q = env_int("KVQ_UNITS_Q");
     h->env_res_tokens = env_int("KVQ_RES_TOKENS");
     h->env_splits = env_int("KVQ_SPLITS");
+    h->env_no_pipe = env_int("KVQ_NO_PIPE");
     const size_t BH = static_cast<size_t>(h->BH());
     for (LayerState &s : h->plan.layers) {
         kvq::LayerDev &d = s.dev;
@@ -944,6 +946,7 @@ static int attention_launch(kvq_handle *h, int layer, const void *q, float *out,
         }
         a.units_q = static_cast<int>(uq);
         a.n_groups = n_groups;
+        a.pipe = h->env_no_pipe ? 0 : 1;
         a.ngcap = d.capq / d.G;
         a.s_log2 = 0;
         while ((16 >> a.s_log2) * g > 16)
@@ -979,7 +982,7 @@ static int attention_launch(kvq_handle *h, int layer, const void *q, float *out,
         a.valu_beg = 0;
         a.valu_tps = tps;
         a.valu_wgs = S;
-        a.units_q = a.unit_groups = a.unit_extra = a.units_r = a.res_tokens = a.mfma_wgs = 0;
+        a.units_q = a.unit_groups = a.unit_extra = a.units_r = a.res_tokens = a.mfma_wgs = a.pipe = 0;
         a.xcd_shift = 0;
         a.n_groups = a.ngcap = a.s_log2 = 0;
     }
