@@ -36,16 +36,18 @@
 namespace kvq {
 namespace {
 
-// Blocks per round of the double-buffered walk (windows of at most this many
-// groups).
-constexpr int kPipeBlocks = 2;
+// Windows (groups) of the double-buffered walk: it serves windows of at most
+// this many groups.
+constexpr int kPipeGroups = 2;
 
-// Types with a double-buffered instantiation: those whose two rounds of
-// kPipeBlocks blocks take no more registers than one round (four-block
-// rounds), 3-bit Key excluded, per-token Key with narrow codes only.
+// Types with a double-buffered instantiation, whose rounds take half the
+// blocks of the plain walk's (two rounds in registers, as many as one round
+// there): 3-bit Key excluded, per-token Key with four-block rounds only for
+// narrow codes (wider ones spill).
 __host__ __device__ constexpr bool mfma_pipe_ok(int kb, int vb, int D, bool kt)
 {
-    return D <= 128 && mfma_round_blocks(kb, vb, D) >= 2 * kPipeBlocks && kb != 3 && (!kt || kb + vb <= 8);
+    return D <= 128 && mfma_round_blocks(kb, vb, D) >= 2 && kb != 3 &&
+           (!kt || kb + vb <= 8 || mfma_round_blocks(kb, vb, D) == 2);
 }
 
 // End of a quantized unit: this lane's column state (l, z-term, o; weights
@@ -458,27 +460,30 @@ __device__ void mfma_unit(const AttnArgs &a, const RaggedTables *rt, int bh, int
 
     static_assert(!PP || mfma_pipe_ok(KB, VB, D, KT), "no double-buffered walk for this type");
     if constexpr (PP) {
-        // A window fits one round of kPipeBlocks blocks (g > 16 / kPipeBlocks):
-        // two round buffers of that size (no more registers than one round of
-        // NB), and the loads of the next round -- with the K scales and zeros
+        // Windows of at most kPipeGroups groups (g > 16 / kPipeGroups), rounds
+        // of PB = NB / 2 blocks: two round buffers (no more registers than one
+        // round of NB), and the loads of the next round -- with the K scales and zeros
         // of the window it belongs to -- are issued before this round is
         // processed, so that the memory round trip overlaps the processing.
         // Those scales come into registers (a pending direct-to-LDS load would
         // make the compiler wait for every load before this round's products)
         // and go to LDS after them, when the next round starts a window; q
         // stays in LDS from the unit's first set-up.
-        RoundData<kPipeBlocks, KW, FW> dA, dB;
-        int w0 = g_beg, r = 0;
+        constexpr int PB = NB / 2;
+        RoundData<PB, KW, FW> dA, dB;
+        // round (w0, r, u): block r of groups w0 + u .. w0 + u + nb - 1
+        int w0 = g_beg, r = 0, u = 0;
         int nwin = __builtin_amdgcn_readfirstlane(min(NG, g_end - w0));
-        bool in_win = jslot < nwin;
+        int nb = min(PB, nwin);
+        bool mine = jslot < nb;
         if (paged && !wp.covers(qa, w0 * G, (w0 + nwin) * G))
             wp.load(qa, lane, w0 * G, g_end * G);
         setup_issue(w0, nwin);
-        load_round(dA, w0 * G, nwin, in_win ? jslot : 0, std::true_type{});
+        load_round(dA, w0 * G, nb, mine ? jslot : 0, std::true_type{});
         setup_compute(nwin, std::true_type{});
         // a window's [nwin][2][D] floats as 16-byte pieces, lane + 64 i (those
         // past the window re-read its last pieces)
-        constexpr int MP = KT ? 1 : (kPipeBlocks * D / 2 + 63) / 64;
+        constexpr int MP = KT ? 1 : (kPipeGroups * D / 2 + 63) / 64;
         u32x4_t mreg[MP];
         auto meta_load = [&](int w1, int nwin1) {
             if constexpr (!KT) {
@@ -499,12 +504,16 @@ __device__ void mfma_unit(const AttnArgs &a, const RaggedTables *rt, int bh, int
                         *reinterpret_cast<u32x4_t *>(meta_lds + 4 * (64 * ip + lane)) = mreg[ip];
             }
         };
-        // one round from cur (window w0, block r) with the loads of the next
-        // into nxt; false after the unit's last round.  The loads are issued
+        // one round from cur (round (w0, r, u)) with the loads of the next into
+        // nxt; false after the unit's last round.  The loads are issued
         // unconditionally (after the last round: a re-read of this one, from
         // L2), so that the wait before the products is for cur's loads only.
         auto pipe_step = [&](auto &cur, auto &nxt) -> bool {
-            int w1 = w0, r1 = r + 1, nwin1 = nwin;
+            int w1 = w0, r1 = r, u1 = u + PB, nwin1 = nwin;
+            if (u1 >= nwin) {
+                u1 = 0;
+                ++r1;
+            }
             const bool new_win = r1 == bpg;
             if (new_win) {
                 w1 = w0 + NG;
@@ -515,22 +524,26 @@ __device__ void mfma_unit(const AttnArgs &a, const RaggedTables *rt, int bh, int
             if (!more) {
                 w1 = w0;
                 r1 = r;
+                u1 = u;
                 nwin1 = nwin;
             }
-            const bool in_win1 = jslot < nwin1;
+            const int nb1 = min(PB, nwin1 - u1);
+            const bool mine1 = jslot >= u1 && jslot < u1 + nb1;
             if (paged && more && new_win && !wp.covers(qa, w1 * G, (w1 + nwin1) * G))
                 wp.load(qa, lane, w1 * G, g_end * G);  // (its own wait: once per 64 pages)
             meta_load(w1, nwin1);
-            load_round(nxt, w1 * G + r1 * 32, nwin1, in_win1 ? jslot : 0, std::true_type{});
-            process_round(cur, nwin, in_win, in_win ? jslot : 0);
+            load_round(nxt, (w1 + u1) * G + r1 * 32, nb1, mine1 ? jslot - u1 : 0, std::true_type{});
+            process_round(cur, nb, mine, mine ? jslot - u : 0);
             if (more && new_win) {
                 meta_store(nwin1);
                 setup_compute(nwin1, std::false_type{});
             }
             w0 = w1;
             r = r1;
+            u = u1;
             nwin = nwin1;
-            in_win = in_win1;
+            nb = nb1;
+            mine = mine1;
             return more;
         };
         while (pipe_step(dA, dB) && pipe_step(dB, dA)) {
@@ -849,13 +862,13 @@ hipError_t launch_kernel(const AttnArgs &a, const RaggedTables *rt, hipStream_t 
 }
 
 // The double-buffered instantiation where the type has one and a window holds
-// at most kPipeBlocks groups (g > 16 / kPipeBlocks); otherwise the plain one
+// at most kPipeGroups groups (g > 16 / kPipeGroups); otherwise the plain one
 // (separate kernels: the plain walk's code is not affected by the other's).
 template <int KB, int VB, bool KT, bool PG>
 hipError_t launch_pair(const AttnArgs &a, const RaggedTables *rt, hipStream_t st)
 {
     if constexpr (mfma_pipe_ok(KB, VB, KVQ_D, KT)) {
-        if (a.pipe && (16 >> a.s_log2) <= kPipeBlocks)
+        if (a.pipe && (16 >> a.s_log2) <= kPipeGroups)
             return launch_kernel<KB, VB, KT, PG, true>(a, rt, st);
     }
     return launch_kernel<KB, VB, KT, PG, false>(a, rt, st);

@@ -180,9 +180,9 @@ struct AttnArgs {
     // matrix-core products (S = 16 / NG, NG the largest power of two with
     // NG * g <= 16)
     int n_groups, ngcap, s_log2;
-    // 1: units whose windows fit one two-block round walk their rounds
-    // double-buffered (next round's loads in flight during this one); 0: one
-    // round at a time
+    // 1: units whose windows hold at most two groups walk their rounds
+    // double-buffered where the type allows (next round's loads in flight
+    // during this one); 0: one round at a time
     int pipe;
     float scale_log2;     // log2(e) / sqrt(D)
     // token new_t (>= 0) has just been appended and is not in the ring yet: it

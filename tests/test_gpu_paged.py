@@ -45,6 +45,7 @@ CASES = {
     "mfma_k8v8_tok_g64": (2, 8, 2, 64, 8, 8, 64, 64, "bf16", "f16", 128, 500, 70, 1, 0),
     "mfma_k2v2_rpc": (2, 8, 1, 128, 2, 2, 32, 160, "bf16", "bf16", 128, 900, 60, 0, 200),
     "mfma_k4v4_g7_G64": (2, 14, 2, 128, 4, 4, 64, 64, "bf16", "f32", 128, 1500, 40, 0, 0),
+    "mfma_k4v8_g6_G64": (2, 12, 2, 128, 4, 8, 64, 64, "bf16", "bf16", 128, 1200, 40, 0, 0),
     "valu_k2v4_g16": (2, 4, 2, 64, 2, 4, 16, 16, "f16", "f32", 128, 350, 35, 0, 0),
     "mfma_k4v4_d256": (2, 4, 2, 256, 4, 4, 32, 32, "bf16", "bf16", 128, 300, 33, 0, 0),
 }
