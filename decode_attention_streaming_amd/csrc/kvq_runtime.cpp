@@ -912,17 +912,19 @@ static int attention_launch(kvq_handle *h, int layer, const void *q, float *out,
             // per SIMD, hide each other's load latency, provided they fit one
             // generation of resident workgroups (Llama-2-70B shape: 39.9 ->
             // 35.2 us per call; the Qwen2.5-7B shape would need a second
-            // generation and keeps its units).  Only recent-token units may
-            // spill past that generation: the quantized units are capped at
-            // its unit slots (Llama-2-70B shape at 257 groups: 130 units left
-            // two quantized units per stream in a late workgroup, 39.6 us;
-            // capped at 128, 36.9 us)
+            // generation and keeps its units).  All units, the recent-token
+            // ones included, stay one workgroup per stream short of that
+            // generation's slots: a launch that fills them exactly ran slower
+            // than one that leaves a few free, and one whose recent-token
+            // workgroups spill past them slower still (Llama-2-70B shape: 128
+            // quantized + 1 recent units per stream 34.4 us, 127 + 1 37.3 us,
+            // 123 + 1 33.5 us)
             const long u_simd = (4L * h->cu_count / BH) / 4 * 4;
             if (env_ug == 0) {
                 const long base = std::max<long>(uq, u_simd - ur);
                 const bool walks = base > 0 && (n_groups + base - 1) / base * (d.G / 32) >= 8;
                 const long wgs2 = static_cast<long>(BH) * ((2 * base + ur + 3) / 4);
-                const long fit = 4 * (res_wgs / BH);
+                const long fit = 4 * (res_wgs / BH) - 4 - ur;  // quantized unit slots, one workgroup spare
                 if (walks && wgs2 * 20 <= res_wgs * 21)
                     uq = std::min<long>(n_groups, std::min<long>(2 * base, std::max<long>(base, fit)));
                 else if (u_simd > uq + ur)
