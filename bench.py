@@ -100,9 +100,10 @@ def kernel_source_digest():
 
 
 def stored_traffic(workload, table, kind="attention"):
-    """The stored FETCH_SIZE / WRITE_SIZE measurement of this workload (decode:
-    the record, with the state it was taken at; prefill: HBM bytes per
-    launch), or None when the kernels have changed since."""
+    """The stored HBM-traffic measurement of this workload (L2-to-fabric read
+    and write requests by size; decode: the record, with the state it was
+    taken at; prefill: HBM bytes per launch), or None when the kernels have
+    changed since."""
     path = os.path.join(ROOT, "profiles", "%s_traffic_workload%d_%s.json" % (kind, workload, table))
     if not os.path.exists(path):
         return None

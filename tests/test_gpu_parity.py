@@ -85,7 +85,7 @@ CASES = {
     "tok_mfma_k2v2_d64_G64": (2, 10, 2, 64, 2, 2, 64, 70, 500, "f16", "f32", [400, 30], 1),
     "tok_mfma_k8v8_long": (1, 4, 1, 128, 8, 8, 32, 32, 2100, "bf16", "bf16", [2050, 1], 1),
     "tok_mfma_k2v2_g8_G64": (2, 16, 2, 128, 2, 2, 64, 64, 1300, "bf16", "f32", [1250, 1], 1),
-    "tok_mfma_k8v8_g7": (2, 14, 2, 128, 8, 8, 32, 32, 700, "f16", "f32", [650, 1], 1),
+    "tok_mfma_k8v4_g7": (2, 14, 2, 128, 8, 4, 32, 32, 700, "f16", "f32", [650, 1], 1),
     "tok_mfma_k4v4_many_streams": (8, 40, 40, 128, 4, 4, 32, 256, 640, "f16", "f16", [600, 1], 1),
     "tok_valu_k4v4_G16": (2, 8, 2, 128, 4, 4, 16, 20, 300, "bf16", "f32", [250, 1, 7], 1),
     "tok_valu_k8v2_G8_d64": (1, 4, 1, 64, 8, 2, 8, 9, 120, "f16", "f16", [1] * 40, 1),
@@ -218,10 +218,10 @@ def test_unit_sizes_and_column_merge(ug, monkeypatch):
     """Matrix-core units of 1, 3 and 40 groups: windows holding up to 16 / g
     groups per column set, merged per head at the end of each unit (g 8 and 7:
     the double-buffered walk over windows of two groups, one odd, in rounds of
-    two blocks, and of one for K8V8)."""
+    two blocks, or of one for K8V4 and K4V8)."""
     monkeypatch.setenv("KVQ_UNIT_GROUPS", ug)
     for (Hq, Hkv, kb, vb, G) in [(2, 2, 2, 2, 32), (16, 4, 4, 2, 32), (16, 2, 8, 4, 64), (2, 2, 3, 4, 32),
-                                 (16, 2, 4, 4, 64), (14, 2, 2, 2, 32), (16, 2, 8, 8, 32)]:
+                                 (16, 2, 4, 4, 64), (14, 2, 2, 2, 32), (16, 2, 4, 8, 32)]:
         w = ad_hoc_workload(400 + Hq + kb, 2, Hq, Hkv, 128, kb, vb, G, G, 1700, "bf16", "bf16")
         print("unit groups", ug, "g", Hq // Hkv, "pair", (kb, vb), flush=True)
         _run_case(w, [1650, 1])
