@@ -323,8 +323,9 @@ def timed_calls(torch, stream, fn, rounds):
 def copy_ceiling(torch, stream, nbytes, L, rounds, dev):
     """Plain device copies timed like the attention calls: L buffers of nbytes
     (read + write = nbytes per call), cycled back to back; a sum over L buffers
-    of nbytes (a read-only pass); and one 256 MiB copy (the box's streaming
-    rate).  GB/s of bytes moved."""
+    of nbytes (a read-only pass); one 256 MiB copy (the box's streaming rate,
+    partly from the last-level cache) and a sum over 1 GiB (the streaming read
+    rate from HBM).  GB/s of bytes moved."""
     nbytes = int(nbytes)
     half = max(16, nbytes // 2 // 16 * 16)
     src = [torch.ones(half // 4, dtype=torch.float32, device=dev) for _ in range(L)]
@@ -342,6 +343,13 @@ def copy_ceiling(torch, stream, nbytes, L, rounds, dev):
     b = torch.empty_like(a)
     t_big = timed_calls(torch, stream, lambda: b.copy_(a), 5)
     del a, b
+    # a read-only pass over 1 GiB (4x the last-level cache): the streaming read
+    # rate from HBM of a plain reduction
+    huge = 1 << 30
+    a = torch.ones(huge // 4, dtype=torch.float32, device=dev)
+    s1 = torch.empty((), dtype=torch.float32, device=dev)
+    t_read = timed_calls(torch, stream, lambda: torch.sum(a, dim=0, out=s1), 5)
+    del a, s1
     res = {
         "bytes_per_call": int(nbytes),
         "copy_gbs": round(2 * half / t_copy / 1e9, 1),
@@ -349,6 +357,7 @@ def copy_ceiling(torch, stream, nbytes, L, rounds, dev):
         "read_sum_gbs": round(full / t_sum / 1e9, 1),
         "read_sum_us": round(t_sum * 1e6, 3),
         "stream_copy_256mib_gbs": round(2 * big / t_big / 1e9, 1),
+        "stream_read_1gib_gbs": round(huge / t_read / 1e9, 1),
     }
     res["ceiling_gbs"] = max(res["copy_gbs"], res["read_sum_gbs"])
     return res
