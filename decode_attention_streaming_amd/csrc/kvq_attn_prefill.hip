@@ -535,13 +535,11 @@ __device__ __forceinline__ void prefill_wg(const PrefillArgs &a, int bh, int wg_
             Frag whi[TW], wlo[TW];
 #pragma unroll
             for (int t = 0; t < TW; ++t) {
-                // scores stay in accumulator units: the score is acc * kscale
-                // (a power of two, > 0), applied in the max and in the exponent
                 float sc[8];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    sc[j] = acc0[t][j];
-                    sc[4 + j] = acc1[t][j];
+                    sc[j] = acc0[t][j] * kscale[t];
+                    sc[4 + j] = acc1[t][j] * kscale[t];
                 }
                 if (t0 + 31 > p_first[t]) {  // causal mask (uniform: only blocks that reach the tile's queries)
 #pragma unroll
@@ -552,7 +550,7 @@ __device__ __forceinline__ void prefill_wg(const PrefillArgs &a, int bh, int wg_
                 }
                 float tmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
                                    fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-                tmax = col_max(tmax) * kscale[t];
+                tmax = col_max(tmax);
                 ColState<MT> &c = st[t];
                 const bool need_m = act[t] && (tmax > c.m_run + kTau);
                 const bool need_e = act[t] && (eb > E[t]);
@@ -569,11 +567,11 @@ __device__ __forceinline__ void prefill_wg(const PrefillArgs &a, int bh, int wg_
                     c.m_run = m_new;
                     E[t] = E_new;
                 }
-                const float nmo = act[t] ? -c.m_run : -INFINITY;
+                const float mo = act[t] ? c.m_run : INFINITY;
                 float p[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    p[j] = weight_exp2(__builtin_fmaf(sc[j], kscale[t], nmo));
+                    p[j] = weight_exp2(sc[j] - mo);
                     c.l_run += p[j];
                     zb_run[t] = __builtin_fmaf(p[j], vz[j], zb_run[t]);
                 }
